@@ -1,0 +1,588 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test ties one part of the oracle to something it cannot agree with by
+construction: exact IEEE-754 rounding computed from rationals, closed forms of
+the pages' probes, brute force over small cases, a scalar per-thread reference,
+and the worked examples printed on the pages (fixtures under tests/golden/).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from workloads import configs as W
+from workloads import small as S
+from workloads.configs import pack_params
+
+from . import ieee32
+from . import scalar_ref
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run(O, w, **kw):
+    g = w.gmem.copy()
+    c, t, rc = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=kw.pop("trace_cap", w.trace_cap), **kw)
+    return g, c, t, rc
+
+
+# ------------------------------------------------------------------ P1 arithmetic
+
+def test_f32_arithmetic_exact_rounding(oracle_mod):
+    """add/sub/mul/fma.rn.f32 equal the exact rational result rounded to binary32
+    (RNE), with subnormals kept and NaN results canonical, on edge crossings and
+    random patterns."""
+    w = S.f32_ops(n=4096)
+    g, c, _, _ = run(oracle_mod, w)
+    ins = w.output(g, "in").reshape(-1, 3)
+    out = w.output(g, "out").reshape(-1, 4)
+    bad = []
+    for i in range(len(ins)):
+        a, b, cc = (int(x) for x in ins[i])
+        exp = (ieee32.add(a, b), ieee32.sub(a, b), ieee32.mul(a, b), ieee32.fma(a, b, cc))
+        got = tuple(int(x) for x in out[i])
+        if exp != got:
+            bad.append((hex(a), hex(b), hex(cc), [hex(x) for x in exp], [hex(x) for x in got]))
+    assert not bad, bad[:5]
+
+
+def test_f32_add_mul_match_numpy_float32(oracle_mod):
+    """Textbook special case: numpy float32 add/mul (IEEE, round to nearest) agree
+    bit for bit with the oracle on 65536 random operand pairs (NaNs canonicalised)."""
+    rng = np.random.default_rng(99)
+    n = 65536
+    ops = rng.integers(0, 1 << 32, size=(n, 3), dtype=np.uint32)
+    w = S.f32_ops(n=8)
+    size = W._align(12 * n) + 16 * n
+    g = np.zeros(size, dtype=np.uint8)
+    g[:12 * n] = ops.reshape(-1).view(np.uint8)
+    params = pack_params([("param_in", "u64", 0), ("param_out", "u64", W._align(12 * n)), ("param_n", "u32", n)])
+    oracle_mod.run(w.ptx, n // 256, 256, params, g)
+    out = g[W._align(12 * n):].view("<u4").reshape(-1, 4)
+    a = ops[:, 0].view(np.float32)
+    b = ops[:, 1].view(np.float32)
+    with np.errstate(all="ignore"):
+        for k, ref in ((0, a + b), (1, a - b), (2, a * b)):
+            rb = ref.view(np.uint32).copy()
+            rb[np.isnan(ref)] = 0x7FFFFFFF
+            assert np.array_equal(out[:, k], rb)
+
+
+# ------------------------------------------------------------------ P2, P3 vector_add
+
+def test_vector_add_values_and_counters(oracle_mod):
+    w = W.vector_add()
+    g, c, _, _ = run(oracle_mod, w)
+    a, b, cc = w.output(g, "a"), w.output(g, "b"), w.output(g, "c")
+    assert np.array_equal(cc.view(np.uint32), (a + b).view(np.uint32))
+    assert len(c) == 32
+    full, tail = c[:31], c[31]
+    assert (full["thread_instrs"] == 608).all() and tail["thread_instrs"] == 416
+    assert c["thread_instrs"].sum() == 19264
+    # a, b, c are 4 KiB aligned: each full-warp access is 4 sectors in 1 line
+    assert (full["gld_n"] == 2).all() and (full["gld_sectors"] == 8).all() and (full["gld_lines"] == 2).all()
+    assert (full["gst_n"] == 1).all() and (full["gst_sectors"] == 4).all() and (full["gst_lines"] == 1).all()
+    assert (full["diverge_n"] == 0).all()
+    # warp 31: lanes 0..7 live -> 1 sector, 1 line per access, one divergence
+    assert tail["gld_sectors"] == 2 and tail["gld_lines"] == 2 and tail["gst_sectors"] == 1
+    assert tail["diverge_n"] == 1
+    assert (c["status"] == oracle_mod.ST_FINISHED).all()
+
+
+def test_vector_add_trace_hand_derived(oracle_mod):
+    """Issue cycles derived by hand from the listing and the default latency table
+    (tests/golden/vector_add_trace.json)."""
+    with open(os.path.join(GOLDEN, "vector_add_trace.json")) as f:
+        gold = json.load(f)
+    w = W.vector_add()
+    _, c, t, _ = run(oracle_mod, w)
+    hdr, rec = oracle_mod.trace_slots(t, w.trace_cap)
+    for wi in range(32):
+        assert hdr[wi]["records_written"] == 19 and hdr[wi]["records_dropped"] == 0
+        assert rec[wi, :19, 0].tolist() == gold["issue_cycles"]
+        assert rec[wi, :19, 1].tolist() == list(range(19))
+        assert hdr[wi]["version"] == 1 and hdr[wi]["warp_in_block"] == wi % 8
+        assert hdr[wi]["flags"] == 8
+    assert (c["cycles"] == gold["cycles"]).all()
+
+
+# ------------------------------------------------------------------ P4 - P6 cycle model
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64])
+def test_dependent_chain_costs_n_times_latency(oracle_mod, n):
+    ptx = S.fma_chain_ptx(n, 1)
+    g = np.zeros(64, np.uint8)
+    _, t, _ = oracle_mod.run(ptx, 1, 32, pack_params([("param_out", "u64", 0)]), g, trace_cap=n + 8)
+    _, rec = oracle_mod.trace_slots(t, n + 8)
+    first_fma = rec[0, 3, 0]
+    st = rec[0, 3 + n, 0]
+    assert st - first_fma == 4 * n
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 8, 16])
+def test_accumulator_sweep_cpi(oracle_mod, k):
+    """FMA i of a chain over k accumulators issues at 4 * (i // k) + i % k when
+    k <= 4 and at i otherwise: in-chain CPI = max(1, 4 / k)."""
+    n = 48
+    ptx = S.fma_chain_ptx(n, k)
+    g = np.zeros(64, np.uint8)
+    _, t, _ = oracle_mod.run(ptx, 1, 32, pack_params([("param_out", "u64", 0)]), g, trace_cap=n + 8)
+    _, rec = oracle_mod.trace_slots(t, n + 8)
+    issues = rec[0, 3:3 + n, 0].astype(int) - int(rec[0, 3, 0])
+    exp = [4 * (i // k) + i % k if k <= 4 else i for i in range(n)]
+    assert issues.tolist() == exp
+
+
+@pytest.mark.parametrize("n_acc,slope", [(1, 128), (8, 35)])
+def test_count_sweep_exactly_affine(oracle_mod, n_acc, slope):
+    """Simulated cycles of the FMA probe loop are exactly affine in the iteration
+    count (the simulator's version of the page's T(N) = L N + C regression)."""
+    xs = [1, 2, 3, 5, 8, 13]
+    ys = []
+    for it in xs:
+        w = W.ffma_probe(n_acc=n_acc, iters=it, grid=1, block=32, trace_cap=4)
+        _, c, _, _ = run(oracle_mod, w)
+        ys.append(int(c["cycles"][0]))
+    diffs = [(ys[i + 1] - ys[i]) / (xs[i + 1] - xs[i]) for i in range(len(xs) - 1)]
+    assert all(d == slope for d in diffs), (ys, diffs)
+    # P2's measured contrast: ~4 cycles per dependent FFMA, ~1 per independent one
+    assert slope / 32 == (4.0 if n_acc == 1 else 35 / 32)
+
+
+def test_ffma_probe_values(oracle_mod):
+    """Probe outputs equal the scalar reference (exact IEEE fma) for a few threads."""
+    for n_acc in (1, 8):
+        w = W.ffma_probe(n_acc=n_acc, iters=3, grid=1, block=32, trace_cap=4)
+        g, _, _, _ = run(oracle_mod, w)
+        g2 = w.gmem.copy()
+        scalar_ref.run_grid(w.ptx, w.grid, w.block, w.params_bytes, g2)
+        assert np.array_equal(g, g2)
+
+
+# ------------------------------------------------------------------ P7 strided sectors
+
+@pytest.mark.parametrize("s", W.STRIDES)
+def test_strided_sectors_lines_closed_form(oracle_mod, s):
+    w = W.strided_gather(s, n=2048)
+    g, c, _, _ = run(oracle_mod, w)
+    assert (c["gld_n"] == 2).all()
+    assert (c["gld_sectors"] == min(32, 4 * s) + 4).all()
+    assert (c["gld_lines"] == min(32, s) + 1).all()
+    assert (c["gst_n"] == 1).all() and (c["gst_sectors"] == 4).all() and (c["gst_lines"] == 1).all()
+    a, b, cc = w.output(g, "a"), w.output(g, "b"), w.output(g, "c")
+    assert np.array_equal(cc.view(np.uint32), (a[::s][:2048] + b).view(np.uint32))
+
+
+# ------------------------------------------------------------------ P8, P9 bank probe
+
+@pytest.mark.parametrize("s", list(range(1, 33)))
+def test_bank_degree_is_gcd(oracle_mod, s):
+    iters = 3
+    w = W.bank_probe(s, iters=iters, grid=2, block=1024, trace_cap=8)
+    g, c, _, _ = run(oracle_mod, w)
+    d = math.gcd(s, 32)
+    assert (c["sh_n"] == 2 * iters).all()
+    assert (c["sh_degree_max"] == d).all()
+    assert (c["sh_degree_sum"] == 2 * iters * d).all()
+    assert (c["barrier_n"] == iters).all()
+    v = w.output(g, "v").view(np.uint32).astype(np.uint64)
+    out = w.output(g, "out")
+    lane = np.arange(2048) % 32
+    assert np.array_equal(out, ((iters * v[lane * s]) % (1 << 32)).astype(np.uint32))
+
+
+# ------------------------------------------------------------------ page examples, P10 brute force
+
+def _bank_degree_page_rule(addrs):
+    # restated from the KernelScope memory-analysis description: group active
+    # lanes by bank; a bank whose lanes all use one address is a broadcast;
+    # degree = largest lane count of a non-broadcast bank, at least 1.
+    banks = {}
+    for a in addrs:
+        banks.setdefault((a // 4) % 32, []).append(a)
+    deg = 1
+    for lst in banks.values():
+        if len(lst) > 1 and len(set(lst)) > 1:
+            deg = max(deg, len(lst))
+    return deg
+
+
+def _analyse_with_oracle(O, gaddr, saddr, guard, data_bytes=1 << 16):
+    """Counters of the probed accesses alone: the probe program's own table loads
+    and output store are removed by subtracting a run with every guard off."""
+    blk = 32 * max(1, min(8, len(gaddr) // 32))
+    mk = lambda gd: S.addr_probe(np.asarray(gaddr, np.uint64), np.asarray(saddr, np.uint32),
+                                 np.asarray(gd, np.uint32), data_bytes, block=blk)
+    _, c, _, _ = run(O, mk(guard))
+    _, c0, _, _ = run(O, mk(np.zeros(len(guard), np.uint32)))
+    out = c.copy()
+    for f in ("gld_n", "gld_sectors", "gld_lines", "gst_n", "gst_sectors", "gst_lines", "sh_n",
+              "sh_degree_sum"):
+        out[f] = c[f] - c0[f]
+    return out
+
+
+def test_page_examples_memory(oracle_mod):
+    """Worked examples of the KernelScope memory-analysis part
+    (tests/golden/memory_examples.json)."""
+    with open(os.path.join(GOLDEN, "memory_examples.json")) as f:
+        gold = json.load(f)
+    for ex in gold["examples"]:
+        addrs = ex["addresses"]
+        lanes = len(addrs)
+        gaddr = list(addrs) + [0] * (32 - lanes)
+        guard = [1] * lanes + [0] * (32 - lanes)
+        saddr = [a % 4096 for a in gaddr]
+        c = _analyse_with_oracle(oracle_mod, gaddr, saddr, guard)[0]
+        if "lines" in ex:
+            assert c["gld_lines"] == ex["lines"], ex
+            assert c["gld_sectors"] == ex["sectors"], ex
+        if "bank_degree" in ex:
+            assert c["sh_degree_max"] == ex["bank_degree"], ex
+
+
+def test_analyser_brute_force(oracle_mod):
+    """Random and structured address vectors and masks: sectors/lines equal
+    len(set(...)) and the bank degree equals the page rule restated above."""
+    rng = np.random.default_rng(5)
+    vecs = []
+    for k in range(256):
+        kind = k % 8
+        base = int(rng.integers(0, 1 << 14)) * 4
+        if kind == 0:
+            g = base + 4 * np.arange(32) * int(rng.integers(0, 40))
+        elif kind == 1:
+            g = rng.integers(0, 1 << 14, size=32) * 4
+        elif kind == 2:
+            g = np.full(32, base)
+        elif kind == 3:
+            g = base + 4 * rng.permutation(32)
+        elif kind == 4:
+            g = base + 4 * (np.arange(32) // int(rng.integers(1, 9)))
+        elif kind == 5:
+            g = base + 4 * rng.integers(0, 64, size=32)
+        elif kind == 6:
+            g = np.sort(rng.integers(0, 1 << 12, size=32)) * 4
+        else:
+            g = base + 32 * np.arange(32) + 4 * rng.integers(0, 8, size=32)
+        s = rng.integers(0, 1024, size=32) * 4 if kind in (1, 5) else (4 * int(rng.integers(0, 33)) * np.arange(32)) % 4096
+        if kind == 2:
+            s = np.full(32, int(rng.integers(0, 1024)) * 4)
+        m = rng.random(32) < (1.0 if k % 3 == 0 else rng.random())
+        vecs.append((g % (1 << 16), s, m.astype(np.uint32)))
+    gaddr = np.concatenate([v[0] for v in vecs])
+    saddr = np.concatenate([v[1] for v in vecs])
+    guard = np.concatenate([v[2] for v in vecs])
+    c = _analyse_with_oracle(oracle_mod, gaddr, saddr, guard)
+    for i, (g, s, m) in enumerate(vecs):
+        act = [int(x) for x, on in zip(g, m) if on]
+        sact = [int(x) for x, on in zip(s, m) if on]
+        if not act:
+            assert c[i]["gld_n"] == 0 and c[i]["sh_n"] == 0
+            continue
+        assert c[i]["gld_n"] == 1 and c[i]["gst_n"] == 1 and c[i]["sh_n"] == 2
+        assert c[i]["gld_sectors"] == len({a // 32 for a in act})
+        assert c[i]["gld_lines"] == len({a // 128 for a in act})
+        assert c[i]["gst_sectors"] == c[i]["gld_sectors"]
+        d = _bank_degree_page_rule(sact)
+        assert c[i]["sh_degree_max"] == d and c[i]["sh_degree_sum"] == 2 * d
+
+
+def test_analyser_counts_faulting_and_misaligned_lanes(oracle_mod):
+    """Out-of-range and misaligned accesses are analysed (both end sectors of a
+    misaligned access count), load 0, store nothing and count as faults."""
+    data = 1 << 16
+    gaddr = np.array([0, 2, 30, data + 64] + [0] * 28, np.uint64)
+    guard = np.array([1, 1, 1, 1] + [0] * 28, np.uint32)
+    saddr = np.zeros(32, np.uint32)
+    c = _analyse_with_oracle(oracle_mod, gaddr, saddr, guard, data_bytes=data)[0]
+    # lane 0: bytes [0,3] sector 0; lane 1: [2,5] misaligned, sector 0; lane 2: [30,33]
+    # misaligned, sectors 0 and 1; lane 3: a valid word past the data region
+    assert c["gld_sectors"] == len({0, 1, (data + 64) // 32})
+    assert c["gld_lines"] == len({0, (data + 64) // 128})
+    assert c["fault_n"] == 2 * 2  # lanes 1 and 2, on the load and on the store
+    assert c["status"] & oracle_mod.ST_FAULT
+    w = S.addr_probe(gaddr, saddr, guard, data, block=32)
+    g, _, _, _ = run(oracle_mod, w)
+    out = w.output(g, "out")
+    assert out[1] == 0 and out[2] == 0
+    assert out[0] == g[:4].view("<u4")[0]
+
+
+# ------------------------------------------------------------------ P11, P12 control flow
+
+def _cfg_case(seed, lanes_data):
+    ptx = S.random_cfg_ptx(seed)
+    n = len(lanes_data)
+    g = np.zeros(8 * n + 4096, np.uint8)
+    g[:4 * n] = np.asarray(lanes_data, np.uint32).view(np.uint8)
+    params = pack_params([("param_in", "u64", 0), ("param_out", "u64", 4 * n)])
+    return ptx, g, params
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_control_flow_matches_scalar_paths(oracle_mod, seed):
+    """Random small CFGs (forward branches, predicated ret) over lanes whose data
+    cover every guard pattern: per-lane results equal each lane's own scalar path
+    and the thread-instruction total equals the sum of scalar path lengths."""
+    rng = np.random.default_rng(seed)
+    data = rng.choice([0, 1, 500, 1500, 2500, 2999], size=64)
+    ptx, g, params = _cfg_case(seed, data)
+    g2 = g.copy()
+    c, _, _ = oracle_mod.run(ptx, 1, 64, params, g, trace_cap=256)
+    steps = scalar_ref.run_grid(ptx, (1, 1, 1), (64, 1, 1), params, g2)
+    assert np.array_equal(g, g2)
+    assert int(c["thread_instrs"].sum()) == sum(steps[0])
+    assert (c["max_stack_depth"] <= 63).all()
+
+
+def test_divergence_runs_fall_through_first(oracle_mod):
+    """if/else split: the fall-through side issues before the taken side and the
+    warp reconverges at the immediate post-dominator with the full mask."""
+    ptx = S.HEADER + """.visible .entry d(.param .u64 param_out)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<4>;
+    .reg .b64 %rd<4>;
+    mov.u32 %r1, %laneid;
+    setp.lt.u32 %p1, %r1, 16;
+    @%p1 bra $L__then;
+    add.s32 %r2, %r1, 100;
+    bra.uni $L__join;
+$L__then:
+    add.s32 %r2, %r1, 200;
+$L__join:
+    ld.param.u64 %rd1, [param_out];
+    mul.wide.u32 %rd2, %r1, 4;
+    add.s64 %rd3, %rd1, %rd2;
+    st.global.u32 [%rd3], %r2;
+    ret;
+}
+"""
+    g = np.zeros(256, np.uint8)
+    c, t, _ = oracle_mod.run(ptx, 1, 32, pack_params([("param_out", "u64", 0)]), g, trace_cap=32)
+    _, rec = oracle_mod.trace_slots(t, 32)
+    pcs = rec[0, :c["warp_instrs"][0], 1].tolist()
+    assert pcs == [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+    out = g[:128].view("<u4")
+    assert out.tolist() == [l + 200 if l < 16 else l + 100 for l in range(32)]
+    # 3 full + 2 half (else side: lanes 16..31) + 1 half (then side) + 5 full
+    assert c["thread_instrs"][0] == 3 * 32 + 2 * 16 + 16 + 5 * 32
+
+
+def test_random_stress_programs_match_scalar_reference(oracle_mod):
+    """Small instances of the random stress generator: SIMT oracle == scalar
+    per-thread reference, and thread-instruction totals agree."""
+    for seed in range(3):
+        nt = 128
+        w = W.random_stress(prog_seed=seed, grid=2, block=64, gmem_bytes=1 << 22, n_instr=300, trace_cap=64)
+        g, c, _, rc = run(oracle_mod, w, check_races=True)
+        assert rc == 0
+        g2 = w.gmem.copy()
+        steps = scalar_ref.run_grid(w.ptx, w.grid, w.block, w.params_bytes, g2)
+        assert np.array_equal(g, g2)
+        assert int(c["thread_instrs"].sum()) == sum(sum(s) for s in steps)
+        assert nt == 128
+
+
+# ------------------------------------------------------------------ P13 post-dominators
+
+def _brute_ipdom(prog):
+    n = len(prog.code)
+    EXIT = n
+    succ = []
+    for i, (guard, parts, ops) in enumerate(prog.code):
+        nx = i + 1
+        if parts[0] == "bra":
+            t = prog.labels[ops[0]]
+            s = {t}
+            if guard is not None:
+                s.add(nx)
+        elif parts[0] in ("ret", "exit"):
+            s = {EXIT}
+            if guard is not None:
+                s.add(nx)
+        else:
+            s = {nx}
+        succ.append({EXIT if x >= n else x for x in s})
+
+    def reaches_exit(v, removed):
+        seen, stack = set(), [v]
+        while stack:
+            x = stack.pop()
+            if x == EXIT:
+                return True
+            if x in seen or x == removed:
+                continue
+            seen.add(x)
+            stack.extend(succ[x])
+        return False
+
+    out = []
+    for v, (guard, parts, ops) in enumerate(prog.code):
+        if parts[0] != "bra" or guard is None:
+            out.append(0xFFFFFFFF)
+            continue
+        if not reaches_exit(v, None):
+            out.append(n)
+            continue
+        strict = [d for d in range(n) if d != v and not reaches_exit(v, d)]
+        best = n
+        for d in strict:
+            if all(d2 == d or not reaches_exit(d, d2) for d2 in strict):
+                best = d
+        out.append(best)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_ipdom_matches_brute_force(oracle_mod, seed):
+    ptx = S.random_cfg_ptx(1000 + seed, n_instr=16, loops=(seed % 2 == 1))
+    got = oracle_mod.ipdom_table(ptx)
+    exp = _brute_ipdom(scalar_ref.Program(ptx))
+    assert got == exp
+
+
+# ------------------------------------------------------------------ P14 trace slots, P15 stack
+
+def test_trace_slot_layout_and_overflow(oracle_mod):
+    w = W.ffma_probe(n_acc=8, iters=4, grid=1, block=64, trace_cap=50)
+    _, c, t, _ = run(oracle_mod, w)
+    assert t.size == 2 * (16 + 8 * 50)
+    hdr, rec = oracle_mod.trace_slots(t, 50)
+    for k in range(2):
+        n = int(c["warp_instrs"][k])
+        assert n > 50
+        assert hdr[k]["records_written"] == 50
+        assert hdr[k]["records_written"] + hdr[k]["records_dropped"] == n
+        assert hdr[k]["flags"] & 1 and c["status"][k] & oracle_mod.ST_TRACE_DROP
+        cyc = rec[k, :, 0].astype(np.int64)
+        assert (np.diff(cyc) >= 1).all()
+    # cap 0: header only
+    _, c0, t0, _ = run(oracle_mod, w, trace_cap=0)
+    h0, _ = oracle_mod.trace_slots(t0, 0)
+    assert t0.size == 32 and (h0["records_written"] == 0).all()
+    assert (h0["records_dropped"] == c0["warp_instrs"]).all()
+
+
+def test_stack_depth_bound_is_reached_exactly(oracle_mod):
+    ptx = S.staircase_ptx(31)
+    g = np.zeros(256, np.uint8)
+    c, _, _ = oracle_mod.run(ptx, 1, 32, pack_params([("param_out", "u64", 0)]), g, trace_cap=8)
+    assert c["max_stack_depth"][0] == 63 and c["diverge_n"][0] == 31
+    out = g[:128].view("<u4").tolist()
+    assert out == [2 * (k + 1) for k in range(31)] + [1031]
+
+
+# ------------------------------------------------------------------ status and error paths
+
+def test_parse_errors_carry_line_numbers(oracle_mod):
+    bad = W.VECTOR_ADD_PTX.replace("add.f32 %f3, %f1, %f2;", "add.f32 %f3, %f1, %f9;")
+    with pytest.raises(oracle_mod.OracleError) as e:
+        oracle_mod.program_info(bad)
+    line = 1 + W.VECTOR_ADD_PTX.split("add.f32 %f3")[0].count("\n")
+    assert ("line %d:" % line) in str(e.value) and "%f9" in str(e.value)
+    with pytest.raises(oracle_mod.OracleError) as e:
+        oracle_mod.program_info(W.VECTOR_ADD_PTX.replace("add.f32 %f3", "div.rn.f32 %f3"))
+    assert e.value.code == -2
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.program_info(W.VECTOR_ADD_PTX.replace("$L__exit;", "$L__nowhere;"))
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.program_info(W.VECTOR_ADD_PTX.replace("mov.u32 %r2, %tid.x;", "mov.u32 %r2, 1.5;"))
+
+
+def test_budget_stops_warps(oracle_mod):
+    w = W.vector_add()
+    g, c, t, _ = run(oracle_mod, w, max_warp_instrs=10)
+    assert (c["warp_instrs"] == 10).all()
+    assert (c["status"] & oracle_mod.ST_BUDGET).all() and not (c["status"] & oracle_mod.ST_FINISHED).any()
+    assert (w.output(g, "c") == 0).all()
+
+
+def test_barrier_in_divergent_region_is_flagged(oracle_mod):
+    ptx = S.HEADER + """.visible .entry b(.param .u64 param_out)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<3>;
+    mov.u32 %r1, %laneid;
+    setp.lt.u32 %p1, %r1, 8;
+    @%p1 bra $L__skip;
+    bar.sync 0;
+$L__skip:
+    ret;
+}
+"""
+    g = np.zeros(64, np.uint8)
+    c, _, _ = oracle_mod.run(ptx, 1, 64, pack_params([("param_out", "u64", 0)]), g, trace_cap=8)
+    assert (c["status"] & oracle_mod.ST_BARDIV).all()
+    assert (c["status"] & oracle_mod.ST_FINISHED).all()
+    assert (c["barrier_n"] == 1).all()
+
+
+def test_cycle_overflow_stops_warp(oracle_mod):
+    ptx = S.HEADER + """.visible .entry o(.param .u64 param_out)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<4>;
+    .reg .b64 %rd<2>;
+    ld.param.u64 %rd1, [param_out];
+    mov.u32 %r2, 0;
+$L__loop:
+    ld.global.u32 %r1, [%rd1];
+    add.s32 %r2, %r2, %r1;
+    setp.lt.u32 %p1, %r2, 1;
+    @%p1 bra $L__loop;
+    ret;
+}
+"""
+    g = np.zeros(64, np.uint8)
+    lat = oracle_mod.default_latency()
+    lat[7] = 65535  # ld.global
+    c, _, _ = oracle_mod.run(ptx, 1, 32, pack_params([("param_out", "u64", 0)]), g, trace_cap=4, latency=lat)
+    assert c["status"][0] & oracle_mod.ST_CYCLE_OVF
+    assert c["cycles"][0] <= 0x80000000
+
+
+def test_race_checker(oracle_mod):
+    for s in (1, 3):
+        w = W.bank_probe(s, iters=2, grid=1, block=128, trace_cap=4)
+        _, _, _, rc = run(oracle_mod, w, check_races=True)
+        assert rc == 0
+    racy = S.HEADER + """.visible .entry r(.param .u64 param_out)
+{
+    .reg .b32 %r<3>;
+    .reg .b64 %rd<2>;
+    ld.param.u64 %rd1, [param_out];
+    mov.u32 %r1, %laneid;
+    st.global.u32 [%rd1], %r1;
+    ret;
+}
+"""
+    g = np.zeros(64, np.uint8)
+    _, _, rc = oracle_mod.run(racy, 1, 32, pack_params([("param_out", "u64", 0)]), g, check_races=True)
+    assert rc == oracle_mod.E_RACE
+    # lane-ascending order: the highest lane's store is the one that remains
+    assert g[:4].view("<u4")[0] == 31
+
+
+def test_block_subset_equals_full_run(oracle_mod):
+    w = W.strided_gather(2, n=4096)
+    g_full, c_full, t_full, _ = run(oracle_mod, w)
+    blocks = [3, 0, 15]
+    g_sub, c_sub, t_sub, _ = run(oracle_mod, w, blocks=blocks)
+    wpb = w.warps_per_block
+    for i, b in enumerate(blocks):
+        assert np.array_equal(c_sub[i * wpb:(i + 1) * wpb], c_full[b * wpb:(b + 1) * wpb])
+    out_full, out_sub = w.output(g_full, "c"), w.output(g_sub, "c")
+    for b in blocks:
+        assert np.array_equal(out_sub[b * 256:(b + 1) * 256], out_full[b * 256:(b + 1) * 256])
+
+
+def test_thread_count_does_not_change_results(oracle_mod):
+    w = W.random_stress(prog_seed=1, grid=16, block=64, gmem_bytes=1 << 22, n_instr=200, trace_cap=64)
+    g1, c1, t1, _ = run(oracle_mod, w, threads=1)
+    g8, c8, t8, _ = run(oracle_mod, w, threads=8)
+    assert np.array_equal(g1, g8) and np.array_equal(c1, c8) and np.array_equal(t1, t8)

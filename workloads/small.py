@@ -1,0 +1,252 @@
+"""Small seeded test programs and inputs (inputs only, no simulator arithmetic).
+
+These exercise single features: f32 arithmetic on edge operands, straight-line
+FMA chains, worst-case divergence nesting, arbitrary per-lane address patterns
+for the memory analyser, and small control-flow shapes.
+"""
+import numpy as np
+
+from .configs import Workload, _align
+
+HEADER = ".version 7.5\n.target sm_80\n.address_size 64\n\n"
+
+F32_EDGE = [0x00000000, 0x80000000, 0x00000001, 0x80000001, 0x007FFFFF, 0x807FFFFF, 0x00800000,
+            0x80800000, 0x3F800000, 0xBF800000, 0x3F800001, 0x3F7FFFFF, 0x7F7FFFFF, 0xFF7FFFFF,
+            0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x7F800001, 0x34000000, 0x33800000,
+            0x4B800000, 0x4B7FFFFF, 0x3EAAAAAB, 0x40490FDB, 0x00400000, 0x0C000000, 0x4C000000,
+            0x5F000000, 0x1F000000, 0x7F000000, 0x01000000]
+
+
+def f32_operands(n: int, seed: int = 11) -> np.ndarray:
+    """(n, 3) uint32 operand bit patterns: edge values crossed with each other,
+    then random patterns with every exponent represented, then near-cancelling
+    and near-overflow/underflow pairs."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    E = np.array(F32_EDGE, dtype=np.uint32)
+    for a in E:
+        for b in E:
+            rows.append((a, b, E[(int(a) ^ int(b)) % len(E)]))
+    out = np.array(rows, dtype=np.uint32)
+    k = max(0, n - len(out))
+    rnd = rng.integers(0, 1 << 32, size=(k, 3), dtype=np.uint32)
+    # a quarter: exponents near each other (cancellation, close magnitudes)
+    q = k // 4
+    if q:
+        a = rnd[:q, 0]
+        b = (a ^ rng.integers(0, 1 << 8, size=q, dtype=np.uint32)) ^ np.uint32(0x80000000)
+        rnd[:q, 1] = b
+        # addend close to -(a*b)'s magnitude range
+        rnd[:q, 2] = (rnd[:q, 2] & np.uint32(0x807FFFFF)) | (((a >> 23) & 0xFF) << 23).astype(np.uint32)
+    # a quarter: small exponents (subnormal results)
+    if q:
+        rnd[q:2 * q, :] &= np.uint32(0x83FFFFFF)
+    out = np.concatenate([out, rnd])[:max(n, len(out))]
+    return out
+
+
+F32_OPS_PTX = HEADER + """\
+.visible .entry f32_ops(
+    .param .u64 param_in,
+    .param .u64 param_out,
+    .param .u32 param_n
+)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<16>;
+    .reg .b64 %rd<8>;
+
+    ld.param.u64 %rd1, [param_in];
+    ld.param.u64 %rd2, [param_out];
+    ld.param.u32 %r1, [param_n];
+    mov.u32 %r2, %tid.x;
+    mov.u32 %r3, %ctaid.x;
+    mov.u32 %r4, %ntid.x;
+    mad.lo.s32 %r5, %r3, %r4, %r2;
+    setp.ge.u32 %p1, %r5, %r1;
+    @%p1 bra $L__exit;
+    mul.wide.u32 %rd3, %r5, 12;
+    add.s64 %rd4, %rd1, %rd3;
+    ld.global.f32 %r6, [%rd4];
+    ld.global.f32 %r7, [%rd4+4];
+    ld.global.f32 %r8, [%rd4+8];
+    add.f32 %r9, %r6, %r7;
+    sub.f32 %r10, %r6, %r7;
+    mul.f32 %r11, %r6, %r7;
+    fma.rn.f32 %r12, %r6, %r7, %r8;
+    mul.wide.u32 %rd5, %r5, 16;
+    add.s64 %rd6, %rd2, %rd5;
+    st.global.f32 [%rd6], %r9;
+    st.global.f32 [%rd6+4], %r10;
+    st.global.f32 [%rd6+8], %r11;
+    st.global.f32 [%rd6+12], %r12;
+$L__exit:
+    ret;
+}
+"""
+
+
+def f32_ops(n: int = 8192, block: int = 256, seed: int = 11) -> Workload:
+    ops = f32_operands(n, seed)
+    n = len(ops)
+    off_in = 0
+    off_out = _align(12 * n)
+    size = _align(off_out + 16 * n)
+    gmem = np.zeros(size, dtype=np.uint8)
+    gmem[: 12 * n] = ops.reshape(-1).view(np.uint8)
+    grid = (n + block - 1) // block
+    return Workload(name="f32_ops", ptx=F32_OPS_PTX, grid=(grid, 1, 1), block=(block, 1, 1),
+                    params=[("param_in", "u64", off_in), ("param_out", "u64", off_out), ("param_n", "u32", n)],
+                    gmem=gmem, trace_cap=32,
+                    outputs={"in": (off_in, 3 * n, "<u4"), "out": (off_out, 4 * n, "<u4")}, meta={"n": n})
+
+
+def fma_chain_ptx(n_fma: int, n_acc: int) -> str:
+    """Straight-line chain: n_fma fma.rn.f32 cycling over n_acc accumulators, then
+    a store of accumulator 0 (which depends on the last FMA into it)."""
+    L = [HEADER + ".visible .entry fma_chain(\n    .param .u64 param_out\n)\n{",
+         "    .reg .f32 %%f<%d>;" % (2 + n_acc), "    .reg .b64 %rd<2>;",
+         "    ld.param.u64 %rd1, [param_out];",
+         "    mov.f32 %f0, 0f3F800000;", "    mov.f32 %f1, 0f3F000000;"]
+    for k in range(n_fma):
+        a = "%%f%d" % (2 + k % n_acc)
+        L.append("    fma.rn.f32 %s, %%f0, %%f1, %s;" % (a, a))
+    last = "%%f%d" % (2 + (n_fma - 1) % n_acc)
+    L.append("    st.global.f32 [%%rd1], %s;" % last)
+    L.append("    ret;\n}\n")
+    return "\n".join(L)
+
+
+def staircase_ptx(levels: int = 31) -> str:
+    """Worst-case divergence nesting: at level k lane k leaves on an if/else whose
+    taken side jumps to its own block; every split adds two stack entries."""
+    L = [HEADER + ".visible .entry staircase(\n    .param .u64 param_out\n)\n{",
+         "    .reg .pred %p<2>;", "    .reg .b32 %r<4>;", "    .reg .b64 %rd<4>;",
+         "    ld.param.u64 %rd1, [param_out];", "    mov.u32 %r1, %laneid;", "    mov.u32 %r2, 0;"]
+    # S_k = setp_k; @p bra t_k; S_{k+1}; bra e_k; t_k: r2 += k+1; e_k: r2 += 1
+    for k in range(levels):
+        L.append("    setp.eq.u32 %%p1, %%r1, %d;" % k)
+        L.append("    @%%p1 bra $L__t%d;" % k)
+    L.append("    add.s32 %r2, %r2, 1000;")
+    for k in range(levels - 1, -1, -1):
+        L.append("    bra.uni $L__e%d;" % k)
+        L.append("$L__t%d:" % k)
+        L.append("    add.s32 %%r2, %%r2, %d;" % (k + 1))
+        L.append("$L__e%d:" % k)
+        L.append("    add.s32 %r2, %r2, 1;")
+    L.append("    mul.wide.u32 %rd2, %r1, 4;")
+    L.append("    add.s64 %rd3, %rd1, %rd2;")
+    L.append("    st.global.u32 [%rd3], %r2;")
+    L.append("    ret;\n}\n")
+    return "\n".join(L)
+
+
+ADDR_PROBE_PTX = HEADER + """\
+.visible .entry addr_probe(
+    .param .u64 param_gaddr,
+    .param .u64 param_saddr,
+    .param .u64 param_guard,
+    .param .u64 param_out
+)
+{
+    .reg .pred %p<3>;
+    .reg .b32 %r<12>;
+    .reg .b64 %rd<12>;
+    .shared .align 8 .b8 win[4096];
+
+    ld.param.u64 %rd1, [param_gaddr];
+    ld.param.u64 %rd2, [param_guard];
+    ld.param.u64 %rd3, [param_out];
+    ld.param.u64 %rd10, [param_saddr];
+    mov.u32 %r2, %tid.x;
+    mov.u32 %r3, %ctaid.x;
+    mov.u32 %r4, %ntid.x;
+    mad.lo.s32 %r5, %r3, %r4, %r2;
+    mul.wide.u32 %rd4, %r5, 8;
+    add.s64 %rd5, %rd1, %rd4;
+    ld.global.u64 %rd6, [%rd5];
+    mul.wide.u32 %rd7, %r5, 4;
+    add.s64 %rd8, %rd2, %rd7;
+    ld.global.u32 %r6, [%rd8];
+    add.s64 %rd11, %rd10, %rd7;
+    ld.global.u32 %r8, [%rd11];
+    setp.ne.u32 %p1, %r6, 0;
+    mov.u32 %r7, 0;
+    @%p1 ld.global.u32 %r7, [%rd6];
+    @%p1 st.global.u32 [%rd6], %r7;
+    @%p1 ld.shared.u32 %r9, [%r8];
+    @%p1 st.shared.u32 [%r8], %r9;
+    add.s64 %rd9, %rd3, %rd7;
+    st.global.u32 [%rd9], %r7;
+    ret;
+}
+"""
+
+
+def addr_probe(gaddr: np.ndarray, saddr: np.ndarray, guard: np.ndarray, data_bytes: int,
+               block: int = 256, seed: int = 12) -> Workload:
+    """One warp per address vector: lane l of warp w loads/stores global address
+    gaddr[32 w + l] (a byte offset into the data region at 0) and shared address
+    saddr[32 w + l] when guard[32 w + l] != 0.  Stores write back what was loaded,
+    so repeated or shared addresses are benign."""
+    n = len(gaddr)
+    assert n % block == 0 and len(saddr) == n and len(guard) == n
+    rng = np.random.default_rng(seed)
+    off_data = 0
+    off_g = _align(data_bytes)
+    off_s = _align(off_g + 8 * n)
+    off_guard = _align(off_s + 4 * n)
+    off_out = _align(off_guard + 4 * n)
+    size = _align(off_out + 4 * n)
+    gmem = np.zeros(size, dtype=np.uint8)
+    gmem[:data_bytes] = rng.integers(0, 256, size=data_bytes, dtype=np.uint8)
+    gmem[off_g: off_g + 8 * n] = np.asarray(gaddr, dtype=np.uint64).view(np.uint8)
+    gmem[off_s: off_s + 4 * n] = np.asarray(saddr, dtype=np.uint32).view(np.uint8)
+    gmem[off_guard: off_guard + 4 * n] = np.asarray(guard, dtype=np.uint32).view(np.uint8)
+    return Workload(name="addr_probe", ptx=ADDR_PROBE_PTX, grid=(n // block, 1, 1), block=(block, 1, 1),
+                    params=[("param_gaddr", "u64", off_g), ("param_saddr", "u64", off_s),
+                            ("param_guard", "u64", off_guard), ("param_out", "u64", off_out)],
+                    gmem=gmem, trace_cap=32, outputs={"out": (off_out, n, "<u4")}, meta={"n": n})
+
+
+def random_cfg_ptx(seed: int, n_instr: int = 24, loops: bool = False, with_ret: bool = True) -> str:
+    """A small random control-flow shape over lanes: guards come from per-lane
+    data (lane id bits and loaded words), branches go forward (or also backward
+    when `loops`, for post-dominator checks only, never executed), predicated
+    ret may appear.  Every instruction body is an add into a per-lane checksum
+    register so executions are observable in memory."""
+    rng = np.random.default_rng(seed)
+    L = [HEADER + ".visible .entry cfg(\n    .param .u64 param_in,\n    .param .u64 param_out\n)\n{",
+         "    .reg .pred %p<4>;", "    .reg .b32 %r<8>;", "    .reg .b64 %rd<6>;",
+         "    ld.param.u64 %rd1, [param_in];", "    ld.param.u64 %rd2, [param_out];",
+         "    mov.u32 %r1, %tid.x;", "    mov.u32 %r2, %ctaid.x;", "    mov.u32 %r3, %ntid.x;",
+         "    mad.lo.s32 %r4, %r2, %r3, %r1;", "    mul.wide.u32 %rd3, %r4, 4;",
+         "    add.s64 %rd4, %rd1, %rd3;", "    ld.global.u32 %r5, [%rd4];", "    mov.u32 %r6, 0;",
+         "    setp.ne.u32 %p0, %r5, 0;", "    setp.lt.u32 %p1, %r5, 1000;",
+         "    setp.gt.u32 %p2, %r5, 2000;", "    setp.eq.u32 %p3, %r1, 0;"]
+    base = len(L) - 5  # number of instructions so far (the header and .reg lines are not instructions)
+    body = []
+    for i in range(n_instr):
+        r = rng.random()
+        if r < 0.35:
+            lo = i + 2 if not loops or rng.random() < 0.7 else 0
+            hi = n_instr + 1
+            tgt = int(rng.integers(lo, hi)) if lo < hi else n_instr
+            neg = "!" if rng.random() < 0.5 else ""
+            body.append(("bra", "@%s%%p%d bra $L__b%d;" % (neg, int(rng.integers(0, 4)), tgt), tgt))
+        elif r < 0.42 and with_ret:
+            body.append(("ret", "@%%p%d ret;" % int(rng.integers(0, 4)), None))
+        elif r < 0.5:
+            body.append(("flip", "setp.lt.u32 %%p%d, %%r5, %d;" % (int(rng.integers(0, 4)),
+                                                                   int(rng.integers(0, 3000))), None))
+        else:
+            body.append(("add", "add.s32 %%r6, %%r6, %d;" % (1 << (i % 24)), None))
+    targets = {t for k, _, t in body if k == "bra"}
+    for i, (_, text, _) in enumerate(body):
+        if i in targets:
+            L.append("$L__b%d:" % i)
+        L.append("    " + text)
+    if n_instr in targets:
+        L.append("$L__b%d:" % n_instr)
+    L += ["    add.s64 %rd5, %rd2, %rd3;", "    st.global.u32 [%rd5], %r6;", "    ret;", "}"]
+    return "\n".join(L) + "\n"

@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Benchmark: simulated thread-instructions/s and analysed warp-accesses/s on one GPU.
+
+One step = one ks_run of the whole hot path (fetch/issue/execute, divergence
+stack, scoreboard, sector/line/bank analyser, trace and counter writes) over
+the random-stress workload: 65536 x 256 = 16.8 M simulated threads running a
+seeded 2000-instruction program of the PTX subset over 1 GiB of simulated
+global memory, trace cap 2048 records per warp.  Inputs are resident in HBM
+before timing starts.
+
+Prints one JSON line (rank 0).  `roofline` prices the interpreter kernel's
+algorithmic bytes (32 B per counted sector + 8 B per written trace record +
+16 B header and 80 B counters per warp) per launch against MI355X's 8 TB/s HBM;
+the launch duration comes from HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "simulated thread-instr/s + analysed warp-accesses/s at 1 GPU; % HBM peak"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("ks_kernel.hip", "ks_isa.h"):
+        with open(os.path.join(ROOT, "analysis_ptxsimulator_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_key)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def make_workload(name):
+    from workloads import configs as W
+    if name == "random_stress":
+        return W.random_stress(prog_seed=0)
+    if name == "ffma_dep":
+        return W.ffma_probe(n_acc=1)
+    if name == "ffma_ind":
+        return W.ffma_probe(n_acc=8)
+    if name.startswith("bank_s"):
+        return W.bank_probe(int(name[6:]))
+    if name.startswith("strided_s"):
+        return W.strided_gather(int(name[9:]))
+    if name == "vector_add":
+        return W.vector_add()
+    raise SystemExit("unknown workload %s" % name)
+
+
+def describe(w):
+    m = w.meta
+    if w.name.startswith("random_stress"):
+        return ("random_stress: %d x %d threads (16.8M), %d-instruction PTX program seed %d, %d MiB simulated "
+                "memory seed %d, trace cap %d" % (w.grid[0], w.block[0], m["n_instr"], m["prog_seed"],
+                                                   w.gmem.size >> 20, m["mem_seed"], w.trace_cap))
+    return "%s: grid %s block %s trace cap %d" % (w.name, w.grid, w.block, w.trace_cap)
+
+
+def cpu_baseline(w, sample_blocks, threads):
+    from oracle import oracle as O
+    import numpy as np
+    blocks = list(range(sample_blocks))
+    g = w.gmem  # the sampled blocks only write their own thread-private words
+    t0 = time.perf_counter()
+    c, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=w.trace_cap, blocks=blocks, threads=threads)
+    dt = time.perf_counter() - t0
+    ti = int(c["thread_instrs"].sum())
+    return {"value": ti / dt, "unit": "thread-instr/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d blocks (%d thread-instructions) of the same workload, %.2f s wall"
+                      % (sample_blocks, w.n_blocks, ti, dt),
+            "warp_accesses_per_s": int((c["gld_n"].astype(np.uint64) + c["gst_n"] + c["sh_n"]).sum()) / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="random_stress")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "
+              "(blocks never communicate; see the sharding note in DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from analysis_ptxsimulator_amd import ks
+
+    w = make_workload(args.workload)
+    dev = torch.device("cuda:0")
+    s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, device=dev)
+    s.load_gmem(w.gmem)
+    params = w.params_bytes
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        s.run(params)
+    torch.cuda.synchronize(dev)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        s.run(params)
+        ends[k].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_per_step = wall * 1000.0 / args.steps
+
+    c = s.read_counters()
+    status = s.status()
+    s.close()
+    thread_instrs = int(c["thread_instrs"].sum())
+    warp_acc = int(c["gld_n"].astype(np.uint64).sum() + c["gst_n"].sum() + c["sh_n"].sum())
+    sectors = int(c["gld_sectors"].astype(np.uint64).sum() + c["gst_sectors"].sum())
+    records = int(np.minimum(c["warp_instrs"], w.trace_cap).astype(np.uint64).sum())
+    alg_bytes = 32 * sectors + 8 * records + (16 + 80) * len(c)
+    avg_launch_s = float(np.mean(launch_ms)) / 1000.0
+    achieved = alg_bytes / avg_launch_s / 1e9
+    traffic = measured_traffic(args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": thread_instrs / (ms_per_step / 1000.0),
+        "unit": "thread-instr/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "threads": w.n_blocks * w.threads_per_block,
+                   "warps": len(c), "parallelism": "single GPU"},
+        "warp_accesses_per_s": warp_acc / (ms_per_step / 1000.0),
+        "thread_instrs_per_step": thread_instrs,
+        "warp_accesses_per_step": warp_acc,
+        "run_status_bits": status,
+        "launch_ms": {"min": min(launch_ms), "median": float(np.median(launch_ms)), "max": max(launch_ms)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel": "ks_interp_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_blocks, w.n_blocks), threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * ks.h -- C ABI of libkscope, a PTX-subset SIMT simulator that runs on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library simulates NVIDIA-style 32-thread warps executing a small PTX
+ * subset.  It models three things:
+ *   - per-warp active masks and a divergence stack that reconverges at immediate
+ *     post-dominators computed on the host;
+ *   - a register-scoreboard cycle model with a per-opcode latency table;
+ *   - a memory analyser (32-byte sectors and 128-byte lines per global warp
+ *     access, the bank-conflict degree over 32 four-byte banks per shared warp
+ *     access).
+ * It also writes a per-warp trace of {issue cycle, pc} records.
+ *
+ * Sources of the semantics, by page and section:
+ *   - KernelScope backend documentation (github.com/briefgaming/kernelscope).
+ *     The PTX-parser part gives the grammar.  The execution-simulator part gives
+ *     warps, the active mask and the SIMT stack of (pc, mask, reconvergence pc).
+ *     The memory-analysis part gives banks, broadcast, lines and sectors.  The
+ *     latency-model part gives the sm_80 latencies.
+ *   - "CuTeDSL IKET 浅析" (zhen8838.github.io/posts/iket.html), section 2
+ *     ("buffer 是怎么定形的"): the trace slot shape.
+ *   - The SASS-probe method page (teach-meaning.tistory.com/1954), sections 2
+ *     and 14: the dependent versus independent FMA contrast that the scoreboard
+ *     model reproduces.
+ *
+ * Conventions
+ *   - Every entry point returns ks_status: 0 (KS_OK) or a negative error code.
+ *     No C++ exception crosses the ABI.
+ *   - ks_last_error() returns the message of the last failing call on this
+ *     thread.  It is valid until the next call on the same thread.
+ *   - Host pointers are plain CPU memory.  Device pointers ("d_") are HIP device
+ *     allocations, owned by the caller.
+ *   - The library owns only what it creates: program and state descriptors, and
+ *     a small device copy of the decoded program (freed by ks_state_free).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  ks_run and
+ *     ks_read_* are ordered on that stream; ks_read_* wait for their copy.
+ *   - All multi-byte data are little-endian.
+ *   - The library computes every result on the GPU.  There is no CPU fallback:
+ *     if no gfx950 device is usable, ks_alloc_state fails with KS_E_HIP.
+ */
+#ifndef KS_H
+#define KS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ks_status;
+#define KS_OK 0
+#define KS_E_PARSE (-1)        /* malformed PTX; message "line N: ..." */
+#define KS_E_UNSUPPORTED (-2)  /* valid PTX outside the subset, or beyond a size limit */
+#define KS_E_INVALID_ARG (-3)  /* bad pointer, size, shape or configuration */
+#define KS_E_HIP (-4)          /* a HIP runtime call failed, or no gfx950 device */
+#define KS_E_NOMEM (-5)        /* a host or device allocation failed */
+#define KS_E_STATE (-6)        /* call out of order (for example a read before any run) */
+
+/* Per-warp status bits (counter field `status`, OR-ed by ks_run_status). */
+#define KS_ST_FINISHED 0x01u   /* every lane exited normally */
+#define KS_ST_BUDGET 0x02u     /* stopped at max_warp_instrs */
+#define KS_ST_FAULT 0x04u      /* at least one lane access out of range or misaligned */
+#define KS_ST_TRACE_DROP 0x08u /* trace records past trace_cap were dropped (and counted) */
+#define KS_ST_BARDIV 0x10u     /* bar.sync reached with a partial (divergent) mask */
+#define KS_ST_CYCLE_OVF 0x20u  /* an issue cycle would exceed 2^31 - 1; warp stopped */
+
+/* Latency classes, the indices of ks_config.latency[]. */
+#define KS_NLAT 16
+enum {
+  KS_LAT_INT32 = 0, KS_LAT_INT64 = 1, KS_LAT_FP32 = 2, KS_LAT_SETP = 3, KS_LAT_SELP = 4,
+  KS_LAT_MOV = 5, KS_LAT_LD_PARAM = 6, KS_LAT_LD_GLOBAL = 7, KS_LAT_LD_SHARED = 8,
+  KS_LAT_ST_GLOBAL = 9, KS_LAT_ST_SHARED = 10, KS_LAT_BRA = 11, KS_LAT_BAR = 12, KS_LAT_RET = 13
+};
+
+/* Limits of this build. */
+#define KS_MAX_REG_SLOTS 64      /* 32-bit register slots per thread (a 64-bit register takes 2) */
+#define KS_MAX_PREDS 32          /* predicate registers */
+#define KS_MAX_INSTRS 65535      /* decoded instructions per program */
+#define KS_MAX_PARAM_BYTES 512   /* parameter block */
+#define KS_MAX_SHARED_BYTES 65536 /* simulated shared window per block */
+#define KS_MAX_BLOCK_THREADS 1024
+
+typedef struct ks_program ks_program; /* opaque; created by ks_load_program */
+typedef struct ks_state ks_state;     /* opaque; created by ks_alloc_state */
+typedef struct { uint32_t x, y, z; } ks_dim3;
+
+typedef struct {
+  ks_dim3 max_grid;          /* largest grid ks_run will accept */
+  ks_dim3 max_block;         /* largest block ks_run will accept (<= 1024 threads) */
+  uint64_t gmem_bytes;       /* size of the simulated global memory d_gmem */
+  uint32_t trace_cap;        /* trace records per warp slot; 0 = headers only */
+  uint32_t max_warp_instrs;  /* per-warp issue budget; a warp reaching it stops with KS_ST_BUDGET */
+  uint16_t latency[KS_NLAT]; /* cycles per latency class (ks_default_config fills sm_80 values) */
+} ks_config;
+
+typedef struct {
+  uint32_t n_instrs;         /* decoded instructions */
+  uint32_t n_params;
+  uint32_t param_bytes;      /* size of the parameter block ks_run expects */
+  uint32_t shared_bytes;     /* simulated shared window per block */
+  uint32_t reg_slots;        /* 32-bit register slots per thread */
+  uint32_t n_preds;          /* predicate registers */
+} ks_program_desc;
+
+typedef struct {
+  uint32_t warps_per_block;  /* ceil(threads per block / 32) for max_block */
+  uint32_t reserved;
+  uint64_t n_warps;          /* warps of the largest grid: max blocks * warps_per_block */
+  uint64_t counters_bytes;   /* n_warps * 80: size of d_counters */
+  uint64_t slot_bytes;       /* 16 + 8 * trace_cap: one trace slot */
+  uint64_t trace_bytes;      /* n_warps * slot_bytes: size of d_trace */
+} ks_layout;
+
+/* Parse a PTX module and decode the entry `entry` (NULL or "" = the first .entry).
+ * `ptx` holds `len` bytes of text.  On success *out owns the decoded program.
+ * The accepted subset and its meaning are those of the KernelScope parser and
+ * simulator pages, restricted as described in the repository's design notes.
+ * Errors: KS_E_PARSE (message "line N: ..."), KS_E_UNSUPPORTED, KS_E_INVALID_ARG. */
+ks_status ks_load_program(const char* ptx, size_t len, const char* entry, ks_program** out);
+
+/* Shape of a decoded program. */
+ks_status ks_program_info(const ks_program* prog, ks_program_desc* out);
+
+/* Parameter `index` (declaration order): byte offset in the parameter block, size
+ * in bytes, and its name (points into `prog`, valid while prog lives).  Parameters
+ * are laid out in declaration order, each at its natural alignment. */
+ks_status ks_param_info(const ks_program* prog, uint32_t index, uint32_t* offset, uint32_t* size,
+                        const char** name);
+
+/* Debug: for each instruction, the reconvergence index of a guarded bra (n_instrs
+ * meaning "exit"), 0xFFFFFFFF for every other instruction.  `out` holds `n`
+ * entries; the first min(n, n_instrs) are written. */
+ks_status ks_ipdom_table(const ks_program* prog, uint32_t* out, uint32_t n);
+
+/* Fill `cfg` with defaults: the sm_80 latency table of the KernelScope latency
+ * page (int/fp32 4, ld.global 200, ld.shared 23, ld.param as ld.const 4,
+ * bar.sync 20), trace_cap 0, max_warp_instrs 0xFFFFFFFF, max grid/block 1. */
+ks_status ks_default_config(ks_config* cfg);
+
+/* Sizes of the caller-owned device buffers for runs up to cfg->max_grid x
+ * cfg->max_block.  The trace slot size follows the IKET page's per-warp slot
+ * (a 16-byte header and fixed 8-byte records, without its 1.15 margin). */
+ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layout* out);
+
+/* Bind a program to caller-owned device buffers on the current HIP device:
+ *   d_gmem      cfg->gmem_bytes of simulated global memory (inputs are written here by
+ *               the caller; ks_run updates it in place and it persists across runs),
+ *   d_counters  layout.counters_bytes: 80-byte per-warp counter records,
+ *   d_trace     layout.trace_bytes: per-warp trace slots.
+ * Uploads the decoded program (latencies baked in from cfg) to a small device
+ * buffer owned by the state.  Errors: KS_E_INVALID_ARG (NULL buffers, limits),
+ * KS_E_UNSUPPORTED (program beyond this build's limits), KS_E_HIP, KS_E_NOMEM. */
+ks_status ks_alloc_state(const ks_program* prog, const ks_config* cfg, void* d_gmem, void* d_counters,
+                         void* d_trace, ks_state** out);
+
+/* Launch one simulation of grid x block threads on `stream` (asynchronous).
+ * `params` holds `params_len` >= param_bytes bytes of the parameter block (host
+ * memory; copied into the launch arguments).  Each run re-initialises registers,
+ * predicates, stacks, scoreboards and shared windows, and rewrites every
+ * counter record and trace header of the grid's warps.  Warps are numbered
+ * linear block id * warps_per_block + warp in block.
+ * Errors: KS_E_INVALID_ARG (shape beyond the allocation, short params), KS_E_HIP. */
+ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, size_t params_len,
+                 void* stream);
+
+/* Copy n bytes of simulated global memory at byte offset sim_addr to host memory
+ * (after the work queued on `stream`).  KS_E_INVALID_ARG if out of range. */
+ks_status ks_read_outputs(ks_state* st, uint64_t sim_addr, void* host, size_t n, void* stream);
+
+/* Copy the counter records of warps [first_warp, first_warp + n_warps) of the last
+ * run to `host` (n >= 80 * n_warps bytes).  KS_E_STATE before any run. */
+ks_status ks_read_counters(ks_state* st, uint64_t first_warp, uint64_t n_warps, void* host, size_t n,
+                           void* stream);
+
+/* Copy the trace slots of warps [first_warp, first_warp + n_warps) of the last run
+ * to `host` (n >= slot_bytes * n_warps).  Record bytes past a slot's
+ * records_written are unspecified.  KS_E_STATE before any run. */
+ks_status ks_read_trace(ks_state* st, uint64_t first_warp, uint64_t n_warps, void* host, size_t n,
+                        void* stream);
+
+/* OR of the status bits of every warp of the last run (reduced on the GPU). */
+ks_status ks_run_status(ks_state* st, uint32_t* or_bits, void* stream);
+
+/* Release a state (and its device copy of the program) or a program.  NULL is a no-op. */
+void ks_state_free(ks_state* st);
+void ks_program_free(ks_program* prog);
+
+/* Message of the last error on this thread ("" if none). */
+const char* ks_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KS_H */

@@ -1,0 +1,329 @@
+"""GPU parity: libkscope on gfx950 against the CPU oracle, bit for bit.
+
+Every case runs the same seeded inputs through the C ABI (ks_load_program,
+ks_alloc_state, ks_run, ks_read_*) and through the oracle, then compares the
+simulated memory, every field of every per-warp counter record, the trace
+headers and every written trace record.  The tolerance is zero everywhere: f32
+results are IEEE round-to-nearest on both sides (0 ULP), and everything else is
+integer.  Full-size workloads are compared on sampled blocks: blocks never
+communicate, so the oracle can simulate any subset exactly.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from workloads import configs as W
+from workloads import small as S
+from workloads.configs import pack_params
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[gpu] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from analysis_ptxsimulator_amd import ks
+    ks.lib()
+    return ks
+
+
+def gpu_run(K, w, trace_cap=None, max_warp_instrs=0xFFFFFFFF, latency=None, runs=1):
+    cap = w.trace_cap if trace_cap is None else trace_cap
+    _say("%s grid=%s block=%s cap=%d" % (w.name, w.grid, w.block, cap))
+    s = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=cap, max_warp_instrs=max_warp_instrs,
+                  latency=latency)
+    try:
+        outs = []
+        for _ in range(runs):
+            s.load_gmem(w.gmem)
+            s.run(w.params_bytes)
+            outs.append((s.read_gmem(), s.read_counters(), s.read_trace(), s.status()))
+        return outs if runs > 1 else outs[0]
+    finally:
+        s.close()
+
+
+def oracle_run(O, w, trace_cap=None, blocks=None, **kw):
+    cap = w.trace_cap if trace_cap is None else trace_cap
+    g = w.gmem.copy()
+    c, t, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=cap, blocks=blocks, **kw)
+    return g, c, t
+
+
+def compare_counters(cg, co, where=""):
+    assert cg.dtype.names == co.dtype.names
+    for f in co.dtype.names:
+        if not np.array_equal(cg[f], co[f]):
+            bad = np.nonzero(cg[f] != co[f])[0][:5]
+            raise AssertionError("%s counter %s differs at warps %s: gpu %s oracle %s" %
+                                 (where, f, bad.tolist(), cg[f][bad].tolist(), co[f][bad].tolist()))
+
+
+def compare_traces(K, tg, to, cap, where=""):
+    hg, rg = K.trace_slots(tg, cap)
+    ho, ro = K.trace_slots(to, cap)
+    for f in ho.dtype.names:
+        assert np.array_equal(hg[f], ho[f]), "%s trace header %s differs" % (where, f)
+    for wi in range(len(ho)):
+        n = int(ho["records_written"][wi])
+        if not np.array_equal(rg[wi, :n], ro[wi, :n]):
+            k = int(np.nonzero((rg[wi, :n] != ro[wi, :n]).any(axis=1))[0][0])
+            raise AssertionError("%s warp %d record %d: gpu %s oracle %s" %
+                                 (where, wi, k, rg[wi, k].tolist(), ro[wi, k].tolist()))
+
+
+def full_parity(K, O, w, trace_cap=None, **kw):
+    cap = w.trace_cap if trace_cap is None else trace_cap
+    gg, cg, tg, st = gpu_run(K, w, trace_cap=cap, **kw)
+    okw = {}
+    if "max_warp_instrs" in kw:
+        okw["max_warp_instrs"] = kw["max_warp_instrs"]
+    if "latency" in kw:
+        okw["latency"] = kw["latency"]
+    go, co, to = oracle_run(O, w, trace_cap=cap, **okw)
+    if not np.array_equal(gg, go):
+        bad = np.nonzero(gg != go)[0]
+        raise AssertionError("%s: %d memory bytes differ, first at %d" % (w.name, bad.size, bad[0]))
+    compare_counters(cg, co, w.name)
+    compare_traces(K, tg, to, cap, w.name)
+    assert st == int(np.bitwise_or.reduce(co["status"])) if len(co) else st == 0
+    return cg
+
+
+def sampled_parity(K, O, w, blocks, regions, trace_cap=None):
+    """GPU runs the whole grid; the oracle simulates only `blocks`.  Compares the
+    sampled blocks' warps and, per region (offset, bytes per thread), the bytes
+    those blocks' threads own."""
+    cap = w.trace_cap if trace_cap is None else trace_cap
+    gg, cg, tg, st = gpu_run(K, w, trace_cap=cap)
+    go, co, to = oracle_run(O, w, trace_cap=cap, blocks=blocks)
+    wpb = w.warps_per_block
+    slot = 16 + 8 * cap
+    tg2 = tg.reshape(-1, slot)
+    for i, b in enumerate(blocks):
+        sl = slice(b * wpb, (b + 1) * wpb)
+        compare_counters(cg[sl], co[i * wpb:(i + 1) * wpb], "%s block %d" % (w.name, b))
+        compare_traces(K, tg2[sl].reshape(-1), to.reshape(-1, slot)[i * wpb:(i + 1) * wpb].reshape(-1), cap,
+                       "%s block %d" % (w.name, b))
+        tpb = w.threads_per_block
+        for off, per_thread, stride in regions:
+            for t0 in (b * tpb,):
+                lo = off + t0 * per_thread
+                hi = off + (t0 + tpb) * per_thread
+                if stride:
+                    for j in range(4):
+                        lo2, hi2 = lo + j * stride, hi + j * stride
+                        assert np.array_equal(gg[lo2:hi2], go[lo2:hi2]), "%s block %d region %d+%d" % (w.name, b, off, j)
+                else:
+                    assert np.array_equal(gg[lo:hi], go[lo:hi]), "%s block %d region %d" % (w.name, b, off)
+    return cg, co
+
+
+# ------------------------------------------------------------------ small, full comparisons
+
+def test_vector_add(K, oracle_mod):
+    cg = full_parity(K, oracle_mod, W.vector_add())
+    assert int(cg["thread_instrs"].sum()) == 19264
+
+
+def test_f32_edge_operands(K, oracle_mod):
+    full_parity(K, oracle_mod, S.f32_ops(n=16384))
+
+
+@pytest.mark.parametrize("s", W.STRIDES)
+def test_strided_small(K, oracle_mod, s):
+    cg = full_parity(K, oracle_mod, W.strided_gather(s, n=1 << 16))
+    assert (cg["gld_sectors"] == min(32, 4 * s) + 4).all()
+
+
+@pytest.mark.parametrize("n_acc", [1, 2, 3, 8])
+def test_ffma_small(K, oracle_mod, n_acc):
+    full_parity(K, oracle_mod, W.ffma_probe(n_acc=n_acc, iters=40, grid=6, block=256, trace_cap=600))
+
+
+@pytest.mark.parametrize("s", list(range(1, 33)))
+def test_bank_small(K, oracle_mod, s):
+    cg = full_parity(K, oracle_mod, W.bank_probe(s, iters=12, grid=3, block=1024, trace_cap=64))
+    assert (cg["sh_degree_max"] == math.gcd(s, 32)).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_stress_small(K, oracle_mod, seed):
+    w = W.random_stress(prog_seed=seed, grid=48, block=256, gmem_bytes=1 << 24, trace_cap=2048)
+    full_parity(K, oracle_mod, w)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_control_flow_shapes(K, oracle_mod, seed):
+    rng = np.random.default_rng(seed)
+    n = 256
+    data = rng.choice([0, 1, 500, 1500, 2500, 2999], size=n).astype(np.uint32)
+    g = np.zeros(8 * n + 4096, np.uint8)
+    g[:4 * n] = data.view(np.uint8)
+    w = W.Workload(name="cfg%d" % seed, ptx=S.random_cfg_ptx(seed), grid=(2, 1, 1), block=(128, 1, 1),
+                   params=[("param_in", "u64", 0), ("param_out", "u64", 4 * n)], gmem=g, trace_cap=128)
+    full_parity(K, oracle_mod, w)
+
+
+def test_staircase_depth_63(K, oracle_mod):
+    g = np.zeros(4096, np.uint8)
+    w = W.Workload(name="staircase", ptx=S.staircase_ptx(31), grid=(2, 1, 1), block=(96, 1, 1),
+                   params=[("param_out", "u64", 0)], gmem=g, trace_cap=256)
+    cg = full_parity(K, oracle_mod, w)
+    assert cg["max_stack_depth"].max() == 63
+
+
+def test_analyser_vectors(K, oracle_mod):
+    rng = np.random.default_rng(17)
+    n = 256 * 8
+    base = rng.integers(0, 1 << 12, size=n // 32) * 4
+    kinds = np.arange(n // 32) % 6
+    ga, sa = [], []
+    for k, b0 in zip(kinds, base):
+        lanes = np.arange(32)
+        if k == 0:
+            g = b0 + 4 * lanes * int(rng.integers(0, 40))
+        elif k == 1:
+            g = rng.integers(0, 1 << 14, size=32) * 4
+        elif k == 2:
+            g = np.full(32, b0)
+        elif k == 3:
+            g = b0 + 4 * rng.permutation(32)
+        elif k == 4:
+            g = b0 + 2 * lanes  # misaligned lanes: faults, both end sectors counted
+        else:
+            g = np.where(rng.random(32) < 0.2, (1 << 17) + 64 * lanes, b0 + 4 * lanes)  # some out of range
+        ga.append(g)
+        sa.append((4 * int(rng.integers(0, 33)) * lanes + int(rng.integers(0, 4)) * 4) % 4096)
+    guard = (rng.random(n) < 0.8).astype(np.uint32)
+    w = S.addr_probe(np.concatenate(ga).astype(np.uint64), np.concatenate(sa).astype(np.uint32), guard, 1 << 16)
+    full_parity(K, oracle_mod, w)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_ragged_and_3d_shapes(K, oracle_mod):
+    ptx = S.random_cfg_ptx(3)
+    for grid, block in [((3, 2, 1), (100, 1, 1)), ((1, 1, 1), (33, 1, 1)), ((2, 1, 2), (8, 4, 3)),
+                        ((1, 1, 1), (1024, 1, 1)), ((5, 1, 1), (1, 1, 1))]:
+        nt = grid[0] * grid[1] * grid[2] * block[0] * block[1] * block[2]
+        rng = np.random.default_rng(nt)
+        g = np.zeros(8 * nt + 4096, np.uint8)
+        g[:4 * nt] = rng.choice([0, 1, 500, 1500, 2500], size=nt).astype(np.uint32).view(np.uint8)
+        w = W.Workload(name="shape%s%s" % (grid, block), ptx=ptx, grid=grid, block=block,
+                       params=[("param_in", "u64", 0), ("param_out", "u64", 4 * nt)], gmem=g, trace_cap=64)
+        full_parity(K, oracle_mod, w)
+
+
+def test_budget_trace_cap_and_latency_table(K, oracle_mod):
+    w = W.ffma_probe(n_acc=4, iters=12, grid=2, block=256, trace_cap=100)
+    full_parity(K, oracle_mod, w, max_warp_instrs=150)
+    full_parity(K, oracle_mod, w, trace_cap=0)
+    lat = oracle_mod.default_latency()
+    lat[2] = 7  # fp32
+    lat[7] = 333
+    full_parity(K, oracle_mod, w, latency=lat)
+
+
+def test_cycle_overflow(K, oracle_mod):
+    ptx = S.HEADER + """.visible .entry o(.param .u64 param_out)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<4>;
+    .reg .b64 %rd<2>;
+    ld.param.u64 %rd1, [param_out];
+    mov.u32 %r2, 0;
+$L__loop:
+    ld.global.u32 %r1, [%rd1];
+    add.s32 %r2, %r2, %r1;
+    setp.lt.u32 %p1, %r2, 1;
+    @%p1 bra $L__loop;
+    ret;
+}
+"""
+    w = W.Workload(name="overflow", ptx=ptx, grid=(1, 1, 1), block=(64, 1, 1), params=[("param_out", "u64", 0)],
+                   gmem=np.zeros(64, np.uint8), trace_cap=8)
+    lat = oracle_mod.default_latency()
+    lat[7] = 65535
+    cg = full_parity(K, oracle_mod, w, latency=lat)
+    assert (cg["status"] & K.ST_CYCLE_OVF).all()
+
+
+def test_barrier_in_divergent_region(K, oracle_mod):
+    ptx = S.HEADER + """.visible .entry b(.param .u64 param_out)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<3>;
+    mov.u32 %r1, %laneid;
+    setp.lt.u32 %p1, %r1, 8;
+    @%p1 bra $L__skip;
+    bar.sync 0;
+$L__skip:
+    ret;
+}
+"""
+    w = W.Workload(name="bardiv", ptx=ptx, grid=(1, 1, 1), block=(200, 1, 1), params=[("param_out", "u64", 0)],
+                   gmem=np.zeros(64, np.uint8), trace_cap=8)
+    cg = full_parity(K, oracle_mod, w)
+    assert (cg["status"] & K.ST_BARDIV).all()
+
+
+def test_runs_are_deterministic_and_rerunnable(K, oracle_mod):
+    w = W.random_stress(prog_seed=1, grid=16, block=256, gmem_bytes=1 << 24, trace_cap=256)
+    outs = gpu_run(K, w, runs=2)
+    for a, b in zip(outs[0], outs[1]):
+        if isinstance(a, np.ndarray):
+            assert np.array_equal(a, b)
+        else:
+            assert a == b
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+
+def test_vector_add_full_config(K, oracle_mod):
+    full_parity(K, oracle_mod, W.vector_add())
+
+
+@pytest.mark.parametrize("s", W.STRIDES)
+def test_strided_full_size(K, oracle_mod, s):
+    w = W.strided_gather(s)
+    blocks = [0, 1, 2047, 4095] + [int(x) for x in np.random.default_rng(s).integers(0, 4096, 4)]
+    n = w.meta["n"]
+    off_c = w.outputs["c"][0]
+    sampled_parity(K, oracle_mod, w, blocks, [(off_c, 4, 0)])
+
+
+@pytest.mark.parametrize("n_acc", [1, 8])
+def test_ffma_full_size(K, oracle_mod, n_acc):
+    w = W.ffma_probe(n_acc=n_acc)
+    cg, co = sampled_parity(K, oracle_mod, w, [0, 1023], [(w.outputs["out"][0], 4, 0)])
+    # 4096 iterations: 128 (dependent) or 35 (independent) cycles each, plus a fixed prologue/epilogue
+    per_iter = 128 if n_acc == 1 else 35
+    assert (cg["cycles"] > per_iter * 4096).all() and (cg["cycles"] < per_iter * 4096 + 2000).all()
+
+
+@pytest.mark.parametrize("s", [1, 2, 3, 8, 16, 31, 32])
+def test_bank_full_size(K, oracle_mod, s):
+    w = W.bank_probe(s)
+    cg, _ = sampled_parity(K, oracle_mod, w, [0, 255], [(w.outputs["out"][0], 4, 0)])
+    assert (cg["sh_degree_max"] == math.gcd(s, 32)).all()
+    assert (cg["sh_degree_sum"] == 2048 * math.gcd(s, 32)).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_stress_full_size(K, oracle_mod, seed):
+    w = W.random_stress(prog_seed=seed)
+    nt = w.n_blocks * w.threads_per_block
+    blocks = [0, 1, 32767, 65535] + [int(x) for x in np.random.default_rng(100 + seed).integers(0, 65536, 4)]
+    w1, w4 = w.outputs["w1"][0], w.outputs["w4"][0]
+    # W1 words j at w1 + 4 gtid + 4 j nt; W4 words at w4 + 16 gtid + 4 j
+    sampled_parity(K, oracle_mod, w, blocks, [(w1, 4, 4 * nt), (w4, 16, 0)])

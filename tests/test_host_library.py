@@ -1,0 +1,144 @@
+"""CPU-side tests of libkscope's host half: exports, parser, reconvergence table,
+layouts and error paths (no GPU needed; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from workloads import configs as W
+from workloads import small as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="session")
+def ks():
+    from analysis_ptxsimulator_amd import build, ks as K
+    build.build(force=False)
+    return K
+
+
+def test_library_exports_every_declared_symbol(ks):
+    with open(os.path.join(ROOT, "include", "ks.h")) as f:
+        header = f.read()
+    names = set(re.findall(r"^(?:ks_status|void|const char\*)\s+(ks_\w+)\s*\(", header, re.M))
+    assert len(names) >= 15
+    L = ctypes.CDLL(ks.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert names == set(ks._EXPORTS)
+
+
+def _all_programs():
+    progs = [W.VECTOR_ADD_PTX, W.STRIDED_PTX, W.ffma_probe_ptx(1), W.ffma_probe_ptx(8), W.bank_probe_ptx(),
+             S.F32_OPS_PTX, S.ADDR_PROBE_PTX, S.staircase_ptx(31), S.fma_chain_ptx(9, 3)]
+    from workloads.randprog import random_program
+    for seed in range(3):
+        progs.append(random_program(seed)[0])
+    for seed in range(20):
+        progs.append(S.random_cfg_ptx(seed))
+    return progs
+
+
+def test_program_shape_matches_oracle(ks, oracle_mod):
+    for ptx in _all_programs():
+        p = ks.ks_load_program(ptx)
+        info = ks.ks_program_info(p)
+        o = oracle_mod.program_info(ptx)
+        assert info["n_instrs"] == o["n_instrs"]
+        assert info["param_bytes"] == o["param_bytes"]
+        assert info["shared_bytes"] == o["shared_bytes"]
+        assert info["reg_slots"] == o["reg_words"]
+        assert info["n_preds"] == o["n_preds"]
+        for i, (name, off, size) in enumerate(oracle_mod.params(ptx)):
+            assert ks.ks_param_info(p, i) == (off, size, name)
+        ks.ks_program_free(p)
+
+
+def test_random_stress_uses_64_slots(ks):
+    from workloads.randprog import random_program
+    p = ks.ks_load_program(random_program(0)[0])
+    assert ks.ks_program_info(p)["reg_slots"] == 64
+    ks.ks_program_free(p)
+
+
+@pytest.mark.parametrize("seed", range(300))
+def test_reconvergence_table_matches_oracle(ks, oracle_mod, seed):
+    """Cooper-Harvey-Kennedy on basic blocks (library) versus post-dominator sets
+    by fixed point on instructions (oracle), loops included."""
+    ptx = S.random_cfg_ptx(5000 + seed, n_instr=10 + seed % 40, loops=(seed % 3 == 0))
+    p = ks.ks_load_program(ptx)
+    assert ks.ks_ipdom_table(p) == oracle_mod.ipdom_table(ptx)
+    ks.ks_program_free(p)
+
+
+def test_reconvergence_on_workloads(ks, oracle_mod):
+    for ptx in _all_programs():
+        p = ks.ks_load_program(ptx)
+        assert ks.ks_ipdom_table(p) == oracle_mod.ipdom_table(ptx)
+        ks.ks_program_free(p)
+
+
+BAD = [
+    ("add.f32 %f3, %f1, %f2;", "add.f32 %f3, %f1, %f9;", -1, "undeclared register %f9"),
+    ("add.f32 %f3, %f1, %f2;", "div.rn.f32 %f3, %f1, %f2;", -2, "unsupported instruction"),
+    ("@%p1 bra $L__exit;", "@%p1 bra $L__nowhere;", -1, "unknown label"),
+    ("mov.u32 %r2, %tid.x;", "mov.u32 %r2, 1.5;", -1, None),
+    ("add.f32 %f3, %f1, %f2;", "add.f32 %f3, %f1, 1;", -2, "0fXXXXXXXX"),
+    ("add.s64 %rd5, %rd1, %rd4;", "add.s64 %rd5, %rd1, %r4;", -1, "is 32-bit"),
+]
+
+
+@pytest.mark.parametrize("old,new,code,msg", BAD)
+def test_parse_errors(ks, old, new, code, msg):
+    ptx = W.VECTOR_ADD_PTX.replace(old, new)
+    assert ptx != W.VECTOR_ADD_PTX
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_load_program(ptx)
+    assert e.value.code == code
+    line = 1 + W.VECTOR_ADD_PTX.split(old)[0].count("\n")
+    if code == -1 or msg:
+        assert ("line %d:" % line) in e.value.msg
+    if msg:
+        assert msg in e.value.msg
+
+
+def test_layout_and_default_config(ks):
+    p = ks.ks_load_program(W.VECTOR_ADD_PTX)
+    cfg = ks.ks_default_config()
+    assert list(cfg.latency)[:14] == [4, 4, 4, 4, 4, 4, 4, 200, 23, 200, 23, 4, 20, 4]
+    cfg.max_grid = ks.ks_dim3(4, 1, 1)
+    cfg.max_block = ks.ks_dim3(256, 1, 1)
+    cfg.trace_cap = 32
+    lay = ks.ks_query_layout(p, cfg)
+    assert lay.warps_per_block == 8 and lay.n_warps == 32
+    assert lay.slot_bytes == 16 + 8 * 32 and lay.trace_bytes == 32 * lay.slot_bytes
+    assert lay.counters_bytes == 32 * 80
+    # oracle and library agree on the default latency table
+    ks.ks_program_free(p)
+
+
+def test_default_latency_matches_oracle(ks, oracle_mod):
+    assert list(ks.ks_default_config().latency) == oracle_mod.default_latency()
+
+
+def test_alloc_rejects_null_buffers(ks):
+    p = ks.ks_load_program(W.VECTOR_ADD_PTX)
+    cfg = ks.ks_default_config()
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_alloc_state(p, cfg, 0, 0, 0)
+    assert e.value.code == -3
+    ks.ks_program_free(p)
+
+
+def test_program_limits(ks):
+    too_many = S.HEADER + ".visible .entry k()\n{\n    .reg .b32 %r<65>;\n    mov.u32 %r64, 1;\n    ret;\n}\n"
+    p = ks.ks_load_program(too_many)
+    assert ks.ks_program_info(p)["reg_slots"] == 65
+    cfg = ks.ks_default_config()
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_alloc_state(p, cfg, 1, 1, 1)
+    assert e.value.code == -2 and "register slots" in e.value.msg
+    ks.ks_program_free(p)

@@ -90,6 +90,25 @@ def cpu_baseline(w, sample_blocks, threads):
             "warp_accesses_per_s": int((c["gld_n"].astype(np.uint64) + c["gst_n"] + c["sh_n"]).sum()) / dt}
 
 
+def copy_calibration(args, dev):
+    """A plain 1 GiB device-to-device copy: the achievable-bandwidth ceiling and the
+    reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"workload": "copy", "bytes_read_per_step": n, "bytes_written_per_step": n,
+                      "ms_per_step": dt * 1e3, "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,8 +129,10 @@ def main():
 
     from analysis_ptxsimulator_amd import ks
 
-    w = make_workload(args.workload)
     dev = torch.device("cuda:0")
+    if args.workload == "copy":
+        return copy_calibration(args, dev)
+    w = make_workload(args.workload)
     s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, device=dev)
     s.load_gmem(w.gmem)
     params = w.params_bytes

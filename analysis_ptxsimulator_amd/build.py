@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
          "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-command-line-argument"]
+         "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
 
 
 def build(force: bool = True, verbose: bool = False) -> str:

@@ -1179,6 +1179,14 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
     if (p->param_bytes) memcpy(a.params, params, p->param_bytes);
     uint64_t warps = nb * a.warps_per_block;
     if (warps > st->max_warps) raise(KS_E_INVALID_ARG, 0, "run needs more warps than the allocation");
+    {
+      const int variant = ks_choose_variant(p->reg_slots, a.threads_per_block);
+      const uint32_t wg = 64u * ((a.warps_per_block + 1u) / 2u);
+      const size_t need = ks_lds_bytes(variant, p->reg_slots, wg, p->shared_bytes);
+      if (need + 64 > ks_lds_limit())
+        raise(KS_E_UNSUPPORTED, 0, "block of %u threads needs %zu bytes of LDS (limit %zu)", a.threads_per_block, need,
+              ks_lds_limit() - 64);
+    }
     hipError_t e = ks_launch_interp(a, (uint32_t)nb, st->slots, (hipStream_t)stream);
     if (!hip_ok(e, "kernel launch")) return KS_E_HIP;
     st->last_warps = warps;

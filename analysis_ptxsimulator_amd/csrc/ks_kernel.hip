@@ -4,14 +4,19 @@
 //   * one workgroup = one simulated block; wave w runs simulated warps 2w
 //     (lanes 0-31) and 2w+1 (lanes 32-63), one GPU lane per simulated thread;
 //   * each wave-step executes ONE decoded instruction: the one at the smaller pc
-//     of the two warps (both warps run it when they share that pc), so the
-//     instruction fetch (s_load), decode, dispatch and operand slot indices are
-//     wave-uniform and live in SGPRs;
-//   * simulated registers live in LDS, structure-of-arrays [slot][thread], so a
-//     register read or write is one conflict-free ds_read/ds_write of 64 lanes;
+//     of the two warps (both warps run it when they share that pc), so fetch
+//     (s_load), decode, dispatch and register slot indices are wave-uniform;
+//   * simulated registers live in a register file of 32-bit slots per lane,
+//     either in physical VGPRs reserved for it (v96 upward, indexed in the
+//     VGPR index mode of s_set_gpr_idx_on: zero latency, exec-masked writes) or,
+//     for programs or blocks that do not fit, in LDS as [slot][thread];
 //   * per-warp control state (stack top, masks, cycle counters) is scalar; the
-//     divergence stack, the scoreboard and the counters live in VGPR lanes and
-//     are accessed with v_readlane / v_writelane;
+//     divergence stack, scoreboard, counters and a 32-record trace staging
+//     buffer live in VGPR lanes;
+//   * the analyser counts distinct sectors/lines of monotone addresses with a
+//     DPP prefix-max within each 32-lane half (any active mask) and the bank
+//     degree of affine shared accesses in closed form; other patterns take an
+//     exact ballot loop over distinct values;
 //   * simulated bar.sync maps onto epochs: each wave runs its two warps until
 //     both wait or finish, then the workgroup meets at a real barrier and the
 //     release cycle is an LDS max-reduction of the arrival cycles.
@@ -64,14 +69,78 @@ __device__ __forceinline__ uint32_t rl(uint32_t v, uint32_t l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
 }
 // Write the wave-uniform `val` into lane `l` of `old`.
-__device__ __forceinline__ uint32_t wl(uint32_t old, uint32_t val, uint32_t l) {
-  return __lane_id() == l ? val : old;
+__device__ __forceinline__ uint32_t wl(uint32_t old, uint32_t val, uint32_t l, uint32_t lane) {
+  return lane == l ? val : old;
 }
 __device__ __forceinline__ uint64_t rl64(uint64_t v, uint32_t l) {
   return (uint64_t)rl((uint32_t)v, l) | ((uint64_t)rl((uint32_t)(v >> 32), l) << 32);
 }
 __device__ __forceinline__ uint64_t ballot(bool c) { return __builtin_amdgcn_ballot_w64(c); }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------------------- register files
+//
+// RF = 0: LDS, [slot][thread of the workgroup].  RF = 32 / 64: physical VGPRs
+// v96 .. v96+RF-1, outside the compiler's allocation (the kernels are built with
+// amdgpu_num_vgpr(96)); slot s of a lane is VGPR v[96 + s] of that lane.
+template <int RF>
+struct RegFile;
+
+template <>
+struct RegFile<0> {
+  uint32_t* base;
+  uint32_t stride;
+  uint32_t tid;
+  __device__ __forceinline__ uint32_t get(uint32_t s) const { return base[s * stride + tid]; }
+  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const { base[s * stride + tid] = v; }
+};
+
+// VGPR index mode: between s_set_gpr_idx_on and s_set_gpr_idx_off the SRC0 (or
+// DST) VGPR of each VALU instruction is offset by the index (kept in M0).
+#define KS_RF_ASM_GET                                                                       \
+  __device__ __forceinline__ uint32_t get(uint32_t s) const {                               \
+    uint32_t r;                                                                             \
+    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\ts_set_gpr_idx_off" \
+                 : "=v"(r) : "s"(s) : "m0");                                               \
+    return r;                                                                               \
+  }                                                                                         \
+  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                       \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v96, %1\n\ts_set_gpr_idx_off"  \
+                 : : "s"(s), "v"(v) : "m0");                                               \
+  }
+
+#define KS_Z(i) "v_mov_b32 v" #i ", 0\n\t"
+#define KS_Z8(a, b, c, d, e, f, g, h) KS_Z(a) KS_Z(b) KS_Z(c) KS_Z(d) KS_Z(e) KS_Z(f) KS_Z(g) KS_Z(h)
+#define KS_C8(a, b, c, d, e, f, g, h) "v" #a, "v" #b, "v" #c, "v" #d, "v" #e, "v" #f, "v" #g, "v" #h
+
+template <>
+struct RegFile<32> {
+  KS_RF_ASM_GET
+  __device__ __forceinline__ static void zero() {
+    asm volatile(KS_Z8(96, 97, 98, 99, 100, 101, 102, 103) KS_Z8(104, 105, 106, 107, 108, 109, 110, 111)
+                     KS_Z8(112, 113, 114, 115, 116, 117, 118, 119) KS_Z8(120, 121, 122, 123, 124, 125, 126, 127)
+                 ::: KS_C8(96, 97, 98, 99, 100, 101, 102, 103), KS_C8(104, 105, 106, 107, 108, 109, 110, 111),
+                     KS_C8(112, 113, 114, 115, 116, 117, 118, 119), KS_C8(120, 121, 122, 123, 124, 125, 126, 127));
+  }
+};
+
+template <>
+struct RegFile<64> {
+  KS_RF_ASM_GET
+  __device__ __forceinline__ static void zero() {
+    asm volatile(KS_Z8(96, 97, 98, 99, 100, 101, 102, 103) KS_Z8(104, 105, 106, 107, 108, 109, 110, 111)
+                     KS_Z8(112, 113, 114, 115, 116, 117, 118, 119) KS_Z8(120, 121, 122, 123, 124, 125, 126, 127)
+                         KS_Z8(128, 129, 130, 131, 132, 133, 134, 135) KS_Z8(136, 137, 138, 139, 140, 141, 142, 143)
+                             KS_Z8(144, 145, 146, 147, 148, 149, 150, 151) KS_Z8(152, 153, 154, 155, 156, 157, 158, 159)
+                 ::: KS_C8(96, 97, 98, 99, 100, 101, 102, 103), KS_C8(104, 105, 106, 107, 108, 109, 110, 111),
+                     KS_C8(112, 113, 114, 115, 116, 117, 118, 119), KS_C8(120, 121, 122, 123, 124, 125, 126, 127),
+                     KS_C8(128, 129, 130, 131, 132, 133, 134, 135), KS_C8(136, 137, 138, 139, 140, 141, 142, 143),
+                     KS_C8(144, 145, 146, 147, 148, 149, 150, 151), KS_C8(152, 153, 154, 155, 156, 157, 158, 159));
+  }
+};
+
+// ---------------------------------------------------------------------------- divergence stack
 
 __device__ __forceinline__ void hs_pop(Half& H, uint32_t spc, uint32_t sm, uint32_t sr) {
   H.sp -= 1;
@@ -83,22 +152,22 @@ __device__ __forceinline__ void hs_pop(Half& H, uint32_t spc, uint32_t sm, uint3
 }
 
 __device__ __forceinline__ void hs_push(Half& H, uint32_t& spc, uint32_t& sm, uint32_t& sr, uint32_t pc, uint32_t mask,
-                                        uint32_t rpc) {
-  spc = wl(spc, H.pc, H.sp - 1);
-  sm = wl(sm, H.mask, H.sp - 1);
-  sr = wl(sr, H.rpc, H.sp - 1);
+                                        uint32_t rpc, uint32_t lane) {
+  spc = wl(spc, H.pc, H.sp - 1, lane);
+  sm = wl(sm, H.mask, H.sp - 1, lane);
+  sr = wl(sr, H.rpc, H.sp - 1, lane);
   H.pc = pc;
   H.mask = mask;
   H.rpc = rpc;
   H.sp += 1;
-  H.max_depth = H.sp > H.max_depth ? H.sp : H.max_depth;
+  H.max_depth = umax(H.max_depth, H.sp);
 }
 
 // Pop finished or reconverged entries; lanes that ran off the end exit at no cost.
 __device__ __forceinline__ void hs_resolve(Half& H, uint32_t spc, uint32_t sm, uint32_t sr, uint32_t n, uint32_t budget) {
   if (H.state != H_RUN) return;
   while (H.sp) {
-    uint32_t m = H.mask & ~H.exited;
+    const uint32_t m = H.mask & ~H.exited;
     if (m == 0 || H.pc == H.rpc) {
       hs_pop(H, spc, sm, sr);
       continue;
@@ -120,25 +189,43 @@ __device__ __forceinline__ void hs_resolve(Half& H, uint32_t spc, uint32_t sm, u
   }
 }
 
+__device__ __forceinline__ void half_init(Half& H, uint32_t w, uint32_t W, uint32_t T) {
+  const bool exists = w < W;
+  const uint32_t live = T > w * 32u ? (T - w * 32u > 32u ? 32u : T - w * 32u) : 0u;
+  H.init_mask = live >= 32u ? 0xFFFFFFFFu : ((1u << live) - 1u);
+  H.pc = 0;
+  H.mask = H.init_mask;
+  H.rpc = RPC_EXIT;
+  H.sp = exists ? 1u : 0u;
+  H.exited = 0;
+  H.next = 0;
+  H.bar_ready = 0;
+  H.arrival = 0;
+  H.state = exists ? H_RUN : H_DONE;
+  H.status = 0;
+  H.warp_instrs = 0;
+  H.max_depth = 1;
+  H.thread_instrs = 0;
+}
+
+// ---------------------------------------------------------------------------- scoreboard
+
 __device__ __forceinline__ uint32_t sb_get(uint32_t lo, uint32_t hi, uint32_t j) {
   return j < 64 ? rl(lo, j) : rl(hi, j - 64);
 }
-__device__ __forceinline__ void sb_set(uint32_t& lo, uint32_t& hi, uint32_t j, uint32_t v) {
-  if (j < 64) lo = wl(lo, v, j);
-  else hi = wl(hi, v, j - 64);
+__device__ __forceinline__ void sb_set(uint32_t& lo, uint32_t& hi, uint32_t j, uint32_t v, uint32_t lane) {
+  if (j < 64) lo = wl(lo, v, j, lane);
+  else hi = wl(hi, v, j - 64, lane);
 }
 
 // Issue cycle: the later of previous issue + 1, the barrier release and the ready
 // cycle of every register source (sb holds four scoreboard indices, 0xFF = none).
 __device__ __forceinline__ uint32_t issue_cycle(const Half& H, uint32_t lo, uint32_t hi, uint32_t sb) {
-  uint32_t t = H.next > H.bar_ready ? H.next : H.bar_ready;
+  uint32_t t = umax(H.next, H.bar_ready);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint32_t j = (sb >> (8 * k)) & 0xFF;
-    if (j != 0xFF) {
-      uint32_t r = sb_get(lo, hi, j);
-      t = r > t ? r : t;
-    }
+    const uint32_t j = (sb >> (8 * k)) & 0xFF;
+    if (j != 0xFF) t = umax(t, sb_get(lo, hi, j));
   }
   return t;
 }
@@ -150,13 +237,30 @@ __device__ __forceinline__ uint32_t cnt_max(uint32_t cnt, uint32_t lane, uint32_
   return (lane == idx && v > cnt) ? v : cnt;
 }
 
+// ---------------------------------------------------------------------------- analyser
+
+// Inclusive prefix maximum within each 32-lane half (rows 0-1 and rows 2-3).
+__device__ __forceinline__ uint32_t half_prefix_max(uint32_t x) {
+  x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true));  // row_shr:1
+  x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true));  // row_shr:2
+  x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true));  // row_shr:4
+  x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true));  // row_shr:8
+  x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false)); // row_bcast:15 -> rows 1, 3
+  return x;
+}
+// Value of the previous lane in the same half (0 for the first lane of each half).
+__device__ __forceinline__ uint32_t prev_in_half(uint32_t x, uint32_t lane) {
+  const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x138, 0xF, 0xF, true);  // wave_shr:1
+  return lane == 32u ? 0u : p;
+}
+
 // Number of distinct values in {k1[l], k2[l] : l in lanes}.  Full exec required.
 __device__ uint32_t distinct2(uint64_t k1, uint64_t k2, uint64_t lanes) {
   uint64_t rem1 = lanes;
   uint64_t rem2 = lanes & ballot(k2 != k1);
   uint32_t n = 0;
   while (rem1 | rem2) {
-    uint64_t key = rem1 ? rl64(k1, (uint32_t)__builtin_ctzll(rem1)) : rl64(k2, (uint32_t)__builtin_ctzll(rem2));
+    const uint64_t key = rem1 ? rl64(k1, (uint32_t)__builtin_ctzll(rem1)) : rl64(k2, (uint32_t)__builtin_ctzll(rem2));
     rem1 &= ~ballot(k1 == key);
     rem2 &= ~ballot(k2 == key);
     ++n;
@@ -188,9 +292,10 @@ __device__ __forceinline__ uint32_t canon_bits(float r) {
   return __builtin_isnan(r) ? 0x7FFFFFFFu : __float_as_uint(r);
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------- the interpreter
 
-__global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
+template <int RF>
+__device__ __forceinline__ void interp(const KsArgs& a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ uint32_t ep_max[3], ep_alive[3];
 
@@ -205,11 +310,20 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
   const uint32_t T = a.threads_per_block;
   const uint32_t n_instr = a.n_instrs;
 
-  uint32_t* rf = lds;                                          // [slot][WG]
-  uint8_t* win = reinterpret_cast<uint8_t*>(lds + a.rf_slots * WG);  // simulated shared window
-
-  {  // zero the register file and the shared window
-    const uint32_t words = a.rf_slots * WG + ((a.shared_bytes + 3u) >> 2);
+  RegFile<RF> R;
+  uint8_t* win;
+  {
+    uint32_t rf_words = 0;
+    if constexpr (RF == 0) {
+      R.base = lds;
+      R.stride = WG;
+      R.tid = tid;
+      rf_words = a.rf_slots * WG;
+    } else {
+      RegFile<RF>::zero();
+    }
+    win = reinterpret_cast<uint8_t*>(lds + rf_words);
+    const uint32_t words = rf_words + ((a.shared_bytes + 3u) >> 2);
     for (uint32_t i = tid; i < words; i += WG) lds[i] = 0;
     if (tid < 3) {
       ep_max[tid] = 0;
@@ -224,39 +338,20 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
   const uint32_t tid_x = t_lin % bx, tid_y = (t_lin / bx) % by, tid_z = t_lin / (bx * by);
   const uint32_t gx = a.grid[0], gy = a.grid[1];
   const uint32_t cta_x = blk % gx, cta_y = (blk / gx) % gy, cta_z = blk / (gx * gy);
+  const bool small_gmem = a.gmem_bytes <= (1ull << 37);  // sector ids of valid accesses fit 32 bits
 
   Half H0, H1;
-  {
-    Half* hs[2] = {&H0, &H1};
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      Half& H = *hs[hh];
-      const uint32_t w = 2u * wave + (uint32_t)hh;
-      const bool exists = w < W;
-      const uint32_t live = T > w * 32u ? (T - w * 32u > 32u ? 32u : T - w * 32u) : 0u;
-      H.init_mask = live >= 32u ? 0xFFFFFFFFu : ((1u << live) - 1u);
-      H.pc = 0;
-      H.mask = H.init_mask;
-      H.rpc = RPC_EXIT;
-      H.sp = exists ? 1u : 0u;
-      H.exited = 0;
-      H.next = 0;
-      H.bar_ready = 0;
-      H.arrival = 0;
-      H.state = exists ? H_RUN : H_DONE;
-      H.status = 0;
-      H.warp_instrs = 0;
-      H.max_depth = 1;
-      H.thread_instrs = 0;
-    }
-  }
+  half_init(H0, 2u * wave, W, T);
+  half_init(H1, 2u * wave + 1u, W, T);
   uint32_t stk_pc0 = 0, stk_m0 = 0, stk_r0 = 0, stk_pc1 = 0, stk_m1 = 0, stk_r1 = 0;
   uint32_t sb_lo0 = 0, sb_hi0 = 0, sb_lo1 = 0, sb_hi1 = 0;
   uint32_t cnt = 0;    // counter d of half h in lane 32 h + d
   uint32_t pbits = 0;  // predicate p of this lane's thread in bit p
+  uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of half h at lane 32 h + k % 32
 
   const uint32_t cap = a.trace_cap;
   const uint64_t gw0 = (uint64_t)blk * W + 2u * wave;  // global warp id of half 0
+  uint8_t* const slot_base = a.trace + (gw0 + hl) * a.slot_bytes + 16u;  // this lane's warp's records
 
   uint32_t epoch = 0;
   while (true) {
@@ -266,16 +361,14 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
       hs_resolve(H1, stk_pc1, stk_m1, stk_r1, n_instr, a.max_warp_instrs);
       const bool r0 = H0.state == H_RUN, r1 = H1.state == H_RUN;
       if (!r0 && !r1) break;
-      const uint32_t pc = (r0 && r1) ? (H0.pc < H1.pc ? H0.pc : H1.pc) : (r0 ? H0.pc : H1.pc);
+      const uint32_t pc = uni((r0 && r1) ? (H0.pc < H1.pc ? H0.pc : H1.pc) : (r0 ? H0.pc : H1.pc));
       bool go0 = r0 && H0.pc == pc, go1 = r1 && H1.pc == pc;
 
       const cu32p I = (cu32p)(uintptr_t)(a.prog + pc);
-      const uint32_t w0 = I[0], w1 = I[1], wsb = I[2], w3 = I[3], w4 = I[4], w5 = I[5];
+      const uint32_t w0 = I[0], w1 = I[1], wsb = I[2], w3 = I[3], w4 = I[4];
       const uint32_t op = w0 & 0xFFu, flags = (w0 >> 8) & 0xFFu, dst = (w0 >> 16) & 0xFFu, guard = w0 >> 24;
       const uint32_t kinds = w1 >> 24;
       const uint32_t sb_dst = w3 & 0xFFu, cmp = (w3 >> 8) & 0xFFu, lat = w3 >> 16;
-      const uint32_t target = w4 & 0xFFFFu, rpc_raw = w4 >> 16;
-      const uint32_t rpc = rpc_raw == KS_RPC_EXIT ? RPC_EXIT : rpc_raw;
 
       uint32_t iss0 = 0, iss1 = 0;
       if (go0) {
@@ -298,14 +391,25 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
       const uint32_t m0 = go0 ? (H0.mask & ~H0.exited) : 0u;
       const uint32_t m1 = go1 ? (H1.mask & ~H1.exited) : 0u;
 
-      // trace records, one lane per warp
+      // trace: stage the record in this warp's lane k % 32; write 32 records at once
       {
         const bool rec0 = go0 && H0.warp_instrs < cap, rec1 = go1 && H1.warp_instrs < cap;
-        if ((lane == 0 && rec0) || (lane == 32 && rec1)) {
-          const uint32_t wi = hl ? H1.warp_instrs : H0.warp_instrs;
-          const uint32_t cyc = hl ? iss1 : iss0;
-          uint8_t* p = a.trace + (gw0 + hl) * a.slot_bytes + 16u + 8ull * wi;
-          *reinterpret_cast<uint2*>(p) = make_uint2(cyc, pc);
+        if (rec0) {
+          const uint32_t li = H0.warp_instrs & 31u;
+          tr_c = wl(tr_c, iss0, li, lane);
+          tr_p = wl(tr_p, pc, li, lane);
+        }
+        if (rec1) {
+          const uint32_t li = 32u + (H1.warp_instrs & 31u);
+          tr_c = wl(tr_c, iss1, li, lane);
+          tr_p = wl(tr_p, pc, li, lane);
+        }
+        const bool fl0 = rec0 && ((H0.warp_instrs & 31u) == 31u || H0.warp_instrs + 1 == cap);
+        const bool fl1 = rec1 && ((H1.warp_instrs & 31u) == 31u || H1.warp_instrs + 1 == cap);
+        if (fl0 || fl1) {
+          const uint32_t k = hl ? H1.warp_instrs : H0.warp_instrs;  // index of the chunk's last record
+          if ((hl ? fl1 : fl0) && sl <= (k & 31u))
+            *reinterpret_cast<uint2*>(slot_base + 8ull * ((k & ~31u) + sl)) = make_uint2(tr_c, tr_p);
         }
       }
       if (go0) {
@@ -351,12 +455,12 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
             }
           };
           auto rd32 = [&](uint32_t kind, uint32_t s, uint32_t imm) -> uint32_t {
-            if (kind == KK_REG) return rf[s * WG + tid];
+            if (kind == KK_REG) return R.get(s);
             if (kind == KK_IMM) return imm;
             return special(s);
           };
           auto rd64 = [&](uint32_t kind, uint32_t s, uint32_t imm_lo, uint32_t imm_hi) -> uint64_t {
-            if (kind == KK_REG) return (uint64_t)rf[s * WG + tid] | ((uint64_t)rf[(s + 1) * WG + tid] << 32);
+            if (kind == KK_REG) return (uint64_t)R.get(s) | ((uint64_t)R.get(s + 1) << 32);
             return (uint64_t)imm_lo | ((uint64_t)imm_hi << 32);
           };
           uint32_t rlo = 0, rhi = 0;
@@ -427,8 +531,7 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
                 }
               } else if (op == KO_SETP_S32 || op == KO_SETP_U32) {
                 const uint32_t x = rd32(k0, s0, I[6]), y = rd32(k1, s1, I[8]);
-                const bool sg = op == KO_SETP_S32;
-                const bool lt = sg ? (int32_t)x < (int32_t)y : x < y;
+                const bool lt = op == KO_SETP_S32 ? (int32_t)x < (int32_t)y : x < y;
                 switch (cmp) {
                   case KC_EQ: c = x == y; break;
                   case KC_NE: c = x != y; break;
@@ -439,8 +542,7 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
                 }
               } else {
                 const uint64_t x = rd64(k0, s0, I[6], I[7]), y = rd64(k1, s1, I[8], I[9]);
-                const bool sg = op == KO_SETP_S64;
-                const bool lt = sg ? (int64_t)x < (int64_t)y : x < y;
+                const bool lt = op == KO_SETP_S64 ? (int64_t)x < (int64_t)y : x < y;
                 switch (cmp) {
                   case KC_EQ: c = x == y; break;
                   case KC_NE: c = x != y; break;
@@ -477,18 +579,18 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
             }
           }
           if (wr) {
-            rf[dst * WG + tid] = rlo;
-            if (wide) rf[(dst + 1) * WG + tid] = rhi;
+            R.put(dst, rlo);
+            if (wide) R.put(dst + 1, rhi);
           }
         }
       } else if (op <= KO_LDP64) {
         // parameter load: uniform value from the launch arguments
-        const uint32_t aux = w5 & 0xFFFFu;
+        const uint32_t aux = I[5] & 0xFFFFu;
         const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + aux);
         const uint32_t hi = op == KO_LDP64 ? *reinterpret_cast<const uint32_t*>(a.params + aux + 4) : 0u;
         if (on) {
-          rf[dst * WG + tid] = lo;
-          if (op == KO_LDP64) rf[(dst + 1) * WG + tid] = hi;
+          R.put(dst, lo);
+          if (op == KO_LDP64) R.put(dst + 1, hi);
         }
       } else if (op <= KO_STS64) {
         const bool is_global = op <= KO_STG64;
@@ -502,8 +604,8 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
         uint64_t A = 0;
         bool ok = false;
         if (on) {
-          uint64_t base = rf[s0 * WG + tid];
-          if (addr_w == 64u) base |= (uint64_t)rf[(s0 + 1) * WG + tid] << 32;
+          uint64_t base = R.get(s0);
+          if (addr_w == 64u) base |= (uint64_t)R.get(s0 + 1) << 32;
           A = base + off;
           ok = (A & (S - 1u)) == 0 && A <= size && size - A >= S;
           if (is_load) {
@@ -522,23 +624,23 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
                 if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
               }
             }
-            rf[dst * WG + tid] = lo;
-            if (w64) rf[(dst + 1) * WG + tid] = hi;
+            R.put(dst, lo);
+            if (w64) R.put(dst + 1, hi);
           } else if (ok) {
-            const uint32_t lo = rf[s1 * WG + tid];
+            const uint32_t lo = R.get(s1);
             if (is_global) {
               if (w64) {
-                *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, rf[(s1 + 1) * WG + tid]);
+                *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, R.get(s1 + 1));
               } else {
                 *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
               }
             } else {
               *reinterpret_cast<uint32_t*>(win + A) = lo;
-              if (w64) *reinterpret_cast<uint32_t*>(win + A + 4) = rf[(s1 + 1) * WG + tid];
+              if (w64) *reinterpret_cast<uint32_t*>(win + A + 4) = R.get(s1 + 1);
             }
           }
         }
-        // analysis and fault counting (full exec)
+        // fault counting and analysis (full exec)
         const uint64_t faults = ballot(on && !ok);
         const uint32_t f0 = (uint32_t)__builtin_popcountll(faults & 0xFFFFFFFFull);
         const uint32_t f1 = (uint32_t)__builtin_popcountll(faults >> 32);
@@ -551,44 +653,93 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
           cnt = cnt_add(cnt, lane, 32 + C_FAULT, f1);
         }
         if (is_global) {
-          const uint64_t last = A + (S - 1u);
+          uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;
+          bool slow0 = g0 != 0, slow1 = g1 != 0;
+          if (!faults && small_gmem) {
+            // monotone fast path: prefix max of sector ids over the active lanes of each half
+            const uint32_t s = on ? (uint32_t)(A >> 5) : 0u;
+            const uint32_t prev = prev_in_half(half_prefix_max(s), lane);
+            const uint64_t nonmono = ballot(on && s < prev);
+            const uint64_t news = ballot(on && s != prev);
+            const uint64_t newl = ballot(on && (s >> 2) != (prev >> 2));
+            if (g0 && !(uint32_t)nonmono) {
+              const uint32_t first = g0 & (0u - g0);
+              sec0 = (uint32_t)__builtin_popcount((uint32_t)news | first);
+              lin0 = (uint32_t)__builtin_popcount((uint32_t)newl | first);
+              slow0 = false;
+            }
+            if (g1 && !(uint32_t)(nonmono >> 32)) {
+              const uint32_t first = g1 & (0u - g1);
+              sec1 = (uint32_t)__builtin_popcount((uint32_t)(news >> 32) | first);
+              lin1 = (uint32_t)__builtin_popcount((uint32_t)(newl >> 32) | first);
+              slow1 = false;
+            }
+          }
+          if (slow0 || slow1) {
+            const uint64_t last = A + (S - 1u);
+            if (slow0) {
+              sec0 = distinct2(A >> 5, last >> 5, (uint64_t)g0);
+              lin0 = distinct2(A >> 7, last >> 7, (uint64_t)g0);
+            }
+            if (slow1) {
+              sec1 = distinct2(A >> 5, last >> 5, (uint64_t)g1 << 32);
+              lin1 = distinct2(A >> 7, last >> 7, (uint64_t)g1 << 32);
+            }
+          }
           const uint32_t cn = is_load ? C_GLD_N : C_GST_N;
           if (g0) {
-            const uint32_t sec = distinct2(A >> 5, last >> 5, (uint64_t)g0);
-            const uint32_t lin = distinct2(A >> 7, last >> 7, (uint64_t)g0);
             cnt = cnt_add(cnt, lane, cn, 1);
-            cnt = cnt_add(cnt, lane, cn + 1, sec);
-            cnt = cnt_add(cnt, lane, cn + 2, lin);
+            cnt = cnt_add(cnt, lane, cn + 1, sec0);
+            cnt = cnt_add(cnt, lane, cn + 2, lin0);
           }
           if (g1) {
-            const uint32_t sec = distinct2(A >> 5, last >> 5, (uint64_t)g1 << 32);
-            const uint32_t lin = distinct2(A >> 7, last >> 7, (uint64_t)g1 << 32);
             cnt = cnt_add(cnt, lane, 32 + cn, 1);
-            cnt = cnt_add(cnt, lane, 32 + cn + 1, sec);
-            cnt = cnt_add(cnt, lane, 32 + cn + 2, lin);
+            cnt = cnt_add(cnt, lane, 32 + cn + 1, sec1);
+            cnt = cnt_add(cnt, lane, 32 + cn + 2, lin1);
           }
         } else {
+          uint32_t d0 = 1, d1 = 1;
+          bool slow0 = g0 != 0, slow1 = g1 != 0;
+          if (!faults) {
+            // affine fast path for full halves: lanes at A0 + l * d
+            const uint32_t a32 = (uint32_t)A;
+            const uint32_t diff = a32 - prev_in_half(a32, lane);
+            const uint32_t dA = rl(diff, 1), dB = rl(diff, 33);
+            const uint64_t same = ballot(diff == (hl ? dB : dA));
+            if (g0 == 0xFFFFFFFFu && ((uint32_t)same | 1u) == 0xFFFFFFFFu && (dA & 3u) == 0) {
+              const uint32_t ws = (dA >> 2) & 31u;
+              d0 = dA == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
+              slow0 = false;
+            }
+            if (g1 == 0xFFFFFFFFu && ((uint32_t)(same >> 32) | 1u) == 0xFFFFFFFFu && (dB & 3u) == 0) {
+              const uint32_t ws = (dB >> 2) & 31u;
+              d1 = dB == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
+              slow1 = false;
+            }
+          }
+          if (slow0) d0 = bank_degree(A, (uint64_t)g0);
+          if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
           if (g0) {
-            const uint32_t d = bank_degree(A, (uint64_t)g0);
             cnt = cnt_add(cnt, lane, C_SH_N, 1);
-            cnt = cnt_add(cnt, lane, C_SH_SUM, d);
-            cnt = cnt_max(cnt, lane, C_SH_MAX, d);
+            cnt = cnt_add(cnt, lane, C_SH_SUM, d0);
+            cnt = cnt_max(cnt, lane, C_SH_MAX, d0);
           }
           if (g1) {
-            const uint32_t d = bank_degree(A, (uint64_t)g1 << 32);
             cnt = cnt_add(cnt, lane, 32 + C_SH_N, 1);
-            cnt = cnt_add(cnt, lane, 32 + C_SH_SUM, d);
-            cnt = cnt_max(cnt, lane, 32 + C_SH_MAX, d);
+            cnt = cnt_add(cnt, lane, 32 + C_SH_SUM, d1);
+            cnt = cnt_max(cnt, lane, 32 + C_SH_MAX, d1);
           }
         }
       }
 
       // ---------------------------------------------------------------- scoreboard and control
       if (sb_dst != 0xFFu) {
-        if (go0) sb_set(sb_lo0, sb_hi0, sb_dst, iss0 + lat);
-        if (go1) sb_set(sb_lo1, sb_hi1, sb_dst, iss1 + lat);
+        if (go0) sb_set(sb_lo0, sb_hi0, sb_dst, iss0 + lat, lane);
+        if (go1) sb_set(sb_lo1, sb_hi1, sb_dst, iss1 + lat, lane);
       }
       if (op == KO_BRA) {
+        const uint32_t target = w4 & 0xFFFFu, rpc_raw = w4 >> 16;
+        const uint32_t rpc = rpc_raw == KS_RPC_EXIT ? RPC_EXIT : rpc_raw;
         if (go0) {
           const uint32_t nt = m0 & ~g0;
           if (nt == 0) {
@@ -598,8 +749,8 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
           } else {
             H0.pc = rpc;
             cnt = cnt_add(cnt, lane, C_DIV, 1);
-            if (target != rpc) hs_push(H0, stk_pc0, stk_m0, stk_r0, target, g0, rpc);
-            if (pc + 1 != rpc) hs_push(H0, stk_pc0, stk_m0, stk_r0, pc + 1, nt, rpc);
+            if (target != rpc) hs_push(H0, stk_pc0, stk_m0, stk_r0, target, g0, rpc, lane);
+            if (pc + 1 != rpc) hs_push(H0, stk_pc0, stk_m0, stk_r0, pc + 1, nt, rpc, lane);
           }
         }
         if (go1) {
@@ -611,8 +762,8 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
           } else {
             H1.pc = rpc;
             cnt = cnt_add(cnt, lane, 32 + C_DIV, 1);
-            if (target != rpc) hs_push(H1, stk_pc1, stk_m1, stk_r1, target, g1, rpc);
-            if (pc + 1 != rpc) hs_push(H1, stk_pc1, stk_m1, stk_r1, pc + 1, nt, rpc);
+            if (target != rpc) hs_push(H1, stk_pc1, stk_m1, stk_r1, target, g1, rpc, lane);
+            if (pc + 1 != rpc) hs_push(H1, stk_pc1, stk_m1, stk_r1, pc + 1, nt, rpc, lane);
           }
         }
       } else if (op == KO_RET) {
@@ -675,26 +826,33 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
     ++epoch;
   }
 
-  // -------------------------------------------------------------------- counters and trace headers
+  // -------------------------------------------------------------------- counters, trace tail, headers
   {
-    const Half& M = hl ? H1 : H0;
     const uint32_t w = 2u * wave + hl;
     if (w < W) {
-      const uint32_t cycles = M.next;
-      const uint32_t written = M.warp_instrs < cap ? M.warp_instrs : cap;
-      const uint32_t dropped = M.warp_instrs - written;
-      const uint32_t status = M.status | (dropped ? KS_ST_TRACE_DROP : 0u);
+      const uint32_t m_next = hl ? H1.next : H0.next;
+      const uint32_t m_wi = hl ? H1.warp_instrs : H0.warp_instrs;
+      const uint32_t m_status = hl ? H1.status : H0.status;
+      const uint32_t m_depth = hl ? H1.max_depth : H0.max_depth;
+      const uint64_t m_ti = hl ? H1.thread_instrs : H0.thread_instrs;
+      const uint32_t cycles = m_next;
+      const uint32_t written = m_wi < cap ? m_wi : cap;
+      const uint32_t dropped = m_wi - written;
+      const uint32_t status = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);
       const uint64_t gw = gw0 + hl;
+      // staged records of a last, partly filled chunk (a full chunk was written when it filled)
+      if (sl < (written & 31u))
+        *reinterpret_cast<uint2*>(slot_base + 8ull * ((written & ~31u) + sl)) = make_uint2(tr_c, tr_p);
       if (sl < 20) {
         uint32_t v;
         switch (sl) {
-          case C_TI_LO: v = (uint32_t)M.thread_instrs; break;
-          case C_TI_HI: v = (uint32_t)(M.thread_instrs >> 32); break;
+          case C_TI_LO: v = (uint32_t)m_ti; break;
+          case C_TI_HI: v = (uint32_t)(m_ti >> 32); break;
           case C_STATUS: v = status; break;
           case C_CYCLES: v = cycles; break;
-          case C_WARP_INSTRS: v = M.warp_instrs; break;
-          case C_STALL: v = cycles - M.warp_instrs; break;
-          case C_MAXDEPTH: v = M.max_depth; break;
+          case C_WARP_INSTRS: v = m_wi; break;
+          case C_STALL: v = cycles - m_wi; break;
+          case C_MAXDEPTH: v = m_depth; break;
           case C_RES: v = 0; break;
           default: v = cnt; break;
         }
@@ -716,13 +874,27 @@ __global__ void __launch_bounds__(1024) ks_interp_kernel(const KsArgs a) {
   }
 }
 
+}  // namespace
+
+// Register file in LDS: any slot count that fits, blocks up to 1024 threads.
+__global__ void __launch_bounds__(1024) ks_interp_lds(const KsArgs a) { interp<0>(a); }
+
+// Register file in 32 reserved VGPRs (v96..v127): 128 VGPRs, blocks up to 1024 threads.
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(96))) ks_interp_v32(const KsArgs a) {
+  interp<32>(a);
+}
+
+// Register file in 64 reserved VGPRs (v96..v159): 160 VGPRs, blocks up to 768 threads.
+__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(96))) ks_interp_v64(const KsArgs a) {
+  interp<64>(a);
+}
+
 __global__ void ks_zero_word(uint32_t* out) { *out = 0; }
 
 __global__ void ks_status_or_kernel(const uint8_t* counters, uint64_t n, uint32_t* out) {
   uint32_t acc = 0;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
     acc |= reinterpret_cast<const uint32_t*>(counters + i * 80u)[C_STATUS];
-  // wave-level OR, then one atomic per wave
   for (int o = 32; o > 0; o >>= 1) acc |= (uint32_t)__shfl_xor((int)acc, o, 64);
   if ((threadIdx.x & 63u) == 0 && acc) atomicOr(out, acc);
 }
@@ -734,20 +906,37 @@ size_t ks_lds_limit() {
   return (size_t)v;
 }
 
+int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
+  const uint32_t waves = ((block_threads + 31u) / 32u + 1u) / 2u;
+  if (slots <= 32) return 32;
+  if (slots <= 64 && waves <= 12) return 64;
+  return 0;
+}
+
+size_t ks_lds_bytes(int variant, uint32_t slots, uint32_t wg, uint32_t shared_bytes) {
+  const size_t rf = variant == 0 ? (size_t)slots * wg * 4u : 0u;
+  return rf + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
+}
+
 hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, hipStream_t s) {
-  (void)slots;
   const uint32_t waves = (a.warps_per_block + 1u) / 2u;
   const uint32_t wg = 64u * waves;
-  const size_t lds = (size_t)a.rf_slots * wg * 4u + (((size_t)a.shared_bytes + 15u) & ~(size_t)15u);
+  const int variant = ks_choose_variant(slots, a.threads_per_block);
+  const size_t lds = ks_lds_bytes(variant, slots, wg, a.shared_bytes);
   if (lds + 64 > ks_lds_limit()) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)ks_interp_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(ks_lds_limit() - 64));
+  const void* fn = variant == 32 ? (const void*)ks_interp_v32
+                   : variant == 64 ? (const void*)ks_interp_v64
+                                   : (const void*)ks_interp_lds;
+  static bool attr_set[3] = {false, false, false};
+  const int vi = variant == 0 ? 0 : (variant == 32 ? 1 : 2);
+  if (!attr_set[vi]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(ks_lds_limit() - 64));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[vi] = true;
   }
-  hipLaunchKernelGGL(ks_interp_kernel, dim3(n_blocks), dim3(wg), lds, s, a);
+  if (variant == 32) hipLaunchKernelGGL(ks_interp_v32, dim3(n_blocks), dim3(wg), lds, s, a);
+  else if (variant == 64) hipLaunchKernelGGL(ks_interp_v64, dim3(n_blocks), dim3(wg), lds, s, a);
+  else hipLaunchKernelGGL(ks_interp_lds, dim3(n_blocks), dim3(wg), lds, s, a);
   return hipGetLastError();
 }
 

@@ -13,3 +13,10 @@ hipError_t ks_launch_status_or(const void* counters, uint64_t n_warps, uint32_t*
 
 // Largest dynamic LDS a workgroup of the interpreter may use on the current device.
 size_t ks_lds_limit();
+
+// Register-file variant for a program and block size: 32 or 64 (reserved VGPRs)
+// or 0 (LDS).
+int ks_choose_variant(uint32_t slots, uint32_t block_threads);
+
+// Dynamic LDS bytes of one workgroup of `wg` lanes for that variant.
+size_t ks_lds_bytes(int variant, uint32_t slots, uint32_t wg, uint32_t shared_bytes);

@@ -1106,6 +1106,9 @@ ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem
     for (size_t i = 0; i < p->code.size(); ++i) {
       table[i] = p->code[i].in;
       table[i].lat = cfg->latency[p->code[i].in.lat];  // class -> cycles
+      // sources without a scoreboard entry read the always-zero sentinel entry
+      for (int k = 0; k < 4; ++k)
+        if (table[i].sb[k] == KS_NO_SB) table[i].sb[k] = KS_SB_ZERO;
     }
     KsInst* d_prog = nullptr;
     uint32_t* d_status = nullptr;

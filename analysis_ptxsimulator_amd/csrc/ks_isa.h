@@ -42,6 +42,8 @@ enum : uint8_t { KF_GUARD = 1, KF_GUARD_NEG = 2 };
 constexpr uint8_t KS_NO_SB = 0xFF;      // no scoreboard entry
 constexpr uint16_t KS_RPC_EXIT = 0xFFFF;
 constexpr uint32_t KS_SB_PRED_BASE = 64; // scoreboard index of predicate p = 64 + p
+constexpr uint8_t KS_SB_ZERO = 127;      // scoreboard entry that always reads 0 (no source)
+constexpr uint32_t KS_SB_ENTRIES = 129;  // scoreboard words per warp in LDS (odd: warps start in different banks)
 
 struct KsInst {            // 64 bytes
   uint8_t op;              // KOp
@@ -50,7 +52,7 @@ struct KsInst {            // 64 bytes
   uint8_t guard;           // guard predicate index
   uint8_t src[3];          // register slot, special id or (selp's third) predicate index
   uint8_t kinds;           // 2 bits per source, KK_*
-  uint8_t sb[4];           // scoreboard index of src0, src1, src2, guard (KS_NO_SB = none)
+  uint8_t sb[4];           // scoreboard index of src0, src1, src2, guard (host: KS_NO_SB; device table: KS_SB_ZERO)
   uint8_t sb_dst;          // scoreboard index of the destination (KS_NO_SB = none)
   uint8_t cmp;             // KC_* for setp
   uint16_t lat;            // latency of the destination (cycles)

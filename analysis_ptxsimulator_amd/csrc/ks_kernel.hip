@@ -53,15 +53,6 @@ enum {
   C_GST_N, C_GST_SEC, C_GST_LINES, C_SH_N, C_SH_SUM, C_SH_MAX, C_DIV, C_BAR, C_FAULT, C_MAXDEPTH, C_RES
 };
 
-// Per-warp control state, wave-uniform (SGPRs).
-struct Half {
-  uint32_t pc, mask, rpc, sp;  // top of the divergence stack and its depth
-  uint32_t exited, init_mask;
-  uint32_t next;               // previous issue cycle + 1
-  uint32_t bar_ready, arrival;
-  uint32_t state, status, warp_instrs, max_depth;
-  uint64_t thread_instrs;
-};
 
 typedef const __attribute__((address_space(4))) uint32_t* cu32p;
 
@@ -142,6 +133,15 @@ struct RegFile<64> {
 
 // ---------------------------------------------------------------------------- divergence stack
 
+// Per-warp control state, wave-uniform (SGPRs).  The cycle and instruction
+// counters of a warp live in VGPRs, uniform over the warp's 32 lanes.
+struct Half {
+  uint32_t pc, mask, rpc, sp;  // top of the divergence stack and its depth
+  uint32_t m;                  // mask & ~exited of the top entry
+  uint32_t exited, init_mask;
+  uint32_t state, status, max_depth, arrival;
+};
+
 __device__ __forceinline__ void hs_pop(Half& H, uint32_t spc, uint32_t sm, uint32_t sr) {
   H.sp -= 1;
   if (H.sp) {
@@ -158,35 +158,33 @@ __device__ __forceinline__ void hs_push(Half& H, uint32_t& spc, uint32_t& sm, ui
   sr = wl(sr, H.rpc, H.sp - 1, lane);
   H.pc = pc;
   H.mask = mask;
+  H.m = mask & ~H.exited;
   H.rpc = rpc;
   H.sp += 1;
   H.max_depth = umax(H.max_depth, H.sp);
 }
 
+// The top entry cannot issue: no live lane, reconverged, or past the end.
+__device__ __forceinline__ bool hs_blocked(const Half& H, uint32_t n) {
+  return H.state == H_RUN && (H.m == 0 || H.pc == H.rpc || H.pc >= n);
+}
+
 // Pop finished or reconverged entries; lanes that ran off the end exit at no cost.
-__device__ __forceinline__ void hs_resolve(Half& H, uint32_t spc, uint32_t sm, uint32_t sr, uint32_t n, uint32_t budget) {
-  if (H.state != H_RUN) return;
+__device__ __forceinline__ void hs_settle(Half& H, uint32_t spc, uint32_t sm, uint32_t sr, uint32_t n) {
   while (H.sp) {
-    const uint32_t m = H.mask & ~H.exited;
-    if (m == 0 || H.pc == H.rpc) {
+    H.m = H.mask & ~H.exited;
+    if (H.m == 0 || H.pc == H.rpc) {
       hs_pop(H, spc, sm, sr);
       continue;
     }
     if (H.pc >= n) {
-      H.exited |= m;
+      H.exited |= H.m;
       continue;
     }
-    break;
-  }
-  if (!H.sp) {
-    H.state = H_DONE;
-    H.status |= KS_ST_FINISHED;
     return;
   }
-  if (H.warp_instrs >= budget) {
-    H.state = H_DONE;
-    H.status |= KS_ST_BUDGET;
-  }
+  H.state = H_DONE;
+  H.status |= KS_ST_FINISHED;
 }
 
 __device__ __forceinline__ void half_init(Half& H, uint32_t w, uint32_t W, uint32_t T) {
@@ -195,46 +193,18 @@ __device__ __forceinline__ void half_init(Half& H, uint32_t w, uint32_t W, uint3
   H.init_mask = live >= 32u ? 0xFFFFFFFFu : ((1u << live) - 1u);
   H.pc = 0;
   H.mask = H.init_mask;
+  H.m = H.init_mask;
   H.rpc = RPC_EXIT;
   H.sp = exists ? 1u : 0u;
   H.exited = 0;
-  H.next = 0;
-  H.bar_ready = 0;
-  H.arrival = 0;
   H.state = exists ? H_RUN : H_DONE;
   H.status = 0;
-  H.warp_instrs = 0;
   H.max_depth = 1;
-  H.thread_instrs = 0;
-}
-
-// ---------------------------------------------------------------------------- scoreboard
-
-__device__ __forceinline__ uint32_t sb_get(uint32_t lo, uint32_t hi, uint32_t j) {
-  return j < 64 ? rl(lo, j) : rl(hi, j - 64);
-}
-__device__ __forceinline__ void sb_set(uint32_t& lo, uint32_t& hi, uint32_t j, uint32_t v, uint32_t lane) {
-  if (j < 64) lo = wl(lo, v, j, lane);
-  else hi = wl(hi, v, j - 64, lane);
-}
-
-// Issue cycle: the later of previous issue + 1, the barrier release and the ready
-// cycle of every register source (sb holds four scoreboard indices, 0xFF = none).
-__device__ __forceinline__ uint32_t issue_cycle(const Half& H, uint32_t lo, uint32_t hi, uint32_t sb) {
-  uint32_t t = umax(H.next, H.bar_ready);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t j = (sb >> (8 * k)) & 0xFF;
-    if (j != 0xFF) t = umax(t, sb_get(lo, hi, j));
-  }
-  return t;
+  H.arrival = 0;
 }
 
 __device__ __forceinline__ uint32_t cnt_add(uint32_t cnt, uint32_t lane, uint32_t idx, uint32_t v) {
   return cnt + (lane == idx ? v : 0u);
-}
-__device__ __forceinline__ uint32_t cnt_max(uint32_t cnt, uint32_t lane, uint32_t idx, uint32_t v) {
-  return (lane == idx && v > cnt) ? v : cnt;
 }
 
 // ---------------------------------------------------------------------------- analyser
@@ -310,20 +280,20 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t T = a.threads_per_block;
   const uint32_t n_instr = a.n_instrs;
 
+  // LDS: [register file (LDS variant)] [scoreboard, 129 words per warp] [shared window]
   RegFile<RF> R;
-  uint8_t* win;
+  const uint32_t rf_words = RF == 0 ? (a.rf_slots ? a.rf_slots : 1u) * WG : 0u;
+  if constexpr (RF == 0) {
+    R.base = lds;
+    R.stride = WG;
+    R.tid = tid;
+  } else {
+    RegFile<RF>::zero();
+  }
+  uint32_t* const sbw = lds + rf_words;
+  uint8_t* const win = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
   {
-    uint32_t rf_words = 0;
-    if constexpr (RF == 0) {
-      R.base = lds;
-      R.stride = WG;
-      R.tid = tid;
-      rf_words = a.rf_slots * WG;
-    } else {
-      RegFile<RF>::zero();
-    }
-    win = reinterpret_cast<uint8_t*>(lds + rf_words);
-    const uint32_t words = rf_words + ((a.shared_bytes + 3u) >> 2);
+    const uint32_t words = rf_words + (WG / 32u) * KS_SB_ENTRIES + ((a.shared_bytes + 3u) >> 2);
     for (uint32_t i = tid; i < words; i += WG) lds[i] = 0;
     if (tid < 3) {
       ep_max[tid] = 0;
@@ -333,23 +303,29 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   __syncthreads();
 
   // special registers of this lane's simulated thread
-  const uint32_t t_lin = (2u * wave + hl) * 32u + sl;
+  const uint32_t my_w = 2u * wave + hl;
+  const uint32_t t_lin = my_w * 32u + sl;
   const uint32_t bx = a.block[0], by = a.block[1];
   const uint32_t tid_x = t_lin % bx, tid_y = (t_lin / bx) % by, tid_z = t_lin / (bx * by);
   const uint32_t gx = a.grid[0], gy = a.grid[1];
   const uint32_t cta_x = blk % gx, cta_y = (blk / gx) % gy, cta_z = blk / (gx * gy);
   const bool small_gmem = a.gmem_bytes <= (1ull << 37);  // sector ids of valid accesses fit 32 bits
+  uint32_t* const my_sb = sbw + my_w * KS_SB_ENTRIES;    // this lane's warp's scoreboard
 
   Half H0, H1;
   half_init(H0, 2u * wave, W, T);
   half_init(H1, 2u * wave + 1u, W, T);
   uint32_t stk_pc0 = 0, stk_m0 = 0, stk_r0 = 0, stk_pc1 = 0, stk_m1 = 0, stk_r1 = 0;
-  uint32_t sb_lo0 = 0, sb_hi0 = 0, sb_lo1 = 0, sb_hi1 = 0;
-  uint32_t cnt = 0;    // counter d of half h in lane 32 h + d
-  uint32_t pbits = 0;  // predicate p of this lane's thread in bit p
-  uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of half h at lane 32 h + k % 32
+  // warp state kept uniform over each warp's 32 lanes
+  uint32_t v_next = 0;      // previous issue cycle + 1
+  uint32_t v_wi = 0;        // issued warp-instructions
+  uint64_t v_ti = 0;        // thread-instructions
+  uint32_t cnt = 0;         // counter d of the lane's warp in lane 32 h + d
+  uint32_t pbits = 0;       // predicate p of this lane's thread in bit p
+  uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
 
   const uint32_t cap = a.trace_cap;
+  const uint32_t budget = a.max_warp_instrs;
   const uint64_t gw0 = (uint64_t)blk * W + 2u * wave;  // global warp id of half 0
   uint8_t* const slot_base = a.trace + (gw0 + hl) * a.slot_bytes + 16u;  // this lane's warp's records
 
@@ -357,70 +333,73 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   while (true) {
     // ------------------------------------------------------------------ run both warps until blocked
     while (true) {
-      hs_resolve(H0, stk_pc0, stk_m0, stk_r0, n_instr, a.max_warp_instrs);
-      hs_resolve(H1, stk_pc1, stk_m1, stk_r1, n_instr, a.max_warp_instrs);
+      if (hs_blocked(H0, n_instr)) hs_settle(H0, stk_pc0, stk_m0, stk_r0, n_instr);
+      if (hs_blocked(H1, n_instr)) hs_settle(H1, stk_pc1, stk_m1, stk_r1, n_instr);
       const bool r0 = H0.state == H_RUN, r1 = H1.state == H_RUN;
       if (!r0 && !r1) break;
       const uint32_t pc = uni((r0 && r1) ? (H0.pc < H1.pc ? H0.pc : H1.pc) : (r0 ? H0.pc : H1.pc));
       bool go0 = r0 && H0.pc == pc, go1 = r1 && H1.pc == pc;
+      {  // issue budget
+        const uint64_t over = ballot((hl ? go1 : go0) && v_wi >= budget);
+        if (over) {
+          if (over & 1u) {
+            H0.state = H_DONE;
+            H0.status |= KS_ST_BUDGET;
+          }
+          if (over >> 32) {
+            H1.state = H_DONE;
+            H1.status |= KS_ST_BUDGET;
+          }
+          continue;
+        }
+      }
 
       const cu32p I = (cu32p)(uintptr_t)(a.prog + pc);
-      const uint32_t w0 = I[0], w1 = I[1], wsb = I[2], w3 = I[3], w4 = I[4];
+      const uint32_t w0 = I[0], w1 = I[1], wsb = I[2], w3 = I[3];
       const uint32_t op = w0 & 0xFFu, flags = (w0 >> 8) & 0xFFu, dst = (w0 >> 16) & 0xFFu, guard = w0 >> 24;
       const uint32_t kinds = w1 >> 24;
       const uint32_t sb_dst = w3 & 0xFFu, cmp = (w3 >> 8) & 0xFFu, lat = w3 >> 16;
 
-      uint32_t iss0 = 0, iss1 = 0;
-      if (go0) {
-        iss0 = issue_cycle(H0, sb_lo0, sb_hi0, wsb);
-        if (iss0 > CYCLE_LIMIT) {
-          H0.state = H_DONE;
-          H0.status |= KS_ST_CYCLE_OVF;
-          go0 = false;
-        }
-      }
-      if (go1) {
-        iss1 = issue_cycle(H1, sb_lo1, sb_hi1, wsb);
-        if (iss1 > CYCLE_LIMIT) {
-          H1.state = H_DONE;
-          H1.status |= KS_ST_CYCLE_OVF;
-          go1 = false;
-        }
-      }
-      if (!go0 && !go1) continue;
-      const uint32_t m0 = go0 ? (H0.mask & ~H0.exited) : 0u;
-      const uint32_t m1 = go1 ? (H1.mask & ~H1.exited) : 0u;
-
-      // trace: stage the record in this warp's lane k % 32; write 32 records at once
+      // issue cycle (per warp, uniform over its lanes): the later of the previous issue
+      // + 1 and the ready cycle of every register source (absent sources read entry 127 = 0)
+      const uint32_t iss = umax(v_next, umax(umax(my_sb[wsb & 0xFFu], my_sb[(wsb >> 8) & 0xFFu]),
+                                             umax(my_sb[(wsb >> 16) & 0xFFu], my_sb[wsb >> 24])));
       {
-        const bool rec0 = go0 && H0.warp_instrs < cap, rec1 = go1 && H1.warp_instrs < cap;
-        if (rec0) {
-          const uint32_t li = H0.warp_instrs & 31u;
-          tr_c = wl(tr_c, iss0, li, lane);
-          tr_p = wl(tr_p, pc, li, lane);
-        }
-        if (rec1) {
-          const uint32_t li = 32u + (H1.warp_instrs & 31u);
-          tr_c = wl(tr_c, iss1, li, lane);
-          tr_p = wl(tr_p, pc, li, lane);
-        }
-        const bool fl0 = rec0 && ((H0.warp_instrs & 31u) == 31u || H0.warp_instrs + 1 == cap);
-        const bool fl1 = rec1 && ((H1.warp_instrs & 31u) == 31u || H1.warp_instrs + 1 == cap);
-        if (fl0 || fl1) {
-          const uint32_t k = hl ? H1.warp_instrs : H0.warp_instrs;  // index of the chunk's last record
-          if ((hl ? fl1 : fl0) && sl <= (k & 31u))
-            *reinterpret_cast<uint2*>(slot_base + 8ull * ((k & ~31u) + sl)) = make_uint2(tr_c, tr_p);
+        const uint64_t ovf = ballot((hl ? go1 : go0) && iss > CYCLE_LIMIT);
+        if (ovf) {
+          if (ovf & 1u) {
+            H0.state = H_DONE;
+            H0.status |= KS_ST_CYCLE_OVF;
+          }
+          if (ovf >> 32) {
+            H1.state = H_DONE;
+            H1.status |= KS_ST_CYCLE_OVF;
+          }
+          continue;
         }
       }
-      if (go0) {
-        H0.warp_instrs += 1;
-        H0.thread_instrs += (uint32_t)__builtin_popcount(m0);
-        H0.next = iss0 + 1;
+      const bool go_lane = hl ? go1 : go0;
+      const uint32_t m0 = go0 ? H0.m : 0u;
+      const uint32_t m1 = go1 ? H1.m : 0u;
+
+      // trace: stage the record in the warp's lane k % 32; write 32 records at once
+      {
+        const bool rec = go_lane && v_wi < cap;
+        if (rec && sl == (v_wi & 31u)) {
+          tr_c = iss;
+          tr_p = pc;
+        }
+        const bool fl = rec && ((v_wi & 31u) == 31u || v_wi + 1u == cap);
+        if (ballot(fl)) {
+          if (fl && sl <= (v_wi & 31u))
+            *reinterpret_cast<uint2*>(slot_base + 8ull * ((v_wi & ~31u) + sl)) = make_uint2(tr_c, tr_p);
+        }
       }
-      if (go1) {
-        H1.warp_instrs += 1;
-        H1.thread_instrs += (uint32_t)__builtin_popcount(m1);
-        H1.next = iss1 + 1;
+      if (go_lane) {
+        v_wi += 1;
+        v_ti += (uint32_t)__builtin_popcount(hl ? m1 : m0);
+        v_next = iss + 1;
+        if (sb_dst != 0xFFu) my_sb[sb_dst] = iss + lat;
       }
 
       // guard
@@ -437,27 +416,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         if (on) {
           const uint32_t s0 = w1 & 0xFFu, s1 = (w1 >> 8) & 0xFFu, s2 = (w1 >> 16) & 0xFFu;
           const uint32_t k0 = kinds & 3u, k1 = (kinds >> 2) & 3u, k2 = (kinds >> 4) & 3u;
-          auto special = [&](uint32_t id) -> uint32_t {
-            switch (id) {
-              case KSP_TID_X: return tid_x;
-              case KSP_TID_Y: return tid_y;
-              case KSP_TID_Z: return tid_z;
-              case KSP_NTID_X: return a.block[0];
-              case KSP_NTID_Y: return a.block[1];
-              case KSP_NTID_Z: return a.block[2];
-              case KSP_CTAID_X: return cta_x;
-              case KSP_CTAID_Y: return cta_y;
-              case KSP_CTAID_Z: return cta_z;
-              case KSP_NCTAID_X: return a.grid[0];
-              case KSP_NCTAID_Y: return a.grid[1];
-              case KSP_NCTAID_Z: return a.grid[2];
-              default: return sl;
-            }
-          };
+          // register or immediate operands, read without branching on the kind (slot 0 for immediates)
           auto rd32 = [&](uint32_t kind, uint32_t s, uint32_t imm) -> uint32_t {
-            if (kind == KK_REG) return R.get(s);
-            if (kind == KK_IMM) return imm;
-            return special(s);
+            const uint32_t r = R.get(s);
+            return kind == KK_REG ? r : imm;
           };
           auto rd64 = [&](uint32_t kind, uint32_t s, uint32_t imm_lo, uint32_t imm_hi) -> uint64_t {
             if (kind == KK_REG) return (uint64_t)R.get(s) | ((uint64_t)R.get(s + 1) << 32);
@@ -560,16 +522,38 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             case KO_SELP64: {
               const bool p = (pbits >> s2) & 1u;
               if (op == KO_SELP32) {
-                rlo = p ? rd32(k0, s0, I[6]) : rd32(k1, s1, I[8]);
+                const uint32_t x = rd32(k0, s0, I[6]), y = rd32(k1, s1, I[8]);
+                rlo = p ? x : y;
               } else {
-                const uint64_t r = p ? rd64(k0, s0, I[6], I[7]) : rd64(k1, s1, I[8], I[9]);
+                const uint64_t x = rd64(k0, s0, I[6], I[7]), y = rd64(k1, s1, I[8], I[9]);
+                const uint64_t r = p ? x : y;
                 rlo = (uint32_t)r;
                 rhi = (uint32_t)(r >> 32);
                 wide = true;
               }
               break;
             }
-            case KO_MOV32: rlo = rd32(k0, s0, I[6]); break;
+            case KO_MOV32:
+              if (k0 == KK_SPECIAL) {
+                switch (s0) {
+                  case KSP_TID_X: rlo = tid_x; break;
+                  case KSP_TID_Y: rlo = tid_y; break;
+                  case KSP_TID_Z: rlo = tid_z; break;
+                  case KSP_NTID_X: rlo = a.block[0]; break;
+                  case KSP_NTID_Y: rlo = a.block[1]; break;
+                  case KSP_NTID_Z: rlo = a.block[2]; break;
+                  case KSP_CTAID_X: rlo = cta_x; break;
+                  case KSP_CTAID_Y: rlo = cta_y; break;
+                  case KSP_CTAID_Z: rlo = cta_z; break;
+                  case KSP_NCTAID_X: rlo = a.grid[0]; break;
+                  case KSP_NCTAID_Y: rlo = a.grid[1]; break;
+                  case KSP_NCTAID_Z: rlo = a.grid[2]; break;
+                  default: rlo = sl; break;
+                }
+              } else {
+                rlo = rd32(k0, s0, I[6]);
+              }
+              break;
             default: {  // KO_MOV64
               const uint64_t r = rd64(k0, s0, I[6], I[7]);
               rlo = (uint32_t)r;
@@ -642,15 +626,17 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         }
         // fault counting and analysis (full exec)
         const uint64_t faults = ballot(on && !ok);
-        const uint32_t f0 = (uint32_t)__builtin_popcountll(faults & 0xFFFFFFFFull);
-        const uint32_t f1 = (uint32_t)__builtin_popcountll(faults >> 32);
-        if (f0) {
-          H0.status |= KS_ST_FAULT;
-          cnt = cnt_add(cnt, lane, C_FAULT, f0);
-        }
-        if (f1) {
-          H1.status |= KS_ST_FAULT;
-          cnt = cnt_add(cnt, lane, 32 + C_FAULT, f1);
+        if (faults) {
+          const uint32_t f0 = (uint32_t)__builtin_popcountll(faults & 0xFFFFFFFFull);
+          const uint32_t f1 = (uint32_t)__builtin_popcountll(faults >> 32);
+          if (f0) {
+            H0.status |= KS_ST_FAULT;
+            cnt = cnt_add(cnt, lane, C_FAULT, f0);
+          }
+          if (f1) {
+            H1.status |= KS_ST_FAULT;
+            cnt = cnt_add(cnt, lane, 32 + C_FAULT, f1);
+          }
         }
         if (is_global) {
           uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;
@@ -686,17 +672,11 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               lin1 = distinct2(A >> 7, last >> 7, (uint64_t)g1 << 32);
             }
           }
+          // counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2}
           const uint32_t cn = is_load ? C_GLD_N : C_GST_N;
-          if (g0) {
-            cnt = cnt_add(cnt, lane, cn, 1);
-            cnt = cnt_add(cnt, lane, cn + 1, sec0);
-            cnt = cnt_add(cnt, lane, cn + 2, lin0);
-          }
-          if (g1) {
-            cnt = cnt_add(cnt, lane, 32 + cn, 1);
-            cnt = cnt_add(cnt, lane, 32 + cn + 1, sec1);
-            cnt = cnt_add(cnt, lane, 32 + cn + 2, lin1);
-          }
+          const uint32_t gh = hl ? g1 : g0;
+          const uint32_t d = sl - cn;
+          if (gh && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0));
         } else {
           uint32_t d0 = 1, d1 = 1;
           bool slow0 = g0 != 0, slow1 = g1 != 0;
@@ -719,25 +699,19 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
           if (slow0) d0 = bank_degree(A, (uint64_t)g0);
           if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
-          if (g0) {
-            cnt = cnt_add(cnt, lane, C_SH_N, 1);
-            cnt = cnt_add(cnt, lane, C_SH_SUM, d0);
-            cnt = cnt_max(cnt, lane, C_SH_MAX, d0);
-          }
-          if (g1) {
-            cnt = cnt_add(cnt, lane, 32 + C_SH_N, 1);
-            cnt = cnt_add(cnt, lane, 32 + C_SH_SUM, d1);
-            cnt = cnt_max(cnt, lane, 32 + C_SH_MAX, d1);
+          const uint32_t gh = hl ? g1 : g0;
+          const uint32_t dh = hl ? d1 : d0;
+          if (gh) {
+            if (sl == C_SH_N) cnt += 1;
+            if (sl == C_SH_SUM) cnt += dh;
+            if (sl == C_SH_MAX) cnt = umax(cnt, dh);
           }
         }
       }
 
-      // ---------------------------------------------------------------- scoreboard and control
-      if (sb_dst != 0xFFu) {
-        if (go0) sb_set(sb_lo0, sb_hi0, sb_dst, iss0 + lat, lane);
-        if (go1) sb_set(sb_lo1, sb_hi1, sb_dst, iss1 + lat, lane);
-      }
+      // ---------------------------------------------------------------- control (scalar)
       if (op == KO_BRA) {
+        const uint32_t w4 = I[4];
         const uint32_t target = w4 & 0xFFFFu, rpc_raw = w4 >> 16;
         const uint32_t rpc = rpc_raw == KS_RPC_EXIT ? RPC_EXIT : rpc_raw;
         if (go0) {
@@ -769,10 +743,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       } else if (op == KO_RET) {
         if (go0) {
           H0.exited |= g0;
+          H0.m = H0.mask & ~H0.exited;
           H0.pc = pc + 1;
         }
         if (go1) {
           H1.exited |= g1;
+          H1.m = H1.mask & ~H1.exited;
           H1.pc = pc + 1;
         }
       } else if (op == KO_BAR) {
@@ -780,19 +756,19 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           cnt = cnt_add(cnt, lane, C_BAR, 1);
           if (m0 != (H0.init_mask & ~H0.exited)) H0.status |= KS_ST_BARDIV;
           H0.state = H_WAIT;
-          H0.arrival = iss0;
+          H0.arrival = rl(iss, 0);
           H0.pc = pc + 1;
         }
         if (go1) {
           cnt = cnt_add(cnt, lane, 32 + C_BAR, 1);
           if (m1 != (H1.init_mask & ~H1.exited)) H1.status |= KS_ST_BARDIV;
           H1.state = H_WAIT;
-          H1.arrival = iss1;
+          H1.arrival = rl(iss, 32);
           H1.pc = pc + 1;
         }
       } else {
-        if (go0) H0.pc = pc + 1;
-        if (go1) H1.pc = pc + 1;
+        H0.pc += go0 ? 1u : 0u;
+        H1.pc += go1 ? 1u : 0u;
       }
     }
 
@@ -814,30 +790,24 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     __syncthreads();
     const uint32_t alive_all = uni(ep_alive[slot]);
     if (alive_all == 0) break;
+    // release: every waiting warp's next issue waits for max(arrival) + lat(bar.sync)
     const uint32_t release = uni(ep_max[slot]) + a.lat_bar;
-    if (H0.state == H_WAIT) {
-      H0.state = H_RUN;
-      H0.bar_ready = release;
-    }
-    if (H1.state == H_WAIT) {
-      H1.state = H_RUN;
-      H1.bar_ready = release;
-    }
+    const bool waiting = hl ? H1.state == H_WAIT : H0.state == H_WAIT;
+    if (waiting) v_next = umax(v_next, release);
+    if (H0.state == H_WAIT) H0.state = H_RUN;
+    if (H1.state == H_WAIT) H1.state = H_RUN;
     ++epoch;
   }
 
   // -------------------------------------------------------------------- counters, trace tail, headers
   {
-    const uint32_t w = 2u * wave + hl;
+    const uint32_t w = my_w;
     if (w < W) {
-      const uint32_t m_next = hl ? H1.next : H0.next;
-      const uint32_t m_wi = hl ? H1.warp_instrs : H0.warp_instrs;
       const uint32_t m_status = hl ? H1.status : H0.status;
       const uint32_t m_depth = hl ? H1.max_depth : H0.max_depth;
-      const uint64_t m_ti = hl ? H1.thread_instrs : H0.thread_instrs;
-      const uint32_t cycles = m_next;
-      const uint32_t written = m_wi < cap ? m_wi : cap;
-      const uint32_t dropped = m_wi - written;
+      const uint32_t cycles = v_next;
+      const uint32_t written = v_wi < cap ? v_wi : cap;
+      const uint32_t dropped = v_wi - written;
       const uint32_t status = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);
       const uint64_t gw = gw0 + hl;
       // staged records of a last, partly filled chunk (a full chunk was written when it filled)
@@ -846,12 +816,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       if (sl < 20) {
         uint32_t v;
         switch (sl) {
-          case C_TI_LO: v = (uint32_t)m_ti; break;
-          case C_TI_HI: v = (uint32_t)(m_ti >> 32); break;
+          case C_TI_LO: v = (uint32_t)v_ti; break;
+          case C_TI_HI: v = (uint32_t)(v_ti >> 32); break;
           case C_STATUS: v = status; break;
           case C_CYCLES: v = cycles; break;
-          case C_WARP_INSTRS: v = m_wi; break;
-          case C_STALL: v = cycles - m_wi; break;
+          case C_WARP_INSTRS: v = v_wi; break;
+          case C_STALL: v = cycles - v_wi; break;
           case C_MAXDEPTH: v = m_depth; break;
           case C_RES: v = 0; break;
           default: v = cnt; break;
@@ -914,8 +884,9 @@ int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
 }
 
 size_t ks_lds_bytes(int variant, uint32_t slots, uint32_t wg, uint32_t shared_bytes) {
-  const size_t rf = variant == 0 ? (size_t)slots * wg * 4u : 0u;
-  return rf + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
+  const size_t rf = variant == 0 ? (size_t)(slots ? slots : 1u) * wg * 4u : 0u;
+  const size_t sb = (size_t)(wg / 32u) * KS_SB_ENTRIES * 4u;
+  return rf + sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
 }
 
 hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, hipStream_t s) {

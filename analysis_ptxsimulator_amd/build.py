@@ -7,8 +7,10 @@ Flags that matter for results:
   -packed-fp32-ops off     no v_pk_* f32 instructions are generated
 """
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -21,11 +23,65 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp
          "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
+# The VGPR register-file kernels keep simulated registers in v96 and up, which
+# the compiler must never allocate (they are reserved by amdgpu_num_vgpr); and no
+# interpreter may use scratch memory.
+RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64")
+INTERP_KERNELS = ("ks_interp_lds",) + RESERVED_VGPR_KERNELS
+RESERVED_BASE = 96
+
+
+def check_device_asm(asm_text: str) -> dict:
+    """Check the interpreter kernels' gfx950 assembly; returns per-kernel resources.
+
+    Raises RuntimeError when a kernel spills to scratch or when compiler-written
+    code (outside inline asm) in a register-file kernel names a VGPR >= 96."""
+    info = {}
+    for k in INTERP_KERNELS:
+        m = re.search(r"^(_Z\d+%sN2ks6KsArgsE):[^\n]*\n(.*?)^\.Lfunc_end" % k, asm_text, re.S | re.M)
+        if not m:
+            raise RuntimeError("kernel %s not found in device assembly" % k)
+        body = m.group(2)
+        meta = re.search(r"\.name:\s+%s\n" % re.escape(m.group(1)), asm_text)
+        md = asm_text[meta.start():meta.start() + 4000] if meta else ""
+        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", md)
+        vg = re.search(r"\.vgpr_count:\s+(\d+)", md)
+        sg = re.search(r"\.sgpr_count:\s+(\d+)", md)
+        info[k] = {"scratch": int(priv.group(1)) if priv else -1, "vgprs": int(vg.group(1)) if vg else -1,
+                   "sgprs": int(sg.group(1)) if sg else -1}
+        if info[k]["scratch"] != 0:
+            raise RuntimeError("%s uses %s bytes of scratch" % (k, info[k]["scratch"]))
+        if k in RESERVED_VGPR_KERNELS:
+            outside, inside = [], False
+            for line in body.split("\n"):
+                if ";;#ASMSTART" in line:
+                    inside = True
+                elif ";;#ASMEND" in line:
+                    inside = False
+                elif not inside:
+                    outside.append(line.split(";")[0])
+            hi = 0
+            for line in outside:
+                # VGPR operands: vN or a range v[N:M]
+                for lo, top, single in re.findall(r"\bv(?:\[(\d+):(\d+)\]|(\d+)\b)", line):
+                    hi = max(hi, int(top or single))
+            info[k]["max_compiler_vgpr"] = hi
+            if hi >= RESERVED_BASE:
+                raise RuntimeError("%s: compiler-allocated code uses v%d (v%d+ hold the register file)"
+                                   % (k, hi, RESERVED_BASE))
+    return info
+
+
+def build(force: bool = True, verbose: bool = False, check: bool = True) -> str:
     if not force and os.path.exists(LIB):
         newest = max(os.path.getmtime(p) for p in SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC)])
         if os.path.getmtime(LIB) >= newest:
             return LIB
+    if check:
+        with tempfile.TemporaryDirectory() as td:
+            info = check_device_asm(open(device_asm(os.path.join(td, "k.s"))).read())
+        if verbose:
+            print(info, file=sys.stderr)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
     if verbose:
@@ -38,7 +94,7 @@ def build(force: bool = True, verbose: bool = False) -> str:
 def device_asm(out_path: str) -> str:
     """Write the gfx950 assembly of the interpreter (for inspection)."""
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", out_path,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-inline-asm", "-o", out_path,
            os.path.join(CSRC, "ks_kernel.hip")]
     subprocess.run(cmd, check=True, cwd=HERE)
     return out_path

@@ -73,8 +73,12 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 // ---------------------------------------------------------------------------- register files
 //
 // RF = 0: LDS, [slot][thread of the workgroup].  RF = 32 / 64: physical VGPRs
-// v96 .. v96+RF-1, outside the compiler's allocation (the kernels are built with
-// amdgpu_num_vgpr(96)); slot s of a lane is VGPR v[96 + s] of that lane.
+// v96 .. v96+RF-1, outside the compiler's allocation; slot s of a lane is VGPR
+// v[96 + s] of that lane.  The kernels carry amdgpu_num_vgpr(48): on targets with
+// the unified VGPR/AGPR file the compiler doubles that figure, so v96 and up are
+// reserved (never allocated).  A larger figure that exceeds what the launch bound
+// allows is silently ignored, which would hand v96+ back to the allocator; the
+// build checks the assembly for any compiler-written use of them.
 template <int RF>
 struct RegFile;
 
@@ -84,21 +88,53 @@ struct RegFile<0> {
   uint32_t stride;
   uint32_t tid;
   __device__ __forceinline__ uint32_t get(uint32_t s) const { return base[s * stride + tid]; }
+  __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const {
+    a = get(i0);
+    b = get(i1);
+  }
+  __device__ __forceinline__ void get3(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t& a, uint32_t& b,
+                                       uint32_t& c) const {
+    a = get(i0);
+    b = get(i1);
+    c = get(i2);
+  }
   __device__ __forceinline__ void put(uint32_t s, uint32_t v) const { base[s * stride + tid] = v; }
+  __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {
+    put(s, lo);
+    put(s + 1, hi);
+  }
 };
 
 // VGPR index mode: between s_set_gpr_idx_on and s_set_gpr_idx_off the SRC0 (or
-// DST) VGPR of each VALU instruction is offset by the index (kept in M0).
-#define KS_RF_ASM_GET                                                                       \
-  __device__ __forceinline__ uint32_t get(uint32_t s) const {                               \
-    uint32_t r;                                                                             \
-    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\ts_set_gpr_idx_off" \
-                 : "=v"(r) : "s"(s) : "m0");                                               \
-    return r;                                                                               \
-  }                                                                                         \
-  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                       \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v96, %1\n\ts_set_gpr_idx_off"  \
-                 : : "s"(s), "v"(v) : "m0");                                               \
+// DST) VGPR operand of each VALU instruction is offset by the index held in M0;
+// s_set_gpr_idx_idx changes the index without leaving the mode.
+#define KS_RF_ASM_ACCESS                                                                          \
+  __device__ __forceinline__ uint32_t get(uint32_t s) const {                                     \
+    uint32_t r;                                                                                   \
+    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\ts_set_gpr_idx_off"  \
+                 : "=v"(r) : "s"(s) : "m0");                                                     \
+    return r;                                                                                     \
+  }                                                                                               \
+  __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const { \
+    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\t"                    \
+                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, v96\n\ts_set_gpr_idx_off"                 \
+                 : "=&v"(a), "=v"(b) : "s"(i0), "s"(i1) : "m0");                                 \
+  }                                                                                               \
+  __device__ __forceinline__ void get3(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t& a, uint32_t& b, \
+                                       uint32_t& c) const {                                       \
+    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\t"                    \
+                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, v96\n\t"                                  \
+                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, v96\n\ts_set_gpr_idx_off"                 \
+                 : "=&v"(a), "=&v"(b), "=v"(c) : "s"(i0), "s"(i1), "s"(i2) : "m0");              \
+  }                                                                                               \
+  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                             \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v96, %1\n\ts_set_gpr_idx_off"   \
+                 : : "s"(s), "v"(v) : "m0");                                                     \
+  }                                                                                               \
+  __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {              \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v96, %1\n\t"                     \
+                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 v96, %2\n\ts_set_gpr_idx_off"                 \
+                 : : "s"(s), "v"(lo), "v"(hi), "s"(s + 1) : "m0");                               \
   }
 
 #define KS_Z(i) "v_mov_b32 v" #i ", 0\n\t"
@@ -107,7 +143,7 @@ struct RegFile<0> {
 
 template <>
 struct RegFile<32> {
-  KS_RF_ASM_GET
+  KS_RF_ASM_ACCESS
   __device__ __forceinline__ static void zero() {
     asm volatile(KS_Z8(96, 97, 98, 99, 100, 101, 102, 103) KS_Z8(104, 105, 106, 107, 108, 109, 110, 111)
                      KS_Z8(112, 113, 114, 115, 116, 117, 118, 119) KS_Z8(120, 121, 122, 123, 124, 125, 126, 127)
@@ -118,7 +154,7 @@ struct RegFile<32> {
 
 template <>
 struct RegFile<64> {
-  KS_RF_ASM_GET
+  KS_RF_ASM_ACCESS
   __device__ __forceinline__ static void zero() {
     asm volatile(KS_Z8(96, 97, 98, 99, 100, 101, 102, 103) KS_Z8(104, 105, 106, 107, 108, 109, 110, 111)
                      KS_Z8(112, 113, 114, 115, 116, 117, 118, 119) KS_Z8(120, 121, 122, 123, 124, 125, 126, 127)
@@ -133,13 +169,14 @@ struct RegFile<64> {
 
 // ---------------------------------------------------------------------------- divergence stack
 
-// Per-warp control state, wave-uniform (SGPRs).  The cycle and instruction
-// counters of a warp live in VGPRs, uniform over the warp's 32 lanes.
+// Per-warp control state, wave-uniform (SGPRs).  The next-issue cycle of a warp
+// lives in a VGPR, uniform over the warp's 32 lanes.
 struct Half {
   uint32_t pc, mask, rpc, sp;  // top of the divergence stack and its depth
   uint32_t m;                  // mask & ~exited of the top entry
   uint32_t exited, init_mask;
   uint32_t state, status, max_depth, arrival;
+  uint32_t wi;                 // issued warp-instructions
 };
 
 __device__ __forceinline__ void hs_pop(Half& H, uint32_t spc, uint32_t sm, uint32_t sr) {
@@ -201,11 +238,13 @@ __device__ __forceinline__ void half_init(Half& H, uint32_t w, uint32_t W, uint3
   H.status = 0;
   H.max_depth = 1;
   H.arrival = 0;
+  H.wi = 0;
 }
 
 __device__ __forceinline__ uint32_t cnt_add(uint32_t cnt, uint32_t lane, uint32_t idx, uint32_t v) {
   return cnt + (lane == idx ? v : 0u);
 }
+
 
 // ---------------------------------------------------------------------------- analyser
 
@@ -272,7 +311,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t WG = blockDim.x;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
-  const uint32_t wave = tid >> 6;
+  const uint32_t wave = uni(tid >> 6);  // wave-uniform: keeps every per-warp value scalar
   const uint32_t hl = lane >> 5;
   const uint32_t sl = lane & 31u;
   const uint32_t blk = blockIdx.x;
@@ -316,13 +355,11 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   half_init(H0, 2u * wave, W, T);
   half_init(H1, 2u * wave + 1u, W, T);
   uint32_t stk_pc0 = 0, stk_m0 = 0, stk_r0 = 0, stk_pc1 = 0, stk_m1 = 0, stk_r1 = 0;
-  // warp state kept uniform over each warp's 32 lanes
-  uint32_t v_next = 0;      // previous issue cycle + 1
-  uint32_t v_wi = 0;        // issued warp-instructions
-  uint64_t v_ti = 0;        // thread-instructions
+  uint32_t v_next = 0;      // previous issue cycle + 1 of the lane's warp (uniform over the warp)
   uint32_t cnt = 0;         // counter d of the lane's warp in lane 32 h + d
   uint32_t pbits = 0;       // predicate p of this lane's thread in bit p
   uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
+  uint32_t act = 0;         // instructions issued with this lane's thread active
 
   const uint32_t cap = a.trace_cap;
   const uint32_t budget = a.max_warp_instrs;
@@ -339,19 +376,16 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       if (!r0 && !r1) break;
       const uint32_t pc = uni((r0 && r1) ? (H0.pc < H1.pc ? H0.pc : H1.pc) : (r0 ? H0.pc : H1.pc));
       bool go0 = r0 && H0.pc == pc, go1 = r1 && H1.pc == pc;
-      {  // issue budget
-        const uint64_t over = ballot((hl ? go1 : go0) && v_wi >= budget);
-        if (over) {
-          if (over & 1u) {
-            H0.state = H_DONE;
-            H0.status |= KS_ST_BUDGET;
-          }
-          if (over >> 32) {
-            H1.state = H_DONE;
-            H1.status |= KS_ST_BUDGET;
-          }
-          continue;
+      if ((go0 && H0.wi >= budget) || (go1 && H1.wi >= budget)) {  // issue budget
+        if (go0 && H0.wi >= budget) {
+          H0.state = H_DONE;
+          H0.status |= KS_ST_BUDGET;
         }
+        if (go1 && H1.wi >= budget) {
+          H1.state = H_DONE;
+          H1.status |= KS_ST_BUDGET;
+        }
+        continue;
       }
 
       const cu32p I = (cu32p)(uintptr_t)(a.prog + pc);
@@ -360,12 +394,15 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const uint32_t kinds = w1 >> 24;
       const uint32_t sb_dst = w3 & 0xFFu, cmp = (w3 >> 8) & 0xFFu, lat = w3 >> 16;
 
+      // lanes of the warps that issue this instruction
+      const uint64_t gm = (go0 ? 0xFFFFFFFFull : 0ull) | (go1 ? 0xFFFFFFFF00000000ull : 0ull);
+
       // issue cycle (per warp, uniform over its lanes): the later of the previous issue
       // + 1 and the ready cycle of every register source (absent sources read entry 127 = 0)
       const uint32_t iss = umax(v_next, umax(umax(my_sb[wsb & 0xFFu], my_sb[(wsb >> 8) & 0xFFu]),
                                              umax(my_sb[(wsb >> 16) & 0xFFu], my_sb[wsb >> 24])));
       {
-        const uint64_t ovf = ballot((hl ? go1 : go0) && iss > CYCLE_LIMIT);
+        const uint64_t ovf = ballot(iss > CYCLE_LIMIT) & gm;
         if (ovf) {
           if (ovf & 1u) {
             H0.state = H_DONE;
@@ -378,60 +415,69 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           continue;
         }
       }
-      const bool go_lane = hl ? go1 : go0;
       const uint32_t m0 = go0 ? H0.m : 0u;
       const uint32_t m1 = go1 ? H1.m : 0u;
 
-      // trace: stage the record in the warp's lane k % 32; write 32 records at once
+      // trace: stage the record in lane k % 32 of the warp; write 32 records at once
       {
-        const bool rec = go_lane && v_wi < cap;
-        if (rec && sl == (v_wi & 31u)) {
+        const bool rec0 = go0 && H0.wi < cap, rec1 = go1 && H1.wi < cap;
+        const uint32_t k0 = H0.wi & 31u, k1 = H1.wi & 31u;
+        const uint64_t smask = (rec0 ? (1ull << k0) : 0ull) | (rec1 ? (1ull << (32 + k1)) : 0ull);
+        if (__builtin_amdgcn_inverse_ballot_w64(smask)) {
           tr_c = iss;
           tr_p = pc;
         }
-        const bool fl = rec && ((v_wi & 31u) == 31u || v_wi + 1u == cap);
-        if (ballot(fl)) {
-          if (fl && sl <= (v_wi & 31u))
-            *reinterpret_cast<uint2*>(slot_base + 8ull * ((v_wi & ~31u) + sl)) = make_uint2(tr_c, tr_p);
+        const bool fl0 = rec0 && (k0 == 31u || H0.wi + 1u == cap);
+        const bool fl1 = rec1 && (k1 == 31u || H1.wi + 1u == cap);
+        if (fl0 || fl1) {
+          const uint64_t fmask = (fl0 ? (0xFFFFFFFFull >> (31u - k0)) : 0ull) |
+                                 (fl1 ? ((0xFFFFFFFFull >> (31u - k1)) << 32) : 0ull);
+          const uint32_t chunk = (hl ? H1.wi : H0.wi) & ~31u;
+          if (__builtin_amdgcn_inverse_ballot_w64(fmask))
+            *reinterpret_cast<uint2*>(slot_base + 8ull * (chunk + sl)) = make_uint2(tr_c, tr_p);
         }
       }
-      if (go_lane) {
-        v_wi += 1;
-        v_ti += (uint32_t)__builtin_popcount(hl ? m1 : m0);
+      H0.wi += go0 ? 1u : 0u;
+      H1.wi += go1 ? 1u : 0u;
+      act += __builtin_amdgcn_inverse_ballot_w64((uint64_t)m0 | ((uint64_t)m1 << 32)) ? 1u : 0u;
+      if (__builtin_amdgcn_inverse_ballot_w64(gm)) {
         v_next = iss + 1;
         if (sb_dst != 0xFFu) my_sb[sb_dst] = iss + lat;
       }
 
-      // guard
-      const uint64_t m64 = (uint64_t)m0 | ((uint64_t)m1 << 32);
-      const bool act = (m64 >> lane) & 1u;
-      bool pass = true;
-      if (flags & KF_GUARD) pass = (((pbits >> guard) & 1u) != 0) != ((flags & KF_GUARD_NEG) != 0);
-      const bool on = act && pass;
-      const uint64_t g64 = ballot(on);
-      const uint32_t g0 = (uint32_t)g64, g1 = (uint32_t)(g64 >> 32);
+      // guard: lanes that execute
+      uint64_t on64 = (uint64_t)m0 | ((uint64_t)m1 << 32);
+      if (flags & KF_GUARD) on64 &= ballot((((pbits >> guard) & 1u) != 0) != ((flags & KF_GUARD_NEG) != 0));
+      const bool on = __builtin_amdgcn_inverse_ballot_w64(on64);
+      const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
 
       // ---------------------------------------------------------------- execute
       if (op < KO_LDP32) {
         if (on) {
           const uint32_t s0 = w1 & 0xFFu, s1 = (w1 >> 8) & 0xFFu, s2 = (w1 >> 16) & 0xFFu;
           const uint32_t k0 = kinds & 3u, k1 = (kinds >> 2) & 3u, k2 = (kinds >> 4) & 3u;
-          // register or immediate operands, read without branching on the kind (slot 0 for immediates)
-          auto rd32 = [&](uint32_t kind, uint32_t s, uint32_t imm) -> uint32_t {
-            const uint32_t r = R.get(s);
-            return kind == KK_REG ? r : imm;
-          };
+          // register or immediate operands: the three slots are read in one go (slot 0 stands
+          // in for an immediate), then immediates replace the values read
+          uint32_t x0, x1, x2;
+          R.get3(s0, s1, s2, x0, x1, x2);
+          x0 = k0 == KK_REG ? x0 : I[6];
+          x1 = k1 == KK_REG ? x1 : I[8];
+          x2 = k2 == KK_REG ? x2 : I[10];
           auto rd64 = [&](uint32_t kind, uint32_t s, uint32_t imm_lo, uint32_t imm_hi) -> uint64_t {
-            if (kind == KK_REG) return (uint64_t)R.get(s) | ((uint64_t)R.get(s + 1) << 32);
+            if (kind == KK_REG) {
+              uint32_t lo, hi;
+              R.get2(s, s + 1, lo, hi);
+              return (uint64_t)lo | ((uint64_t)hi << 32);
+            }
             return (uint64_t)imm_lo | ((uint64_t)imm_hi << 32);
           };
           uint32_t rlo = 0, rhi = 0;
           bool wide = false, wr = true;
           switch (op) {
-            case KO_ADD32: rlo = rd32(k0, s0, I[6]) + rd32(k1, s1, I[8]); break;
-            case KO_SUB32: rlo = rd32(k0, s0, I[6]) - rd32(k1, s1, I[8]); break;
-            case KO_MUL32: rlo = rd32(k0, s0, I[6]) * rd32(k1, s1, I[8]); break;
-            case KO_MAD32: rlo = rd32(k0, s0, I[6]) * rd32(k1, s1, I[8]) + rd32(k2, s2, I[10]); break;
+            case KO_ADD32: rlo = x0 + x1; break;
+            case KO_SUB32: rlo = x0 - x1; break;
+            case KO_MUL32: rlo = x0 * x1; break;
+            case KO_MAD32: rlo = x0 * x1 + x2; break;
             case KO_ADD64:
             case KO_SUB64:
             case KO_MUL64:
@@ -448,31 +494,31 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               break;
             }
             case KO_MULWIDE_S: {
-              const int64_t r = (int64_t)(int32_t)rd32(k0, s0, I[6]) * (int64_t)(int32_t)rd32(k1, s1, I[8]);
+              const int64_t r = (int64_t)(int32_t)x0 * (int64_t)(int32_t)x1;
               rlo = (uint32_t)r;
               rhi = (uint32_t)((uint64_t)r >> 32);
               wide = true;
               break;
             }
             case KO_MULWIDE_U: {
-              const uint64_t r = (uint64_t)rd32(k0, s0, I[6]) * (uint64_t)rd32(k1, s1, I[8]);
+              const uint64_t r = (uint64_t)x0 * (uint64_t)x1;
               rlo = (uint32_t)r;
               rhi = (uint32_t)(r >> 32);
               wide = true;
               break;
             }
             case KO_FADD:
-              rlo = canon_bits(__uint_as_float(rd32(k0, s0, I[6])) + __uint_as_float(rd32(k1, s1, I[8])));
+              rlo = canon_bits(__uint_as_float(x0) + __uint_as_float(x1));
               break;
             case KO_FSUB:
-              rlo = canon_bits(__uint_as_float(rd32(k0, s0, I[6])) - __uint_as_float(rd32(k1, s1, I[8])));
+              rlo = canon_bits(__uint_as_float(x0) - __uint_as_float(x1));
               break;
             case KO_FMUL:
-              rlo = canon_bits(__uint_as_float(rd32(k0, s0, I[6])) * __uint_as_float(rd32(k1, s1, I[8])));
+              rlo = canon_bits(__uint_as_float(x0) * __uint_as_float(x1));
               break;
             case KO_FFMA:
-              rlo = canon_bits(__builtin_fmaf(__uint_as_float(rd32(k0, s0, I[6])), __uint_as_float(rd32(k1, s1, I[8])),
-                                              __uint_as_float(rd32(k2, s2, I[10]))));
+              rlo = canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1),
+                                              __uint_as_float(x2)));
               break;
             case KO_SETP_S32:
             case KO_SETP_U32:
@@ -481,7 +527,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             case KO_SETP_F32: {
               bool c;
               if (op == KO_SETP_F32) {
-                const float x = __uint_as_float(rd32(k0, s0, I[6])), y = __uint_as_float(rd32(k1, s1, I[8]));
+                const float x = __uint_as_float(x0), y = __uint_as_float(x1);
                 // ordered comparisons: false whenever an input is NaN
                 switch (cmp) {
                   case KC_EQ: c = x == y; break;
@@ -492,7 +538,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
                   default: c = x >= y; break;
                 }
               } else if (op == KO_SETP_S32 || op == KO_SETP_U32) {
-                const uint32_t x = rd32(k0, s0, I[6]), y = rd32(k1, s1, I[8]);
+                const uint32_t x = x0, y = x1;
                 const bool lt = op == KO_SETP_S32 ? (int32_t)x < (int32_t)y : x < y;
                 switch (cmp) {
                   case KC_EQ: c = x == y; break;
@@ -522,7 +568,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             case KO_SELP64: {
               const bool p = (pbits >> s2) & 1u;
               if (op == KO_SELP32) {
-                const uint32_t x = rd32(k0, s0, I[6]), y = rd32(k1, s1, I[8]);
+                const uint32_t x = x0, y = x1;
                 rlo = p ? x : y;
               } else {
                 const uint64_t x = rd64(k0, s0, I[6], I[7]), y = rd64(k1, s1, I[8], I[9]);
@@ -551,7 +597,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
                   default: rlo = sl; break;
                 }
               } else {
-                rlo = rd32(k0, s0, I[6]);
+                rlo = x0;
               }
               break;
             default: {  // KO_MOV64
@@ -805,9 +851,17 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     if (w < W) {
       const uint32_t m_status = hl ? H1.status : H0.status;
       const uint32_t m_depth = hl ? H1.max_depth : H0.max_depth;
+      const uint32_t m_wi = hl ? H1.wi : H0.wi;
+      // thread-instructions: the sum over the warp's lanes of their active counts
+      uint64_t ti0 = 0, ti1 = 0;
+      for (uint32_t l = 0; l < 32u; ++l) {
+        ti0 += rl(act, l);
+        ti1 += rl(act, 32u + l);
+      }
+      const uint64_t m_ti = hl ? ti1 : ti0;
       const uint32_t cycles = v_next;
-      const uint32_t written = v_wi < cap ? v_wi : cap;
-      const uint32_t dropped = v_wi - written;
+      const uint32_t written = m_wi < cap ? m_wi : cap;
+      const uint32_t dropped = m_wi - written;
       const uint32_t status = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);
       const uint64_t gw = gw0 + hl;
       // staged records of a last, partly filled chunk (a full chunk was written when it filled)
@@ -816,12 +870,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       if (sl < 20) {
         uint32_t v;
         switch (sl) {
-          case C_TI_LO: v = (uint32_t)v_ti; break;
-          case C_TI_HI: v = (uint32_t)(v_ti >> 32); break;
+          case C_TI_LO: v = (uint32_t)m_ti; break;
+          case C_TI_HI: v = (uint32_t)(m_ti >> 32); break;
           case C_STATUS: v = status; break;
           case C_CYCLES: v = cycles; break;
-          case C_WARP_INSTRS: v = v_wi; break;
-          case C_STALL: v = cycles - v_wi; break;
+          case C_WARP_INSTRS: v = m_wi; break;
+          case C_STALL: v = cycles - m_wi; break;
           case C_MAXDEPTH: v = m_depth; break;
           case C_RES: v = 0; break;
           default: v = cnt; break;
@@ -844,18 +898,19 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   }
 }
 
+
 }  // namespace
 
 // Register file in LDS: any slot count that fits, blocks up to 1024 threads.
 __global__ void __launch_bounds__(1024) ks_interp_lds(const KsArgs a) { interp<0>(a); }
 
 // Register file in 32 reserved VGPRs (v96..v127): 128 VGPRs, blocks up to 1024 threads.
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(96))) ks_interp_v32(const KsArgs a) {
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(48))) ks_interp_v32(const KsArgs a) {
   interp<32>(a);
 }
 
 // Register file in 64 reserved VGPRs (v96..v159): 160 VGPRs, blocks up to 768 threads.
-__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(96))) ks_interp_v64(const KsArgs a) {
+__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(48))) ks_interp_v64(const KsArgs a) {
   interp<64>(a);
 }
 

@@ -1,0 +1,63 @@
+"""Resource checks of the gfx950 interpreter kernels (CPU: compile to assembly only).
+
+The VGPR register-file kernels keep simulated registers in v96 and up, outside
+the compiler's allocation; if compiler-written code ever touched them, simulated
+register values (and the compiler's own) would be silently corrupted.  These
+tests compile the kernels and check that no compiler-allocated instruction
+names a VGPR >= 96 and that no kernel spills to scratch, and that the checker
+itself rejects such assembly.
+"""
+import os
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.join(HERE, "..", "analysis_ptxsimulator_amd"))
+import build as kbuild  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(kbuild.HIPCC):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("asm") / "k.s")
+    return open(kbuild.device_asm(out)).read()
+
+
+def test_interpreters_leave_reserved_vgprs_alone(asm):
+    info = kbuild.check_device_asm(asm)
+    for k in kbuild.RESERVED_VGPR_KERNELS:
+        assert info[k]["max_compiler_vgpr"] < kbuild.RESERVED_BASE
+    for k in kbuild.INTERP_KERNELS:
+        assert info[k]["scratch"] == 0
+
+
+def _fake(kernel, body, scratch=0):
+    name = "_Z%d%sN2ks6KsArgsE" % (len(kernel), kernel)
+    text = ""
+    for k in kbuild.INTERP_KERNELS:
+        n = "_Z%d%sN2ks6KsArgsE" % (len(k), k)
+        b = body if k == kernel else "\ts_endpgm\n"
+        text += "%s:  ; @%s\n%s.Lfunc_end_%s:\n" % (n, n, b, k)
+    for k in kbuild.INTERP_KERNELS:
+        n = "_Z%d%sN2ks6KsArgsE" % (len(k), k)
+        text += "  - .name: %s\n    .private_segment_fixed_size: %d\n    .sgpr_count: 90\n    .vgpr_count: 128\n" % (
+            n, scratch if n == name else 0)
+    return text
+
+
+def test_checker_rejects_compiler_use_of_reserved_vgprs():
+    ok = "\t;;#ASMSTART\n\tv_mov_b32 v3, v96\n\t;;#ASMEND\n\tv_add_u32_e32 v95, v1, v2\n\ts_endpgm\n"
+    kbuild.check_device_asm(_fake("ks_interp_v32", ok))
+    for bad in ("\tv_add_u32_e32 v96, v1, v2\n", "\tv_mov_b64_e32 v[95:96], 0\n",
+                "\tglobal_load_dwordx4 v[100:103], v[0:1], off\n"):
+        with pytest.raises(RuntimeError, match="v9[6-9]|v10"):
+            kbuild.check_device_asm(_fake("ks_interp_v64", ok + bad))
+    # the LDS register-file kernel may use any VGPR
+    kbuild.check_device_asm(_fake("ks_interp_lds", "\tv_add_u32_e32 v120, v1, v2\n"))
+
+
+def test_checker_rejects_scratch():
+    with pytest.raises(RuntimeError, match="scratch"):
+        kbuild.check_device_asm(_fake("ks_interp_lds", "\ts_endpgm\n", scratch=16))

@@ -1197,6 +1197,17 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
   });
 }
 
+ks_status ks_interp_kernel(const ks_program* prog, ks_dim3 block, const char** name) {
+  return guarded([&]() -> ks_status {
+    if (!prog || !name) raise(KS_E_INVALID_ARG, 0, "NULL argument");
+    const uint64_t tpb = dim_count(block);
+    if (!tpb || tpb > KS_MAX_BLOCK_THREADS) raise(KS_E_INVALID_ARG, 0, "block of %llu threads", (unsigned long long)tpb);
+    const int variant = ks_choose_variant(prog->reg_slots, (uint32_t)tpb);
+    *name = variant == 32 ? "ks_interp_v32" : variant == 64 ? "ks_interp_v64" : "ks_interp_lds";
+    return KS_OK;
+  });
+}
+
 ks_status ks_read_outputs(ks_state* st, uint64_t sim_addr, void* host, size_t n, void* stream) {
   return guarded([&]() -> ks_status {
     if (!st || (!host && n)) raise(KS_E_INVALID_ARG, 0, "NULL argument");

@@ -67,6 +67,7 @@ _EXPORTS = {
     "ks_query_layout": ([_P, ctypes.POINTER(ks_config), ctypes.POINTER(ks_layout)], ctypes.c_int32),
     "ks_alloc_state": ([_P, ctypes.POINTER(ks_config), _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int32),
     "ks_run": ([_P, ks_dim3, ks_dim3, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
+    "ks_interp_kernel": ([_P, ks_dim3, ctypes.POINTER(ctypes.c_char_p)], ctypes.c_int32),
     "ks_read_outputs": ([_P, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
     "ks_read_counters": ([_P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
     "ks_read_trace": ([_P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
@@ -132,6 +133,12 @@ def ks_ipdom_table(prog):
     arr = (ctypes.c_uint32 * max(n, 1))()
     _check(lib().ks_ipdom_table(prog, arr, n))
     return [int(arr[i]) for i in range(n)]
+
+
+def ks_interp_kernel(prog, block):
+    name = ctypes.c_char_p()
+    _check(lib().ks_interp_kernel(prog, _dim3(block), ctypes.byref(name)))
+    return name.value.decode()
 
 
 def ks_default_config():

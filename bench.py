@@ -116,7 +116,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="random_stress")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=4096)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=32768)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "
@@ -156,6 +156,7 @@ def main():
 
     c = s.read_counters()
     status = s.status()
+    kernel = ks.ks_interp_kernel(s.prog, w.block)
     s.close()
     thread_instrs = int(c["thread_instrs"].sum())
     warp_acc = int(c["gld_n"].astype(np.uint64).sum() + c["gst_n"].sum() + c["sh_n"].sum())
@@ -189,7 +190,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
-                     "kernel": "ks_interp_kernel"},
+                     "kernel": kernel},
     }
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)

@@ -23,19 +23,21 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp
          "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
 
 
-# The VGPR register-file kernels keep simulated registers in v96 and up, which
-# the compiler must never allocate (they are reserved by amdgpu_num_vgpr); and no
-# interpreter may use scratch memory.
+# The VGPR register-file kernels keep simulated registers in v64 and up, which
+# the compiler must never allocate (they are reserved by amdgpu_num_vgpr), and
+# their VGPR count must cover the file; no interpreter may use scratch memory.
 RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64")
 INTERP_KERNELS = ("ks_interp_lds",) + RESERVED_VGPR_KERNELS
-RESERVED_BASE = 96
+RESERVED_BASE = 64
+RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72}  # register-file VGPRs from RESERVED_BASE on
 
 
 def check_device_asm(asm_text: str) -> dict:
     """Check the interpreter kernels' gfx950 assembly; returns per-kernel resources.
 
-    Raises RuntimeError when a kernel spills to scratch or when compiler-written
-    code (outside inline asm) in a register-file kernel names a VGPR >= 96."""
+    Raises RuntimeError when a kernel spills to scratch, when compiler-written
+    code (outside inline asm) in a register-file kernel names a VGPR at or above
+    RESERVED_BASE, or when such a kernel's VGPR count does not cover its file."""
     info = {}
     for k in INTERP_KERNELS:
         m = re.search(r"^(_Z\d+%sN2ks6KsArgsE):[^\n]*\n(.*?)^\.Lfunc_end" % k, asm_text, re.S | re.M)
@@ -66,6 +68,10 @@ def check_device_asm(asm_text: str) -> dict:
                 for lo, top, single in re.findall(r"\bv(?:\[(\d+):(\d+)\]|(\d+)\b)", line):
                     hi = max(hi, int(top or single))
             info[k]["max_compiler_vgpr"] = hi
+            need = RESERVED_BASE + RF_VGPRS[k]
+            if info[k]["vgprs"] < need:
+                raise RuntimeError("%s: VGPR count %d does not cover the register file (v%d..v%d)"
+                                   % (k, info[k]["vgprs"], RESERVED_BASE, need - 1))
             if hi >= RESERVED_BASE:
                 raise RuntimeError("%s: compiler-allocated code uses v%d (v%d+ hold the register file)"
                                    % (k, hi, RESERVED_BASE))

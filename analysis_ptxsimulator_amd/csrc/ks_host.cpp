@@ -941,6 +941,149 @@ void compute_reconvergence(ks_program* P) {
   }
 }
 
+// ---------------------------------------------------------------------------- device records
+//
+// Lower the parsed records to the interpreter's DInst records (n + 1 of them: a
+// DC_END sentinel after the last instruction).  Immediate source k goes to the
+// immediate slots reg_slots + 2k (low) and + 2k + 1 (high); f32 add, sub and mul
+// become one fused multiply-add with constant operands, which rounds exactly as
+// the separate operation does (x + y = fma(x, 1, y), x - y = fma(x, 1, -y),
+// x * y = fma(x, y, -0)); integer add/sub and mul/mad differ only in constants.
+std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
+  const uint32_t n = (uint32_t)P->code.size();
+  const uint32_t ib = P->reg_slots;
+  std::vector<DInst> out(n + 1);
+  auto sbo = [](uint8_t sb) -> uint32_t { return (uint32_t)(sb == KS_NO_SB ? KS_SB_ZERO : sb) * 4u; };
+  for (uint32_t i = 0; i <= n; ++i) {
+    DInst& d = out[i];
+    memset(&d, 0, sizeof d);
+    for (int k = 0; k < 4; ++k) d.sbo[k] = KS_SB_ZERO * 4u;
+    d.sbod = KS_SB_DUMP * 4u;
+    d.gmode = 2;
+    if (i == n) {
+      d.cls = DC_END;
+      continue;
+    }
+    const KsInst& in = P->code[i].in;
+    uint32_t slot[3];
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t kind = (in.kinds >> (2 * k)) & 3u;
+      if (kind == KK_IMM) {
+        slot[k] = ib + 2u * k;
+        d.imm[2 * k] = (uint32_t)in.imm[k];
+        d.imm[2 * k + 1] = (uint32_t)(in.imm[k] >> 32);
+        d.xf |= XF_IMM;
+      } else {
+        slot[k] = kind == KK_REG ? in.src[k] : 0u;
+      }
+    }
+    d.s0 = slot[0];
+    d.s1 = slot[1];
+    d.s2 = slot[2];
+    d.dst = in.dst;
+    for (int k = 0; k < 4; ++k) d.sbo[k] = sbo(in.sb[k]);
+    d.sbod = in.sb_dst == KS_NO_SB ? KS_SB_DUMP * 4u : (uint32_t)in.sb_dst * 4u;
+    d.lat = cfg->latency[in.lat];
+    if (in.flags & KF_GUARD) {
+      d.gp = in.guard;
+      d.gmode = (in.flags & KF_GUARD_NEG) ? 1u : 0u;
+    }
+    switch (in.op) {
+      case KO_ADD32: case KO_SUB32:
+        d.cls = DC_IADD;
+        d.a0 = in.op == KO_SUB32 ? 0xFFFFFFFFu : 0u;
+        d.a1 = in.op == KO_SUB32 ? 1u : 0u;
+        break;
+      case KO_MUL32: case KO_MAD32:
+        d.cls = DC_IMAD;
+        d.a0 = in.op == KO_MAD32 ? 0xFFFFFFFFu : 0u;
+        break;
+      case KO_ADD64: case KO_SUB64: case KO_MUL64: case KO_MAD64:
+        d.cls = DC_I64;
+        d.a0 = in.op == KO_ADD64 ? DI_ADD : in.op == KO_SUB64 ? DI_SUB : in.op == KO_MUL64 ? DI_MUL : DI_MAD;
+        break;
+      case KO_MULWIDE_S: case KO_MULWIDE_U:
+        d.cls = DC_I64;
+        d.a0 = in.op == KO_MULWIDE_S ? DI_WIDE_S : DI_WIDE_U;
+        break;
+      case KO_FADD: case KO_FSUB:  // fma(x0, 1.0, +-x1): x1 is read as the third operand
+        d.cls = DC_FARITH;
+        d.s1 = slot[0];
+        d.s2 = slot[1];
+        d.a0 = 0xFFFFFFFFu;
+        d.a1 = 0xFFFFFFFFu;
+        d.a2 = in.op == KO_FSUB ? 0x80000000u : 0u;
+        break;
+      case KO_FMUL:  // fma(x0, x1, -0.0)
+        d.cls = DC_FARITH;
+        d.s2 = slot[0];
+        d.a0 = 0;
+        d.a1 = 0;
+        d.a2 = 0x80000000u;
+        break;
+      case KO_FFMA:
+        d.cls = DC_FFMA;
+        break;
+      case KO_SETP_S32: case KO_SETP_U32: case KO_SETP_F32: case KO_SETP_S64: case KO_SETP_U64: {
+        d.cls = DC_SETP;
+        d.a0 = in.op == KO_SETP_S32 ? DS_S32 : in.op == KO_SETP_U32 ? DS_U32 : in.op == KO_SETP_F32 ? DS_F32
+             : in.op == KO_SETP_S64 ? DS_S64 : DS_U64;
+        static const uint32_t rel[6] = {2u, 5u, 1u, 3u, 4u, 6u};  // eq ne lt le gt ge over {lt, eq, gt}
+        d.a1 = rel[in.cmp];
+        break;
+      }
+      case KO_SELP32: case KO_SELP64:
+        d.cls = DC_SELP;
+        d.a0 = in.op == KO_SELP64 ? 1u : 0u;
+        d.s2 = in.src[2];  // predicate index
+        break;
+      case KO_MOV32: case KO_MOV64:
+        if ((in.kinds & 3u) == KK_SPECIAL) {
+          d.cls = DC_MOVSP;
+          d.a0 = in.src[0];
+        } else {
+          d.cls = DC_MOV;
+          d.a0 = in.op == KO_MOV64 ? 1u : 0u;
+        }
+        break;
+      case KO_LDP32: case KO_LDP64:
+        d.cls = DC_LDP;
+        d.a0 = in.aux;
+        d.a1 = in.op == KO_LDP64 ? 1u : 0u;
+        break;
+      case KO_LDG32: case KO_LDG64: case KO_STG32: case KO_STG64:
+      case KO_LDS32: case KO_LDS64: case KO_STS32: case KO_STS64: {
+        const bool g = in.op <= KO_STG64;
+        d.cls = g ? DC_MEMG : DC_MEMS;
+        const bool ld = in.op == KO_LDG32 || in.op == KO_LDG64 || in.op == KO_LDS32 || in.op == KO_LDS64;
+        const bool w64 = in.op == KO_LDG64 || in.op == KO_STG64 || in.op == KO_LDS64 || in.op == KO_STS64;
+        d.xf = (ld ? XF_LOAD : 0u) | (w64 ? XF_W64 : 0u) | (in.imm[0] == 64 ? XF_A64 : 0u);
+        d.s0 = in.src[0];
+        d.s1 = ld ? 0u : in.src[1];
+        d.a0 = (uint32_t)(uint64_t)in.off;
+        d.a1 = (uint32_t)((uint64_t)in.off >> 32);
+        break;
+      }
+      case KO_BRA:
+        d.cls = DC_BRA;
+        d.a0 = in.target;
+        d.a1 = in.rpc == KS_RPC_EXIT ? 0xFFFFFFFFu : in.rpc;
+        break;
+      case KO_BAR:
+        d.cls = DC_BAR;
+        break;
+      default:
+        d.cls = DC_RET;
+        break;
+    }
+  }
+  for (uint32_t i = 0; i < n; ++i) {
+    const KsInst& in = P->code[i].in;
+    if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].xf |= XF_RPC;
+  }
+  return out;
+}
+
 template <class F>
 ks_status guarded(F&& f) {
   try {
@@ -969,12 +1112,11 @@ struct ks_state {
   const ks_program* prog;
   ks_config cfg;
   int device;
-  KsInst* d_prog;
+  DInst* d_prog;
   void* d_gmem;
   void* d_counters;
   void* d_trace;
   uint32_t* d_status;
-  uint32_t slots;             // register-file capacity chosen for the kernel (32 or 64)
   uint64_t last_warps = 0;    // warps of the last run (0 = no run yet)
   uint64_t slot_bytes;
   uint64_t max_warps;
@@ -1102,22 +1244,15 @@ ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem
     hipDeviceProp_t prop;
     if (!hip_ok(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties")) return KS_E_HIP;
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) raise(KS_E_HIP, 0, "device %d is %s, not gfx950", dev, prop.gcnArchName);
-    std::vector<KsInst> table(p->code.size());
-    for (size_t i = 0; i < p->code.size(); ++i) {
-      table[i] = p->code[i].in;
-      table[i].lat = cfg->latency[p->code[i].in.lat];  // class -> cycles
-      // sources without a scoreboard entry read the always-zero sentinel entry
-      for (int k = 0; k < 4; ++k)
-        if (table[i].sb[k] == KS_NO_SB) table[i].sb[k] = KS_SB_ZERO;
-    }
-    KsInst* d_prog = nullptr;
+    const std::vector<DInst> table = lower_program(p, cfg);
+    DInst* d_prog = nullptr;
     uint32_t* d_status = nullptr;
-    if (!hip_ok(hipMalloc((void**)&d_prog, table.size() * sizeof(KsInst)), "hipMalloc(program)")) return KS_E_NOMEM;
+    if (!hip_ok(hipMalloc((void**)&d_prog, table.size() * sizeof(DInst)), "hipMalloc(program)")) return KS_E_NOMEM;
     if (!hip_ok(hipMalloc((void**)&d_status, 256), "hipMalloc(status)")) {
       (void)hipFree(d_prog);
       return KS_E_NOMEM;
     }
-    if (!hip_ok(hipMemcpy(d_prog, table.data(), table.size() * sizeof(KsInst), hipMemcpyHostToDevice), "hipMemcpy(program)")) {
+    if (!hip_ok(hipMemcpy(d_prog, table.data(), table.size() * sizeof(DInst), hipMemcpyHostToDevice), "hipMemcpy(program)")) {
       (void)hipFree(d_prog);
       (void)hipFree(d_status);
       return KS_E_HIP;
@@ -1131,7 +1266,6 @@ ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem
     st->d_counters = d_counters;
     st->d_trace = d_trace;
     st->d_status = d_status;
-    st->slots = p->reg_slots <= 32 ? 32 : 64;
     st->slot_bytes = lay.slot_bytes;
     st->max_warps = lay.n_warps;
     *out = st;
@@ -1178,7 +1312,7 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
     a.threads_per_block = (uint32_t)tpb;
     a.warps_per_block = (uint32_t)((tpb + 31) / 32);
     a.lat_bar = st->cfg.latency[KS_LAT_BAR];
-    a.rf_slots = p->reg_slots;
+    a.rf_slots = p->reg_slots + KS_IMM_SLOTS;
     if (p->param_bytes) memcpy(a.params, params, p->param_bytes);
     uint64_t warps = nb * a.warps_per_block;
     if (warps > st->max_warps) raise(KS_E_INVALID_ARG, 0, "run needs more warps than the allocation");
@@ -1190,7 +1324,7 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
         raise(KS_E_UNSUPPORTED, 0, "block of %u threads needs %zu bytes of LDS (limit %zu)", a.threads_per_block, need,
               ks_lds_limit() - 64);
     }
-    hipError_t e = ks_launch_interp(a, (uint32_t)nb, st->slots, (hipStream_t)stream);
+    hipError_t e = ks_launch_interp(a, (uint32_t)nb, p->reg_slots, (hipStream_t)stream);
     if (!hip_ok(e, "kernel launch")) return KS_E_HIP;
     st->last_warps = warps;
     return KS_OK;

@@ -1,8 +1,12 @@
 // ks_isa.h -- decoded-instruction records and launch arguments of libkscope.
 //
-// Internal to the library: the host encoder (ks_host.cpp) writes these records
-// and the gfx950 interpreter (ks_kernel.hip) reads them with scalar loads, one
-// 64-byte record per instruction, so that one s_load_dwordx16 fetches it.
+// Internal to the library.  The front end (ks_host.cpp) parses PTX into KsInst
+// records (one per instruction, operand kinds kept as written); when a state is
+// allocated they are lowered to DInst records, the form the gfx950 interpreter
+// (ks_kernel.hip) executes: every field the per-instruction path reads is a
+// whole dword, so the interpreter reads it with a scalar load and no bit
+// extraction, and operations are grouped into classes whose variants differ
+// only in per-instruction constants.
 #pragma once
 #include <stdint.h>
 
@@ -42,8 +46,10 @@ enum : uint8_t { KF_GUARD = 1, KF_GUARD_NEG = 2 };
 constexpr uint8_t KS_NO_SB = 0xFF;      // no scoreboard entry
 constexpr uint16_t KS_RPC_EXIT = 0xFFFF;
 constexpr uint32_t KS_SB_PRED_BASE = 64; // scoreboard index of predicate p = 64 + p
+constexpr uint8_t KS_SB_DUMP = 126;      // scoreboard entry written by instructions without a destination
 constexpr uint8_t KS_SB_ZERO = 127;      // scoreboard entry that always reads 0 (no source)
 constexpr uint32_t KS_SB_ENTRIES = 129;  // scoreboard words per warp in LDS (odd: warps start in different banks)
+constexpr uint32_t KS_IMM_SLOTS = 6;     // register slots after the program's that hold an instruction's immediates
 
 struct KsInst {            // 64 bytes
   uint8_t op;              // KOp
@@ -66,16 +72,68 @@ struct KsInst {            // 64 bytes
 };
 static_assert(sizeof(KsInst) == 64, "KsInst must be 64 bytes");
 
+// ---------------------------------------------------------------- device records
+//
+// Interpreter classes.  Register-writing classes first (their issue ends with
+// pc + 1), then memory, then control.
+enum DClass : uint32_t {
+  DC_FFMA,     // r = fma(x0, x1, x2)
+  DC_FARITH,   // add/sub/mul.f32 as one rounding: r = fma(x0, a0 ? 1.0 : x1, (x2 & a1) ^ a2)
+  DC_IADD,     // add/sub.{s,u}32: r = x0 + (x1 ^ a0) + a1
+  DC_IMAD,     // mul.lo/mad.lo.{s,u}32: r = x0 * x1 + (x2 & a0)
+  DC_MOV,      // mov (register or immediate); a0 = 1: 64-bit
+  DC_SELP,     // selp; s2 = predicate index; a0 = 1: 64-bit
+  DC_SETP,     // setp; a0 = DS_* operand type, a1 = relation mask (bit0 lt, bit1 eq, bit2 gt)
+  DC_I64,      // 64-bit integer ops and mul.wide; a0 = DI_*
+  DC_MOVSP,    // mov from a special register; a0 = KSP_*
+  DC_LDP,      // ld.param; a0 = byte offset in the parameter block, a1 = 1: 64-bit
+  DC_MEMG,     // ld/st.global; xf: XF_LOAD, XF_W64, XF_A64; (a0, a1) = byte offset (signed 64-bit)
+  DC_MEMS,     // ld/st.shared; as DC_MEMG
+  DC_BRA,      // bra; a0 = target, a1 = reconvergence index (0xFFFFFFFF = exit)
+  DC_BAR,      // bar.sync 0
+  DC_RET,      // ret / exit
+  DC_END,      // sentinel after the last instruction: lanes that get here exit at no cost
+};
+
+enum : uint32_t { DS_S32, DS_U32, DS_F32, DS_S64, DS_U64 };                 // DC_SETP operand types
+enum : uint32_t { DI_ADD, DI_SUB, DI_MUL, DI_MAD, DI_WIDE_S, DI_WIDE_U };  // DC_I64 operations
+
+// DInst::xf flags
+enum : uint32_t {
+  XF_IMM = 1,    // some source is an immediate: imm[] goes into the immediate slots first
+  XF_RPC = 2,    // a divergent branch reconverges here
+  XF_LOAD = 4,   // memory: load (else store)
+  XF_W64 = 8,    // memory: 8-byte access
+  XF_A64 = 16,   // memory: 64-bit address register
+};
+
+struct DInst {         // 128 bytes; dwords 0-15 are read for every instruction
+  uint32_t cls;        // DClass
+  uint32_t xf;         // XF_*
+  uint32_t s0, s1, s2; // source register slots (immediates: the immediate slots)
+  uint32_t dst;        // destination slot (low slot of a 64-bit register) or predicate index
+  uint32_t sbo[4];     // byte offsets in the warp's scoreboard of src0, src1, src2 and the guard
+  uint32_t sbod;       // byte offset of the destination's scoreboard word (the dump word if none)
+  uint32_t lat;        // cycles until the destination is ready
+  uint32_t gp;         // guard predicate index
+  uint32_t gmode;      // 0: @p, 1: @!p, 2: unguarded (compared with the predicate bit: on = bit != gmode)
+  uint32_t a0, a1;     // class-specific
+  uint32_t imm[6];     // immediate slot values: source k at imm[2k] (low) and imm[2k+1] (high)
+  uint32_t a2, a3;     // class-specific
+  uint32_t pad[8];
+};
+static_assert(sizeof(DInst) == 128, "DInst must be 128 bytes");
+
 constexpr int KS_PARAM_MAX = 512;
 
 struct KsArgs {
-  const KsInst* prog;
+  const DInst* prog;
   uint8_t* gmem;
   uint8_t* counters;
   uint8_t* trace;
   uint64_t gmem_bytes;
   uint64_t slot_bytes;
-  uint32_t n_instrs;
+  uint32_t n_instrs;       // instructions (the device table holds n_instrs + 1 records: DC_END last)
   uint32_t trace_cap;
   uint32_t max_warp_instrs;
   uint32_t shared_bytes;
@@ -84,7 +142,7 @@ struct KsArgs {
   uint32_t threads_per_block;
   uint32_t warps_per_block;
   uint32_t lat_bar;
-  uint32_t rf_slots;       // 32-bit register slots per simulated thread (LDS register file)
+  uint32_t rf_slots;       // register slots per simulated thread, immediate slots included
   uint8_t params[KS_PARAM_MAX];
 };
 

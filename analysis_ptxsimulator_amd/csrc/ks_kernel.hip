@@ -3,16 +3,23 @@
 // Mapping (CDNA4, wave64):
 //   * one workgroup = one simulated block; wave w runs simulated warps 2w
 //     (lanes 0-31) and 2w+1 (lanes 32-63), one GPU lane per simulated thread;
-//   * each wave-step executes ONE decoded instruction: the one at the smaller pc
+//   * each wave step executes ONE decoded instruction: the one at the smaller pc
 //     of the two warps (both warps run it when they share that pc), so fetch
-//     (s_load), decode, dispatch and register slot indices are wave-uniform;
+//     (scalar loads), dispatch and register slot indices are wave-uniform;
 //   * simulated registers live in a register file of 32-bit slots per lane,
-//     either in physical VGPRs reserved for it (v96 upward, indexed in the
-//     VGPR index mode of s_set_gpr_idx_on: zero latency, exec-masked writes) or,
-//     for programs or blocks that do not fit, in LDS as [slot][thread];
-//   * per-warp control state (stack top, masks, cycle counters) is scalar; the
-//     divergence stack, scoreboard, counters and a 32-record trace staging
-//     buffer live in VGPR lanes;
+//     either in physical VGPRs reserved for it (v64 upward, reached through the
+//     VGPR index mode of s_set_gpr_idx_on: exec-masked, no memory traffic) or,
+//     for programs or blocks that do not fit, in LDS as [slot][thread].  Six
+//     slots after the program's hold the current instruction's immediates, so
+//     every source operand is a register read;
+//   * lane masks of the two warps are 64-bit scalars (warp 2w in the low half),
+//     so one scalar operation updates both; per-warp values that the lanes use
+//     (next issue cycle, instruction count, trace state) are VGPRs that are
+//     uniform over each warp's 32 lanes; the divergence stack, counters and a
+//     32-record trace staging buffer live in VGPR lanes; the register
+//     scoreboard of each warp is an LDS array;
+//   * trace flushes, the issue budget and the cycle limit are one per-lane
+//     comparison per step against a precomputed event threshold;
 //   * the analyser counts distinct sectors/lines of monotone addresses with a
 //     DPP prefix-max within each 32-lane half (any active mask) and the bank
 //     degree of affine shared accesses in closed form; other patterns take an
@@ -42,9 +49,11 @@ using namespace ks;
 
 namespace {
 
-constexpr uint32_t H_RUN = 0, H_WAIT = 1, H_DONE = 2;
-constexpr uint32_t RPC_EXIT = 0xFFFFFFFFu;
+constexpr uint32_t INF = 0xFFFFFFFFu;
 constexpr uint32_t CYCLE_LIMIT = 0x7FFFFFFFu;
+constexpr uint64_t LO = 0x00000000FFFFFFFFull, HI = 0xFFFFFFFF00000000ull;
+// per-warp run state bits (one scalar for both warps of a wave)
+constexpr uint32_t WAIT0 = 1, WAIT1 = 2, DONE0 = 4, DONE1 = 8;
 
 // dword index of each field in the 80-byte counter record; the counter VGPR keeps
 // counter d of half h in lane 32 h + d
@@ -53,8 +62,7 @@ enum {
   C_GST_N, C_GST_SEC, C_GST_LINES, C_SH_N, C_SH_SUM, C_SH_MAX, C_DIV, C_BAR, C_FAULT, C_MAXDEPTH, C_RES
 };
 
-
-typedef const __attribute__((address_space(4))) uint32_t* cu32p;
+typedef const __attribute__((address_space(4))) DInst* cdinst;
 
 __device__ __forceinline__ uint32_t rl(uint32_t v, uint32_t l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
@@ -67,19 +75,24 @@ __device__ __forceinline__ uint64_t rl64(uint64_t v, uint32_t l) {
   return (uint64_t)rl((uint32_t)v, l) | ((uint64_t)rl((uint32_t)(v >> 32), l) << 32);
 }
 __device__ __forceinline__ uint64_t ballot(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+__device__ __forceinline__ bool lanes(uint64_t m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t popc(uint32_t m) { return (uint32_t)__builtin_popcount(m); }
 
 // ---------------------------------------------------------------------------- register files
 //
-// RF = 0: LDS, [slot][thread of the workgroup].  RF = 32 / 64: physical VGPRs
-// v96 .. v96+RF-1, outside the compiler's allocation; slot s of a lane is VGPR
-// v[96 + s] of that lane.  The kernels carry amdgpu_num_vgpr(48): on targets with
-// the unified VGPR/AGPR file the compiler doubles that figure, so v96 and up are
-// reserved (never allocated).  A larger figure that exceeds what the launch bound
-// allows is silently ignored, which would hand v96+ back to the allocator; the
-// build checks the assembly for any compiler-written use of them.
-template <int RF>
+// RFN = 0: LDS, [slot][thread of the workgroup].  RFN = 40 / 72: physical VGPRs
+// v64 .. v64+RFN-1, outside the compiler's allocation; slot s of a lane is VGPR
+// v[64 + s] of that lane.  The kernels carry amdgpu_num_vgpr(32): on targets with
+// the unified VGPR/AGPR file the compiler doubles that figure, so v64 and up are
+// reserved (never allocated).  A figure the launch bound cannot honour is
+// silently ignored, which would hand v64+ back to the allocator; the build checks
+// the assembly for any compiler-written use of them and that the kernel's VGPR
+// count covers the file (the zero() clobber lists make the compiler count it).
+
+template <int RFN>
 struct RegFile;
 
 template <>
@@ -103,148 +116,63 @@ struct RegFile<0> {
     put(s, lo);
     put(s + 1, hi);
   }
+  // the six immediate slots from slot `ib` on
+  __device__ __forceinline__ void put_imm(uint32_t ib, const uint32_t* v) const {
+    for (int k = 0; k < 6; ++k) put(ib + k, v[k]);
+  }
 };
 
 // VGPR index mode: between s_set_gpr_idx_on and s_set_gpr_idx_off the SRC0 (or
 // DST) VGPR operand of each VALU instruction is offset by the index held in M0;
 // s_set_gpr_idx_idx changes the index without leaving the mode.
-#define KS_RF_ASM_ACCESS                                                                          \
-  __device__ __forceinline__ uint32_t get(uint32_t s) const {                                     \
-    uint32_t r;                                                                                   \
-    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\ts_set_gpr_idx_off"  \
-                 : "=v"(r) : "s"(s) : "m0");                                                     \
-    return r;                                                                                     \
-  }                                                                                               \
-  __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const { \
-    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\t"                    \
-                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, v96\n\ts_set_gpr_idx_off"                 \
-                 : "=&v"(a), "=v"(b) : "s"(i0), "s"(i1) : "m0");                                 \
-  }                                                                                               \
+#define KS_RF_ASM_ACCESS                                                                           \
+  __device__ __forceinline__ uint32_t get(uint32_t s) const {                                      \
+    uint32_t r;                                                                                    \
+    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, v64\n\ts_set_gpr_idx_off"   \
+                 : "=v"(r) : "s"(s) : "m0");                                                      \
+    return r;                                                                                      \
+  }                                                                                                \
+  __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const {  \
+    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, v64\n\t"                     \
+                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, v64\n\ts_set_gpr_idx_off"                  \
+                 : "=&v"(a), "=v"(b) : "s"(i0), "s"(i1) : "m0");                                  \
+  }                                                                                                \
   __device__ __forceinline__ void get3(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t& a, uint32_t& b, \
-                                       uint32_t& c) const {                                       \
-    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, v96\n\t"                    \
-                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, v96\n\t"                                  \
-                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, v96\n\ts_set_gpr_idx_off"                 \
-                 : "=&v"(a), "=&v"(b), "=v"(c) : "s"(i0), "s"(i1), "s"(i2) : "m0");              \
-  }                                                                                               \
-  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                             \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v96, %1\n\ts_set_gpr_idx_off"   \
-                 : : "s"(s), "v"(v) : "m0");                                                     \
-  }                                                                                               \
-  __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {              \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v96, %1\n\t"                     \
-                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 v96, %2\n\ts_set_gpr_idx_off"                 \
-                 : : "s"(s), "v"(lo), "v"(hi), "s"(s + 1) : "m0");                               \
+                                       uint32_t& c) const {                                        \
+    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, v64\n\t"                     \
+                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, v64\n\t"                                   \
+                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, v64\n\ts_set_gpr_idx_off"                  \
+                 : "=&v"(a), "=&v"(b), "=v"(c) : "s"(i0), "s"(i1), "s"(i2) : "m0");               \
+  }                                                                                                \
+  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                              \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v64, %1\n\ts_set_gpr_idx_off"    \
+                 : : "s"(s), "v"(v) : "m0");                                                      \
+  }                                                                                                \
+  __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {               \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v64, %1\n\t"                      \
+                 "v_mov_b32 v65, %2\n\ts_set_gpr_idx_off"                                          \
+                 : : "s"(s), "v"(lo), "v"(hi) : "m0");                                            \
+  }                                                                                                \
+  __device__ __forceinline__ void put_imm(uint32_t ib, const uint32_t* v) const {                  \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\t"                                           \
+                 "v_mov_b32 v64, %1\n\tv_mov_b32 v65, %2\n\tv_mov_b32 v66, %3\n\t"                  \
+                 "v_mov_b32 v67, %4\n\tv_mov_b32 v68, %5\n\tv_mov_b32 v69, %6\n\t"                  \
+                 "s_set_gpr_idx_off"                                                               \
+                 : : "s"(ib), "s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5])     \
+                 : "m0");                                                                          \
   }
-
-#define KS_Z(i) "v_mov_b32 v" #i ", 0\n\t"
-#define KS_Z8(a, b, c, d, e, f, g, h) KS_Z(a) KS_Z(b) KS_Z(c) KS_Z(d) KS_Z(e) KS_Z(f) KS_Z(g) KS_Z(h)
-#define KS_C8(a, b, c, d, e, f, g, h) "v" #a, "v" #b, "v" #c, "v" #d, "v" #e, "v" #f, "v" #g, "v" #h
 
 template <>
-struct RegFile<32> {
+struct RegFile<40> {
   KS_RF_ASM_ACCESS
-  __device__ __forceinline__ static void zero() {
-    asm volatile(KS_Z8(96, 97, 98, 99, 100, 101, 102, 103) KS_Z8(104, 105, 106, 107, 108, 109, 110, 111)
-                     KS_Z8(112, 113, 114, 115, 116, 117, 118, 119) KS_Z8(120, 121, 122, 123, 124, 125, 126, 127)
-                 ::: KS_C8(96, 97, 98, 99, 100, 101, 102, 103), KS_C8(104, 105, 106, 107, 108, 109, 110, 111),
-                     KS_C8(112, 113, 114, 115, 116, 117, 118, 119), KS_C8(120, 121, 122, 123, 124, 125, 126, 127));
-  }
+  __device__ __forceinline__ static void zero() { asm volatile("v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t""v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t""v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t""v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t""v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t""v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t""v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t""v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t""v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t""v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t" ::: "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103"); }
 };
 
 template <>
-struct RegFile<64> {
+struct RegFile<72> {
   KS_RF_ASM_ACCESS
-  __device__ __forceinline__ static void zero() {
-    asm volatile(KS_Z8(96, 97, 98, 99, 100, 101, 102, 103) KS_Z8(104, 105, 106, 107, 108, 109, 110, 111)
-                     KS_Z8(112, 113, 114, 115, 116, 117, 118, 119) KS_Z8(120, 121, 122, 123, 124, 125, 126, 127)
-                         KS_Z8(128, 129, 130, 131, 132, 133, 134, 135) KS_Z8(136, 137, 138, 139, 140, 141, 142, 143)
-                             KS_Z8(144, 145, 146, 147, 148, 149, 150, 151) KS_Z8(152, 153, 154, 155, 156, 157, 158, 159)
-                 ::: KS_C8(96, 97, 98, 99, 100, 101, 102, 103), KS_C8(104, 105, 106, 107, 108, 109, 110, 111),
-                     KS_C8(112, 113, 114, 115, 116, 117, 118, 119), KS_C8(120, 121, 122, 123, 124, 125, 126, 127),
-                     KS_C8(128, 129, 130, 131, 132, 133, 134, 135), KS_C8(136, 137, 138, 139, 140, 141, 142, 143),
-                     KS_C8(144, 145, 146, 147, 148, 149, 150, 151), KS_C8(152, 153, 154, 155, 156, 157, 158, 159));
-  }
+  __device__ __forceinline__ static void zero() { asm volatile("v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t""v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t""v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t""v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t""v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t""v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t""v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t""v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t""v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t""v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t""v_mov_b32 v104, 0\n\t""v_mov_b32 v105, 0\n\t""v_mov_b32 v106, 0\n\t""v_mov_b32 v107, 0\n\t""v_mov_b32 v108, 0\n\t""v_mov_b32 v109, 0\n\t""v_mov_b32 v110, 0\n\t""v_mov_b32 v111, 0\n\t""v_mov_b32 v112, 0\n\t""v_mov_b32 v113, 0\n\t""v_mov_b32 v114, 0\n\t""v_mov_b32 v115, 0\n\t""v_mov_b32 v116, 0\n\t""v_mov_b32 v117, 0\n\t""v_mov_b32 v118, 0\n\t""v_mov_b32 v119, 0\n\t""v_mov_b32 v120, 0\n\t""v_mov_b32 v121, 0\n\t""v_mov_b32 v122, 0\n\t""v_mov_b32 v123, 0\n\t""v_mov_b32 v124, 0\n\t""v_mov_b32 v125, 0\n\t""v_mov_b32 v126, 0\n\t""v_mov_b32 v127, 0\n\t""v_mov_b32 v128, 0\n\t""v_mov_b32 v129, 0\n\t""v_mov_b32 v130, 0\n\t""v_mov_b32 v131, 0\n\t""v_mov_b32 v132, 0\n\t""v_mov_b32 v133, 0\n\t""v_mov_b32 v134, 0\n\t""v_mov_b32 v135, 0\n\t" ::: "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127", "v128", "v129", "v130", "v131", "v132", "v133", "v134", "v135"); }
 };
-
-// ---------------------------------------------------------------------------- divergence stack
-
-// Per-warp control state, wave-uniform (SGPRs).  The next-issue cycle of a warp
-// lives in a VGPR, uniform over the warp's 32 lanes.
-struct Half {
-  uint32_t pc, mask, rpc, sp;  // top of the divergence stack and its depth
-  uint32_t m;                  // mask & ~exited of the top entry
-  uint32_t exited, init_mask;
-  uint32_t state, status, max_depth, arrival;
-  uint32_t wi;                 // issued warp-instructions
-};
-
-__device__ __forceinline__ void hs_pop(Half& H, uint32_t spc, uint32_t sm, uint32_t sr) {
-  H.sp -= 1;
-  if (H.sp) {
-    H.pc = rl(spc, H.sp - 1);
-    H.mask = rl(sm, H.sp - 1);
-    H.rpc = rl(sr, H.sp - 1);
-  }
-}
-
-__device__ __forceinline__ void hs_push(Half& H, uint32_t& spc, uint32_t& sm, uint32_t& sr, uint32_t pc, uint32_t mask,
-                                        uint32_t rpc, uint32_t lane) {
-  spc = wl(spc, H.pc, H.sp - 1, lane);
-  sm = wl(sm, H.mask, H.sp - 1, lane);
-  sr = wl(sr, H.rpc, H.sp - 1, lane);
-  H.pc = pc;
-  H.mask = mask;
-  H.m = mask & ~H.exited;
-  H.rpc = rpc;
-  H.sp += 1;
-  H.max_depth = umax(H.max_depth, H.sp);
-}
-
-// The top entry cannot issue: no live lane, reconverged, or past the end.
-__device__ __forceinline__ bool hs_blocked(const Half& H, uint32_t n) {
-  return H.state == H_RUN && (H.m == 0 || H.pc == H.rpc || H.pc >= n);
-}
-
-// Pop finished or reconverged entries; lanes that ran off the end exit at no cost.
-__device__ __forceinline__ void hs_settle(Half& H, uint32_t spc, uint32_t sm, uint32_t sr, uint32_t n) {
-  while (H.sp) {
-    H.m = H.mask & ~H.exited;
-    if (H.m == 0 || H.pc == H.rpc) {
-      hs_pop(H, spc, sm, sr);
-      continue;
-    }
-    if (H.pc >= n) {
-      H.exited |= H.m;
-      continue;
-    }
-    return;
-  }
-  H.state = H_DONE;
-  H.status |= KS_ST_FINISHED;
-}
-
-__device__ __forceinline__ void half_init(Half& H, uint32_t w, uint32_t W, uint32_t T) {
-  const bool exists = w < W;
-  const uint32_t live = T > w * 32u ? (T - w * 32u > 32u ? 32u : T - w * 32u) : 0u;
-  H.init_mask = live >= 32u ? 0xFFFFFFFFu : ((1u << live) - 1u);
-  H.pc = 0;
-  H.mask = H.init_mask;
-  H.m = H.init_mask;
-  H.rpc = RPC_EXIT;
-  H.sp = exists ? 1u : 0u;
-  H.exited = 0;
-  H.state = exists ? H_RUN : H_DONE;
-  H.status = 0;
-  H.max_depth = 1;
-  H.arrival = 0;
-  H.wi = 0;
-}
-
-__device__ __forceinline__ uint32_t cnt_add(uint32_t cnt, uint32_t lane, uint32_t idx, uint32_t v) {
-  return cnt + (lane == idx ? v : 0u);
-}
-
 
 // ---------------------------------------------------------------------------- analyser
 
@@ -301,9 +229,52 @@ __device__ __forceinline__ uint32_t canon_bits(float r) {
   return __builtin_isnan(r) ? 0x7FFFFFFFu : __float_as_uint(r);
 }
 
+// Add v to counter d of the warps in `hm` (bit 0: warp 2w, bit 1: warp 2w+1).
+__device__ __forceinline__ uint32_t cnt_add2(uint32_t cnt, uint32_t sl, uint32_t hl, uint32_t d, uint32_t hm, uint32_t v) {
+  return cnt + ((sl == d && ((hm >> hl) & 1u)) ? v : 0u);
+}
+
+// ---------------------------------------------------------------------------- divergence stack
+//
+// The top entry of each warp's stack is scalar state: mask (in the 64-bit mask
+// pair), reconvergence pc, depth, and pc.  While the warp runs its top pc is its
+// scheduled pc; Stk::pc holds it across a barrier wait and inside stack updates.
+// Entries below it live in lanes 0..depth-2 of two VGPRs per warp: pc | rpc << 16
+// (0xFFFF = exit) and mask.
+
+struct Stk {
+  uint32_t pc, rpc, sp, md;   // top pc (see above), top reconvergence pc (INF = exit), depth, maximum depth
+  uint32_t pr, m;             // VGPRs: saved entries
+};
+
+__device__ __forceinline__ uint32_t enc_rpc(uint32_t r) { return r == INF ? 0xFFFFu : r; }
+
+// Pop: the entry below becomes the top (returns its mask).
+__device__ __forceinline__ uint32_t stk_pop(Stk& S) {
+  S.sp -= 1;
+  uint32_t mask = 0;
+  if (S.sp) {
+    const uint32_t pr = rl(S.pr, S.sp - 1);
+    S.pc = pr & 0xFFFFu;
+    S.rpc = (pr >> 16) == 0xFFFFu ? INF : (pr >> 16);
+    mask = rl(S.m, S.sp - 1);
+  }
+  return mask;
+}
+
+// Push (pc, rpc) with `mask` over the current top (whose mask is `top_mask`).
+__device__ __forceinline__ void stk_push(Stk& S, uint32_t top_mask, uint32_t pc, uint32_t rpc, uint32_t lane) {
+  S.pr = wl(S.pr, (S.pc & 0xFFFFu) | (enc_rpc(S.rpc) << 16), S.sp - 1, lane);
+  S.m = wl(S.m, top_mask, S.sp - 1, lane);
+  S.pc = pc;
+  S.rpc = rpc;
+  S.sp += 1;
+  S.md = umax(S.md, S.sp);
+}
+
 // ---------------------------------------------------------------------------- the interpreter
 
-template <int RF>
+template <int RFN>
 __device__ __forceinline__ void interp(const KsArgs& a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ uint32_t ep_max[3], ep_alive[3];
@@ -318,16 +289,18 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t W = a.warps_per_block;
   const uint32_t T = a.threads_per_block;
   const uint32_t n_instr = a.n_instrs;
+  const cdinst prog = (cdinst)(uintptr_t)a.prog;
+  const uint32_t ib = a.rf_slots - KS_IMM_SLOTS;  // first immediate slot
 
   // LDS: [register file (LDS variant)] [scoreboard, 129 words per warp] [shared window]
-  RegFile<RF> R;
-  const uint32_t rf_words = RF == 0 ? (a.rf_slots ? a.rf_slots : 1u) * WG : 0u;
-  if constexpr (RF == 0) {
+  RegFile<RFN> R;
+  const uint32_t rf_words = RFN == 0 ? a.rf_slots * WG : 0u;
+  if constexpr (RFN == 0) {
     R.base = lds;
     R.stride = WG;
     R.tid = tid;
   } else {
-    RegFile<RF>::zero();
+    RegFile<RFN>::zero();
   }
   uint32_t* const sbw = lds + rf_words;
   uint8_t* const win = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
@@ -341,349 +314,350 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   }
   __syncthreads();
 
-  // special registers of this lane's simulated thread
   const uint32_t my_w = 2u * wave + hl;
-  const uint32_t t_lin = my_w * 32u + sl;
-  const uint32_t bx = a.block[0], by = a.block[1];
-  const uint32_t tid_x = t_lin % bx, tid_y = (t_lin / bx) % by, tid_z = t_lin / (bx * by);
-  const uint32_t gx = a.grid[0], gy = a.grid[1];
-  const uint32_t cta_x = blk % gx, cta_y = (blk / gx) % gy, cta_z = blk / (gx * gy);
   const bool small_gmem = a.gmem_bytes <= (1ull << 37);  // sector ids of valid accesses fit 32 bits
-  uint32_t* const my_sb = sbw + my_w * KS_SB_ENTRIES;    // this lane's warp's scoreboard
+  uint8_t* const my_sb = reinterpret_cast<uint8_t*>(sbw + my_w * KS_SB_ENTRIES);  // this lane's warp's scoreboard
+  auto sb_at = [&](uint32_t off) -> uint32_t& { return *reinterpret_cast<uint32_t*>(my_sb + off); };
 
-  Half H0, H1;
-  half_init(H0, 2u * wave, W, T);
-  half_init(H1, 2u * wave + 1u, W, T);
-  uint32_t stk_pc0 = 0, stk_m0 = 0, stk_r0 = 0, stk_pc1 = 0, stk_m1 = 0, stk_r1 = 0;
-  uint32_t v_next = 0;      // previous issue cycle + 1 of the lane's warp (uniform over the warp)
-  uint32_t cnt = 0;         // counter d of the lane's warp in lane 32 h + d
-  uint32_t pbits = 0;       // predicate p of this lane's thread in bit p
-  uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
-  uint32_t act = 0;         // instructions issued with this lane's thread active
+  // per-warp scalar state (warp 2w = half 0, warp 2w+1 = half 1)
+  const uint32_t w0 = 2u * wave, w1 = w0 + 1u;
+  auto live_mask = [&](uint32_t w) -> uint32_t {
+    if (w >= W) return 0u;
+    const uint32_t live = T - w * 32u;
+    return live >= 32u ? 0xFFFFFFFFu : ((1u << live) - 1u);
+  };
+  const uint64_t init64 = (uint64_t)live_mask(w0) | ((uint64_t)live_mask(w1) << 32);
+  uint64_t mask64 = init64;   // masks of the two top entries
+  uint64_t ex64 = 0;          // exited lanes
+  uint64_t m64 = init64;      // mask64 & ~ex64
+  Stk S0, S1;
+  S0.pc = 0; S0.rpc = INF; S0.sp = w0 < W ? 1u : 0u; S0.md = 1; S0.pr = 0; S0.m = 0;
+  S1.pc = 0; S1.rpc = INF; S1.sp = w1 < W ? 1u : 0u; S1.md = 1; S1.pr = 0; S1.m = 0;
+  uint32_t spc0 = w0 < W ? 0u : INF, spc1 = w1 < W ? 0u : INF;  // scheduled pc: top pc while running, else INF
+  uint32_t hst = (w0 < W ? 0u : DONE0) | (w1 < W ? 0u : DONE1);
+  uint32_t status = 0;        // KS_ST_* of warp 2w in bits 0-7, of warp 2w+1 in bits 8-15
 
+  // per-lane state (uniform over each warp's lanes where noted)
   const uint32_t cap = a.trace_cap;
   const uint32_t budget = a.max_warp_instrs;
+  uint32_t v_next = 0;        // warp: previous issue cycle + 1
+  uint32_t wi = 0;            // warp: issued warp-instructions
+  uint32_t fl = 0;            // warp: trace records written to memory
+  uint32_t nf = cap == 0 ? INF : umin(cap, 32u);  // warp: record count at which the next chunk is written
+  uint32_t ev = umin(nf, budget);                 // warp: next event (chunk write or budget)
+  uint32_t act = 0;           // instructions issued with this lane's thread active
+  uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
+  uint32_t pbits = 0;         // predicate p of this lane's thread in bit p
+  uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
   const uint64_t gw0 = (uint64_t)blk * W + 2u * wave;  // global warp id of half 0
   uint8_t* const slot_base = a.trace + (gw0 + hl) * a.slot_bytes + 16u;  // this lane's warp's records
+
+  // Pop entries of warp h that cannot issue (no live lane, reconverged); lanes past
+  // the end exit at no cost; an empty stack finishes the warp.  Leaves spc_h.
+#define KS_SETTLE(h, S, spc)                                                   \
+  {                                                                            \
+    while (true) {                                                             \
+      if (S.sp == 0) {                                                         \
+        spc = INF;                                                             \
+        hst |= DONE0 << (h);                                                   \
+        status |= KS_ST_FINISHED << (8 * (h));                                 \
+        break;                                                                 \
+      }                                                                        \
+      const uint32_t mk = (uint32_t)(mask64 >> (32 * (h)));                    \
+      const uint32_t lv = mk & ~(uint32_t)(ex64 >> (32 * (h)));                \
+      if (lv == 0 || S.pc == S.rpc) {                                          \
+        const uint32_t nm = stk_pop(S);                                        \
+        mask64 = (mask64 & ~((uint64_t)0xFFFFFFFFu << (32 * (h)))) | ((uint64_t)nm << (32 * (h))); \
+        continue;                                                              \
+      }                                                                        \
+      if (S.pc >= n_instr) {                                                   \
+        ex64 |= (uint64_t)lv << (32 * (h));                                    \
+        continue;                                                              \
+      }                                                                        \
+      spc = S.pc;                                                              \
+      break;                                                                   \
+    }                                                                          \
+    m64 = mask64 & ~ex64;                                                      \
+  }
 
   uint32_t epoch = 0;
   while (true) {
     // ------------------------------------------------------------------ run both warps until blocked
     while (true) {
-      if (hs_blocked(H0, n_instr)) hs_settle(H0, stk_pc0, stk_m0, stk_r0, n_instr);
-      if (hs_blocked(H1, n_instr)) hs_settle(H1, stk_pc1, stk_m1, stk_r1, n_instr);
-      const bool r0 = H0.state == H_RUN, r1 = H1.state == H_RUN;
-      if (!r0 && !r1) break;
-      const uint32_t pc = uni((r0 && r1) ? (H0.pc < H1.pc ? H0.pc : H1.pc) : (r0 ? H0.pc : H1.pc));
-      bool go0 = r0 && H0.pc == pc, go1 = r1 && H1.pc == pc;
-      if ((go0 && H0.wi >= budget) || (go1 && H1.wi >= budget)) {  // issue budget
-        if (go0 && H0.wi >= budget) {
-          H0.state = H_DONE;
-          H0.status |= KS_ST_BUDGET;
+      const uint32_t pc = umin(spc0, spc1);
+      if (pc == INF) break;
+      const bool go0 = spc0 == pc, go1 = spc1 == pc;
+      const uint64_t gm = (go0 ? LO : 0ull) | (go1 ? HI : 0ull);
+      const cdinst I = prog + pc;
+      const uint32_t cls = I->cls;
+      const uint32_t xf = I->xf;
+
+      if (cls == DC_END) {  // past the last instruction: those lanes exit, no issue
+        ex64 |= m64 & gm;
+        if (go0) {
+          S0.pc = pc;
+          KS_SETTLE(0, S0, spc0);
         }
-        if (go1 && H1.wi >= budget) {
-          H1.state = H_DONE;
-          H1.status |= KS_ST_BUDGET;
+        if (go1) {
+          S1.pc = pc;
+          KS_SETTLE(1, S1, spc1);
         }
         continue;
       }
-
-      const cu32p I = (cu32p)(uintptr_t)(a.prog + pc);
-      const uint32_t w0 = I[0], w1 = I[1], wsb = I[2], w3 = I[3];
-      const uint32_t op = w0 & 0xFFu, flags = (w0 >> 8) & 0xFFu, dst = (w0 >> 16) & 0xFFu, guard = w0 >> 24;
-      const uint32_t kinds = w1 >> 24;
-      const uint32_t sb_dst = w3 & 0xFFu, cmp = (w3 >> 8) & 0xFFu, lat = w3 >> 16;
-
-      // lanes of the warps that issue this instruction
-      const uint64_t gm = (go0 ? 0xFFFFFFFFull : 0ull) | (go1 ? 0xFFFFFFFF00000000ull : 0ull);
-
-      // issue cycle (per warp, uniform over its lanes): the later of the previous issue
-      // + 1 and the ready cycle of every register source (absent sources read entry 127 = 0)
-      const uint32_t iss = umax(v_next, umax(umax(my_sb[wsb & 0xFFu], my_sb[(wsb >> 8) & 0xFFu]),
-                                             umax(my_sb[(wsb >> 16) & 0xFFu], my_sb[wsb >> 24])));
-      {
-        const uint64_t ovf = ballot(iss > CYCLE_LIMIT) & gm;
-        if (ovf) {
-          if (ovf & 1u) {
-            H0.state = H_DONE;
-            H0.status |= KS_ST_CYCLE_OVF;
+      if (xf & XF_RPC) {  // reconvergence point: warps whose top entry ends here pop first
+        const bool p0 = go0 && S0.rpc == pc, p1 = go1 && S1.rpc == pc;
+        if (p0 || p1) {
+          if (p0) {
+            S0.pc = pc;
+            KS_SETTLE(0, S0, spc0);
           }
-          if (ovf >> 32) {
-            H1.state = H_DONE;
-            H1.status |= KS_ST_CYCLE_OVF;
+          if (p1) {
+            S1.pc = pc;
+            KS_SETTLE(1, S1, spc1);
           }
           continue;
         }
       }
-      const uint32_t m0 = go0 ? H0.m : 0u;
-      const uint32_t m1 = go1 ? H1.m : 0u;
 
-      // trace: stage the record in lane k % 32 of the warp; write 32 records at once
+      // issue cycle (per warp, uniform over its lanes): the later of the previous issue
+      // + 1 and the ready cycle of every register source (absent sources read a zero word)
+      const uint32_t iss = umax(umax(v_next, sb_at(I->sbo[0])),
+                                umax(umax(sb_at(I->sbo[1]), sb_at(I->sbo[2])), sb_at(I->sbo[3])));
+
+      // events: trace chunk complete, issue budget reached, cycle limit passed
       {
-        const bool rec0 = go0 && H0.wi < cap, rec1 = go1 && H1.wi < cap;
-        const uint32_t k0 = H0.wi & 31u, k1 = H1.wi & 31u;
-        const uint64_t smask = (rec0 ? (1ull << k0) : 0ull) | (rec1 ? (1ull << (32 + k1)) : 0ull);
-        if (__builtin_amdgcn_inverse_ballot_w64(smask)) {
+        const uint64_t evm = ballot(wi == ev || iss > CYCLE_LIMIT) & gm;
+        if (evm) {
+          const uint64_t bm = ballot(wi == budget) & gm;                 // budget first
+          const uint64_t om = ballot(iss > CYCLE_LIMIT) & gm & ~bm;
+          const uint64_t fm = ballot(wi == nf) & gm & ~om;               // a full chunk (or the cap) to write
+          if (lanes(fm)) {
+            if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+            fl = wi;
+            nf = wi < cap ? umin(cap, wi + 32u) : INF;
+          }
+          if (lanes(gm)) ev = umin(nf, budget);
+          const uint64_t stop = bm | om;
+          if (stop & LO) {
+            spc0 = INF;
+            hst |= DONE0;
+            status |= (bm & LO) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF;
+          }
+          if (stop & HI) {
+            spc1 = INF;
+            hst |= DONE1;
+            status |= ((bm & HI) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF) << 8;
+          }
+          continue;
+        }
+      }
+
+      // issue
+      const uint64_t mm = m64 & gm;  // live lanes of the issuing warps
+      const uint64_t on64 = mm & ballot(((pbits >> I->gp) & 1u) != I->gmode);  // guard
+      if (lanes(gm)) {
+        if (sl == (wi & 31u)) {
           tr_c = iss;
           tr_p = pc;
         }
-        const bool fl0 = rec0 && (k0 == 31u || H0.wi + 1u == cap);
-        const bool fl1 = rec1 && (k1 == 31u || H1.wi + 1u == cap);
-        if (fl0 || fl1) {
-          const uint64_t fmask = (fl0 ? (0xFFFFFFFFull >> (31u - k0)) : 0ull) |
-                                 (fl1 ? ((0xFFFFFFFFull >> (31u - k1)) << 32) : 0ull);
-          const uint32_t chunk = (hl ? H1.wi : H0.wi) & ~31u;
-          if (__builtin_amdgcn_inverse_ballot_w64(fmask))
-            *reinterpret_cast<uint2*>(slot_base + 8ull * (chunk + sl)) = make_uint2(tr_c, tr_p);
-        }
-      }
-      H0.wi += go0 ? 1u : 0u;
-      H1.wi += go1 ? 1u : 0u;
-      act += __builtin_amdgcn_inverse_ballot_w64((uint64_t)m0 | ((uint64_t)m1 << 32)) ? 1u : 0u;
-      if (__builtin_amdgcn_inverse_ballot_w64(gm)) {
+        wi += 1;
         v_next = iss + 1;
-        if (sb_dst != 0xFFu) my_sb[sb_dst] = iss + lat;
+        sb_at(I->sbod) = iss + I->lat;
       }
-
-      // guard: lanes that execute
-      uint64_t on64 = (uint64_t)m0 | ((uint64_t)m1 << 32);
-      if (flags & KF_GUARD) on64 &= ballot((((pbits >> guard) & 1u) != 0) != ((flags & KF_GUARD_NEG) != 0));
-      const bool on = __builtin_amdgcn_inverse_ballot_w64(on64);
+      act += lanes(mm) ? 1u : 0u;
       const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
 
       // ---------------------------------------------------------------- execute
-      if (op < KO_LDP32) {
-        if (on) {
-          const uint32_t s0 = w1 & 0xFFu, s1 = (w1 >> 8) & 0xFFu, s2 = (w1 >> 16) & 0xFFu;
-          const uint32_t k0 = kinds & 3u, k1 = (kinds >> 2) & 3u, k2 = (kinds >> 4) & 3u;
-          // register or immediate operands: the three slots are read in one go (slot 0 stands
-          // in for an immediate), then immediates replace the values read
-          uint32_t x0, x1, x2;
-          R.get3(s0, s1, s2, x0, x1, x2);
-          x0 = k0 == KK_REG ? x0 : I[6];
-          x1 = k1 == KK_REG ? x1 : I[8];
-          x2 = k2 == KK_REG ? x2 : I[10];
-          auto rd64 = [&](uint32_t kind, uint32_t s, uint32_t imm_lo, uint32_t imm_hi) -> uint64_t {
-            if (kind == KK_REG) {
+      if (cls <= DC_LDP) {
+        if (xf & XF_IMM) {
+          uint32_t iv[6];
+          for (int k = 0; k < 6; ++k) iv[k] = I->imm[k];
+          R.put_imm(ib, iv);
+        }
+        if (lanes(on64)) {
+          const uint32_t s0 = I->s0, s1 = I->s1, s2 = I->s2, dst = I->dst;
+          const uint32_t a0 = I->a0, a1 = I->a1;
+          if (cls == DC_FFMA) {
+            uint32_t x0, x1, x2;
+            R.get3(s0, s1, s2, x0, x1, x2);
+            R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1), __uint_as_float(x2))));
+          } else if (cls == DC_FARITH) {
+            uint32_t x0, x1, x2;
+            R.get3(s0, s1, s2, x0, x1, x2);
+            const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
+            const uint32_t c = (x2 & a1) ^ I->a2;                 // x2, -x2 or -0.0f
+            R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(c))));
+          } else if (cls == DC_IADD) {
+            uint32_t x0, x1;
+            R.get2(s0, s1, x0, x1);
+            R.put(dst, x0 + (x1 ^ a0) + a1);
+          } else if (cls == DC_IMAD) {
+            uint32_t x0, x1, x2;
+            R.get3(s0, s1, s2, x0, x1, x2);
+            R.put(dst, x0 * x1 + (x2 & a0));
+          } else if (cls == DC_MOV) {
+            if (a0) {
               uint32_t lo, hi;
-              R.get2(s, s + 1, lo, hi);
-              return (uint64_t)lo | ((uint64_t)hi << 32);
+              R.get2(s0, s0 + 1u, lo, hi);
+              R.put2(dst, lo, hi);
+            } else {
+              R.put(dst, R.get(s0));
             }
-            return (uint64_t)imm_lo | ((uint64_t)imm_hi << 32);
-          };
-          uint32_t rlo = 0, rhi = 0;
-          bool wide = false, wr = true;
-          switch (op) {
-            case KO_ADD32: rlo = x0 + x1; break;
-            case KO_SUB32: rlo = x0 - x1; break;
-            case KO_MUL32: rlo = x0 * x1; break;
-            case KO_MAD32: rlo = x0 * x1 + x2; break;
-            case KO_ADD64:
-            case KO_SUB64:
-            case KO_MUL64:
-            case KO_MAD64: {
-              const uint64_t x = rd64(k0, s0, I[6], I[7]), y = rd64(k1, s1, I[8], I[9]);
-              uint64_t r;
-              if (op == KO_ADD64) r = x + y;
-              else if (op == KO_SUB64) r = x - y;
-              else if (op == KO_MUL64) r = x * y;
-              else r = x * y + rd64(k2, s2, I[10], I[11]);
-              rlo = (uint32_t)r;
-              rhi = (uint32_t)(r >> 32);
-              wide = true;
-              break;
+          } else if (cls == DC_SELP) {
+            const bool p = (pbits >> s2) & 1u;
+            if (a0) {
+              uint32_t xl, xh, yl, yh;
+              R.get2(s0, s0 + 1u, xl, xh);
+              R.get2(s1, s1 + 1u, yl, yh);
+              R.put2(dst, p ? xl : yl, p ? xh : yh);
+            } else {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              R.put(dst, p ? x0 : x1);
             }
-            case KO_MULWIDE_S: {
-              const int64_t r = (int64_t)(int32_t)x0 * (int64_t)(int32_t)x1;
-              rlo = (uint32_t)r;
-              rhi = (uint32_t)((uint64_t)r >> 32);
-              wide = true;
-              break;
+          } else if (cls == DC_SETP) {
+            bool lt, eq, gt;
+            if (a0 == DS_F32) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              const float x = __uint_as_float(x0), y = __uint_as_float(x1);
+              lt = x < y;
+              eq = x == y;
+              gt = x > y;  // all false when an input is NaN
+            } else if (a0 <= DS_U32) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              lt = a0 == DS_S32 ? (int32_t)x0 < (int32_t)x1 : x0 < x1;
+              eq = x0 == x1;
+              gt = !lt && !eq;
+            } else {
+              uint32_t xl, xh, yl, yh;
+              R.get2(s0, s0 + 1u, xl, xh);
+              R.get2(s1, s1 + 1u, yl, yh);
+              const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
+              lt = a0 == DS_S64 ? (int64_t)x < (int64_t)y : x < y;
+              eq = x == y;
+              gt = !lt && !eq;
             }
-            case KO_MULWIDE_U: {
-              const uint64_t r = (uint64_t)x0 * (uint64_t)x1;
-              rlo = (uint32_t)r;
-              rhi = (uint32_t)(r >> 32);
-              wide = true;
-              break;
-            }
-            case KO_FADD:
-              rlo = canon_bits(__uint_as_float(x0) + __uint_as_float(x1));
-              break;
-            case KO_FSUB:
-              rlo = canon_bits(__uint_as_float(x0) - __uint_as_float(x1));
-              break;
-            case KO_FMUL:
-              rlo = canon_bits(__uint_as_float(x0) * __uint_as_float(x1));
-              break;
-            case KO_FFMA:
-              rlo = canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1),
-                                              __uint_as_float(x2)));
-              break;
-            case KO_SETP_S32:
-            case KO_SETP_U32:
-            case KO_SETP_S64:
-            case KO_SETP_U64:
-            case KO_SETP_F32: {
-              bool c;
-              if (op == KO_SETP_F32) {
-                const float x = __uint_as_float(x0), y = __uint_as_float(x1);
-                // ordered comparisons: false whenever an input is NaN
-                switch (cmp) {
-                  case KC_EQ: c = x == y; break;
-                  case KC_NE: c = x < y || x > y; break;
-                  case KC_LT: c = x < y; break;
-                  case KC_LE: c = x <= y; break;
-                  case KC_GT: c = x > y; break;
-                  default: c = x >= y; break;
-                }
-              } else if (op == KO_SETP_S32 || op == KO_SETP_U32) {
-                const uint32_t x = x0, y = x1;
-                const bool lt = op == KO_SETP_S32 ? (int32_t)x < (int32_t)y : x < y;
-                switch (cmp) {
-                  case KC_EQ: c = x == y; break;
-                  case KC_NE: c = x != y; break;
-                  case KC_LT: c = lt; break;
-                  case KC_LE: c = lt || x == y; break;
-                  case KC_GT: c = !lt && x != y; break;
-                  default: c = !lt; break;
-                }
-              } else {
-                const uint64_t x = rd64(k0, s0, I[6], I[7]), y = rd64(k1, s1, I[8], I[9]);
-                const bool lt = op == KO_SETP_S64 ? (int64_t)x < (int64_t)y : x < y;
-                switch (cmp) {
-                  case KC_EQ: c = x == y; break;
-                  case KC_NE: c = x != y; break;
-                  case KC_LT: c = lt; break;
-                  case KC_LE: c = lt || x == y; break;
-                  case KC_GT: c = !lt && x != y; break;
-                  default: c = !lt; break;
-                }
+            const bool c = (lt && (a1 & 1u)) || (eq && (a1 & 2u)) || (gt && (a1 & 4u));
+            pbits = (pbits & ~(1u << dst)) | ((c ? 1u : 0u) << dst);
+          } else if (cls == DC_I64) {
+            uint64_t r;
+            if (a0 >= DI_WIDE_S) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              r = a0 == DI_WIDE_S ? (uint64_t)((int64_t)(int32_t)x0 * (int64_t)(int32_t)x1)
+                                  : (uint64_t)x0 * (uint64_t)x1;
+            } else {
+              uint32_t xl, xh, yl, yh;
+              R.get2(s0, s0 + 1u, xl, xh);
+              R.get2(s1, s1 + 1u, yl, yh);
+              const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
+              if (a0 == DI_ADD) r = x + y;
+              else if (a0 == DI_SUB) r = x - y;
+              else if (a0 == DI_MUL) r = x * y;
+              else {
+                uint32_t zl, zh;
+                R.get2(s2, s2 + 1u, zl, zh);
+                r = x * y + ((uint64_t)zl | ((uint64_t)zh << 32));
               }
-              pbits = (pbits & ~(1u << dst)) | ((c ? 1u : 0u) << dst);
-              wr = false;
-              break;
             }
-            case KO_SELP32:
-            case KO_SELP64: {
-              const bool p = (pbits >> s2) & 1u;
-              if (op == KO_SELP32) {
-                const uint32_t x = x0, y = x1;
-                rlo = p ? x : y;
-              } else {
-                const uint64_t x = rd64(k0, s0, I[6], I[7]), y = rd64(k1, s1, I[8], I[9]);
-                const uint64_t r = p ? x : y;
-                rlo = (uint32_t)r;
-                rhi = (uint32_t)(r >> 32);
-                wide = true;
-              }
-              break;
+            R.put2(dst, (uint32_t)r, (uint32_t)(r >> 32));
+          } else if (cls == DC_MOVSP) {
+            const uint32_t t_lin = my_w * 32u + sl;
+            const uint32_t bx = a.block[0], by = a.block[1];
+            const uint32_t gx = a.grid[0], gy = a.grid[1];
+            uint32_t v;
+            switch (a0) {
+              case KSP_TID_X: v = t_lin % bx; break;
+              case KSP_TID_Y: v = (t_lin / bx) % by; break;
+              case KSP_TID_Z: v = t_lin / (bx * by); break;
+              case KSP_NTID_X: v = a.block[0]; break;
+              case KSP_NTID_Y: v = a.block[1]; break;
+              case KSP_NTID_Z: v = a.block[2]; break;
+              case KSP_CTAID_X: v = blk % gx; break;
+              case KSP_CTAID_Y: v = (blk / gx) % gy; break;
+              case KSP_CTAID_Z: v = blk / (gx * gy); break;
+              case KSP_NCTAID_X: v = a.grid[0]; break;
+              case KSP_NCTAID_Y: v = a.grid[1]; break;
+              case KSP_NCTAID_Z: v = a.grid[2]; break;
+              default: v = sl; break;
             }
-            case KO_MOV32:
-              if (k0 == KK_SPECIAL) {
-                switch (s0) {
-                  case KSP_TID_X: rlo = tid_x; break;
-                  case KSP_TID_Y: rlo = tid_y; break;
-                  case KSP_TID_Z: rlo = tid_z; break;
-                  case KSP_NTID_X: rlo = a.block[0]; break;
-                  case KSP_NTID_Y: rlo = a.block[1]; break;
-                  case KSP_NTID_Z: rlo = a.block[2]; break;
-                  case KSP_CTAID_X: rlo = cta_x; break;
-                  case KSP_CTAID_Y: rlo = cta_y; break;
-                  case KSP_CTAID_Z: rlo = cta_z; break;
-                  case KSP_NCTAID_X: rlo = a.grid[0]; break;
-                  case KSP_NCTAID_Y: rlo = a.grid[1]; break;
-                  case KSP_NCTAID_Z: rlo = a.grid[2]; break;
-                  default: rlo = sl; break;
-                }
-              } else {
-                rlo = x0;
-              }
-              break;
-            default: {  // KO_MOV64
-              const uint64_t r = rd64(k0, s0, I[6], I[7]);
-              rlo = (uint32_t)r;
-              rhi = (uint32_t)(r >> 32);
-              wide = true;
-              break;
-            }
-          }
-          if (wr) {
-            R.put(dst, rlo);
-            if (wide) R.put(dst + 1, rhi);
+            R.put(dst, v);
+          } else {  // DC_LDP: a uniform value from the launch arguments
+            const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + a0);
+            if (a1) R.put2(dst, lo, *reinterpret_cast<const uint32_t*>(a.params + a0 + 4u));
+            else R.put(dst, lo);
           }
         }
-      } else if (op <= KO_LDP64) {
-        // parameter load: uniform value from the launch arguments
-        const uint32_t aux = I[5] & 0xFFFFu;
-        const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + aux);
-        const uint32_t hi = op == KO_LDP64 ? *reinterpret_cast<const uint32_t*>(a.params + aux + 4) : 0u;
-        if (on) {
-          R.put(dst, lo);
-          if (op == KO_LDP64) R.put(dst + 1, hi);
-        }
-      } else if (op <= KO_STS64) {
-        const bool is_global = op <= KO_STG64;
-        const bool is_load = op == KO_LDG32 || op == KO_LDG64 || op == KO_LDS32 || op == KO_LDS64;
-        const bool w64 = op == KO_LDG64 || op == KO_STG64 || op == KO_LDS64 || op == KO_STS64;
+        spc0 = go0 ? pc + 1u : spc0;
+        spc1 = go1 ? pc + 1u : spc1;
+      } else if (cls <= DC_MEMS) {
+        const bool is_global = cls == DC_MEMG;
+        const bool is_load = xf & XF_LOAD;
+        const bool w64 = xf & XF_W64;
         const uint32_t S = w64 ? 8u : 4u;
         const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
-        const uint32_t s0 = w1 & 0xFFu, s1 = (w1 >> 8) & 0xFFu;
-        const uint32_t addr_w = I[6];
-        const uint64_t off = (uint64_t)I[12] | ((uint64_t)I[13] << 32);
-        uint64_t A = 0;
-        bool ok = false;
-        if (on) {
-          uint64_t base = R.get(s0);
-          if (addr_w == 64u) base |= (uint64_t)R.get(s0 + 1) << 32;
-          A = base + off;
-          ok = (A & (S - 1u)) == 0 && A <= size && size - A >= S;
-          if (is_load) {
-            uint32_t lo = 0, hi = 0;
-            if (ok) {
-              if (is_global) {
-                if (w64) {
-                  const uint2 v = *reinterpret_cast<const uint2*>(a.gmem + A);
-                  lo = v.x;
-                  hi = v.y;
-                } else {
-                  lo = *reinterpret_cast<const uint32_t*>(a.gmem + A);
-                }
-              } else {
-                lo = *reinterpret_cast<const uint32_t*>(win + A);
-                if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
-              }
-            }
-            R.put(dst, lo);
-            if (w64) R.put(dst + 1, hi);
-          } else if (ok) {
-            const uint32_t lo = R.get(s1);
+        const uint64_t off = (uint64_t)I->a0 | ((uint64_t)I->a1 << 32);
+        const uint32_t s0 = I->s0;
+        uint64_t base;
+        if (xf & XF_A64) {
+          uint32_t lo, hi;
+          R.get2(s0, s0 + 1u, lo, hi);
+          base = (uint64_t)lo | ((uint64_t)hi << 32);
+        } else {
+          base = R.get(s0);
+        }
+        const uint64_t A = base + off;
+        const bool ok = (A & (S - 1u)) == 0 && A <= size && size - A >= S;
+        const uint64_t okm = ballot(ok) & on64;
+        if (is_load) {
+          uint32_t lo = 0, hi = 0;
+          if (lanes(okm)) {
             if (is_global) {
               if (w64) {
-                *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, R.get(s1 + 1));
+                const uint2 v = *reinterpret_cast<const uint2*>(a.gmem + A);
+                lo = v.x;
+                hi = v.y;
               } else {
-                *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
+                lo = *reinterpret_cast<const uint32_t*>(a.gmem + A);
               }
             } else {
-              *reinterpret_cast<uint32_t*>(win + A) = lo;
-              if (w64) *reinterpret_cast<uint32_t*>(win + A + 4) = R.get(s1 + 1);
+              lo = *reinterpret_cast<const uint32_t*>(win + A);
+              if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
             }
+          }
+          if (lanes(on64)) {
+            if (w64) R.put2(I->dst, lo, hi);
+            else R.put(I->dst, lo);
+          }
+        } else if (lanes(okm)) {
+          const uint32_t s1 = I->s1;
+          if (w64) {
+            uint32_t lo, hi;
+            R.get2(s1, s1 + 1u, lo, hi);
+            if (is_global) {
+              *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, hi);
+            } else {
+              *reinterpret_cast<uint32_t*>(win + A) = lo;
+              *reinterpret_cast<uint32_t*>(win + A + 4) = hi;
+            }
+          } else {
+            const uint32_t lo = R.get(s1);
+            if (is_global) *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
+            else *reinterpret_cast<uint32_t*>(win + A) = lo;
           }
         }
         // fault counting and analysis (full exec)
-        const uint64_t faults = ballot(on && !ok);
+        const uint64_t faults = on64 & ~okm;
         if (faults) {
-          const uint32_t f0 = (uint32_t)__builtin_popcountll(faults & 0xFFFFFFFFull);
-          const uint32_t f1 = (uint32_t)__builtin_popcountll(faults >> 32);
-          if (f0) {
-            H0.status |= KS_ST_FAULT;
-            cnt = cnt_add(cnt, lane, C_FAULT, f0);
-          }
-          if (f1) {
-            H1.status |= KS_ST_FAULT;
-            cnt = cnt_add(cnt, lane, 32 + C_FAULT, f1);
-          }
+          const uint32_t f0 = popc((uint32_t)faults), f1 = popc((uint32_t)(faults >> 32));
+          if (f0) status |= KS_ST_FAULT;
+          if (f1) status |= KS_ST_FAULT << 8;
+          cnt += sl == C_FAULT ? (hl ? f1 : f0) : 0u;
         }
+        const bool on = lanes(on64);
+        const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
         if (is_global) {
           uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;
           bool slow0 = g0 != 0, slow1 = g1 != 0;
@@ -696,14 +670,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             const uint64_t newl = ballot(on && (s >> 2) != (prev >> 2));
             if (g0 && !(uint32_t)nonmono) {
               const uint32_t first = g0 & (0u - g0);
-              sec0 = (uint32_t)__builtin_popcount((uint32_t)news | first);
-              lin0 = (uint32_t)__builtin_popcount((uint32_t)newl | first);
+              sec0 = popc((uint32_t)news | first);
+              lin0 = popc((uint32_t)newl | first);
               slow0 = false;
             }
             if (g1 && !(uint32_t)(nonmono >> 32)) {
               const uint32_t first = g1 & (0u - g1);
-              sec1 = (uint32_t)__builtin_popcount((uint32_t)(news >> 32) | first);
-              lin1 = (uint32_t)__builtin_popcount((uint32_t)(newl >> 32) | first);
+              sec1 = popc((uint32_t)(news >> 32) | first);
+              lin1 = popc((uint32_t)(newl >> 32) | first);
               slow1 = false;
             }
           }
@@ -720,9 +694,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
           // counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2}
           const uint32_t cn = is_load ? C_GLD_N : C_GST_N;
-          const uint32_t gh = hl ? g1 : g0;
           const uint32_t d = sl - cn;
-          if (gh && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0));
+          if (((hm >> hl) & 1u) && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0));
         } else {
           uint32_t d0 = 1, d1 = 1;
           bool slow0 = g0 != 0, slow1 = g1 != 0;
@@ -745,88 +718,105 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
           if (slow0) d0 = bank_degree(A, (uint64_t)g0);
           if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
-          const uint32_t gh = hl ? g1 : g0;
           const uint32_t dh = hl ? d1 : d0;
-          if (gh) {
+          if ((hm >> hl) & 1u) {
             if (sl == C_SH_N) cnt += 1;
             if (sl == C_SH_SUM) cnt += dh;
             if (sl == C_SH_MAX) cnt = umax(cnt, dh);
           }
         }
-      }
-
-      // ---------------------------------------------------------------- control (scalar)
-      if (op == KO_BRA) {
-        const uint32_t w4 = I[4];
-        const uint32_t target = w4 & 0xFFFFu, rpc_raw = w4 >> 16;
-        const uint32_t rpc = rpc_raw == KS_RPC_EXIT ? RPC_EXIT : rpc_raw;
+        spc0 = go0 ? pc + 1u : spc0;
+        spc1 = go1 ? pc + 1u : spc1;
+      } else if (cls == DC_BRA) {
+        const uint32_t target = I->a0, rpc = I->a1;
+        const uint32_t mm0 = (uint32_t)mm, mm1 = (uint32_t)(mm >> 32);
+        uint32_t divm = 0;
         if (go0) {
-          const uint32_t nt = m0 & ~g0;
+          const uint32_t nt = mm0 & ~g0;
           if (nt == 0) {
-            H0.pc = target;
+            spc0 = target;
           } else if (g0 == 0) {
-            H0.pc = pc + 1;
+            spc0 = pc + 1u;
           } else {
-            H0.pc = rpc;
-            cnt = cnt_add(cnt, lane, C_DIV, 1);
-            if (target != rpc) hs_push(H0, stk_pc0, stk_m0, stk_r0, target, g0, rpc, lane);
-            if (pc + 1 != rpc) hs_push(H0, stk_pc0, stk_m0, stk_r0, pc + 1, nt, rpc, lane);
+            divm |= 1u;
+            const uint32_t mk = (uint32_t)mask64;
+            S0.pc = rpc;
+            if (target != rpc) stk_push(S0, mk, target, rpc, lane);
+            uint32_t top = target != rpc ? g0 : mk;
+            if (pc + 1u != rpc) {
+              stk_push(S0, top, pc + 1u, rpc, lane);
+              top = nt;
+            }
+            mask64 = (mask64 & HI) | top;
+            spc0 = S0.pc;
           }
         }
         if (go1) {
-          const uint32_t nt = m1 & ~g1;
+          const uint32_t nt = mm1 & ~g1;
           if (nt == 0) {
-            H1.pc = target;
+            spc1 = target;
           } else if (g1 == 0) {
-            H1.pc = pc + 1;
+            spc1 = pc + 1u;
           } else {
-            H1.pc = rpc;
-            cnt = cnt_add(cnt, lane, 32 + C_DIV, 1);
-            if (target != rpc) hs_push(H1, stk_pc1, stk_m1, stk_r1, target, g1, rpc, lane);
-            if (pc + 1 != rpc) hs_push(H1, stk_pc1, stk_m1, stk_r1, pc + 1, nt, rpc, lane);
+            divm |= 2u;
+            const uint32_t mk = (uint32_t)(mask64 >> 32);
+            S1.pc = rpc;
+            if (target != rpc) stk_push(S1, mk, target, rpc, lane);
+            uint32_t top = target != rpc ? g1 : mk;
+            if (pc + 1u != rpc) {
+              stk_push(S1, top, pc + 1u, rpc, lane);
+              top = nt;
+            }
+            mask64 = (mask64 & LO) | ((uint64_t)top << 32);
+            spc1 = S1.pc;
           }
         }
-      } else if (op == KO_RET) {
+        if (divm) {
+          m64 = mask64 & ~ex64;
+          cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
+        }
+      } else if (cls == DC_RET) {
+        ex64 |= on64;
+        m64 = mask64 & ~ex64;
         if (go0) {
-          H0.exited |= g0;
-          H0.m = H0.mask & ~H0.exited;
-          H0.pc = pc + 1;
+          spc0 = pc + 1u;
+          S0.pc = pc + 1u;
+          if ((uint32_t)m64 == 0) KS_SETTLE(0, S0, spc0);
         }
         if (go1) {
-          H1.exited |= g1;
-          H1.m = H1.mask & ~H1.exited;
-          H1.pc = pc + 1;
+          spc1 = pc + 1u;
+          S1.pc = pc + 1u;
+          if ((uint32_t)(m64 >> 32) == 0) KS_SETTLE(1, S1, spc1);
         }
-      } else if (op == KO_BAR) {
+      } else {  // DC_BAR: the issuing warps wait for the block
+        const uint64_t conv = init64 & ~ex64;
+        const uint32_t hm = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
+        cnt = cnt_add2(cnt, sl, hl, C_BAR, hm, 1u);
         if (go0) {
-          cnt = cnt_add(cnt, lane, C_BAR, 1);
-          if (m0 != (H0.init_mask & ~H0.exited)) H0.status |= KS_ST_BARDIV;
-          H0.state = H_WAIT;
-          H0.arrival = rl(iss, 0);
-          H0.pc = pc + 1;
+          if ((uint32_t)mm != (uint32_t)conv) status |= KS_ST_BARDIV;
+          S0.pc = pc + 1u;
+          spc0 = INF;
+          hst |= WAIT0;
         }
         if (go1) {
-          cnt = cnt_add(cnt, lane, 32 + C_BAR, 1);
-          if (m1 != (H1.init_mask & ~H1.exited)) H1.status |= KS_ST_BARDIV;
-          H1.state = H_WAIT;
-          H1.arrival = rl(iss, 32);
-          H1.pc = pc + 1;
+          if ((uint32_t)(mm >> 32) != (uint32_t)(conv >> 32)) status |= KS_ST_BARDIV << 8;
+          S1.pc = pc + 1u;
+          spc1 = INF;
+          hst |= WAIT1;
         }
-      } else {
-        H0.pc += go0 ? 1u : 0u;
-        H1.pc += go1 ? 1u : 0u;
       }
     }
 
     // ------------------------------------------------------------------ barrier epoch
     const uint32_t slot = epoch % 3u;
     if (lane == 0) {
-      const uint32_t alive = (H0.state != H_DONE ? 1u : 0u) + (H1.state != H_DONE ? 1u : 0u);
-      uint32_t mx = H0.state == H_WAIT ? H0.arrival : 0u;
-      if (H1.state == H_WAIT && H1.arrival > mx) mx = H1.arrival;
+      const uint32_t alive = ((hst & DONE0) ? 0u : 1u) + ((hst & DONE1) ? 0u : 1u);
+      // a waiting warp arrived at its last issue cycle: v_next - 1
+      const uint32_t a0 = (hst & WAIT0) ? rl(v_next, 0) - 1u : 0u;
+      const uint32_t a1 = (hst & WAIT1) ? rl(v_next, 32) - 1u : 0u;
       if (alive) {
         atomicAdd(&ep_alive[slot], alive);
-        atomicMax(&ep_max[slot], mx);
+        atomicMax(&ep_max[slot], umax(a0, a1));
       }
     }
     if (tid == 0) {  // clear the slot of the next epoch (last read two epochs ago)
@@ -838,44 +828,44 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     if (alive_all == 0) break;
     // release: every waiting warp's next issue waits for max(arrival) + lat(bar.sync)
     const uint32_t release = uni(ep_max[slot]) + a.lat_bar;
-    const bool waiting = hl ? H1.state == H_WAIT : H0.state == H_WAIT;
+    const bool waiting = (hst >> hl) & 1u;
     if (waiting) v_next = umax(v_next, release);
-    if (H0.state == H_WAIT) H0.state = H_RUN;
-    if (H1.state == H_WAIT) H1.state = H_RUN;
+    if (hst & WAIT0) spc0 = S0.pc;
+    if (hst & WAIT1) spc1 = S1.pc;
+    hst &= ~(WAIT0 | WAIT1);
     ++epoch;
   }
+#undef KS_SETTLE
 
   // -------------------------------------------------------------------- counters, trace tail, headers
   {
     const uint32_t w = my_w;
+    // thread-instructions: the sum over the warp's lanes of their active counts
+    uint64_t ti0 = 0, ti1 = 0;
+    for (uint32_t l = 0; l < 32u; ++l) {
+      ti0 += rl(act, l);
+      ti1 += rl(act, 32u + l);
+    }
     if (w < W) {
-      const uint32_t m_status = hl ? H1.status : H0.status;
-      const uint32_t m_depth = hl ? H1.max_depth : H0.max_depth;
-      const uint32_t m_wi = hl ? H1.wi : H0.wi;
-      // thread-instructions: the sum over the warp's lanes of their active counts
-      uint64_t ti0 = 0, ti1 = 0;
-      for (uint32_t l = 0; l < 32u; ++l) {
-        ti0 += rl(act, l);
-        ti1 += rl(act, 32u + l);
-      }
+      const uint32_t m_status = (status >> (8u * hl)) & 0xFFu;
+      const uint32_t m_depth = hl ? S1.md : S0.md;
       const uint64_t m_ti = hl ? ti1 : ti0;
       const uint32_t cycles = v_next;
-      const uint32_t written = m_wi < cap ? m_wi : cap;
-      const uint32_t dropped = m_wi - written;
-      const uint32_t status = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);
+      const uint32_t written = umin(wi, cap);
+      const uint32_t dropped = wi - written;
+      const uint32_t st = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);
       const uint64_t gw = gw0 + hl;
-      // staged records of a last, partly filled chunk (a full chunk was written when it filled)
-      if (sl < (written & 31u))
-        *reinterpret_cast<uint2*>(slot_base + 8ull * ((written & ~31u) + sl)) = make_uint2(tr_c, tr_p);
+      // records staged since the last chunk write
+      if (sl < written - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
       if (sl < 20) {
         uint32_t v;
         switch (sl) {
           case C_TI_LO: v = (uint32_t)m_ti; break;
           case C_TI_HI: v = (uint32_t)(m_ti >> 32); break;
-          case C_STATUS: v = status; break;
+          case C_STATUS: v = st; break;
           case C_CYCLES: v = cycles; break;
-          case C_WARP_INSTRS: v = m_wi; break;
-          case C_STALL: v = cycles - m_wi; break;
+          case C_WARP_INSTRS: v = wi; break;
+          case C_STALL: v = cycles - wi; break;
           case C_MAXDEPTH: v = m_depth; break;
           case C_RES: v = 0; break;
           default: v = cnt; break;
@@ -883,8 +873,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         reinterpret_cast<uint32_t*>(a.counters + gw * 80u)[sl] = v;
       }
       if (sl < 4) {
-        const uint32_t flags = (dropped ? 1u : 0u) | ((status & KS_ST_FAULT) ? 2u : 0u) |
-                               ((status & KS_ST_BUDGET) ? 4u : 0u) | ((status & KS_ST_FINISHED) ? 8u : 0u);
+        const uint32_t flags = (dropped ? 1u : 0u) | ((st & KS_ST_FAULT) ? 2u : 0u) |
+                               ((st & KS_ST_BUDGET) ? 4u : 0u) | ((st & KS_ST_FINISHED) ? 8u : 0u);
         uint32_t v;
         switch (sl) {
           case 0: v = written; break;
@@ -898,20 +888,21 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   }
 }
 
-
 }  // namespace
 
 // Register file in LDS: any slot count that fits, blocks up to 1024 threads.
 __global__ void __launch_bounds__(1024) ks_interp_lds(const KsArgs a) { interp<0>(a); }
 
-// Register file in 32 reserved VGPRs (v96..v127): 128 VGPRs, blocks up to 1024 threads.
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(48))) ks_interp_v32(const KsArgs a) {
-  interp<32>(a);
+// Register file in 40 reserved VGPRs (v64..v103): 104 VGPRs, 4 waves per SIMD,
+// blocks up to 1024 threads.
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v32(const KsArgs a) {
+  interp<40>(a);
 }
 
-// Register file in 64 reserved VGPRs (v96..v159): 160 VGPRs, blocks up to 768 threads.
-__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(48))) ks_interp_v64(const KsArgs a) {
-  interp<64>(a);
+// Register file in 72 reserved VGPRs (v64..v135): 136 VGPRs, 3 waves per SIMD,
+// blocks up to 768 threads.
+__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64(const KsArgs a) {
+  interp<72>(a);
 }
 
 __global__ void ks_zero_word(uint32_t* out) { *out = 0; }
@@ -931,15 +922,17 @@ size_t ks_lds_limit() {
   return (size_t)v;
 }
 
+// Register-file variant: total slots = program slots + the immediate slots.
 int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
   const uint32_t waves = ((block_threads + 31u) / 32u + 1u) / 2u;
-  if (slots <= 32) return 32;
-  if (slots <= 64 && waves <= 12) return 64;
+  const uint32_t total = slots + KS_IMM_SLOTS;
+  if (total <= 40) return 32;
+  if (total <= 72 && waves <= 12) return 64;
   return 0;
 }
 
 size_t ks_lds_bytes(int variant, uint32_t slots, uint32_t wg, uint32_t shared_bytes) {
-  const size_t rf = variant == 0 ? (size_t)(slots ? slots : 1u) * wg * 4u : 0u;
+  const size_t rf = variant == 0 ? (size_t)(slots + KS_IMM_SLOTS) * wg * 4u : 0u;
   const size_t sb = (size_t)(wg / 32u) * KS_SB_ENTRIES * 4u;
   return rf + sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
 }
@@ -950,6 +943,7 @@ hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, 
   const int variant = ks_choose_variant(slots, a.threads_per_block);
   const size_t lds = ks_lds_bytes(variant, slots, wg, a.shared_bytes);
   if (lds + 64 > ks_lds_limit()) return hipErrorInvalidValue;
+  if (a.rf_slots != slots + KS_IMM_SLOTS) return hipErrorInvalidValue;
   const void* fn = variant == 32 ? (const void*)ks_interp_v32
                    : variant == 64 ? (const void*)ks_interp_v64
                                    : (const void*)ks_interp_lds;

@@ -1,11 +1,13 @@
 """Resource checks of the gfx950 interpreter kernels (CPU: compile to assembly only).
 
-The VGPR register-file kernels keep simulated registers in v96 and up, outside
+The VGPR register-file kernels keep simulated registers in v64 and up, outside
 the compiler's allocation; if compiler-written code ever touched them, simulated
-register values (and the compiler's own) would be silently corrupted.  These
-tests compile the kernels and check that no compiler-allocated instruction
-names a VGPR >= 96 and that no kernel spills to scratch, and that the checker
-itself rejects such assembly.
+register values (and the compiler's own) would be silently corrupted, and if the
+kernel's VGPR count did not cover the file, indexed accesses would reach past
+the wave's allocation.  These tests compile the kernels and check that no
+compiler-allocated instruction names a VGPR at or above the base, that the VGPR
+count covers the file and that no kernel spills to scratch, and that the checker
+itself rejects assembly that breaks any of these.
 """
 import os
 import sys
@@ -33,7 +35,7 @@ def test_interpreters_leave_reserved_vgprs_alone(asm):
         assert info[k]["scratch"] == 0
 
 
-def _fake(kernel, body, scratch=0):
+def _fake(kernel, body, scratch=0, vgprs=None):
     name = "_Z%d%sN2ks6KsArgsE" % (len(kernel), kernel)
     text = ""
     for k in kbuild.INTERP_KERNELS:
@@ -42,20 +44,29 @@ def _fake(kernel, body, scratch=0):
         text += "%s:  ; @%s\n%s.Lfunc_end_%s:\n" % (n, n, b, k)
     for k in kbuild.INTERP_KERNELS:
         n = "_Z%d%sN2ks6KsArgsE" % (len(k), k)
-        text += "  - .name: %s\n    .private_segment_fixed_size: %d\n    .sgpr_count: 90\n    .vgpr_count: 128\n" % (
-            n, scratch if n == name else 0)
+        v = vgprs if (vgprs is not None and n == name) else 200
+        text += "  - .name: %s\n    .private_segment_fixed_size: %d\n    .sgpr_count: 90\n    .vgpr_count: %d\n" % (
+            n, scratch if n == name else 0, v)
     return text
 
 
 def test_checker_rejects_compiler_use_of_reserved_vgprs():
-    ok = "\t;;#ASMSTART\n\tv_mov_b32 v3, v96\n\t;;#ASMEND\n\tv_add_u32_e32 v95, v1, v2\n\ts_endpgm\n"
+    b = kbuild.RESERVED_BASE
+    ok = "\t;;#ASMSTART\n\tv_mov_b32 v3, v%d\n\t;;#ASMEND\n\tv_add_u32_e32 v%d, v1, v2\n\ts_endpgm\n" % (b, b - 1)
     kbuild.check_device_asm(_fake("ks_interp_v32", ok))
-    for bad in ("\tv_add_u32_e32 v96, v1, v2\n", "\tv_mov_b64_e32 v[95:96], 0\n",
-                "\tglobal_load_dwordx4 v[100:103], v[0:1], off\n"):
-        with pytest.raises(RuntimeError, match="v9[6-9]|v10"):
+    for bad in ("\tv_add_u32_e32 v%d, v1, v2\n" % b, "\tv_mov_b64_e32 v[%d:%d], 0\n" % (b - 1, b),
+                "\tglobal_load_dwordx4 v[%d:%d], v[0:1], off\n" % (b + 4, b + 7)):
+        with pytest.raises(RuntimeError, match="compiler-allocated code uses v"):
             kbuild.check_device_asm(_fake("ks_interp_v64", ok + bad))
     # the LDS register-file kernel may use any VGPR
     kbuild.check_device_asm(_fake("ks_interp_lds", "\tv_add_u32_e32 v120, v1, v2\n"))
+
+
+def test_checker_rejects_short_vgpr_count():
+    for k, n in kbuild.RF_VGPRS.items():
+        kbuild.check_device_asm(_fake(k, "\ts_endpgm\n", vgprs=kbuild.RESERVED_BASE + n))
+        with pytest.raises(RuntimeError, match="does not cover"):
+            kbuild.check_device_asm(_fake(k, "\ts_endpgm\n", vgprs=kbuild.RESERVED_BASE + n - 8))
 
 
 def test_checker_rejects_scratch():

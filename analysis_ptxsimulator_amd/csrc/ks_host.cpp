@@ -962,6 +962,7 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
     d.gmode = 2;
     if (i == n) {
       d.cls = DC_END;
+      d.xf = XF_FIX;
       continue;
     }
     const KsInst& in = P->code[i].in;
@@ -1057,7 +1058,7 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         d.cls = g ? DC_MEMG : DC_MEMS;
         const bool ld = in.op == KO_LDG32 || in.op == KO_LDG64 || in.op == KO_LDS32 || in.op == KO_LDS64;
         const bool w64 = in.op == KO_LDG64 || in.op == KO_STG64 || in.op == KO_LDS64 || in.op == KO_STS64;
-        d.xf = (ld ? XF_LOAD : 0u) | (w64 ? XF_W64 : 0u) | (in.imm[0] == 64 ? XF_A64 : 0u);
+        d.xf |= (ld ? XF_LOAD : 0u) | (w64 ? XF_W64 : 0u) | (in.imm[0] == 64 ? XF_A64 : 0u);
         d.s0 = in.src[0];
         d.s1 = ld ? 0u : in.src[1];
         d.a0 = (uint32_t)(uint64_t)in.off;
@@ -1079,7 +1080,7 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
   }
   for (uint32_t i = 0; i < n; ++i) {
     const KsInst& in = P->code[i].in;
-    if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].xf |= XF_RPC;
+    if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].xf |= XF_FIX;
   }
   return out;
 }

@@ -101,7 +101,7 @@ enum : uint32_t { DI_ADD, DI_SUB, DI_MUL, DI_MAD, DI_WIDE_S, DI_WIDE_U };  // DC
 // DInst::xf flags
 enum : uint32_t {
   XF_IMM = 1,    // some source is an immediate: imm[] goes into the immediate slots first
-  XF_RPC = 2,    // a divergent branch reconverges here
+  XF_FIX = 2,    // the end sentinel, or a divergent branch reconverges here
   XF_LOAD = 4,   // memory: load (else store)
   XF_W64 = 8,    // memory: 8-byte access
   XF_A64 = 16,   // memory: 64-bit address register

@@ -63,6 +63,7 @@ enum {
 };
 
 typedef const __attribute__((address_space(4))) DInst* cdinst;
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));  // the 16 dwords every instruction reads
 
 __device__ __forceinline__ uint32_t rl(uint32_t v, uint32_t l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
@@ -386,425 +387,408 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     while (true) {
       const uint32_t pc = umin(spc0, spc1);
       if (pc == INF) break;
-      const bool go0 = spc0 == pc, go1 = spc1 == pc;
-      const uint64_t gm = (go0 ? LO : 0ull) | (go1 ? HI : 0ull);
+      const uint64_t gm = (spc0 == pc ? LO : 0ull) | (spc1 == pc ? HI : 0ull);  // lanes of the issuing warps
+      const bool go0 = (uint32_t)gm != 0u, go1 = (gm >> 32) != 0u;
       const cdinst I = prog + pc;
-      const uint32_t cls = I->cls;
-      const uint32_t xf = I->xf;
-
-      if (cls == DC_END) {  // past the last instruction: those lanes exit, no issue
-        ex64 |= m64 & gm;
-        if (go0) {
-          S0.pc = pc;
-          KS_SETTLE(0, S0, spc0);
-        }
-        if (go1) {
-          S1.pc = pc;
-          KS_SETTLE(1, S1, spc1);
-        }
-        continue;
-      }
-      if (xf & XF_RPC) {  // reconvergence point: warps whose top entry ends here pop first
-        const bool p0 = go0 && S0.rpc == pc, p1 = go1 && S1.rpc == pc;
-        if (p0 || p1) {
-          if (p0) {
-            S0.pc = pc;
-            KS_SETTLE(0, S0, spc0);
-          }
-          if (p1) {
-            S1.pc = pc;
-            KS_SETTLE(1, S1, spc1);
-          }
-          continue;
-        }
-      }
+      const u32x16 hot = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(I);
+      const uint32_t cls = hot[0], xf = hot[1];
+      const uint32_t s0 = hot[2], s1 = hot[3], s2 = hot[4], dst = hot[5];
+      const uint32_t sbod = hot[10], lat = hot[11], gp = hot[12], gmode = hot[13];
+      const uint32_t a0 = hot[14], a1 = hot[15];
 
       // issue cycle (per warp, uniform over its lanes): the later of the previous issue
       // + 1 and the ready cycle of every register source (absent sources read a zero word)
-      const uint32_t iss = umax(umax(v_next, sb_at(I->sbo[0])),
-                                umax(umax(sb_at(I->sbo[1]), sb_at(I->sbo[2])), sb_at(I->sbo[3])));
+      const uint32_t iss = umax(umax(v_next, sb_at(hot[6])), umax(umax(sb_at(hot[7]), sb_at(hot[8])), sb_at(hot[9])));
 
-      // events: trace chunk complete, issue budget reached, cycle limit passed
-      {
-        const uint64_t evm = ballot(wi == ev || iss > CYCLE_LIMIT) & gm;
-        if (evm) {
-          const uint64_t bm = ballot(wi == budget) & gm;                 // budget first
-          const uint64_t om = ballot(iss > CYCLE_LIMIT) & gm & ~bm;
-          const uint64_t fm = ballot(wi == nf) & gm & ~om;               // a full chunk (or the cap) to write
-          if (lanes(fm)) {
-            if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
-            fl = wi;
-            nf = wi < cap ? umin(cap, wi + 32u) : INF;
-          }
-          if (lanes(gm)) ev = umin(nf, budget);
-          const uint64_t stop = bm | om;
-          if (stop & LO) {
-            spc0 = INF;
-            hst |= DONE0;
-            status |= (bm & LO) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF;
-          }
-          if (stop & HI) {
-            spc1 = INF;
-            hst |= DONE1;
-            status |= ((bm & HI) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF) << 8;
-          }
-          continue;
-        }
-      }
-
-      // issue
-      const uint64_t mm = m64 & gm;  // live lanes of the issuing warps
-      const uint64_t on64 = mm & ballot(((pbits >> I->gp) & 1u) != I->gmode);  // guard
-      if (lanes(gm)) {
-        if (sl == (wi & 31u)) {
-          tr_c = iss;
-          tr_p = pc;
-        }
-        wi += 1;
-        v_next = iss + 1;
-        sb_at(I->sbod) = iss + I->lat;
-      }
-      act += lanes(mm) ? 1u : 0u;
-      const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
-
-      // ---------------------------------------------------------------- execute
-      if (cls <= DC_LDP) {
-        if (xf & XF_IMM) {
-          uint32_t iv[6];
-          for (int k = 0; k < 6; ++k) iv[k] = I->imm[k];
-          R.put_imm(ib, iv);
-        }
-        if (lanes(on64)) {
-          const uint32_t s0 = I->s0, s1 = I->s1, s2 = I->s2, dst = I->dst;
-          const uint32_t a0 = I->a0, a1 = I->a1;
-          if (cls == DC_FFMA) {
-            uint32_t x0, x1, x2;
-            R.get3(s0, s1, s2, x0, x1, x2);
-            R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1), __uint_as_float(x2))));
-          } else if (cls == DC_FARITH) {
-            uint32_t x0, x1, x2;
-            R.get3(s0, s1, s2, x0, x1, x2);
-            const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
-            const uint32_t c = (x2 & a1) ^ I->a2;                 // x2, -x2 or -0.0f
-            R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(c))));
-          } else if (cls == DC_IADD) {
-            uint32_t x0, x1;
-            R.get2(s0, s1, x0, x1);
-            R.put(dst, x0 + (x1 ^ a0) + a1);
-          } else if (cls == DC_IMAD) {
-            uint32_t x0, x1, x2;
-            R.get3(s0, s1, s2, x0, x1, x2);
-            R.put(dst, x0 * x1 + (x2 & a0));
-          } else if (cls == DC_MOV) {
-            if (a0) {
-              uint32_t lo, hi;
-              R.get2(s0, s0 + 1u, lo, hi);
-              R.put2(dst, lo, hi);
-            } else {
-              R.put(dst, R.get(s0));
-            }
-          } else if (cls == DC_SELP) {
-            const bool p = (pbits >> s2) & 1u;
-            if (a0) {
-              uint32_t xl, xh, yl, yh;
-              R.get2(s0, s0 + 1u, xl, xh);
-              R.get2(s1, s1 + 1u, yl, yh);
-              R.put2(dst, p ? xl : yl, p ? xh : yh);
-            } else {
-              uint32_t x0, x1;
-              R.get2(s0, s1, x0, x1);
-              R.put(dst, p ? x0 : x1);
-            }
-          } else if (cls == DC_SETP) {
-            bool lt, eq, gt;
-            if (a0 == DS_F32) {
-              uint32_t x0, x1;
-              R.get2(s0, s1, x0, x1);
-              const float x = __uint_as_float(x0), y = __uint_as_float(x1);
-              lt = x < y;
-              eq = x == y;
-              gt = x > y;  // all false when an input is NaN
-            } else if (a0 <= DS_U32) {
-              uint32_t x0, x1;
-              R.get2(s0, s1, x0, x1);
-              lt = a0 == DS_S32 ? (int32_t)x0 < (int32_t)x1 : x0 < x1;
-              eq = x0 == x1;
-              gt = !lt && !eq;
-            } else {
-              uint32_t xl, xh, yl, yh;
-              R.get2(s0, s0 + 1u, xl, xh);
-              R.get2(s1, s1 + 1u, yl, yh);
-              const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
-              lt = a0 == DS_S64 ? (int64_t)x < (int64_t)y : x < y;
-              eq = x == y;
-              gt = !lt && !eq;
-            }
-            const bool c = (lt && (a1 & 1u)) || (eq && (a1 & 2u)) || (gt && (a1 & 4u));
-            pbits = (pbits & ~(1u << dst)) | ((c ? 1u : 0u) << dst);
-          } else if (cls == DC_I64) {
-            uint64_t r;
-            if (a0 >= DI_WIDE_S) {
-              uint32_t x0, x1;
-              R.get2(s0, s1, x0, x1);
-              r = a0 == DI_WIDE_S ? (uint64_t)((int64_t)(int32_t)x0 * (int64_t)(int32_t)x1)
-                                  : (uint64_t)x0 * (uint64_t)x1;
-            } else {
-              uint32_t xl, xh, yl, yh;
-              R.get2(s0, s0 + 1u, xl, xh);
-              R.get2(s1, s1 + 1u, yl, yh);
-              const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
-              if (a0 == DI_ADD) r = x + y;
-              else if (a0 == DI_SUB) r = x - y;
-              else if (a0 == DI_MUL) r = x * y;
-              else {
-                uint32_t zl, zh;
-                R.get2(s2, s2 + 1u, zl, zh);
-                r = x * y + ((uint64_t)zl | ((uint64_t)zh << 32));
-              }
-            }
-            R.put2(dst, (uint32_t)r, (uint32_t)(r >> 32));
-          } else if (cls == DC_MOVSP) {
-            const uint32_t t_lin = my_w * 32u + sl;
-            const uint32_t bx = a.block[0], by = a.block[1];
-            const uint32_t gx = a.grid[0], gy = a.grid[1];
-            uint32_t v;
-            switch (a0) {
-              case KSP_TID_X: v = t_lin % bx; break;
-              case KSP_TID_Y: v = (t_lin / bx) % by; break;
-              case KSP_TID_Z: v = t_lin / (bx * by); break;
-              case KSP_NTID_X: v = a.block[0]; break;
-              case KSP_NTID_Y: v = a.block[1]; break;
-              case KSP_NTID_Z: v = a.block[2]; break;
-              case KSP_CTAID_X: v = blk % gx; break;
-              case KSP_CTAID_Y: v = (blk / gx) % gy; break;
-              case KSP_CTAID_Z: v = blk / (gx * gy); break;
-              case KSP_NCTAID_X: v = a.grid[0]; break;
-              case KSP_NCTAID_Y: v = a.grid[1]; break;
-              case KSP_NCTAID_Z: v = a.grid[2]; break;
-              default: v = sl; break;
-            }
-            R.put(dst, v);
-          } else {  // DC_LDP: a uniform value from the launch arguments
-            const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + a0);
-            if (a1) R.put2(dst, lo, *reinterpret_cast<const uint32_t*>(a.params + a0 + 4u));
-            else R.put(dst, lo);
-          }
-        }
-        spc0 = go0 ? pc + 1u : spc0;
-        spc1 = go1 ? pc + 1u : spc1;
-      } else if (cls <= DC_MEMS) {
-        const bool is_global = cls == DC_MEMG;
-        const bool is_load = xf & XF_LOAD;
-        const bool w64 = xf & XF_W64;
-        const uint32_t S = w64 ? 8u : 4u;
-        const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
-        const uint64_t off = (uint64_t)I->a0 | ((uint64_t)I->a1 << 32);
-        const uint32_t s0 = I->s0;
-        uint64_t base;
-        if (xf & XF_A64) {
-          uint32_t lo, hi;
-          R.get2(s0, s0 + 1u, lo, hi);
-          base = (uint64_t)lo | ((uint64_t)hi << 32);
+      uint32_t need = 0;  // warps whose top stack entry must be settled (bit h)
+      if (xf & XF_FIX) {  // the end sentinel, or a reconvergence point: warps whose top entry ends here pop
+        if (cls == DC_END) {
+          need = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
+          ex64 |= m64 & gm;  // lanes that get past the last instruction exit, at no cost
         } else {
-          base = R.get(s0);
+          need = (go0 && S0.rpc == pc ? 1u : 0u) | (go1 && S1.rpc == pc ? 2u : 0u);
         }
-        const uint64_t A = base + off;
-        const bool ok = (A & (S - 1u)) == 0 && A <= size && size - A >= S;
-        const uint64_t okm = ballot(ok) & on64;
-        if (is_load) {
-          uint32_t lo = 0, hi = 0;
-          if (lanes(okm)) {
-            if (is_global) {
-              if (w64) {
-                const uint2 v = *reinterpret_cast<const uint2*>(a.gmem + A);
-                lo = v.x;
-                hi = v.y;
-              } else {
-                lo = *reinterpret_cast<const uint32_t*>(a.gmem + A);
-              }
-            } else {
-              lo = *reinterpret_cast<const uint32_t*>(win + A);
-              if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
-            }
+        if (need & 1u) S0.pc = pc;
+        if (need & 2u) S1.pc = pc;
+      }
+      const uint64_t evm = ballot(wi == ev || iss > CYCLE_LIMIT) & gm;
+      if (need) {
+        // no issue this step
+      } else if (evm) {
+        // events: trace chunk complete, issue budget reached (checked first), cycle limit passed
+        const uint64_t bm = ballot(wi == budget) & gm;
+        const uint64_t om = ballot(iss > CYCLE_LIMIT) & gm & ~bm;
+        const uint64_t fm = ballot(wi == nf) & gm & ~om;  // a full chunk (or the cap) to write
+        if (lanes(fm)) {
+          if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+          fl = wi;
+          nf = wi < cap ? umin(cap, wi + 32u) : INF;
+        }
+        if (lanes(gm)) ev = umin(nf, budget);
+        const uint64_t stop = bm | om;
+        if (stop & LO) {
+          spc0 = INF;
+          hst |= DONE0;
+          status |= (bm & LO) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF;
+        }
+        if (stop & HI) {
+          spc1 = INF;
+          hst |= DONE1;
+          status |= ((bm & HI) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF) << 8;
+        }
+      } else {
+        // issue
+        const uint64_t mm = m64 & gm;  // live lanes of the issuing warps
+        const uint64_t on64 = mm & ballot(((pbits >> gp) & 1u) != gmode);  // guard
+        if (lanes(gm)) {
+          if (sl == (wi & 31u)) {
+            tr_c = iss;
+            tr_p = pc;
+          }
+          wi += 1;
+          v_next = iss + 1;
+          sb_at(sbod) = iss + lat;
+        }
+        act += lanes(mm) ? 1u : 0u;
+        const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
+
+        // ---------------------------------------------------------------- execute
+        if (cls <= DC_LDP) {
+          if (xf & XF_IMM) {
+            uint32_t iv[6];
+            for (int k = 0; k < 6; ++k) iv[k] = I->imm[k];
+            R.put_imm(ib, iv);
           }
           if (lanes(on64)) {
-            if (w64) R.put2(I->dst, lo, hi);
-            else R.put(I->dst, lo);
+            if (cls == DC_FFMA) {
+              uint32_t x0, x1, x2;
+              R.get3(s0, s1, s2, x0, x1, x2);
+              R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1), __uint_as_float(x2))));
+            } else if (cls == DC_FARITH) {
+              uint32_t x0, x1, x2;
+              R.get3(s0, s1, s2, x0, x1, x2);
+              const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
+              const uint32_t c = (x2 & a1) ^ I->a2;                 // x2, -x2 or -0.0f
+              R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(c))));
+            } else if (cls == DC_IADD) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              R.put(dst, x0 + (x1 ^ a0) + a1);
+            } else if (cls == DC_IMAD) {
+              uint32_t x0, x1, x2;
+              R.get3(s0, s1, s2, x0, x1, x2);
+              R.put(dst, x0 * x1 + (x2 & a0));
+            } else if (cls == DC_MOV) {
+              if (a0) {
+                uint32_t lo, hi;
+                R.get2(s0, s0 + 1u, lo, hi);
+                R.put2(dst, lo, hi);
+              } else {
+                R.put(dst, R.get(s0));
+              }
+            } else if (cls == DC_SELP) {
+              const bool p = (pbits >> s2) & 1u;
+              if (a0) {
+                uint32_t xl, xh, yl, yh;
+                R.get2(s0, s0 + 1u, xl, xh);
+                R.get2(s1, s1 + 1u, yl, yh);
+                R.put2(dst, p ? xl : yl, p ? xh : yh);
+              } else {
+                uint32_t x0, x1;
+                R.get2(s0, s1, x0, x1);
+                R.put(dst, p ? x0 : x1);
+              }
+            } else if (cls == DC_SETP) {
+              bool lt, eq, gt;
+              if (a0 == DS_F32) {
+                uint32_t x0, x1;
+                R.get2(s0, s1, x0, x1);
+                const float x = __uint_as_float(x0), y = __uint_as_float(x1);
+                lt = x < y;
+                eq = x == y;
+                gt = x > y;  // all false when an input is NaN
+              } else if (a0 <= DS_U32) {
+                uint32_t x0, x1;
+                R.get2(s0, s1, x0, x1);
+                lt = a0 == DS_S32 ? (int32_t)x0 < (int32_t)x1 : x0 < x1;
+                eq = x0 == x1;
+                gt = !lt && !eq;
+              } else {
+                uint32_t xl, xh, yl, yh;
+                R.get2(s0, s0 + 1u, xl, xh);
+                R.get2(s1, s1 + 1u, yl, yh);
+                const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
+                lt = a0 == DS_S64 ? (int64_t)x < (int64_t)y : x < y;
+                eq = x == y;
+                gt = !lt && !eq;
+              }
+              const bool c = (lt && (a1 & 1u)) || (eq && (a1 & 2u)) || (gt && (a1 & 4u));
+              pbits = (pbits & ~(1u << dst)) | ((c ? 1u : 0u) << dst);
+            } else if (cls == DC_I64) {
+              uint64_t r;
+              if (a0 >= DI_WIDE_S) {
+                uint32_t x0, x1;
+                R.get2(s0, s1, x0, x1);
+                r = a0 == DI_WIDE_S ? (uint64_t)((int64_t)(int32_t)x0 * (int64_t)(int32_t)x1)
+                                    : (uint64_t)x0 * (uint64_t)x1;
+              } else {
+                uint32_t xl, xh, yl, yh;
+                R.get2(s0, s0 + 1u, xl, xh);
+                R.get2(s1, s1 + 1u, yl, yh);
+                const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
+                if (a0 == DI_ADD) r = x + y;
+                else if (a0 == DI_SUB) r = x - y;
+                else if (a0 == DI_MUL) r = x * y;
+                else {
+                  uint32_t zl, zh;
+                  R.get2(s2, s2 + 1u, zl, zh);
+                  r = x * y + ((uint64_t)zl | ((uint64_t)zh << 32));
+                }
+              }
+              R.put2(dst, (uint32_t)r, (uint32_t)(r >> 32));
+            } else if (cls == DC_MOVSP) {
+              const uint32_t t_lin = my_w * 32u + sl;
+              const uint32_t bx = a.block[0], by = a.block[1];
+              const uint32_t gx = a.grid[0], gy = a.grid[1];
+              uint32_t v;
+              switch (a0) {
+                case KSP_TID_X: v = t_lin % bx; break;
+                case KSP_TID_Y: v = (t_lin / bx) % by; break;
+                case KSP_TID_Z: v = t_lin / (bx * by); break;
+                case KSP_NTID_X: v = a.block[0]; break;
+                case KSP_NTID_Y: v = a.block[1]; break;
+                case KSP_NTID_Z: v = a.block[2]; break;
+                case KSP_CTAID_X: v = blk % gx; break;
+                case KSP_CTAID_Y: v = (blk / gx) % gy; break;
+                case KSP_CTAID_Z: v = blk / (gx * gy); break;
+                case KSP_NCTAID_X: v = a.grid[0]; break;
+                case KSP_NCTAID_Y: v = a.grid[1]; break;
+                case KSP_NCTAID_Z: v = a.grid[2]; break;
+                default: v = sl; break;
+              }
+              R.put(dst, v);
+            } else {  // DC_LDP: a uniform value from the launch arguments
+              const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + a0);
+              if (a1) R.put2(dst, lo, *reinterpret_cast<const uint32_t*>(a.params + a0 + 4u));
+              else R.put(dst, lo);
+            }
           }
-        } else if (lanes(okm)) {
-          const uint32_t s1 = I->s1;
-          if (w64) {
+          spc0 = go0 ? pc + 1u : spc0;
+          spc1 = go1 ? pc + 1u : spc1;
+        } else if (cls <= DC_MEMS) {
+          const bool is_global = cls == DC_MEMG;
+          const bool is_load = xf & XF_LOAD;
+          const bool w64 = xf & XF_W64;
+          const uint32_t S = w64 ? 8u : 4u;
+          const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
+          const uint64_t off = (uint64_t)a0 | ((uint64_t)a1 << 32);
+          uint64_t base;
+          if (xf & XF_A64) {
             uint32_t lo, hi;
-            R.get2(s1, s1 + 1u, lo, hi);
-            if (is_global) {
-              *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, hi);
+            R.get2(s0, s0 + 1u, lo, hi);
+            base = (uint64_t)lo | ((uint64_t)hi << 32);
+          } else {
+            base = R.get(s0);
+          }
+          const uint64_t A = base + off;
+          const bool ok = (A & (S - 1u)) == 0 && A <= size && size - A >= S;
+          const uint64_t okm = ballot(ok) & on64;
+          if (is_load) {
+            uint32_t lo = 0, hi = 0;
+            if (lanes(okm)) {
+              if (is_global) {
+                if (w64) {
+                  const uint2 v = *reinterpret_cast<const uint2*>(a.gmem + A);
+                  lo = v.x;
+                  hi = v.y;
+                } else {
+                  lo = *reinterpret_cast<const uint32_t*>(a.gmem + A);
+                }
+              } else {
+                lo = *reinterpret_cast<const uint32_t*>(win + A);
+                if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
+              }
+            }
+            if (lanes(on64)) {
+              if (w64) R.put2(dst, lo, hi);
+              else R.put(dst, lo);
+            }
+          } else if (lanes(okm)) {
+            if (w64) {
+              uint32_t lo, hi;
+              R.get2(s1, s1 + 1u, lo, hi);
+              if (is_global) {
+                *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, hi);
+              } else {
+                *reinterpret_cast<uint32_t*>(win + A) = lo;
+                *reinterpret_cast<uint32_t*>(win + A + 4) = hi;
+              }
             } else {
-              *reinterpret_cast<uint32_t*>(win + A) = lo;
-              *reinterpret_cast<uint32_t*>(win + A + 4) = hi;
+              const uint32_t lo = R.get(s1);
+              if (is_global) *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
+              else *reinterpret_cast<uint32_t*>(win + A) = lo;
             }
+          }
+          // fault counting and analysis (full exec)
+          const uint64_t faults = on64 & ~okm;
+          if (faults) {
+            const uint32_t f0 = popc((uint32_t)faults), f1 = popc((uint32_t)(faults >> 32));
+            if (f0) status |= KS_ST_FAULT;
+            if (f1) status |= KS_ST_FAULT << 8;
+            cnt += sl == C_FAULT ? (hl ? f1 : f0) : 0u;
+          }
+          const bool on = lanes(on64);
+          const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
+          if (is_global) {
+            uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;
+            bool slow0 = g0 != 0, slow1 = g1 != 0;
+            if (!faults && small_gmem) {
+              // monotone fast path: prefix max of sector ids over the active lanes of each half
+              const uint32_t s = on ? (uint32_t)(A >> 5) : 0u;
+              const uint32_t prev = prev_in_half(half_prefix_max(s), lane);
+              const uint64_t nonmono = ballot(on && s < prev);
+              const uint64_t news = ballot(on && s != prev);
+              const uint64_t newl = ballot(on && (s >> 2) != (prev >> 2));
+              if (g0 && !(uint32_t)nonmono) {
+                const uint32_t first = g0 & (0u - g0);
+                sec0 = popc((uint32_t)news | first);
+                lin0 = popc((uint32_t)newl | first);
+                slow0 = false;
+              }
+              if (g1 && !(uint32_t)(nonmono >> 32)) {
+                const uint32_t first = g1 & (0u - g1);
+                sec1 = popc((uint32_t)(news >> 32) | first);
+                lin1 = popc((uint32_t)(newl >> 32) | first);
+                slow1 = false;
+              }
+            }
+            if (slow0 || slow1) {
+              const uint64_t last = A + (S - 1u);
+              if (slow0) {
+                sec0 = distinct2(A >> 5, last >> 5, (uint64_t)g0);
+                lin0 = distinct2(A >> 7, last >> 7, (uint64_t)g0);
+              }
+              if (slow1) {
+                sec1 = distinct2(A >> 5, last >> 5, (uint64_t)g1 << 32);
+                lin1 = distinct2(A >> 7, last >> 7, (uint64_t)g1 << 32);
+              }
+            }
+            // counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2}
+            const uint32_t cn = is_load ? C_GLD_N : C_GST_N;
+            const uint32_t d = sl - cn;
+            if (((hm >> hl) & 1u) && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0));
           } else {
-            const uint32_t lo = R.get(s1);
-            if (is_global) *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
-            else *reinterpret_cast<uint32_t*>(win + A) = lo;
-          }
-        }
-        // fault counting and analysis (full exec)
-        const uint64_t faults = on64 & ~okm;
-        if (faults) {
-          const uint32_t f0 = popc((uint32_t)faults), f1 = popc((uint32_t)(faults >> 32));
-          if (f0) status |= KS_ST_FAULT;
-          if (f1) status |= KS_ST_FAULT << 8;
-          cnt += sl == C_FAULT ? (hl ? f1 : f0) : 0u;
-        }
-        const bool on = lanes(on64);
-        const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
-        if (is_global) {
-          uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;
-          bool slow0 = g0 != 0, slow1 = g1 != 0;
-          if (!faults && small_gmem) {
-            // monotone fast path: prefix max of sector ids over the active lanes of each half
-            const uint32_t s = on ? (uint32_t)(A >> 5) : 0u;
-            const uint32_t prev = prev_in_half(half_prefix_max(s), lane);
-            const uint64_t nonmono = ballot(on && s < prev);
-            const uint64_t news = ballot(on && s != prev);
-            const uint64_t newl = ballot(on && (s >> 2) != (prev >> 2));
-            if (g0 && !(uint32_t)nonmono) {
-              const uint32_t first = g0 & (0u - g0);
-              sec0 = popc((uint32_t)news | first);
-              lin0 = popc((uint32_t)newl | first);
-              slow0 = false;
+            uint32_t d0 = 1, d1 = 1;
+            bool slow0 = g0 != 0, slow1 = g1 != 0;
+            if (!faults) {
+              // affine fast path for full halves: lanes at A0 + l * d
+              const uint32_t a32 = (uint32_t)A;
+              const uint32_t diff = a32 - prev_in_half(a32, lane);
+              const uint32_t dA = rl(diff, 1), dB = rl(diff, 33);
+              const uint64_t same = ballot(diff == (hl ? dB : dA));
+              if (g0 == 0xFFFFFFFFu && ((uint32_t)same | 1u) == 0xFFFFFFFFu && (dA & 3u) == 0) {
+                const uint32_t ws = (dA >> 2) & 31u;
+                d0 = dA == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
+                slow0 = false;
+              }
+              if (g1 == 0xFFFFFFFFu && ((uint32_t)(same >> 32) | 1u) == 0xFFFFFFFFu && (dB & 3u) == 0) {
+                const uint32_t ws = (dB >> 2) & 31u;
+                d1 = dB == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
+                slow1 = false;
+              }
             }
-            if (g1 && !(uint32_t)(nonmono >> 32)) {
-              const uint32_t first = g1 & (0u - g1);
-              sec1 = popc((uint32_t)(news >> 32) | first);
-              lin1 = popc((uint32_t)(newl >> 32) | first);
-              slow1 = false;
+            if (slow0) d0 = bank_degree(A, (uint64_t)g0);
+            if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
+            const uint32_t dh = hl ? d1 : d0;
+            if ((hm >> hl) & 1u) {
+              if (sl == C_SH_N) cnt += 1;
+              if (sl == C_SH_SUM) cnt += dh;
+              if (sl == C_SH_MAX) cnt = umax(cnt, dh);
             }
           }
-          if (slow0 || slow1) {
-            const uint64_t last = A + (S - 1u);
-            if (slow0) {
-              sec0 = distinct2(A >> 5, last >> 5, (uint64_t)g0);
-              lin0 = distinct2(A >> 7, last >> 7, (uint64_t)g0);
-            }
-            if (slow1) {
-              sec1 = distinct2(A >> 5, last >> 5, (uint64_t)g1 << 32);
-              lin1 = distinct2(A >> 7, last >> 7, (uint64_t)g1 << 32);
-            }
-          }
-          // counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2}
-          const uint32_t cn = is_load ? C_GLD_N : C_GST_N;
-          const uint32_t d = sl - cn;
-          if (((hm >> hl) & 1u) && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0));
-        } else {
-          uint32_t d0 = 1, d1 = 1;
-          bool slow0 = g0 != 0, slow1 = g1 != 0;
-          if (!faults) {
-            // affine fast path for full halves: lanes at A0 + l * d
-            const uint32_t a32 = (uint32_t)A;
-            const uint32_t diff = a32 - prev_in_half(a32, lane);
-            const uint32_t dA = rl(diff, 1), dB = rl(diff, 33);
-            const uint64_t same = ballot(diff == (hl ? dB : dA));
-            if (g0 == 0xFFFFFFFFu && ((uint32_t)same | 1u) == 0xFFFFFFFFu && (dA & 3u) == 0) {
-              const uint32_t ws = (dA >> 2) & 31u;
-              d0 = dA == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
-              slow0 = false;
-            }
-            if (g1 == 0xFFFFFFFFu && ((uint32_t)(same >> 32) | 1u) == 0xFFFFFFFFu && (dB & 3u) == 0) {
-              const uint32_t ws = (dB >> 2) & 31u;
-              d1 = dB == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
-              slow1 = false;
+          spc0 = go0 ? pc + 1u : spc0;
+          spc1 = go1 ? pc + 1u : spc1;
+        } else if (cls == DC_BRA) {
+          const uint32_t target = a0, rpc = a1;
+          const uint32_t mm0 = (uint32_t)mm, mm1 = (uint32_t)(mm >> 32);
+          uint32_t divm = 0;
+          if (go0) {
+            const uint32_t nt = mm0 & ~g0;
+            if (nt == 0) {
+              spc0 = target;
+            } else if (g0 == 0) {
+              spc0 = pc + 1u;
+            } else {
+              divm |= 1u;
+              const uint32_t mk = (uint32_t)mask64;
+              S0.pc = rpc;
+              if (target != rpc) stk_push(S0, mk, target, rpc, lane);
+              uint32_t top = target != rpc ? g0 : mk;
+              if (pc + 1u != rpc) {
+                stk_push(S0, top, pc + 1u, rpc, lane);
+                top = nt;
+              }
+              mask64 = (mask64 & HI) | top;
+              spc0 = S0.pc;
             }
           }
-          if (slow0) d0 = bank_degree(A, (uint64_t)g0);
-          if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
-          const uint32_t dh = hl ? d1 : d0;
-          if ((hm >> hl) & 1u) {
-            if (sl == C_SH_N) cnt += 1;
-            if (sl == C_SH_SUM) cnt += dh;
-            if (sl == C_SH_MAX) cnt = umax(cnt, dh);
-          }
-        }
-        spc0 = go0 ? pc + 1u : spc0;
-        spc1 = go1 ? pc + 1u : spc1;
-      } else if (cls == DC_BRA) {
-        const uint32_t target = I->a0, rpc = I->a1;
-        const uint32_t mm0 = (uint32_t)mm, mm1 = (uint32_t)(mm >> 32);
-        uint32_t divm = 0;
-        if (go0) {
-          const uint32_t nt = mm0 & ~g0;
-          if (nt == 0) {
-            spc0 = target;
-          } else if (g0 == 0) {
-            spc0 = pc + 1u;
-          } else {
-            divm |= 1u;
-            const uint32_t mk = (uint32_t)mask64;
-            S0.pc = rpc;
-            if (target != rpc) stk_push(S0, mk, target, rpc, lane);
-            uint32_t top = target != rpc ? g0 : mk;
-            if (pc + 1u != rpc) {
-              stk_push(S0, top, pc + 1u, rpc, lane);
-              top = nt;
+          if (go1) {
+            const uint32_t nt = mm1 & ~g1;
+            if (nt == 0) {
+              spc1 = target;
+            } else if (g1 == 0) {
+              spc1 = pc + 1u;
+            } else {
+              divm |= 2u;
+              const uint32_t mk = (uint32_t)(mask64 >> 32);
+              S1.pc = rpc;
+              if (target != rpc) stk_push(S1, mk, target, rpc, lane);
+              uint32_t top = target != rpc ? g1 : mk;
+              if (pc + 1u != rpc) {
+                stk_push(S1, top, pc + 1u, rpc, lane);
+                top = nt;
+              }
+              mask64 = (mask64 & LO) | ((uint64_t)top << 32);
+              spc1 = S1.pc;
             }
-            mask64 = (mask64 & HI) | top;
-            spc0 = S0.pc;
           }
-        }
-        if (go1) {
-          const uint32_t nt = mm1 & ~g1;
-          if (nt == 0) {
-            spc1 = target;
-          } else if (g1 == 0) {
-            spc1 = pc + 1u;
-          } else {
-            divm |= 2u;
-            const uint32_t mk = (uint32_t)(mask64 >> 32);
-            S1.pc = rpc;
-            if (target != rpc) stk_push(S1, mk, target, rpc, lane);
-            uint32_t top = target != rpc ? g1 : mk;
-            if (pc + 1u != rpc) {
-              stk_push(S1, top, pc + 1u, rpc, lane);
-              top = nt;
-            }
-            mask64 = (mask64 & LO) | ((uint64_t)top << 32);
-            spc1 = S1.pc;
+          if (divm) {
+            m64 = mask64 & ~ex64;
+            cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
           }
-        }
-        if (divm) {
+        } else if (cls == DC_RET) {
+          ex64 |= on64;
           m64 = mask64 & ~ex64;
-          cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
-        }
-      } else if (cls == DC_RET) {
-        ex64 |= on64;
-        m64 = mask64 & ~ex64;
-        if (go0) {
-          spc0 = pc + 1u;
-          S0.pc = pc + 1u;
-          if ((uint32_t)m64 == 0) KS_SETTLE(0, S0, spc0);
-        }
-        if (go1) {
-          spc1 = pc + 1u;
-          S1.pc = pc + 1u;
-          if ((uint32_t)(m64 >> 32) == 0) KS_SETTLE(1, S1, spc1);
-        }
-      } else {  // DC_BAR: the issuing warps wait for the block
-        const uint64_t conv = init64 & ~ex64;
-        const uint32_t hm = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
-        cnt = cnt_add2(cnt, sl, hl, C_BAR, hm, 1u);
-        if (go0) {
-          if ((uint32_t)mm != (uint32_t)conv) status |= KS_ST_BARDIV;
-          S0.pc = pc + 1u;
-          spc0 = INF;
-          hst |= WAIT0;
-        }
-        if (go1) {
-          if ((uint32_t)(mm >> 32) != (uint32_t)(conv >> 32)) status |= KS_ST_BARDIV << 8;
-          S1.pc = pc + 1u;
-          spc1 = INF;
-          hst |= WAIT1;
+          if (go0) {
+            spc0 = pc + 1u;
+            S0.pc = pc + 1u;
+            need |= (uint32_t)m64 == 0 ? 1u : 0u;  // every lane has exited: pop
+          }
+          if (go1) {
+            spc1 = pc + 1u;
+            S1.pc = pc + 1u;
+            need |= (uint32_t)(m64 >> 32) == 0 ? 2u : 0u;
+          }
+        } else {  // DC_BAR: the issuing warps wait for the block
+          const uint64_t conv = init64 & ~ex64;
+          const uint32_t hm = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
+          cnt = cnt_add2(cnt, sl, hl, C_BAR, hm, 1u);
+          if (go0) {
+            if ((uint32_t)mm != (uint32_t)conv) status |= KS_ST_BARDIV;
+            S0.pc = pc + 1u;
+            spc0 = INF;
+            hst |= WAIT0;
+          }
+          if (go1) {
+            if ((uint32_t)(mm >> 32) != (uint32_t)(conv >> 32)) status |= KS_ST_BARDIV << 8;
+            S1.pc = pc + 1u;
+            spc1 = INF;
+            hst |= WAIT1;
+          }
         }
       }
+      if (need & 1u) KS_SETTLE(0, S0, spc0);
+      if (need & 2u) KS_SETTLE(1, S1, spc1);
     }
 
     // ------------------------------------------------------------------ barrier epoch

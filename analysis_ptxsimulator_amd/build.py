@@ -23,12 +23,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp
          "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
 
 
-# The VGPR register-file kernels keep simulated registers in v64 and up, which
+# The VGPR register-file kernels keep simulated registers in v56 and up, which
 # the compiler must never allocate (they are reserved by amdgpu_num_vgpr), and
 # their VGPR count must cover the file; no interpreter may use scratch memory.
 RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64")
-INTERP_KERNELS = ("ks_interp_lds",) + RESERVED_VGPR_KERNELS
-RESERVED_BASE = 64
+INTERP_KERNELS = RESERVED_VGPR_KERNELS
+RESERVED_BASE = 56
 RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72}  # register-file VGPRs from RESERVED_BASE on
 
 

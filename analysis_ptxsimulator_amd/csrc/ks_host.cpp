@@ -961,8 +961,7 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
     d.sbod = KS_SB_DUMP * 4u;
     d.gmode = 2;
     if (i == n) {
-      d.cls = DC_END;
-      d.xf = XF_FIX;
+      d.ctl = CB(DC_END) | XF_FIX;
       continue;
     }
     const KsInst& in = P->code[i].in;
@@ -973,7 +972,7 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         slot[k] = ib + 2u * k;
         d.imm[2 * k] = (uint32_t)in.imm[k];
         d.imm[2 * k + 1] = (uint32_t)(in.imm[k] >> 32);
-        d.xf |= XF_IMM;
+        d.ctl |= XF_IMM;
       } else {
         slot[k] = kind == KK_REG ? in.src[k] : 0u;
       }
@@ -989,26 +988,27 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
       d.gp = in.guard;
       d.gmode = (in.flags & KF_GUARD_NEG) ? 1u : 0u;
     }
+    uint32_t cls = DC_RET;
     switch (in.op) {
       case KO_ADD32: case KO_SUB32:
-        d.cls = DC_IADD;
+        cls = DC_IADD;
         d.a0 = in.op == KO_SUB32 ? 0xFFFFFFFFu : 0u;
         d.a1 = in.op == KO_SUB32 ? 1u : 0u;
         break;
       case KO_MUL32: case KO_MAD32:
-        d.cls = DC_IMAD;
+        cls = DC_IMAD;
         d.a0 = in.op == KO_MAD32 ? 0xFFFFFFFFu : 0u;
         break;
       case KO_ADD64: case KO_SUB64: case KO_MUL64: case KO_MAD64:
-        d.cls = DC_I64;
+        cls = DC_I64;
         d.a0 = in.op == KO_ADD64 ? DI_ADD : in.op == KO_SUB64 ? DI_SUB : in.op == KO_MUL64 ? DI_MUL : DI_MAD;
         break;
       case KO_MULWIDE_S: case KO_MULWIDE_U:
-        d.cls = DC_I64;
+        cls = DC_I64;
         d.a0 = in.op == KO_MULWIDE_S ? DI_WIDE_S : DI_WIDE_U;
         break;
       case KO_FADD: case KO_FSUB:  // fma(x0, 1.0, +-x1): x1 is read as the third operand
-        d.cls = DC_FARITH;
+        cls = DC_FMA;
         d.s1 = slot[0];
         d.s2 = slot[1];
         d.a0 = 0xFFFFFFFFu;
@@ -1016,17 +1016,20 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         d.a2 = in.op == KO_FSUB ? 0x80000000u : 0u;
         break;
       case KO_FMUL:  // fma(x0, x1, -0.0)
-        d.cls = DC_FARITH;
+        cls = DC_FMA;
         d.s2 = slot[0];
         d.a0 = 0;
         d.a1 = 0;
         d.a2 = 0x80000000u;
         break;
-      case KO_FFMA:
-        d.cls = DC_FFMA;
+      case KO_FFMA:  // fma(x0, x1, x2)
+        cls = DC_FMA;
+        d.a0 = 0;
+        d.a1 = 0xFFFFFFFFu;
+        d.a2 = 0;
         break;
       case KO_SETP_S32: case KO_SETP_U32: case KO_SETP_F32: case KO_SETP_S64: case KO_SETP_U64: {
-        d.cls = DC_SETP;
+        cls = DC_SETP;
         d.a0 = in.op == KO_SETP_S32 ? DS_S32 : in.op == KO_SETP_U32 ? DS_U32 : in.op == KO_SETP_F32 ? DS_F32
              : in.op == KO_SETP_S64 ? DS_S64 : DS_U64;
         static const uint32_t rel[6] = {2u, 5u, 1u, 3u, 4u, 6u};  // eq ne lt le gt ge over {lt, eq, gt}
@@ -1034,31 +1037,31 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         break;
       }
       case KO_SELP32: case KO_SELP64:
-        d.cls = DC_SELP;
+        cls = DC_SELP;
         d.a0 = in.op == KO_SELP64 ? 1u : 0u;
         d.s2 = in.src[2];  // predicate index
         break;
       case KO_MOV32: case KO_MOV64:
         if ((in.kinds & 3u) == KK_SPECIAL) {
-          d.cls = DC_MOVSP;
+          cls = DC_MOVSP;
           d.a0 = in.src[0];
         } else {
-          d.cls = DC_MOV;
+          cls = DC_MOV;
           d.a0 = in.op == KO_MOV64 ? 1u : 0u;
         }
         break;
       case KO_LDP32: case KO_LDP64:
-        d.cls = DC_LDP;
+        cls = DC_LDP;
         d.a0 = in.aux;
         d.a1 = in.op == KO_LDP64 ? 1u : 0u;
         break;
       case KO_LDG32: case KO_LDG64: case KO_STG32: case KO_STG64:
       case KO_LDS32: case KO_LDS64: case KO_STS32: case KO_STS64: {
         const bool g = in.op <= KO_STG64;
-        d.cls = g ? DC_MEMG : DC_MEMS;
+        cls = g ? DC_MEMG : DC_MEMS;
         const bool ld = in.op == KO_LDG32 || in.op == KO_LDG64 || in.op == KO_LDS32 || in.op == KO_LDS64;
         const bool w64 = in.op == KO_LDG64 || in.op == KO_STG64 || in.op == KO_LDS64 || in.op == KO_STS64;
-        d.xf |= (ld ? XF_LOAD : 0u) | (w64 ? XF_W64 : 0u) | (in.imm[0] == 64 ? XF_A64 : 0u);
+        d.ctl |= (ld ? XF_LOAD : 0u) | (w64 ? XF_W64 : 0u) | (in.imm[0] == 64 ? XF_A64 : 0u);
         d.s0 = in.src[0];
         d.s1 = ld ? 0u : in.src[1];
         d.a0 = (uint32_t)(uint64_t)in.off;
@@ -1066,21 +1069,22 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         break;
       }
       case KO_BRA:
-        d.cls = DC_BRA;
+        cls = DC_BRA;
         d.a0 = in.target;
         d.a1 = in.rpc == KS_RPC_EXIT ? 0xFFFFFFFFu : in.rpc;
         break;
       case KO_BAR:
-        d.cls = DC_BAR;
+        cls = DC_BAR;
         break;
       default:
-        d.cls = DC_RET;
+        cls = DC_RET;
         break;
     }
+    d.ctl |= CB(cls);
   }
   for (uint32_t i = 0; i < n; ++i) {
     const KsInst& in = P->code[i].in;
-    if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].xf |= XF_FIX;
+    if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].ctl |= XF_FIX;
   }
   return out;
 }
@@ -1318,9 +1322,10 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
     uint64_t warps = nb * a.warps_per_block;
     if (warps > st->max_warps) raise(KS_E_INVALID_ARG, 0, "run needs more warps than the allocation");
     {
-      const int variant = ks_choose_variant(p->reg_slots, a.threads_per_block);
+      if (ks_choose_variant(p->reg_slots, a.threads_per_block) == 0)
+        raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots", p->reg_slots);
       const uint32_t wg = 64u * ((a.warps_per_block + 1u) / 2u);
-      const size_t need = ks_lds_bytes(variant, p->reg_slots, wg, p->shared_bytes);
+      const size_t need = ks_lds_bytes(wg, p->shared_bytes);
       if (need + 64 > ks_lds_limit())
         raise(KS_E_UNSUPPORTED, 0, "block of %u threads needs %zu bytes of LDS (limit %zu)", a.threads_per_block, need,
               ks_lds_limit() - 64);
@@ -1338,7 +1343,8 @@ ks_status ks_interp_kernel(const ks_program* prog, ks_dim3 block, const char** n
     const uint64_t tpb = dim_count(block);
     if (!tpb || tpb > KS_MAX_BLOCK_THREADS) raise(KS_E_INVALID_ARG, 0, "block of %llu threads", (unsigned long long)tpb);
     const int variant = ks_choose_variant(prog->reg_slots, (uint32_t)tpb);
-    *name = variant == 32 ? "ks_interp_v32" : variant == 64 ? "ks_interp_v64" : "ks_interp_lds";
+    if (variant == 0) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots", prog->reg_slots);
+    *name = variant == 32 ? "ks_interp_v32" : "ks_interp_v64";
     return KS_OK;
   });
 }

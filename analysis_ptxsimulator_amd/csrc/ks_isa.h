@@ -77,39 +77,44 @@ static_assert(sizeof(KsInst) == 64, "KsInst must be 64 bytes");
 // Interpreter classes.  Register-writing classes first (their issue ends with
 // pc + 1), then memory, then control.
 enum DClass : uint32_t {
-  DC_FFMA,     // r = fma(x0, x1, x2)
-  DC_FARITH,   // add/sub/mul.f32 as one rounding: r = fma(x0, a0 ? 1.0 : x1, (x2 & a1) ^ a2)
+  DC_FMA,      // f32 add/sub/mul/fma as one rounding: r = fma(x0, a0 ? 1.0 : x1, (x2 & a1) ^ a2)
   DC_IADD,     // add/sub.{s,u}32: r = x0 + (x1 ^ a0) + a1
   DC_IMAD,     // mul.lo/mad.lo.{s,u}32: r = x0 * x1 + (x2 & a0)
   DC_MOV,      // mov (register or immediate); a0 = 1: 64-bit
-  DC_SELP,     // selp; s2 = predicate index; a0 = 1: 64-bit
   DC_SETP,     // setp; a0 = DS_* operand type, a1 = relation mask (bit0 lt, bit1 eq, bit2 gt)
+  DC_SELP,     // selp; s2 = predicate index; a0 = 1: 64-bit
   DC_I64,      // 64-bit integer ops and mul.wide; a0 = DI_*
   DC_MOVSP,    // mov from a special register; a0 = KSP_*
   DC_LDP,      // ld.param; a0 = byte offset in the parameter block, a1 = 1: 64-bit
-  DC_MEMG,     // ld/st.global; xf: XF_LOAD, XF_W64, XF_A64; (a0, a1) = byte offset (signed 64-bit)
+  DC_MEMG,     // ld/st.global; XF_LOAD, XF_W64, XF_A64; (a0, a1) = byte offset (signed 64-bit)
   DC_MEMS,     // ld/st.shared; as DC_MEMG
   DC_BRA,      // bra; a0 = target, a1 = reconvergence index (0xFFFFFFFF = exit)
   DC_BAR,      // bar.sync 0
   DC_RET,      // ret / exit
   DC_END,      // sentinel after the last instruction: lanes that get here exit at no cost
+  DC_COUNT
 };
+constexpr uint32_t CB(uint32_t c) { return 1u << c; }  // class bit in DInst::ctl
+// classes that write a register (or predicate) and continue at pc + 1
+constexpr uint32_t CB_REG = CB(DC_FMA) | CB(DC_IADD) | CB(DC_IMAD) | CB(DC_MOV) | CB(DC_SETP) | CB(DC_SELP) |
+                            CB(DC_I64) | CB(DC_MOVSP) | CB(DC_LDP);
+constexpr uint32_t CB_MEM = CB(DC_MEMG) | CB(DC_MEMS);
 
 enum : uint32_t { DS_S32, DS_U32, DS_F32, DS_S64, DS_U64 };                 // DC_SETP operand types
 enum : uint32_t { DI_ADD, DI_SUB, DI_MUL, DI_MAD, DI_WIDE_S, DI_WIDE_U };  // DC_I64 operations
 
-// DInst::xf flags
+// DInst::ctl flags (above the class bits)
 enum : uint32_t {
-  XF_IMM = 1,    // some source is an immediate: imm[] goes into the immediate slots first
-  XF_FIX = 2,    // the end sentinel, or a divergent branch reconverges here
-  XF_LOAD = 4,   // memory: load (else store)
-  XF_W64 = 8,    // memory: 8-byte access
-  XF_A64 = 16,   // memory: 64-bit address register
+  XF_IMM = 1u << 16,   // some source is an immediate: imm[] goes into the immediate slots first
+  XF_FIX = 1u << 17,   // the end sentinel, or a divergent branch reconverges here
+  XF_LOAD = 1u << 18,  // memory: load (else store)
+  XF_W64 = 1u << 19,   // memory: 8-byte access
+  XF_A64 = 1u << 20,   // memory: 64-bit address register
 };
 
 struct DInst {         // 128 bytes; dwords 0-15 are read for every instruction
-  uint32_t cls;        // DClass
-  uint32_t xf;         // XF_*
+  uint32_t ctl;        // CB(class) | XF_* flags
+  uint32_t a2;         // class-specific
   uint32_t s0, s1, s2; // source register slots (immediates: the immediate slots)
   uint32_t dst;        // destination slot (low slot of a 64-bit register) or predicate index
   uint32_t sbo[4];     // byte offsets in the warp's scoreboard of src0, src1, src2 and the guard
@@ -119,8 +124,7 @@ struct DInst {         // 128 bytes; dwords 0-15 are read for every instruction
   uint32_t gmode;      // 0: @p, 1: @!p, 2: unguarded (compared with the predicate bit: on = bit != gmode)
   uint32_t a0, a1;     // class-specific
   uint32_t imm[6];     // immediate slot values: source k at imm[2k] (low) and imm[2k+1] (high)
-  uint32_t a2, a3;     // class-specific
-  uint32_t pad[8];
+  uint32_t pad[10];
 };
 static_assert(sizeof(DInst) == 128, "DInst must be 128 bytes");
 

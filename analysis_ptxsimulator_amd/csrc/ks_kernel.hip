@@ -6,10 +6,9 @@
 //   * each wave step executes ONE decoded instruction: the one at the smaller pc
 //     of the two warps (both warps run it when they share that pc), so fetch
 //     (scalar loads), dispatch and register slot indices are wave-uniform;
-//   * simulated registers live in a register file of 32-bit slots per lane,
-//     either in physical VGPRs reserved for it (v64 upward, reached through the
-//     VGPR index mode of s_set_gpr_idx_on: exec-masked, no memory traffic) or,
-//     for programs or blocks that do not fit, in LDS as [slot][thread].  Six
+//   * simulated registers live in a register file of 32-bit slots per lane in
+//     physical VGPRs reserved for it (v56 upward, reached through the VGPR
+//     index mode of s_set_gpr_idx_on: exec-masked, no memory traffic).  Six
 //     slots after the program's hold the current instruction's immediates, so
 //     every source operand is a register read;
 //   * lane masks of the two warps are 64-bit scalars (warp 2w in the low half),
@@ -84,80 +83,65 @@ __device__ __forceinline__ uint32_t popc(uint32_t m) { return (uint32_t)__builti
 
 // ---------------------------------------------------------------------------- register files
 //
-// RFN = 0: LDS, [slot][thread of the workgroup].  RFN = 40 / 72: physical VGPRs
-// v64 .. v64+RFN-1, outside the compiler's allocation; slot s of a lane is VGPR
-// v[64 + s] of that lane.  The kernels carry amdgpu_num_vgpr(32): on targets with
-// the unified VGPR/AGPR file the compiler doubles that figure, so v64 and up are
+// RFN = 40 / 72 physical VGPRs v56 .. v56+RFN-1, outside the compiler's
+// allocation, hold the register file: slot s of a lane is VGPR
+// v[56 + s] of that lane.  The kernels carry amdgpu_num_vgpr(28): on targets with
+// the unified VGPR/AGPR file the compiler doubles that figure, so v56 and up are
 // reserved (never allocated).  A figure the launch bound cannot honour is
-// silently ignored, which would hand v64+ back to the allocator; the build checks
+// silently ignored, which would hand v56+ back to the allocator; the build checks
 // the assembly for any compiler-written use of them and that the kernel's VGPR
 // count covers the file (the zero() clobber lists make the compiler count it).
 
 template <int RFN>
 struct RegFile;
 
-template <>
-struct RegFile<0> {
-  uint32_t* base;
-  uint32_t stride;
-  uint32_t tid;
-  __device__ __forceinline__ uint32_t get(uint32_t s) const { return base[s * stride + tid]; }
-  __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const {
-    a = get(i0);
-    b = get(i1);
-  }
-  __device__ __forceinline__ void get3(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t& a, uint32_t& b,
-                                       uint32_t& c) const {
-    a = get(i0);
-    b = get(i1);
-    c = get(i2);
-  }
-  __device__ __forceinline__ void put(uint32_t s, uint32_t v) const { base[s * stride + tid] = v; }
-  __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {
-    put(s, lo);
-    put(s + 1, hi);
-  }
-  // the six immediate slots from slot `ib` on
-  __device__ __forceinline__ void put_imm(uint32_t ib, const uint32_t* v) const {
-    for (int k = 0; k < 6; ++k) put(ib + k, v[k]);
-  }
-};
-
 // VGPR index mode: between s_set_gpr_idx_on and s_set_gpr_idx_off the SRC0 (or
 // DST) VGPR operand of each VALU instruction is offset by the index held in M0;
 // s_set_gpr_idx_idx changes the index without leaving the mode.
+// First six VGPRs of the register file (RF_V0 = slot 0 before indexing).  The
+// build's RESERVED_BASE must name the same register.
+#define KS_RF_V0 "v56"
+#define KS_RF_V1 "v57"
+#define KS_RF_V2 "v58"
+#define KS_RF_V3 "v59"
+#define KS_RF_V4 "v60"
+#define KS_RF_V5 "v61"
+
 #define KS_RF_ASM_ACCESS                                                                           \
   __device__ __forceinline__ uint32_t get(uint32_t s) const {                                      \
     uint32_t r;                                                                                    \
-    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, v64\n\ts_set_gpr_idx_off"   \
+    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, " KS_RF_V0                  \
+                 "\n\ts_set_gpr_idx_off"                                                          \
                  : "=v"(r) : "s"(s) : "m0");                                                      \
     return r;                                                                                      \
   }                                                                                                \
   __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const {  \
-    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, v64\n\t"                     \
-                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, v64\n\ts_set_gpr_idx_off"                  \
+    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, " KS_RF_V0 "\n\t"          \
+                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, " KS_RF_V0 "\n\ts_set_gpr_idx_off"         \
                  : "=&v"(a), "=v"(b) : "s"(i0), "s"(i1) : "m0");                                  \
   }                                                                                                \
   __device__ __forceinline__ void get3(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t& a, uint32_t& b, \
                                        uint32_t& c) const {                                        \
-    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, v64\n\t"                     \
-                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, v64\n\t"                                   \
-                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, v64\n\ts_set_gpr_idx_off"                  \
+    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, " KS_RF_V0 "\n\t"          \
+                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, " KS_RF_V0 "\n\t"                          \
+                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, " KS_RF_V0 "\n\ts_set_gpr_idx_off"         \
                  : "=&v"(a), "=&v"(b), "=v"(c) : "s"(i0), "s"(i1), "s"(i2) : "m0");               \
   }                                                                                                \
   __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                              \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v64, %1\n\ts_set_gpr_idx_off"    \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 " KS_RF_V0 ", %1"                 \
+                 "\n\ts_set_gpr_idx_off"                                                          \
                  : : "s"(s), "v"(v) : "m0");                                                      \
   }                                                                                                \
   __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {               \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 v64, %1\n\t"                      \
-                 "v_mov_b32 v65, %2\n\ts_set_gpr_idx_off"                                          \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 " KS_RF_V0 ", %1\n\t"           \
+                 "v_mov_b32 " KS_RF_V1 ", %2\n\ts_set_gpr_idx_off"                                 \
                  : : "s"(s), "v"(lo), "v"(hi) : "m0");                                            \
   }                                                                                                \
   __device__ __forceinline__ void put_imm(uint32_t ib, const uint32_t* v) const {                  \
     asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\t"                                           \
-                 "v_mov_b32 v64, %1\n\tv_mov_b32 v65, %2\n\tv_mov_b32 v66, %3\n\t"                  \
-                 "v_mov_b32 v67, %4\n\tv_mov_b32 v68, %5\n\tv_mov_b32 v69, %6\n\t"                  \
+                 "v_mov_b32 " KS_RF_V0 ", %1\n\tv_mov_b32 " KS_RF_V1 ", %2\n\t"                     \
+                 "v_mov_b32 " KS_RF_V2 ", %3\n\tv_mov_b32 " KS_RF_V3 ", %4\n\t"                     \
+                 "v_mov_b32 " KS_RF_V4 ", %5\n\tv_mov_b32 " KS_RF_V5 ", %6\n\t"                     \
                  "s_set_gpr_idx_off"                                                               \
                  : : "s"(ib), "s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5])     \
                  : "m0");                                                                          \
@@ -166,13 +150,59 @@ struct RegFile<0> {
 template <>
 struct RegFile<40> {
   KS_RF_ASM_ACCESS
-  __device__ __forceinline__ static void zero() { asm volatile("v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t""v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t""v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t""v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t""v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t""v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t""v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t""v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t""v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t""v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t" ::: "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103"); }
+  __device__ __forceinline__ static void zero() {
+    asm volatile("v_mov_b32 v56, 0\n\t""v_mov_b32 v57, 0\n\t""v_mov_b32 v58, 0\n\t""v_mov_b32 v59, 0\n\t"
+                 "v_mov_b32 v60, 0\n\t""v_mov_b32 v61, 0\n\t""v_mov_b32 v62, 0\n\t""v_mov_b32 v63, 0\n\t"
+                 "v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t"
+                 "v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t"
+                 "v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t"
+                 "v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t"
+                 "v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t"
+                 "v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t"
+                 "v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t"
+                 "v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t"
+                 :::
+                 "v56", "v57", "v58", "v59", "v60", "v61", "v62", "v63",
+                 "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71",
+                 "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79",
+                 "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87",
+                 "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95");
+  }
 };
 
 template <>
 struct RegFile<72> {
   KS_RF_ASM_ACCESS
-  __device__ __forceinline__ static void zero() { asm volatile("v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t""v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t""v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t""v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t""v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t""v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t""v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t""v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t""v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t""v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t""v_mov_b32 v104, 0\n\t""v_mov_b32 v105, 0\n\t""v_mov_b32 v106, 0\n\t""v_mov_b32 v107, 0\n\t""v_mov_b32 v108, 0\n\t""v_mov_b32 v109, 0\n\t""v_mov_b32 v110, 0\n\t""v_mov_b32 v111, 0\n\t""v_mov_b32 v112, 0\n\t""v_mov_b32 v113, 0\n\t""v_mov_b32 v114, 0\n\t""v_mov_b32 v115, 0\n\t""v_mov_b32 v116, 0\n\t""v_mov_b32 v117, 0\n\t""v_mov_b32 v118, 0\n\t""v_mov_b32 v119, 0\n\t""v_mov_b32 v120, 0\n\t""v_mov_b32 v121, 0\n\t""v_mov_b32 v122, 0\n\t""v_mov_b32 v123, 0\n\t""v_mov_b32 v124, 0\n\t""v_mov_b32 v125, 0\n\t""v_mov_b32 v126, 0\n\t""v_mov_b32 v127, 0\n\t""v_mov_b32 v128, 0\n\t""v_mov_b32 v129, 0\n\t""v_mov_b32 v130, 0\n\t""v_mov_b32 v131, 0\n\t""v_mov_b32 v132, 0\n\t""v_mov_b32 v133, 0\n\t""v_mov_b32 v134, 0\n\t""v_mov_b32 v135, 0\n\t" ::: "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127", "v128", "v129", "v130", "v131", "v132", "v133", "v134", "v135"); }
+  __device__ __forceinline__ static void zero() {
+    asm volatile("v_mov_b32 v56, 0\n\t""v_mov_b32 v57, 0\n\t""v_mov_b32 v58, 0\n\t""v_mov_b32 v59, 0\n\t"
+                 "v_mov_b32 v60, 0\n\t""v_mov_b32 v61, 0\n\t""v_mov_b32 v62, 0\n\t""v_mov_b32 v63, 0\n\t"
+                 "v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t"
+                 "v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t"
+                 "v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t"
+                 "v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t"
+                 "v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t"
+                 "v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t"
+                 "v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t"
+                 "v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t"
+                 "v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t"
+                 "v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t"
+                 "v_mov_b32 v104, 0\n\t""v_mov_b32 v105, 0\n\t""v_mov_b32 v106, 0\n\t""v_mov_b32 v107, 0\n\t"
+                 "v_mov_b32 v108, 0\n\t""v_mov_b32 v109, 0\n\t""v_mov_b32 v110, 0\n\t""v_mov_b32 v111, 0\n\t"
+                 "v_mov_b32 v112, 0\n\t""v_mov_b32 v113, 0\n\t""v_mov_b32 v114, 0\n\t""v_mov_b32 v115, 0\n\t"
+                 "v_mov_b32 v116, 0\n\t""v_mov_b32 v117, 0\n\t""v_mov_b32 v118, 0\n\t""v_mov_b32 v119, 0\n\t"
+                 "v_mov_b32 v120, 0\n\t""v_mov_b32 v121, 0\n\t""v_mov_b32 v122, 0\n\t""v_mov_b32 v123, 0\n\t"
+                 "v_mov_b32 v124, 0\n\t""v_mov_b32 v125, 0\n\t""v_mov_b32 v126, 0\n\t""v_mov_b32 v127, 0\n\t"
+                 :::
+                 "v56", "v57", "v58", "v59", "v60", "v61", "v62", "v63",
+                 "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71",
+                 "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79",
+                 "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87",
+                 "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95",
+                 "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103",
+                 "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111",
+                 "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119",
+                 "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127");
+  }
 };
 
 // ---------------------------------------------------------------------------- analyser
@@ -293,20 +323,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const cdinst prog = (cdinst)(uintptr_t)a.prog;
   const uint32_t ib = a.rf_slots - KS_IMM_SLOTS;  // first immediate slot
 
-  // LDS: [register file (LDS variant)] [scoreboard, 129 words per warp] [shared window]
+  // LDS: [scoreboard, 129 words per warp] [shared window]
   RegFile<RFN> R;
-  const uint32_t rf_words = RFN == 0 ? a.rf_slots * WG : 0u;
-  if constexpr (RFN == 0) {
-    R.base = lds;
-    R.stride = WG;
-    R.tid = tid;
-  } else {
-    RegFile<RFN>::zero();
-  }
-  uint32_t* const sbw = lds + rf_words;
+  RegFile<RFN>::zero();
+  uint32_t* const sbw = lds;
   uint8_t* const win = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
   {
-    const uint32_t words = rf_words + (WG / 32u) * KS_SB_ENTRIES + ((a.shared_bytes + 3u) >> 2);
+    const uint32_t words = (WG / 32u) * KS_SB_ENTRIES + ((a.shared_bytes + 3u) >> 2);
     for (uint32_t i = tid; i < words; i += WG) lds[i] = 0;
     if (tid < 3) {
       ep_max[tid] = 0;
@@ -391,18 +414,18 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const bool go0 = (uint32_t)gm != 0u, go1 = (gm >> 32) != 0u;
       const cdinst I = prog + pc;
       const u32x16 hot = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(I);
-      const uint32_t cls = hot[0], xf = hot[1];
+      const uint32_t ctl = hot[0];  // class bit | flags
       const uint32_t s0 = hot[2], s1 = hot[3], s2 = hot[4], dst = hot[5];
       const uint32_t sbod = hot[10], lat = hot[11], gp = hot[12], gmode = hot[13];
-      const uint32_t a0 = hot[14], a1 = hot[15];
+      const uint32_t a0 = hot[14], a1 = hot[15], a2 = hot[1];
 
       // issue cycle (per warp, uniform over its lanes): the later of the previous issue
       // + 1 and the ready cycle of every register source (absent sources read a zero word)
       const uint32_t iss = umax(umax(v_next, sb_at(hot[6])), umax(umax(sb_at(hot[7]), sb_at(hot[8])), sb_at(hot[9])));
 
       uint32_t need = 0;  // warps whose top stack entry must be settled (bit h)
-      if (xf & XF_FIX) {  // the end sentinel, or a reconvergence point: warps whose top entry ends here pop
-        if (cls == DC_END) {
+      if (ctl & XF_FIX) {  // the end sentinel, or a reconvergence point: warps whose top entry ends here pop
+        if (ctl & CB(DC_END)) {
           need = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
           ex64 |= m64 & gm;  // lanes that get past the last instruction exit, at no cost
         } else {
@@ -453,32 +476,28 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
 
         // ---------------------------------------------------------------- execute
-        if (cls <= DC_LDP) {
-          if (xf & XF_IMM) {
+        if (ctl & CB_REG) {
+          if (ctl & XF_IMM) {
             uint32_t iv[6];
             for (int k = 0; k < 6; ++k) iv[k] = I->imm[k];
             R.put_imm(ib, iv);
           }
           if (lanes(on64)) {
-            if (cls == DC_FFMA) {
-              uint32_t x0, x1, x2;
-              R.get3(s0, s1, s2, x0, x1, x2);
-              R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1), __uint_as_float(x2))));
-            } else if (cls == DC_FARITH) {
+            if (ctl & CB(DC_FMA)) {
               uint32_t x0, x1, x2;
               R.get3(s0, s1, s2, x0, x1, x2);
               const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
-              const uint32_t c = (x2 & a1) ^ I->a2;                 // x2, -x2 or -0.0f
+              const uint32_t c = (x2 & a1) ^ a2;                    // x2, -x2 or -0.0f
               R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(c))));
-            } else if (cls == DC_IADD) {
+            } else if (ctl & CB(DC_IADD)) {
               uint32_t x0, x1;
               R.get2(s0, s1, x0, x1);
               R.put(dst, x0 + (x1 ^ a0) + a1);
-            } else if (cls == DC_IMAD) {
+            } else if (ctl & CB(DC_IMAD)) {
               uint32_t x0, x1, x2;
               R.get3(s0, s1, s2, x0, x1, x2);
               R.put(dst, x0 * x1 + (x2 & a0));
-            } else if (cls == DC_MOV) {
+            } else if (ctl & CB(DC_MOV)) {
               if (a0) {
                 uint32_t lo, hi;
                 R.get2(s0, s0 + 1u, lo, hi);
@@ -486,7 +505,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               } else {
                 R.put(dst, R.get(s0));
               }
-            } else if (cls == DC_SELP) {
+            } else if (ctl & CB(DC_SELP)) {
               const bool p = (pbits >> s2) & 1u;
               if (a0) {
                 uint32_t xl, xh, yl, yh;
@@ -498,7 +517,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
                 R.get2(s0, s1, x0, x1);
                 R.put(dst, p ? x0 : x1);
               }
-            } else if (cls == DC_SETP) {
+            } else if (ctl & CB(DC_SETP)) {
               bool lt, eq, gt;
               if (a0 == DS_F32) {
                 uint32_t x0, x1;
@@ -524,7 +543,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               }
               const bool c = (lt && (a1 & 1u)) || (eq && (a1 & 2u)) || (gt && (a1 & 4u));
               pbits = (pbits & ~(1u << dst)) | ((c ? 1u : 0u) << dst);
-            } else if (cls == DC_I64) {
+            } else if (ctl & CB(DC_I64)) {
               uint64_t r;
               if (a0 >= DI_WIDE_S) {
                 uint32_t x0, x1;
@@ -546,7 +565,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
                 }
               }
               R.put2(dst, (uint32_t)r, (uint32_t)(r >> 32));
-            } else if (cls == DC_MOVSP) {
+            } else if (ctl & CB(DC_MOVSP)) {
               const uint32_t t_lin = my_w * 32u + sl;
               const uint32_t bx = a.block[0], by = a.block[1];
               const uint32_t gx = a.grid[0], gy = a.grid[1];
@@ -575,15 +594,15 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
           spc0 = go0 ? pc + 1u : spc0;
           spc1 = go1 ? pc + 1u : spc1;
-        } else if (cls <= DC_MEMS) {
-          const bool is_global = cls == DC_MEMG;
-          const bool is_load = xf & XF_LOAD;
-          const bool w64 = xf & XF_W64;
+        } else if (ctl & CB_MEM) {
+          const bool is_global = ctl & CB(DC_MEMG);
+          const bool is_load = ctl & XF_LOAD;
+          const bool w64 = ctl & XF_W64;
           const uint32_t S = w64 ? 8u : 4u;
           const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
           const uint64_t off = (uint64_t)a0 | ((uint64_t)a1 << 32);
           uint64_t base;
-          if (xf & XF_A64) {
+          if (ctl & XF_A64) {
             uint32_t lo, hi;
             R.get2(s0, s0 + 1u, lo, hi);
             base = (uint64_t)lo | ((uint64_t)hi << 32);
@@ -708,7 +727,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
           spc0 = go0 ? pc + 1u : spc0;
           spc1 = go1 ? pc + 1u : spc1;
-        } else if (cls == DC_BRA) {
+        } else if (ctl & CB(DC_BRA)) {
           const uint32_t target = a0, rpc = a1;
           const uint32_t mm0 = (uint32_t)mm, mm1 = (uint32_t)(mm >> 32);
           uint32_t divm = 0;
@@ -756,7 +775,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             m64 = mask64 & ~ex64;
             cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
           }
-        } else if (cls == DC_RET) {
+        } else if (ctl & CB(DC_RET)) {
           ex64 |= on64;
           m64 = mask64 & ~ex64;
           if (go0) {
@@ -874,18 +893,15 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 
 }  // namespace
 
-// Register file in LDS: any slot count that fits, blocks up to 1024 threads.
-__global__ void __launch_bounds__(1024) ks_interp_lds(const KsArgs a) { interp<0>(a); }
-
-// Register file in 40 reserved VGPRs (v64..v103): 104 VGPRs, 4 waves per SIMD,
+// Register file in 40 reserved VGPRs (v56..v95): 96 VGPRs, 5 waves per SIMD,
 // blocks up to 1024 threads.
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v32(const KsArgs a) {
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v32(const KsArgs a) {
   interp<40>(a);
 }
 
-// Register file in 72 reserved VGPRs (v64..v135): 136 VGPRs, 3 waves per SIMD,
-// blocks up to 768 threads.
-__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64(const KsArgs a) {
+// Register file in 72 reserved VGPRs (v56..v127): 128 VGPRs, 4 waves per SIMD,
+// blocks up to 1024 threads.
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v64(const KsArgs a) {
   interp<72>(a);
 }
 
@@ -906,41 +922,38 @@ size_t ks_lds_limit() {
   return (size_t)v;
 }
 
-// Register-file variant: total slots = program slots + the immediate slots.
+// Register-file variant for a program of `slots` slots (plus the immediate slots):
+// 32 (40-VGPR file) or 64 (72-VGPR file); 0 if it fits neither.
 int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
-  const uint32_t waves = ((block_threads + 31u) / 32u + 1u) / 2u;
+  (void)block_threads;  // both variants run blocks of up to 1024 threads
   const uint32_t total = slots + KS_IMM_SLOTS;
   if (total <= 40) return 32;
-  if (total <= 72 && waves <= 12) return 64;
+  if (total <= 72) return 64;
   return 0;
 }
 
-size_t ks_lds_bytes(int variant, uint32_t slots, uint32_t wg, uint32_t shared_bytes) {
-  const size_t rf = variant == 0 ? (size_t)(slots + KS_IMM_SLOTS) * wg * 4u : 0u;
+size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes) {
   const size_t sb = (size_t)(wg / 32u) * KS_SB_ENTRIES * 4u;
-  return rf + sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
+  return sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
 }
 
 hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, hipStream_t s) {
   const uint32_t waves = (a.warps_per_block + 1u) / 2u;
   const uint32_t wg = 64u * waves;
   const int variant = ks_choose_variant(slots, a.threads_per_block);
-  const size_t lds = ks_lds_bytes(variant, slots, wg, a.shared_bytes);
-  if (lds + 64 > ks_lds_limit()) return hipErrorInvalidValue;
+  const size_t lds = ks_lds_bytes(wg, a.shared_bytes);
+  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > 1024) return hipErrorInvalidValue;
   if (a.rf_slots != slots + KS_IMM_SLOTS) return hipErrorInvalidValue;
-  const void* fn = variant == 32 ? (const void*)ks_interp_v32
-                   : variant == 64 ? (const void*)ks_interp_v64
-                                   : (const void*)ks_interp_lds;
-  static bool attr_set[3] = {false, false, false};
-  const int vi = variant == 0 ? 0 : (variant == 32 ? 1 : 2);
+  const void* fn = variant == 32 ? (const void*)ks_interp_v32 : (const void*)ks_interp_v64;
+  static bool attr_set[2] = {false, false};
+  const int vi = variant == 32 ? 0 : 1;
   if (!attr_set[vi]) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(ks_lds_limit() - 64));
     if (e != hipSuccess) return e;
     attr_set[vi] = true;
   }
   if (variant == 32) hipLaunchKernelGGL(ks_interp_v32, dim3(n_blocks), dim3(wg), lds, s, a);
-  else if (variant == 64) hipLaunchKernelGGL(ks_interp_v64, dim3(n_blocks), dim3(wg), lds, s, a);
-  else hipLaunchKernelGGL(ks_interp_lds, dim3(n_blocks), dim3(wg), lds, s, a);
+  else hipLaunchKernelGGL(ks_interp_v64, dim3(n_blocks), dim3(wg), lds, s, a);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@
 #include "ks_isa.h"
 
 // Interpreter: one workgroup per simulated block, ceil(warps/2) wave64s per
-// workgroup.  `slots` is the program's register-slot count.
+// workgroup.  `slots` is the program's register-slot count (a.rf_slots must be
+// slots plus the immediate slots).
 hipError_t ks_launch_interp(const ks::KsArgs& a, uint32_t n_blocks, uint32_t slots, hipStream_t s);
 
 // OR of the status words of `n_warps` counter records into *d_out.
@@ -14,9 +15,9 @@ hipError_t ks_launch_status_or(const void* counters, uint64_t n_warps, uint32_t*
 // Largest dynamic LDS a workgroup of the interpreter may use on the current device.
 size_t ks_lds_limit();
 
-// Register-file variant for a program and block size: 32 or 64 (reserved VGPRs)
-// or 0 (LDS).
+// Register-file variant for a program of `slots` register slots: 32 (40 reserved
+// VGPRs) or 64 (72 reserved VGPRs), immediate slots included; 0 if neither fits.
 int ks_choose_variant(uint32_t slots, uint32_t block_threads);
 
-// Dynamic LDS bytes of one workgroup of `wg` lanes for that variant.
-size_t ks_lds_bytes(int variant, uint32_t slots, uint32_t wg, uint32_t shared_bytes);
+// Dynamic LDS bytes of one workgroup of `wg` lanes (scoreboards and the shared window).
+size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes);

@@ -165,11 +165,11 @@ ks_status ks_alloc_state(const ks_program* prog, const ks_config* cfg, void* d_g
 ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, size_t params_len,
                  void* stream);
 
-/* Name of the interpreter kernel ks_run launches for this program and block shape
- * ("ks_interp_v32", "ks_interp_v64": register file in 32 or 64 reserved VGPRs per
- * lane; "ks_interp_lds": register file in LDS), as profilers list it.  *name
- * points to a static string.  Errors: KS_E_INVALID_ARG (NULL arguments, empty or
- * oversized block). */
+/* Name of the interpreter kernel ks_run launches for this program and block shape,
+ * as profilers list it: "ks_interp_v32" (programs of up to 34 register slots: a
+ * 40-VGPR register file per lane, six slots of it for immediates) or
+ * "ks_interp_v64" (up to 64 slots: a 72-VGPR file).  *name points to a static
+ * string.  Errors: KS_E_INVALID_ARG (NULL arguments, empty or oversized block). */
 ks_status ks_interp_kernel(const ks_program* prog, ks_dim3 block, const char** name);
 
 /* Copy n bytes of simulated global memory at byte offset sim_addr to host memory

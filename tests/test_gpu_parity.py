@@ -162,6 +162,16 @@ def test_random_stress_small(K, oracle_mod, seed):
     full_parity(K, oracle_mod, w)
 
 
+@pytest.mark.parametrize("block", [1024, 992, 96])
+def test_random_stress_block_sizes(K, oracle_mod, block):
+    """The 64-slot program (72-VGPR register file) on full-size, ragged and small
+    blocks: 16 waves per workgroup, a last wave with one warp, one and a half waves."""
+    w = W.random_stress(prog_seed=2, grid=12 if block > 256 else 40, block=block, gmem_bytes=1 << 24,
+                        trace_cap=512)
+    assert K.ks_interp_kernel(K.ks_load_program(w.ptx), w.block) == "ks_interp_v64"
+    full_parity(K, oracle_mod, w)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_control_flow_shapes(K, oracle_mod, seed):
     rng = np.random.default_rng(seed)

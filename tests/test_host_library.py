@@ -145,20 +145,16 @@ def test_program_limits(ks):
 
 
 def test_interp_kernel_choice(ks):
-    """Register-file variant: 32 reserved VGPRs when the program needs at most 32
-    slots, 64 when it needs at most 64 and the block has at most 768 threads
-    (12 waves of 160 VGPRs), else the LDS register file."""
+    """Register-file variant: 40 reserved VGPRs when the program needs at most 34
+    slots (six more hold immediates), else 72; blocks of up to 1024 threads."""
     small = ks.ks_load_program(W.vector_add().ptx)
     big = ks.ks_load_program(W.random_stress(prog_seed=0, grid=4, gmem_bytes=1 << 20).ptx)
     try:
-        assert ks.ks_program_info(small)["reg_slots"] <= 32
+        assert ks.ks_program_info(small)["reg_slots"] <= 34
         assert ks.ks_program_info(big)["reg_slots"] == 64
-        assert ks.ks_interp_kernel(small, (256,)) == "ks_interp_v32"
-        assert ks.ks_interp_kernel(small, (1024,)) == "ks_interp_v32"
-        assert ks.ks_interp_kernel(big, (256,)) == "ks_interp_v64"
-        assert ks.ks_interp_kernel(big, (768,)) == "ks_interp_v64"
-        assert ks.ks_interp_kernel(big, (769,)) == "ks_interp_lds"
-        assert ks.ks_interp_kernel(big, (32, 32)) == "ks_interp_lds"
+        for block in ((32,), (256,), (1024,), (32, 32)):
+            assert ks.ks_interp_kernel(small, block) == "ks_interp_v32"
+            assert ks.ks_interp_kernel(big, block) == "ks_interp_v64"
         for bad in ((0,), (1025,), (64, 32)):
             with pytest.raises(ks.KsError):
                 ks.ks_interp_kernel(small, bad)

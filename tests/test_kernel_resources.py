@@ -58,8 +58,6 @@ def test_checker_rejects_compiler_use_of_reserved_vgprs():
                 "\tglobal_load_dwordx4 v[%d:%d], v[0:1], off\n" % (b + 4, b + 7)):
         with pytest.raises(RuntimeError, match="compiler-allocated code uses v"):
             kbuild.check_device_asm(_fake("ks_interp_v64", ok + bad))
-    # the LDS register-file kernel may use any VGPR
-    kbuild.check_device_asm(_fake("ks_interp_lds", "\tv_add_u32_e32 v120, v1, v2\n"))
 
 
 def test_checker_rejects_short_vgpr_count():
@@ -71,4 +69,24 @@ def test_checker_rejects_short_vgpr_count():
 
 def test_checker_rejects_scratch():
     with pytest.raises(RuntimeError, match="scratch"):
-        kbuild.check_device_asm(_fake("ks_interp_lds", "\ts_endpgm\n", scratch=16))
+        kbuild.check_device_asm(_fake("ks_interp_v32", "\ts_endpgm\n", scratch=16))
+
+
+def test_register_file_names_match_the_reserved_base():
+    """The interpreter's inline assembly names the register file's first six VGPRs
+    (slot 0 onward, offset by the index mode); they must start at the reserved base
+    and be consecutive, and every explicitly named VGPR in the register-file code
+    must lie inside the file."""
+    import re
+    src = open(os.path.join(kbuild.CSRC, "ks_kernel.hip")).read()
+    names = dict(re.findall(r'#define (KS_RF_V\d) "v(\d+)"', src))
+    assert sorted(names) == ["KS_RF_V%d" % k for k in range(6)]
+    for k in range(6):
+        assert int(names["KS_RF_V%d" % k]) == kbuild.RESERVED_BASE + k
+    access = src[src.index("#define KS_RF_ASM_ACCESS"):src.index("template <>\nstruct RegFile<40>")]
+    assert not re.findall(r'"[^"]*\bv\d+', access.replace('"v_mov_b32 "', '')), "literal VGPR in the accessors"
+    for n in (40, 72):
+        body = src[src.index("struct RegFile<%d>" % n):]
+        body = body[:body.index("};")]
+        regs = sorted({int(r) for r in re.findall(r'\bv(\d+)\b', body)})
+        assert regs == list(range(kbuild.RESERVED_BASE, kbuild.RESERVED_BASE + n)), n

@@ -80,6 +80,14 @@ __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint32_t popc(uint32_t m) { return (uint32_t)__builtin_popcount(m); }
+// a == b ? ~0 : 0 for wave-uniform a, b, as a scalar word.  Written as scalar
+// assembly so that the result stays an integer: the optimiser turns the plain
+// expression into a boolean, which it keeps as a lane mask across blocks.
+__device__ __forceinline__ uint32_t s_eq_mask(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("s_cmp_eq_u32 %1, %2\n\ts_cselect_b32 %0, -1, 0" : "=s"(r) : "s"(a), "s"(b) : "scc");
+  return r;
+}
 
 // ---------------------------------------------------------------------------- register files
 //
@@ -339,7 +347,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   __syncthreads();
 
   const uint32_t my_w = 2u * wave + hl;
-  const bool small_gmem = a.gmem_bytes <= (1ull << 37);  // sector ids of valid accesses fit 32 bits
+  const uint32_t small_gmem = a.gmem_bytes <= (1ull << 37) ? 1u : 0u;  // sector ids of valid accesses fit 32 bits
   uint8_t* const my_sb = reinterpret_cast<uint8_t*>(sbw + my_w * KS_SB_ENTRIES);  // this lane's warp's scoreboard
   auto sb_at = [&](uint32_t off) -> uint32_t& { return *reinterpret_cast<uint32_t*>(my_sb + off); };
 
@@ -369,12 +377,22 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   uint32_t fl = 0;            // warp: trace records written to memory
   uint32_t nf = cap == 0 ? INF : umin(cap, 32u);  // warp: record count at which the next chunk is written
   uint32_t ev = umin(nf, budget);                 // warp: next event (chunk write or budget)
-  uint32_t act = 0;           // instructions issued with this lane's thread active
+  uint32_t act = 0;           // instructions issued with this lane's thread active, up to the last mask change
+  uint32_t mk = 0;            // warp: issued warp-instructions at the last change of the live masks
   uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
   uint32_t pbits = 0;         // predicate p of this lane's thread in bit p
   uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
   const uint64_t gw0 = (uint64_t)blk * W + 2u * wave;  // global warp id of half 0
   uint8_t* const slot_base = a.trace + (gw0 + hl) * a.slot_bytes + 16u;  // this lane's warp's records
+
+  // Every instruction a warp issues between two changes of its live mask runs with
+  // the same mask, so thread-instructions are counted per lane only when the live
+  // masks change: each live lane adds the instructions issued since the last change.
+#define KS_ACT_FLUSH()                            \
+  {                                               \
+    act += lanes(m64) ? wi - mk : 0u;             \
+    mk = wi;                                      \
+  }
 
   // Pop entries of warp h that cannot issue (no live lane, reconverged); lanes past
   // the end exit at no cost; an empty stack finishes the warp.  Leaves spc_h.
@@ -401,6 +419,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       spc = S.pc;                                                              \
       break;                                                                   \
     }                                                                          \
+    KS_ACT_FLUSH();                                                            \
     m64 = mask64 & ~ex64;                                                      \
   }
 
@@ -410,8 +429,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     while (true) {
       const uint32_t pc = umin(spc0, spc1);
       if (pc == INF) break;
-      const uint64_t gm = (spc0 == pc ? LO : 0ull) | (spc1 == pc ? HI : 0ull);  // lanes of the issuing warps
-      const bool go0 = (uint32_t)gm != 0u, go1 = (gm >> 32) != 0u;
+      // issuing warps, as all-ones / zero words (integers, not bools: a bool that lives
+      // across blocks becomes a lane mask, and turning it back into a value costs VALU work)
+      const uint32_t go0 = s_eq_mask(spc0, pc), go1 = s_eq_mask(spc1, pc);
+      const uint64_t gm = ((uint64_t)go1 << 32) | go0;  // lanes of the issuing warps
       const cdinst I = prog + pc;
       const u32x16 hot = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(I);
       const uint32_t ctl = hot[0];  // class bit | flags
@@ -426,15 +447,15 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       uint32_t need = 0;  // warps whose top stack entry must be settled (bit h)
       if (ctl & XF_FIX) {  // the end sentinel, or a reconvergence point: warps whose top entry ends here pop
         if (ctl & CB(DC_END)) {
-          need = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
+          need = (go0 & 1u) | (go1 & 2u);
           ex64 |= m64 & gm;  // lanes that get past the last instruction exit, at no cost
         } else {
-          need = (go0 && S0.rpc == pc ? 1u : 0u) | (go1 && S1.rpc == pc ? 2u : 0u);
+          need = (S0.rpc == pc ? go0 & 1u : 0u) | (S1.rpc == pc ? go1 & 2u : 0u);
         }
         if (need & 1u) S0.pc = pc;
         if (need & 2u) S1.pc = pc;
       }
-      const uint64_t evm = ballot(wi == ev || iss > CYCLE_LIMIT) & gm;
+      const uint64_t evm = (ballot(wi == ev) | ballot(iss > CYCLE_LIMIT)) & gm;
       if (need) {
         // no issue this step
       } else if (evm) {
@@ -472,7 +493,6 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           v_next = iss + 1;
           sb_at(sbod) = iss + lat;
         }
-        act += lanes(mm) ? 1u : 0u;
         const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
 
         // ---------------------------------------------------------------- execute
@@ -595,9 +615,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           spc0 = go0 ? pc + 1u : spc0;
           spc1 = go1 ? pc + 1u : spc1;
         } else if (ctl & CB_MEM) {
-          const bool is_global = ctl & CB(DC_MEMG);
-          const bool is_load = ctl & XF_LOAD;
-          const bool w64 = ctl & XF_W64;
+          const uint32_t is_global = ctl & CB(DC_MEMG);
+          const uint32_t is_load = ctl & XF_LOAD;
+          const uint32_t w64 = ctl & XF_W64;
           const uint32_t S = w64 ? 8u : 4u;
           const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
           const uint64_t off = (uint64_t)a0 | ((uint64_t)a1 << 32);
@@ -772,11 +792,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             }
           }
           if (divm) {
+            KS_ACT_FLUSH();
             m64 = mask64 & ~ex64;
             cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
           }
         } else if (ctl & CB(DC_RET)) {
           ex64 |= on64;
+          KS_ACT_FLUSH();
           m64 = mask64 & ~ex64;
           if (go0) {
             spc0 = pc + 1u;
@@ -790,7 +812,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
         } else {  // DC_BAR: the issuing warps wait for the block
           const uint64_t conv = init64 & ~ex64;
-          const uint32_t hm = (go0 ? 1u : 0u) | (go1 ? 2u : 0u);
+          const uint32_t hm = (go0 & 1u) | (go1 & 2u);
           cnt = cnt_add2(cnt, sl, hl, C_BAR, hm, 1u);
           if (go0) {
             if ((uint32_t)mm != (uint32_t)conv) status |= KS_ST_BARDIV;
@@ -839,6 +861,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     ++epoch;
   }
 #undef KS_SETTLE
+  KS_ACT_FLUSH();
+#undef KS_ACT_FLUSH
 
   // -------------------------------------------------------------------- counters, trace tail, headers
   {

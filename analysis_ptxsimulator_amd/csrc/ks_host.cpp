@@ -1061,6 +1061,7 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         cls = g ? DC_MEMG : DC_MEMS;
         const bool ld = in.op == KO_LDG32 || in.op == KO_LDG64 || in.op == KO_LDS32 || in.op == KO_LDS64;
         const bool w64 = in.op == KO_LDG64 || in.op == KO_STG64 || in.op == KO_LDS64 || in.op == KO_STS64;
+        if (g && !w64 && in.imm[0] == 64) cls = ld ? DC_LDG : DC_STG;  // the common form has its own class
         d.ctl |= (ld ? XF_LOAD : 0u) | (w64 ? XF_W64 : 0u) | (in.imm[0] == 64 ? XF_A64 : 0u);
         d.s0 = in.src[0];
         d.s1 = ld ? 0u : in.src[1];

@@ -86,7 +86,9 @@ enum DClass : uint32_t {
   DC_I64,      // 64-bit integer ops and mul.wide; a0 = DI_*
   DC_MOVSP,    // mov from a special register; a0 = KSP_*
   DC_LDP,      // ld.param; a0 = byte offset in the parameter block, a1 = 1: 64-bit
-  DC_MEMG,     // ld/st.global; XF_LOAD, XF_W64, XF_A64; (a0, a1) = byte offset (signed 64-bit)
+  DC_LDG,      // ld.global 32-bit through a 64-bit address register; (a0, a1) = byte offset
+  DC_STG,      // st.global 32-bit through a 64-bit address register; (a0, a1) = byte offset
+  DC_MEMG,     // other ld/st.global; XF_LOAD, XF_W64, XF_A64; (a0, a1) = byte offset (signed 64-bit)
   DC_MEMS,     // ld/st.shared; as DC_MEMG
   DC_BRA,      // bra; a0 = target, a1 = reconvergence index (0xFFFFFFFF = exit)
   DC_BAR,      // bar.sync 0
@@ -98,18 +100,20 @@ constexpr uint32_t CB(uint32_t c) { return 1u << c; }  // class bit in DInst::ct
 // classes that write a register (or predicate) and continue at pc + 1
 constexpr uint32_t CB_REG = CB(DC_FMA) | CB(DC_IADD) | CB(DC_IMAD) | CB(DC_MOV) | CB(DC_SETP) | CB(DC_SELP) |
                             CB(DC_I64) | CB(DC_MOVSP) | CB(DC_LDP);
-constexpr uint32_t CB_MEM = CB(DC_MEMG) | CB(DC_MEMS);
+constexpr uint32_t CB_MEM = CB(DC_MEMG) | CB(DC_MEMS);  // the general memory classes
 
 enum : uint32_t { DS_S32, DS_U32, DS_F32, DS_S64, DS_U64 };                 // DC_SETP operand types
 enum : uint32_t { DI_ADD, DI_SUB, DI_MUL, DI_MAD, DI_WIDE_S, DI_WIDE_U };  // DC_I64 operations
 
 // DInst::ctl flags (above the class bits)
+constexpr uint32_t XF_SHIFT = 20;
+static_assert(DC_COUNT <= XF_SHIFT, "class bits overlap the flags");
 enum : uint32_t {
-  XF_IMM = 1u << 16,   // some source is an immediate: imm[] goes into the immediate slots first
-  XF_FIX = 1u << 17,   // the end sentinel, or a divergent branch reconverges here
-  XF_LOAD = 1u << 18,  // memory: load (else store)
-  XF_W64 = 1u << 19,   // memory: 8-byte access
-  XF_A64 = 1u << 20,   // memory: 64-bit address register
+  XF_IMM = 1u << XF_SHIFT,        // some source is an immediate: imm[] goes into the immediate slots first
+  XF_FIX = 1u << (XF_SHIFT + 1),  // the end sentinel, or a divergent branch reconverges here
+  XF_LOAD = 1u << (XF_SHIFT + 2), // memory: load (else store)
+  XF_W64 = 1u << (XF_SHIFT + 3),  // memory: 8-byte access
+  XF_A64 = 1u << (XF_SHIFT + 4),  // memory: 64-bit address register
 };
 
 struct DInst {         // 128 bytes; dwords 0-15 are read for every instruction

@@ -348,6 +348,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 
   const uint32_t my_w = 2u * wave + hl;
   const uint32_t small_gmem = a.gmem_bytes <= (1ull << 37) ? 1u : 0u;  // sector ids of valid accesses fit 32 bits
+  const uint64_t glim4 = a.gmem_bytes >= 4 ? a.gmem_bytes - 3u : 0u;   // a 4-byte access at A is inside iff A < glim4
   uint8_t* const my_sb = reinterpret_cast<uint8_t*>(sbw + my_w * KS_SB_ENTRIES);  // this lane's warp's scoreboard
   auto sb_at = [&](uint32_t off) -> uint32_t& { return *reinterpret_cast<uint32_t*>(my_sb + off); };
 
@@ -421,6 +422,60 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     }                                                                          \
     KS_ACT_FLUSH();                                                            \
     m64 = mask64 & ~ex64;                                                      \
+  }
+
+  // Faulting lanes (invalid address or alignment): status FAULT and the fault counter.
+#define KS_COUNT_FAULTS(faults)                                                      \
+  if (faults) {                                                                     \
+    const uint32_t f0 = popc((uint32_t)(faults)), f1 = popc((uint32_t)((faults) >> 32)); \
+    if (f0) status |= KS_ST_FAULT;                                                   \
+    if (f1) status |= KS_ST_FAULT << 8;                                              \
+    cnt += sl == C_FAULT ? (hl ? f1 : f0) : 0u;                                      \
+  }
+
+  // Distinct 32-byte sectors and 128-byte lines of a global warp access of S bytes
+  // per lane at A over the guard lanes on64, per warp; then the n / sectors /
+  // lines counters of the load or store.  Full exec.
+#define KS_GLOBAL_ACCOUNT(A, S, faults, is_load)                                     \
+  {                                                                                 \
+    uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;                                 \
+    bool slow0 = g0 != 0, slow1 = g1 != 0;                                           \
+    if (!(faults) && small_gmem) {                                                   \
+      /* monotone fast path: prefix max of sector ids over the guard lanes of each half */ \
+      const uint32_t sid = lanes(on64) ? (uint32_t)((A) >> 5) : 0u;                   \
+      const uint32_t prev = prev_in_half(half_prefix_max(sid), lane);                \
+      const uint64_t nonmono = ballot(sid < prev) & on64;                            \
+      const uint64_t news = ballot(sid != prev) & on64;                              \
+      const uint64_t newl = ballot((sid >> 2) != (prev >> 2)) & on64;                \
+      if (g0 && !(uint32_t)nonmono) {                                                \
+        const uint32_t first = g0 & (0u - g0);                                       \
+        sec0 = popc((uint32_t)news | first);                                         \
+        lin0 = popc((uint32_t)newl | first);                                         \
+        slow0 = false;                                                               \
+      }                                                                             \
+      if (g1 && !(uint32_t)(nonmono >> 32)) {                                        \
+        const uint32_t first = g1 & (0u - g1);                                       \
+        sec1 = popc((uint32_t)(news >> 32) | first);                                 \
+        lin1 = popc((uint32_t)(newl >> 32) | first);                                 \
+        slow1 = false;                                                               \
+      }                                                                             \
+    }                                                                               \
+    if (slow0 || slow1) {                                                            \
+      const uint64_t last = (A) + ((S) - 1u);                                        \
+      if (slow0) {                                                                  \
+        sec0 = distinct2((A) >> 5, last >> 5, (uint64_t)g0);                        \
+        lin0 = distinct2((A) >> 7, last >> 7, (uint64_t)g0);                        \
+      }                                                                             \
+      if (slow1) {                                                                  \
+        sec1 = distinct2((A) >> 5, last >> 5, (uint64_t)g1 << 32);                  \
+        lin1 = distinct2((A) >> 7, last >> 7, (uint64_t)g1 << 32);                  \
+      }                                                                             \
+    }                                                                               \
+    /* counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2} */ \
+    const uint32_t cn = (is_load) ? C_GLD_N : C_GST_N;                                \
+    const uint32_t d = sl - cn;                                                      \
+    const uint32_t gh = hl ? g1 : g0;                                                \
+    if (gh && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0)); \
   }
 
   uint32_t epoch = 0;
@@ -614,6 +669,25 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           }
           spc0 = go0 ? pc + 1u : spc0;
           spc1 = go1 ? pc + 1u : spc1;
+        } else if (ctl & (CB(DC_LDG) | CB(DC_STG))) {
+          // 32-bit global load or store through a 64-bit address register
+          uint32_t blo, bhi;
+          R.get2(s0, s0 + 1u, blo, bhi);
+          const uint64_t A = (((uint64_t)bhi << 32) | blo) + (((uint64_t)a1 << 32) | a0);
+          const uint64_t okm = ballot(((uint32_t)A & 3u) == 0u && A < glim4) & on64;
+          const uint32_t is_load = ctl & CB(DC_LDG);
+          if (is_load) {
+            uint32_t v = 0;
+            if (lanes(okm)) v = *reinterpret_cast<const uint32_t*>(a.gmem + A);
+            if (lanes(on64)) R.put(dst, v);
+          } else if (lanes(okm)) {
+            *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
+          }
+          const uint64_t faults = on64 & ~okm;
+          KS_COUNT_FAULTS(faults);
+          KS_GLOBAL_ACCOUNT(A, 4u, faults, is_load);
+          spc0 = go0 ? pc + 1u : spc0;
+          spc1 = go1 ? pc + 1u : spc1;
         } else if (ctl & CB_MEM) {
           const uint32_t is_global = ctl & CB(DC_MEMG);
           const uint32_t is_load = ctl & XF_LOAD;
@@ -630,8 +704,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             base = R.get(s0);
           }
           const uint64_t A = base + off;
-          const bool ok = (A & (S - 1u)) == 0 && A <= size && size - A >= S;
-          const uint64_t okm = ballot(ok) & on64;
+          const uint64_t okm = ballot((A & (S - 1u)) == 0 && A <= size && size - A >= S) & on64;
           if (is_load) {
             uint32_t lo = 0, hi = 0;
             if (lanes(okm)) {
@@ -668,55 +741,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               else *reinterpret_cast<uint32_t*>(win + A) = lo;
             }
           }
-          // fault counting and analysis (full exec)
           const uint64_t faults = on64 & ~okm;
-          if (faults) {
-            const uint32_t f0 = popc((uint32_t)faults), f1 = popc((uint32_t)(faults >> 32));
-            if (f0) status |= KS_ST_FAULT;
-            if (f1) status |= KS_ST_FAULT << 8;
-            cnt += sl == C_FAULT ? (hl ? f1 : f0) : 0u;
-          }
-          const bool on = lanes(on64);
-          const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
+          KS_COUNT_FAULTS(faults);
           if (is_global) {
-            uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;
-            bool slow0 = g0 != 0, slow1 = g1 != 0;
-            if (!faults && small_gmem) {
-              // monotone fast path: prefix max of sector ids over the active lanes of each half
-              const uint32_t s = on ? (uint32_t)(A >> 5) : 0u;
-              const uint32_t prev = prev_in_half(half_prefix_max(s), lane);
-              const uint64_t nonmono = ballot(on && s < prev);
-              const uint64_t news = ballot(on && s != prev);
-              const uint64_t newl = ballot(on && (s >> 2) != (prev >> 2));
-              if (g0 && !(uint32_t)nonmono) {
-                const uint32_t first = g0 & (0u - g0);
-                sec0 = popc((uint32_t)news | first);
-                lin0 = popc((uint32_t)newl | first);
-                slow0 = false;
-              }
-              if (g1 && !(uint32_t)(nonmono >> 32)) {
-                const uint32_t first = g1 & (0u - g1);
-                sec1 = popc((uint32_t)(news >> 32) | first);
-                lin1 = popc((uint32_t)(newl >> 32) | first);
-                slow1 = false;
-              }
-            }
-            if (slow0 || slow1) {
-              const uint64_t last = A + (S - 1u);
-              if (slow0) {
-                sec0 = distinct2(A >> 5, last >> 5, (uint64_t)g0);
-                lin0 = distinct2(A >> 7, last >> 7, (uint64_t)g0);
-              }
-              if (slow1) {
-                sec1 = distinct2(A >> 5, last >> 5, (uint64_t)g1 << 32);
-                lin1 = distinct2(A >> 7, last >> 7, (uint64_t)g1 << 32);
-              }
-            }
-            // counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2}
-            const uint32_t cn = is_load ? C_GLD_N : C_GST_N;
-            const uint32_t d = sl - cn;
-            if (((hm >> hl) & 1u) && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0));
+            KS_GLOBAL_ACCOUNT(A, S, faults, is_load);
           } else {
+            const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
             uint32_t d0 = 1, d1 = 1;
             bool slow0 = g0 != 0, slow1 = g1 != 0;
             if (!faults) {
@@ -861,6 +891,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     ++epoch;
   }
 #undef KS_SETTLE
+#undef KS_COUNT_FAULTS
+#undef KS_GLOBAL_ACCOUNT
   KS_ACT_FLUSH();
 #undef KS_ACT_FLUSH
 

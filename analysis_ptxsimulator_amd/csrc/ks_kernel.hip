@@ -376,10 +376,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   uint32_t v_next = 0;        // warp: previous issue cycle + 1
   uint32_t wi = 0;            // warp: issued warp-instructions
   uint32_t fl = 0;            // warp: trace records written to memory
-  uint32_t nf = cap == 0 ? INF : umin(cap, 32u);  // warp: record count at which the next chunk is written
-  uint32_t ev = umin(nf, budget);                 // warp: next event (chunk write or budget)
-  uint32_t act = 0;           // instructions issued with this lane's thread active, up to the last mask change
-  uint32_t mk = 0;            // warp: issued warp-instructions at the last change of the live masks
+  // warp: record count at which the next chunk is written (from the records written so far)
+  auto next_flush = [&](uint32_t written) -> uint32_t { return written < cap ? umin(cap, written + 32u) : INF; };
+  uint32_t ev = umin(next_flush(0), budget);      // warp: next event (chunk write or budget)
+  uint32_t act = 0;           // instructions issued with this lane's thread active (see KS_SET_LIVE)
   uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
   uint32_t pbits = 0;         // predicate p of this lane's thread in bit p
   uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
@@ -388,11 +388,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 
   // Every instruction a warp issues between two changes of its live mask runs with
   // the same mask, so thread-instructions are counted per lane only when the live
-  // masks change: each live lane adds the instructions issued since the last change.
-#define KS_ACT_FLUSH()                            \
+  // masks change: a lane that becomes live subtracts its warp's issue count, one
+  // that stops being live adds it (and so does every live lane at the end).
+#define KS_SET_LIVE(newm)                         \
   {                                               \
-    act += lanes(m64) ? wi - mk : 0u;             \
-    mk = wi;                                      \
+    const uint64_t nm_ = (newm);                  \
+    act += lanes(m64 & ~nm_) ? wi : 0u;           \
+    act -= lanes(nm_ & ~m64) ? wi : 0u;           \
+    m64 = nm_;                                    \
   }
 
   // Pop entries of warp h that cannot issue (no live lane, reconverged); lanes past
@@ -420,8 +423,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       spc = S.pc;                                                              \
       break;                                                                   \
     }                                                                          \
-    KS_ACT_FLUSH();                                                            \
-    m64 = mask64 & ~ex64;                                                      \
+    KS_SET_LIVE(mask64 & ~ex64);                                               \
   }
 
   // Faulting lanes (invalid address or alignment): status FAULT and the fault counter.
@@ -517,13 +519,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         // events: trace chunk complete, issue budget reached (checked first), cycle limit passed
         const uint64_t bm = ballot(wi == budget) & gm;
         const uint64_t om = ballot(iss > CYCLE_LIMIT) & gm & ~bm;
-        const uint64_t fm = ballot(wi == nf) & gm & ~om;  // a full chunk (or the cap) to write
+        const uint64_t fm = ballot(wi == next_flush(fl)) & gm & ~om;  // a full chunk (or the cap) to write
         if (lanes(fm)) {
           if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
           fl = wi;
-          nf = wi < cap ? umin(cap, wi + 32u) : INF;
         }
-        if (lanes(gm)) ev = umin(nf, budget);
+        if (lanes(gm)) ev = umin(next_flush(fl), budget);
         const uint64_t stop = bm | om;
         if (stop & LO) {
           spc0 = INF;
@@ -822,14 +823,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             }
           }
           if (divm) {
-            KS_ACT_FLUSH();
-            m64 = mask64 & ~ex64;
+            KS_SET_LIVE(mask64 & ~ex64);
             cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
           }
         } else if (ctl & CB(DC_RET)) {
           ex64 |= on64;
-          KS_ACT_FLUSH();
-          m64 = mask64 & ~ex64;
+          KS_SET_LIVE(mask64 & ~ex64);
           if (go0) {
             spc0 = pc + 1u;
             S0.pc = pc + 1u;
@@ -893,8 +892,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 #undef KS_SETTLE
 #undef KS_COUNT_FAULTS
 #undef KS_GLOBAL_ACCOUNT
-  KS_ACT_FLUSH();
-#undef KS_ACT_FLUSH
+  act += lanes(m64) ? wi : 0u;
+#undef KS_SET_LIVE
 
   // -------------------------------------------------------------------- counters, trace tail, headers
   {

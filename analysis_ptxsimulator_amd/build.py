@@ -1,8 +1,7 @@
 """Build libkscope.so (host front end + gfx950 interpreter) in-tree with hipcc.
 
 Flags that matter for results:
-  -ffp-contract=off        single-precision add/mul stay separately rounded
-                           (fma.rn.f32 is an explicit fused multiply-add)
+  -ffp-contract=off        no multiply-add contraction beyond the explicit fmaf
   no fast-math, no flush   subnormals are kept
   -packed-fp32-ops off     no v_pk_* f32 instructions are generated
 """
@@ -18,9 +17,13 @@ LIB = os.path.join(HERE, "libkscope.so")
 SOURCES = [os.path.join(CSRC, "ks_host.cpp"), os.path.join(CSRC, "ks_kernel.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# Uniform branches (all of the interpreter's dispatch) need no structurizing: the
+# hardware takes them as scalar branches.  Leaving those regions alone removes the
+# flow-mask bookkeeping the structurizer would add to every step.
+CODEGEN = ["-mllvm", "-structurizecfg-skip-uniform-regions=true"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
          "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
+         "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm"] + CODEGEN
 
 
 # The VGPR register-file kernels keep simulated registers in v56 and up, which
@@ -100,7 +103,7 @@ def build(force: bool = True, verbose: bool = False, check: bool = True) -> str:
 def device_asm(out_path: str) -> str:
     """Write the gfx950 assembly of the interpreter (for inspection)."""
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-inline-asm", "-o", out_path,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-inline-asm"] + CODEGEN + ["-o", out_path,
            os.path.join(CSRC, "ks_kernel.hip")]
     subprocess.run(cmd, check=True, cwd=HERE)
     return out_path

@@ -1087,6 +1087,15 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
     const KsInst& in = P->code[i].in;
     if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].ctl |= XF_FIX;
   }
+  // straight runs, from the end: a control instruction ends its run; a run stops
+  // before a reconvergence point or the end sentinel
+  uint32_t next = 0;  // run length of instruction i + 1
+  for (uint32_t i = n; i-- > 0;) {
+    uint32_t run = 1;
+    if (!(out[i].ctl & CB_CTRL) && !(out[i + 1].ctl & XF_FIX)) run = next + 1 > RUN_MAX ? RUN_MAX : next + 1;
+    out[i].ctl |= run << RUN_SHIFT;
+    next = run;
+  }
   return out;
 }
 
@@ -1318,6 +1327,13 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
     a.threads_per_block = (uint32_t)tpb;
     a.warps_per_block = (uint32_t)((tpb + 31) / 32);
     a.lat_bar = st->cfg.latency[KS_LAT_BAR];
+    {
+      // each issue of a run is at most (the largest latency + 1) after the previous one
+      uint64_t step = 1;
+      for (int k = 0; k < KS_NLAT; ++k) step = std::max<uint64_t>(step, (uint64_t)st->cfg.latency[k] + 1);
+      const uint64_t limit = 0x7FFFFFFFull, span = (uint64_t)RUN_MAX * step;
+      a.cyc_safe = span < limit ? (uint32_t)(limit - span) : 0u;
+    }
     a.rf_slots = p->reg_slots + KS_IMM_SLOTS;
     if (p->param_bytes) memcpy(a.params, params, p->param_bytes);
     uint64_t warps = nb * a.warps_per_block;

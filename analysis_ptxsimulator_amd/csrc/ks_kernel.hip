@@ -668,8 +668,68 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               else R.put(dst, lo);
             }
           }
-          spc0 = go0 ? pc + 1u : spc0;
-          spc1 = go1 ? pc + 1u : spc1;
+          // Continue the straight run with simple ALU instructions, without rescheduling:
+          // the same warps issue them, no reconvergence point or control instruction
+          // intervenes, none of them may reach an event (chunk write, budget) and none may
+          // pass the cycle limit.
+          uint32_t p = pc + 1u;
+          {
+            uint32_t n = (ctl >> RUN_SHIFT) - 1u;  // instructions after this one in its run
+            const uint32_t room = ev - wi;          // per warp: issues before its next event
+            if (go0) n = umin(n, rl(room, 0));
+            if (go1) n = umin(n, rl(room, 32));
+            if (umax(rl(v_next, 0), rl(v_next, 32)) > a.cyc_safe) n = 0;
+            while (n) {
+              const cdinst J = prog + p;
+              const u32x16 h = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(J);
+              const uint32_t c = h[0];
+              if (!(c & CB_SIMPLE)) break;
+              const uint32_t is2 = umax(umax(v_next, sb_at(h[6])), umax(umax(sb_at(h[7]), sb_at(h[8])), sb_at(h[9])));
+              const uint64_t on2 = mm & ballot(((pbits >> h[12]) & 1u) != h[13]);
+              if (lanes(gm)) {
+                if (sl == (wi & 31u)) {
+                  tr_c = is2;
+                  tr_p = p;
+                }
+                wi += 1;
+                v_next = is2 + 1;
+                sb_at(h[10]) = is2 + h[11];
+              }
+              if (c & XF_IMM) {
+                uint32_t iv[6];
+                for (int k = 0; k < 6; ++k) iv[k] = J->imm[k];
+                R.put_imm(ib, iv);
+              }
+              if (lanes(on2)) {
+                const uint32_t t0 = h[2], t1 = h[3], t2 = h[4], d2 = h[5], b0 = h[14], b1 = h[15];
+                if (c & CB(DC_FMA)) {
+                  uint32_t x0, x1, x2;
+                  R.get3(t0, t1, t2, x0, x1, x2);
+                  const uint32_t b = (b0 & 0x3F800000u) | (~b0 & x1);
+                  const uint32_t cc = (x2 & b1) ^ h[1];
+                  R.put(d2, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(cc))));
+                } else if (c & CB(DC_IADD)) {
+                  uint32_t x0, x1;
+                  R.get2(t0, t1, x0, x1);
+                  R.put(d2, x0 + (x1 ^ b0) + b1);
+                } else if (c & CB(DC_IMAD)) {
+                  uint32_t x0, x1, x2;
+                  R.get3(t0, t1, t2, x0, x1, x2);
+                  R.put(d2, x0 * x1 + (x2 & b0));
+                } else if (b0) {  // DC_MOV, 64-bit
+                  uint32_t lo, hi;
+                  R.get2(t0, t0 + 1u, lo, hi);
+                  R.put2(d2, lo, hi);
+                } else {          // DC_MOV, 32-bit
+                  R.put(d2, R.get(t0));
+                }
+              }
+              ++p;
+              --n;
+            }
+          }
+          spc0 = go0 ? p : spc0;
+          spc1 = go1 ? p : spc1;
         } else if (ctl & (CB(DC_LDG) | CB(DC_STG))) {
           // 32-bit global load or store through a 64-bit address register
           uint32_t blo, bhi;

@@ -735,18 +735,19 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           uint32_t blo, bhi;
           R.get2(s0, s0 + 1u, blo, bhi);
           const uint64_t A = (((uint64_t)bhi << 32) | blo) + (((uint64_t)a1 << 32) | a0);
-          const uint64_t okm = ballot(((uint32_t)A & 3u) == 0u && A < glim4) & on64;
+          const uint64_t okm = ballot(((uint32_t)A & 3u) == 0u) & ballot(A < glim4) & on64;
           const uint32_t is_load = ctl & CB(DC_LDG);
+          uint32_t v = 0;
           if (is_load) {
-            uint32_t v = 0;
             if (lanes(okm)) v = *reinterpret_cast<const uint32_t*>(a.gmem + A);
-            if (lanes(on64)) R.put(dst, v);
           } else if (lanes(okm)) {
             *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
           }
+          // the accounting does not depend on the loaded value: it runs while the load is in flight
           const uint64_t faults = on64 & ~okm;
           KS_COUNT_FAULTS(faults);
           KS_GLOBAL_ACCOUNT(A, 4u, faults, is_load);
+          if (is_load && lanes(on64)) R.put(dst, v);
           spc0 = go0 ? pc + 1u : spc0;
           spc1 = go1 ? pc + 1u : spc1;
         } else if (ctl & CB_MEM) {

@@ -116,7 +116,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="random_stress")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=32768)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=65536)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "

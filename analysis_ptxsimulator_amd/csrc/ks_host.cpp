@@ -1087,14 +1087,14 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
     const KsInst& in = P->code[i].in;
     if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].ctl |= XF_FIX;
   }
-  // straight runs, from the end: a control instruction ends its run; a run stops
-  // before a reconvergence point or the end sentinel
-  uint32_t next = 0;  // run length of instruction i + 1
+  // straight runs, from the end: the run of a non-control instruction is itself and
+  // the instructions after it that may follow it without rescheduling (neither a
+  // control instruction, nor a reconvergence point, nor the end sentinel)
+  uint32_t next = 0;  // run length of instruction i + 1, 0 if it cannot continue a run
   for (uint32_t i = n; i-- > 0;) {
-    uint32_t run = 1;
-    if (!(out[i].ctl & CB_CTRL) && !(out[i + 1].ctl & XF_FIX)) run = next + 1 > RUN_MAX ? RUN_MAX : next + 1;
+    const uint32_t run = (out[i].ctl & CB_CTRL) ? 1u : (next + 1u > RUN_MAX ? RUN_MAX : next + 1u);
     out[i].ctl |= run << RUN_SHIFT;
-    next = run;
+    next = (out[i].ctl & (CB_CTRL | XF_FIX)) ? 0u : run;
   }
   return out;
 }

@@ -102,7 +102,6 @@ constexpr uint32_t CB_REG = CB(DC_FMA) | CB(DC_IADD) | CB(DC_IMAD) | CB(DC_MOV) 
                             CB(DC_I64) | CB(DC_MOVSP) | CB(DC_LDP);
 constexpr uint32_t CB_MEM = CB(DC_MEMG) | CB(DC_MEMS);  // the general memory classes
 constexpr uint32_t CB_CTRL = CB(DC_BRA) | CB(DC_BAR) | CB(DC_RET);  // classes that set the next pc
-constexpr uint32_t CB_SIMPLE = CB(DC_FMA) | CB(DC_IADD) | CB(DC_IMAD) | CB(DC_MOV);  // continue a straight run
 
 enum : uint32_t { DS_S32, DS_U32, DS_F32, DS_S64, DS_U64 };                 // DC_SETP operand types
 enum : uint32_t { DI_ADD, DI_SUB, DI_MUL, DI_MAD, DI_WIDE_S, DI_WIDE_U };  // DC_I64 operations
@@ -119,8 +118,9 @@ enum : uint32_t {
 };
 // DInst::ctl bits 25-31: length of the straight run that starts here (1..127):
 // the instructions from here on that the interpreter may issue back to back
-// without rescheduling.  Only the first may be a reconvergence point and only the
-// last may set the next pc (a control class).
+// without rescheduling.  None is a control class (a control instruction has run
+// length 1 and is issued on its own), and only the first may be a reconvergence
+// point.
 constexpr uint32_t RUN_SHIFT = 25, RUN_MAX = 127;
 
 struct DInst {         // 128 bytes; dwords 0-15 are read for every instruction
@@ -158,8 +158,8 @@ struct KsArgs {
   uint32_t warps_per_block;
   uint32_t lat_bar;
   uint32_t rf_slots;       // register slots per simulated thread, immediate slots included
-  uint32_t cyc_safe;       // a run may start when every warp's next issue cycle is at most this:
-                           // RUN_MAX instructions cannot then pass the cycle limit
+  uint32_t cyc_safe;       // a run may continue past its first instruction when that one issues
+                           // at most at this cycle: RUN_MAX issues cannot then pass the cycle limit
   uint8_t params[KS_PARAM_MAX];
 };
 

@@ -145,6 +145,19 @@ struct RegFile;
                  "v_mov_b32 " KS_RF_V1 ", %2\n\ts_set_gpr_idx_off"                                 \
                  : : "s"(s), "v"(lo), "v"(hi) : "m0");                                            \
   }                                                                                                \
+  /* slot s of the lanes in m takes v, the other lanes keep their value: SRC0 and DST */          \
+  /* are both indexed, so v_cndmask reads the old value and writes the slot under full exec */    \
+  __device__ __forceinline__ void put_m(uint32_t s, uint32_t v, uint64_t m) const {                \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(SRC0,DST)\n\tv_cndmask_b32_e64 " KS_RF_V0 ", "      \
+                 KS_RF_V0 ", %1, %2\n\ts_set_gpr_idx_off"                                          \
+                 : : "s"(s), "v"(v), "s"(m) : "m0");                                              \
+  }                                                                                                \
+  __device__ __forceinline__ void put2_m(uint32_t s, uint32_t lo, uint32_t hi, uint64_t m) const { \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(SRC0,DST)\n\tv_cndmask_b32_e64 " KS_RF_V0 ", "      \
+                 KS_RF_V0 ", %1, %3\n\tv_cndmask_b32_e64 " KS_RF_V1 ", " KS_RF_V1 ", %2, %3\n\t"    \
+                 "s_set_gpr_idx_off"                                                               \
+                 : : "s"(s), "v"(lo), "v"(hi), "s"(m) : "m0");                                    \
+  }                                                                                                \
   __device__ __forceinline__ void put_imm(uint32_t ib, const uint32_t* v) const {                  \
     asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\t"                                           \
                  "v_mov_b32 " KS_RF_V0 ", %1\n\tv_mov_b32 " KS_RF_V1 ", %2\n\t"                     \
@@ -222,6 +235,15 @@ __device__ __forceinline__ uint32_t half_prefix_max(uint32_t x) {
   x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true));  // row_shr:4
   x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true));  // row_shr:8
   x = umax(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false)); // row_bcast:15 -> rows 1, 3
+  return x;
+}
+// Inclusive prefix sum within each 32-lane half (lanes 31 and 63 hold the totals).
+__device__ __forceinline__ uint32_t half_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15 -> rows 1, 3
   return x;
 }
 // Value of the previous lane in the same half (0 for the first lane of each half).
@@ -329,15 +351,17 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t T = a.threads_per_block;
   const uint32_t n_instr = a.n_instrs;
   const cdinst prog = (cdinst)(uintptr_t)a.prog;
+  const __attribute__((address_space(4))) uint8_t* const prog_b = (const __attribute__((address_space(4))) uint8_t*)prog;
   const uint32_t ib = a.rf_slots - KS_IMM_SLOTS;  // first immediate slot
 
-  // LDS: [scoreboard, 129 words per warp] [shared window]
+  // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] [shared window]
   RegFile<RFN> R;
   RegFile<RFN>::zero();
   uint32_t* const sbw = lds;
-  uint8_t* const win = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
+  uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
+  uint8_t* const win = dump_sb + 4u * KS_SB_ENTRIES;
   {
-    const uint32_t words = (WG / 32u) * KS_SB_ENTRIES + ((a.shared_bytes + 3u) >> 2);
+    const uint32_t words = (WG / 32u + 1u) * KS_SB_ENTRIES + ((a.shared_bytes + 3u) >> 2);
     for (uint32_t i = tid; i < words; i += WG) lds[i] = 0;
     if (tid < 3) {
       ep_max[tid] = 0;
@@ -347,7 +371,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   __syncthreads();
 
   const uint32_t my_w = 2u * wave + hl;
-  const uint32_t small_gmem = a.gmem_bytes <= (1ull << 37) ? 1u : 0u;  // sector ids of valid accesses fit 32 bits
+  // sector ids + 1 of valid accesses fit 32 bits (and stay non-zero)
+  const uint32_t small_gmem = a.gmem_bytes <= (1ull << 37) - 64u ? 1u : 0u;
   const uint64_t glim4 = a.gmem_bytes >= 4 ? a.gmem_bytes - 3u : 0u;   // a 4-byte access at A is inside iff A < glim4
   uint8_t* const my_sb = reinterpret_cast<uint8_t*>(sbw + my_w * KS_SB_ENTRIES);  // this lane's warp's scoreboard
   auto sb_at = [&](uint32_t off) -> uint32_t& { return *reinterpret_cast<uint32_t*>(my_sb + off); };
@@ -383,6 +408,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
   uint32_t pbits = 0;         // predicate p of this lane's thread in bit p
   uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
+  // global loads / stores: per-lane shares of the access, sector and line counters of
+  // the fast analyser path (summed over each warp's lanes at the end)
+  uint32_t q_ln = 0, q_ls = 0, q_ll = 0, q_sn = 0, q_ss = 0, q_sl = 0;
   const uint64_t gw0 = (uint64_t)blk * W + 2u * wave;  // global warp id of half 0
   uint8_t* const slot_base = a.trace + (gw0 + hl) * a.slot_bytes + 16u;  // this lane's warp's records
 
@@ -436,49 +464,82 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   }
 
   // Distinct 32-byte sectors and 128-byte lines of a global warp access of S bytes
-  // per lane at A over the guard lanes on64, per warp; then the n / sectors /
-  // lines counters of the load or store.  Full exec.
+  // per lane at A over the guard lanes on64, added to the access / sector / line
+  // counters of the load or store.  Where a warp's sector ids do not decrease over
+  // its guard lanes in lane order, a lane opens a new sector exactly when its id
+  // exceeds the largest id of the guard lanes before it (and a new line likewise),
+  // so each lane adds its own 0/1 flags to per-lane counters that are summed per
+  // warp at the end; other warps (and any access with a faulting lane) count the
+  // distinct values exactly.  Full exec.
 #define KS_GLOBAL_ACCOUNT(A, S, faults, is_load)                                     \
   {                                                                                 \
-    uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;                                 \
-    bool slow0 = g0 != 0, slow1 = g1 != 0;                                           \
-    if (!(faults) && small_gmem) {                                                   \
-      /* monotone fast path: prefix max of sector ids over the guard lanes of each half */ \
-      const uint32_t sid = lanes(on64) ? (uint32_t)((A) >> 5) : 0u;                   \
-      const uint32_t prev = prev_in_half(half_prefix_max(sid), lane);                \
-      const uint64_t nonmono = ballot(sid < prev) & on64;                            \
-      const uint64_t news = ballot(sid != prev) & on64;                              \
-      const uint64_t newl = ballot((sid >> 2) != (prev >> 2)) & on64;                \
-      if (g0 && !(uint32_t)nonmono) {                                                \
-        const uint32_t first = g0 & (0u - g0);                                       \
-        sec0 = popc((uint32_t)news | first);                                         \
-        lin0 = popc((uint32_t)newl | first);                                         \
-        slow0 = false;                                                               \
+    uint64_t exact = on64;                                                          \
+    if (!(faults) && small_gmem) {                                                  \
+      const bool on_ = lanes(on64);                                                 \
+      /* sector id + 1 on guard lanes, 0 elsewhere; prev: the largest over the earlier lanes of the half */ \
+      const uint32_t sid1 = on_ ? (uint32_t)((A) >> 5) + 1u : 0u;                   \
+      const uint32_t prev = prev_in_half(half_prefix_max(sid1), lane);              \
+      uint64_t fast = on64;                                                         \
+      const uint64_t nonmono = ballot(sid1 < prev) & on64;                          \
+      if (nonmono) {                                                                \
+        if ((uint32_t)nonmono) fast &= HI;                                          \
+        if (nonmono >> 32) fast &= LO;                                              \
       }                                                                             \
-      if (g1 && !(uint32_t)(nonmono >> 32)) {                                        \
-        const uint32_t first = g1 & (0u - g1);                                       \
-        sec1 = popc((uint32_t)(news >> 32) | first);                                 \
-        lin1 = popc((uint32_t)(newl >> 32) | first);                                 \
-        slow1 = false;                                                               \
-      }                                                                             \
-    }                                                                               \
-    if (slow0 || slow1) {                                                            \
-      const uint64_t last = (A) + ((S) - 1u);                                        \
-      if (slow0) {                                                                  \
-        sec0 = distinct2((A) >> 5, last >> 5, (uint64_t)g0);                        \
-        lin0 = distinct2((A) >> 7, last >> 7, (uint64_t)g0);                        \
-      }                                                                             \
-      if (slow1) {                                                                  \
-        sec1 = distinct2((A) >> 5, last >> 5, (uint64_t)g1 << 32);                  \
-        lin1 = distinct2((A) >> 7, last >> 7, (uint64_t)g1 << 32);                  \
+      exact = on64 & ~fast;                                                         \
+      const bool f_ = lanes(fast);                                                  \
+      const uint32_t fn_ = (f_ && prev == 0u) ? 1u : 0u;                            \
+      const uint32_t fs_ = (f_ && sid1 != prev) ? 1u : 0u;                          \
+      const uint32_t fl_ = (f_ && (prev == 0u || ((sid1 - 1u) >> 2) != ((prev - 1u) >> 2))) ? 1u : 0u; \
+      if (is_load) {                                                                \
+        q_ln += fn_;                                                                \
+        q_ls += fs_;                                                                \
+        q_ll += fl_;                                                                \
+      } else {                                                                      \
+        q_sn += fn_;                                                                \
+        q_ss += fs_;                                                                \
+        q_sl += fl_;                                                                \
       }                                                                             \
     }                                                                               \
-    /* counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2} */ \
-    const uint32_t cn = (is_load) ? C_GLD_N : C_GST_N;                                \
-    const uint32_t d = sl - cn;                                                      \
-    const uint32_t gh = hl ? g1 : g0;                                                \
-    if (gh && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0)); \
+    if (exact) {                                                                    \
+      const uint32_t e0 = (uint32_t)exact, e1 = (uint32_t)(exact >> 32);            \
+      const uint64_t last = (A) + ((S) - 1u);                                       \
+      uint32_t sec0 = 0, lin0 = 0, sec1 = 0, lin1 = 0;                              \
+      if (e0) {                                                                     \
+        sec0 = distinct2((A) >> 5, last >> 5, (uint64_t)e0);                        \
+        lin0 = distinct2((A) >> 7, last >> 7, (uint64_t)e0);                        \
+      }                                                                             \
+      if (e1) {                                                                     \
+        sec1 = distinct2((A) >> 5, last >> 5, (uint64_t)e1 << 32);                  \
+        lin1 = distinct2((A) >> 7, last >> 7, (uint64_t)e1 << 32);                  \
+      }                                                                             \
+      /* counters n, sectors, lines of the lane's warp: lanes 32 h + {cn, cn+1, cn+2} */ \
+      const uint32_t cn = (is_load) ? C_GLD_N : C_GST_N;                            \
+      const uint32_t d = sl - cn;                                                   \
+      const uint32_t eh = hl ? e1 : e0;                                             \
+      if (eh && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0)); \
+    }                                                                               \
   }
+
+  // Issue of one instruction by the warps of gm, written as per-lane selects so
+  // that exec stays full: lane wi % 32 of each issuing warp stages the trace record
+  // (issue cycle, pc); the issue count and the next issue cycle advance; the
+  // destination's scoreboard entry gets its ready cycle (the other warp's lanes
+  // write a scratch scoreboard instead).
+#define KS_ISSUE(is_, p_, sbod_, lat_)                                               \
+  {                                                                                 \
+    const bool tr_ = sl == ((wi & 31u) | tnm);                                      \
+    tr_c = tr_ ? (is_) : tr_c;                                                      \
+    tr_p = tr_ ? (p_) : tr_p;                                                       \
+    wi += ginc;                                                                     \
+    v_next = gl ? (is_) + 1u : v_next;                                              \
+    *reinterpret_cast<uint32_t*>(sb_sel + (sbod_)) = (is_) + (lat_);                 \
+  }
+
+  // Issue cycle of the instruction whose hot words are h: the later of the warp's
+  // previous issue + 1 and the ready cycle of every register source (absent
+  // sources read a zero entry).
+#define KS_ISSUE_CYCLE(h)                                                            \
+  umax(umax(v_next, sb_at((h)[6])), umax(umax(sb_at((h)[7]), sb_at((h)[8])), sb_at((h)[9])))
 
   uint32_t epoch = 0;
   while (true) {
@@ -490,16 +551,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       // across blocks becomes a lane mask, and turning it back into a value costs VALU work)
       const uint32_t go0 = s_eq_mask(spc0, pc), go1 = s_eq_mask(spc1, pc);
       const uint64_t gm = ((uint64_t)go1 << 32) | go0;  // lanes of the issuing warps
-      const cdinst I = prog + pc;
-      const u32x16 hot = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(I);
-      const uint32_t ctl = hot[0];  // class bit | flags
-      const uint32_t s0 = hot[2], s1 = hot[3], s2 = hot[4], dst = hot[5];
-      const uint32_t sbod = hot[10], lat = hot[11], gp = hot[12], gmode = hot[13];
-      const uint32_t a0 = hot[14], a1 = hot[15], a2 = hot[1];
-
-      // issue cycle (per warp, uniform over its lanes): the later of the previous issue
-      // + 1 and the ready cycle of every register source (absent sources read a zero word)
-      const uint32_t iss = umax(umax(v_next, sb_at(hot[6])), umax(umax(sb_at(hot[7]), sb_at(hot[8])), sb_at(hot[9])));
+      const u32x16 hot = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(prog + pc);
+      const uint32_t ctl = hot[0];  // class bit | flags | run length
+      const uint32_t iss = KS_ISSUE_CYCLE(hot);
 
       uint32_t need = 0;  // warps whose top stack entry must be settled (bit h)
       if (ctl & XF_FIX) {  // the end sentinel, or a reconvergence point: warps whose top entry ends here pop
@@ -513,6 +567,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         if (need & 2u) S1.pc = pc;
       }
       const uint64_t evm = (ballot(wi == ev) | ballot(iss > CYCLE_LIMIT)) & gm;
+      // per-step selects of the issuing lanes
+      const bool gl = lanes(gm);
+      const uint32_t ginc = gl ? 1u : 0u;   // issue count step
+      const uint32_t tnm = gl ? 0u : 64u;   // trace lane offset (64: no lane matches)
+      uint8_t* const sb_sel = gl ? my_sb : dump_sb;
+      const uint64_t mm = m64 & gm;        // live lanes of the issuing warps
       if (need) {
         // no issue this step
       } else if (evm) {
@@ -524,7 +584,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
           fl = wi;
         }
-        if (lanes(gm)) ev = umin(next_flush(fl), budget);
+        if (gl) ev = umin(next_flush(fl), budget);
         const uint64_t stop = bm | om;
         if (stop & LO) {
           spc0 = INF;
@@ -536,311 +596,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           hst |= DONE1;
           status |= ((bm & HI) ? KS_ST_BUDGET : KS_ST_CYCLE_OVF) << 8;
         }
-      } else {
-        // issue
-        const uint64_t mm = m64 & gm;  // live lanes of the issuing warps
-        const uint64_t on64 = mm & ballot(((pbits >> gp) & 1u) != gmode);  // guard
-        if (lanes(gm)) {
-          if (sl == (wi & 31u)) {
-            tr_c = iss;
-            tr_p = pc;
-          }
-          wi += 1;
-          v_next = iss + 1;
-          sb_at(sbod) = iss + lat;
-        }
+      } else if (ctl & CB_CTRL) {
+        // ---------------------------------------------------------------- control instructions
+        const uint64_t on64 = mm & ballot(((pbits >> hot[12]) & 1u) != hot[13]);  // guard
+        KS_ISSUE(iss, pc, hot[10], hot[11]);
         const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
-
-        // ---------------------------------------------------------------- execute
-        if (ctl & CB_REG) {
-          if (ctl & XF_IMM) {
-            uint32_t iv[6];
-            for (int k = 0; k < 6; ++k) iv[k] = I->imm[k];
-            R.put_imm(ib, iv);
-          }
-          if (lanes(on64)) {
-            if (ctl & CB(DC_FMA)) {
-              uint32_t x0, x1, x2;
-              R.get3(s0, s1, s2, x0, x1, x2);
-              const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
-              const uint32_t c = (x2 & a1) ^ a2;                    // x2, -x2 or -0.0f
-              R.put(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(c))));
-            } else if (ctl & CB(DC_IADD)) {
-              uint32_t x0, x1;
-              R.get2(s0, s1, x0, x1);
-              R.put(dst, x0 + (x1 ^ a0) + a1);
-            } else if (ctl & CB(DC_IMAD)) {
-              uint32_t x0, x1, x2;
-              R.get3(s0, s1, s2, x0, x1, x2);
-              R.put(dst, x0 * x1 + (x2 & a0));
-            } else if (ctl & CB(DC_MOV)) {
-              if (a0) {
-                uint32_t lo, hi;
-                R.get2(s0, s0 + 1u, lo, hi);
-                R.put2(dst, lo, hi);
-              } else {
-                R.put(dst, R.get(s0));
-              }
-            } else if (ctl & CB(DC_SELP)) {
-              const bool p = (pbits >> s2) & 1u;
-              if (a0) {
-                uint32_t xl, xh, yl, yh;
-                R.get2(s0, s0 + 1u, xl, xh);
-                R.get2(s1, s1 + 1u, yl, yh);
-                R.put2(dst, p ? xl : yl, p ? xh : yh);
-              } else {
-                uint32_t x0, x1;
-                R.get2(s0, s1, x0, x1);
-                R.put(dst, p ? x0 : x1);
-              }
-            } else if (ctl & CB(DC_SETP)) {
-              bool lt, eq, gt;
-              if (a0 == DS_F32) {
-                uint32_t x0, x1;
-                R.get2(s0, s1, x0, x1);
-                const float x = __uint_as_float(x0), y = __uint_as_float(x1);
-                lt = x < y;
-                eq = x == y;
-                gt = x > y;  // all false when an input is NaN
-              } else if (a0 <= DS_U32) {
-                uint32_t x0, x1;
-                R.get2(s0, s1, x0, x1);
-                lt = a0 == DS_S32 ? (int32_t)x0 < (int32_t)x1 : x0 < x1;
-                eq = x0 == x1;
-                gt = !lt && !eq;
-              } else {
-                uint32_t xl, xh, yl, yh;
-                R.get2(s0, s0 + 1u, xl, xh);
-                R.get2(s1, s1 + 1u, yl, yh);
-                const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
-                lt = a0 == DS_S64 ? (int64_t)x < (int64_t)y : x < y;
-                eq = x == y;
-                gt = !lt && !eq;
-              }
-              const bool c = (lt && (a1 & 1u)) || (eq && (a1 & 2u)) || (gt && (a1 & 4u));
-              pbits = (pbits & ~(1u << dst)) | ((c ? 1u : 0u) << dst);
-            } else if (ctl & CB(DC_I64)) {
-              uint64_t r;
-              if (a0 >= DI_WIDE_S) {
-                uint32_t x0, x1;
-                R.get2(s0, s1, x0, x1);
-                r = a0 == DI_WIDE_S ? (uint64_t)((int64_t)(int32_t)x0 * (int64_t)(int32_t)x1)
-                                    : (uint64_t)x0 * (uint64_t)x1;
-              } else {
-                uint32_t xl, xh, yl, yh;
-                R.get2(s0, s0 + 1u, xl, xh);
-                R.get2(s1, s1 + 1u, yl, yh);
-                const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
-                if (a0 == DI_ADD) r = x + y;
-                else if (a0 == DI_SUB) r = x - y;
-                else if (a0 == DI_MUL) r = x * y;
-                else {
-                  uint32_t zl, zh;
-                  R.get2(s2, s2 + 1u, zl, zh);
-                  r = x * y + ((uint64_t)zl | ((uint64_t)zh << 32));
-                }
-              }
-              R.put2(dst, (uint32_t)r, (uint32_t)(r >> 32));
-            } else if (ctl & CB(DC_MOVSP)) {
-              const uint32_t t_lin = my_w * 32u + sl;
-              const uint32_t bx = a.block[0], by = a.block[1];
-              const uint32_t gx = a.grid[0], gy = a.grid[1];
-              uint32_t v;
-              switch (a0) {
-                case KSP_TID_X: v = t_lin % bx; break;
-                case KSP_TID_Y: v = (t_lin / bx) % by; break;
-                case KSP_TID_Z: v = t_lin / (bx * by); break;
-                case KSP_NTID_X: v = a.block[0]; break;
-                case KSP_NTID_Y: v = a.block[1]; break;
-                case KSP_NTID_Z: v = a.block[2]; break;
-                case KSP_CTAID_X: v = blk % gx; break;
-                case KSP_CTAID_Y: v = (blk / gx) % gy; break;
-                case KSP_CTAID_Z: v = blk / (gx * gy); break;
-                case KSP_NCTAID_X: v = a.grid[0]; break;
-                case KSP_NCTAID_Y: v = a.grid[1]; break;
-                case KSP_NCTAID_Z: v = a.grid[2]; break;
-                default: v = sl; break;
-              }
-              R.put(dst, v);
-            } else {  // DC_LDP: a uniform value from the launch arguments
-              const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + a0);
-              if (a1) R.put2(dst, lo, *reinterpret_cast<const uint32_t*>(a.params + a0 + 4u));
-              else R.put(dst, lo);
-            }
-          }
-          // Continue the straight run with simple ALU instructions, without rescheduling:
-          // the same warps issue them, no reconvergence point or control instruction
-          // intervenes, none of them may reach an event (chunk write, budget) and none may
-          // pass the cycle limit.
-          uint32_t p = pc + 1u;
-          {
-            uint32_t n = (ctl >> RUN_SHIFT) - 1u;  // instructions after this one in its run
-            const uint32_t room = ev - wi;          // per warp: issues before its next event
-            if (go0) n = umin(n, rl(room, 0));
-            if (go1) n = umin(n, rl(room, 32));
-            if (umax(rl(v_next, 0), rl(v_next, 32)) > a.cyc_safe) n = 0;
-            while (n) {
-              const cdinst J = prog + p;
-              const u32x16 h = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(J);
-              const uint32_t c = h[0];
-              if (!(c & CB_SIMPLE)) break;
-              const uint32_t is2 = umax(umax(v_next, sb_at(h[6])), umax(umax(sb_at(h[7]), sb_at(h[8])), sb_at(h[9])));
-              const uint64_t on2 = mm & ballot(((pbits >> h[12]) & 1u) != h[13]);
-              if (lanes(gm)) {
-                if (sl == (wi & 31u)) {
-                  tr_c = is2;
-                  tr_p = p;
-                }
-                wi += 1;
-                v_next = is2 + 1;
-                sb_at(h[10]) = is2 + h[11];
-              }
-              if (c & XF_IMM) {
-                uint32_t iv[6];
-                for (int k = 0; k < 6; ++k) iv[k] = J->imm[k];
-                R.put_imm(ib, iv);
-              }
-              if (lanes(on2)) {
-                const uint32_t t0 = h[2], t1 = h[3], t2 = h[4], d2 = h[5], b0 = h[14], b1 = h[15];
-                if (c & CB(DC_FMA)) {
-                  uint32_t x0, x1, x2;
-                  R.get3(t0, t1, t2, x0, x1, x2);
-                  const uint32_t b = (b0 & 0x3F800000u) | (~b0 & x1);
-                  const uint32_t cc = (x2 & b1) ^ h[1];
-                  R.put(d2, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(cc))));
-                } else if (c & CB(DC_IADD)) {
-                  uint32_t x0, x1;
-                  R.get2(t0, t1, x0, x1);
-                  R.put(d2, x0 + (x1 ^ b0) + b1);
-                } else if (c & CB(DC_IMAD)) {
-                  uint32_t x0, x1, x2;
-                  R.get3(t0, t1, t2, x0, x1, x2);
-                  R.put(d2, x0 * x1 + (x2 & b0));
-                } else if (b0) {  // DC_MOV, 64-bit
-                  uint32_t lo, hi;
-                  R.get2(t0, t0 + 1u, lo, hi);
-                  R.put2(d2, lo, hi);
-                } else {          // DC_MOV, 32-bit
-                  R.put(d2, R.get(t0));
-                }
-              }
-              ++p;
-              --n;
-            }
-          }
-          spc0 = go0 ? p : spc0;
-          spc1 = go1 ? p : spc1;
-        } else if (ctl & (CB(DC_LDG) | CB(DC_STG))) {
-          // 32-bit global load or store through a 64-bit address register
-          uint32_t blo, bhi;
-          R.get2(s0, s0 + 1u, blo, bhi);
-          const uint64_t A = (((uint64_t)bhi << 32) | blo) + (((uint64_t)a1 << 32) | a0);
-          const uint64_t okm = ballot(((uint32_t)A & 3u) == 0u) & ballot(A < glim4) & on64;
-          const uint32_t is_load = ctl & CB(DC_LDG);
-          uint32_t v = 0;
-          if (is_load) {
-            if (lanes(okm)) v = *reinterpret_cast<const uint32_t*>(a.gmem + A);
-          } else if (lanes(okm)) {
-            *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
-          }
-          // the accounting does not depend on the loaded value: it runs while the load is in flight
-          const uint64_t faults = on64 & ~okm;
-          KS_COUNT_FAULTS(faults);
-          KS_GLOBAL_ACCOUNT(A, 4u, faults, is_load);
-          if (is_load && lanes(on64)) R.put(dst, v);
-          spc0 = go0 ? pc + 1u : spc0;
-          spc1 = go1 ? pc + 1u : spc1;
-        } else if (ctl & CB_MEM) {
-          const uint32_t is_global = ctl & CB(DC_MEMG);
-          const uint32_t is_load = ctl & XF_LOAD;
-          const uint32_t w64 = ctl & XF_W64;
-          const uint32_t S = w64 ? 8u : 4u;
-          const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
-          const uint64_t off = (uint64_t)a0 | ((uint64_t)a1 << 32);
-          uint64_t base;
-          if (ctl & XF_A64) {
-            uint32_t lo, hi;
-            R.get2(s0, s0 + 1u, lo, hi);
-            base = (uint64_t)lo | ((uint64_t)hi << 32);
-          } else {
-            base = R.get(s0);
-          }
-          const uint64_t A = base + off;
-          const uint64_t okm = ballot((A & (S - 1u)) == 0 && A <= size && size - A >= S) & on64;
-          if (is_load) {
-            uint32_t lo = 0, hi = 0;
-            if (lanes(okm)) {
-              if (is_global) {
-                if (w64) {
-                  const uint2 v = *reinterpret_cast<const uint2*>(a.gmem + A);
-                  lo = v.x;
-                  hi = v.y;
-                } else {
-                  lo = *reinterpret_cast<const uint32_t*>(a.gmem + A);
-                }
-              } else {
-                lo = *reinterpret_cast<const uint32_t*>(win + A);
-                if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
-              }
-            }
-            if (lanes(on64)) {
-              if (w64) R.put2(dst, lo, hi);
-              else R.put(dst, lo);
-            }
-          } else if (lanes(okm)) {
-            if (w64) {
-              uint32_t lo, hi;
-              R.get2(s1, s1 + 1u, lo, hi);
-              if (is_global) {
-                *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, hi);
-              } else {
-                *reinterpret_cast<uint32_t*>(win + A) = lo;
-                *reinterpret_cast<uint32_t*>(win + A + 4) = hi;
-              }
-            } else {
-              const uint32_t lo = R.get(s1);
-              if (is_global) *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
-              else *reinterpret_cast<uint32_t*>(win + A) = lo;
-            }
-          }
-          const uint64_t faults = on64 & ~okm;
-          KS_COUNT_FAULTS(faults);
-          if (is_global) {
-            KS_GLOBAL_ACCOUNT(A, S, faults, is_load);
-          } else {
-            const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
-            uint32_t d0 = 1, d1 = 1;
-            bool slow0 = g0 != 0, slow1 = g1 != 0;
-            if (!faults) {
-              // affine fast path for full halves: lanes at A0 + l * d
-              const uint32_t a32 = (uint32_t)A;
-              const uint32_t diff = a32 - prev_in_half(a32, lane);
-              const uint32_t dA = rl(diff, 1), dB = rl(diff, 33);
-              const uint64_t same = ballot(diff == (hl ? dB : dA));
-              if (g0 == 0xFFFFFFFFu && ((uint32_t)same | 1u) == 0xFFFFFFFFu && (dA & 3u) == 0) {
-                const uint32_t ws = (dA >> 2) & 31u;
-                d0 = dA == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
-                slow0 = false;
-              }
-              if (g1 == 0xFFFFFFFFu && ((uint32_t)(same >> 32) | 1u) == 0xFFFFFFFFu && (dB & 3u) == 0) {
-                const uint32_t ws = (dB >> 2) & 31u;
-                d1 = dB == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
-                slow1 = false;
-              }
-            }
-            if (slow0) d0 = bank_degree(A, (uint64_t)g0);
-            if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
-            const uint32_t dh = hl ? d1 : d0;
-            if ((hm >> hl) & 1u) {
-              if (sl == C_SH_N) cnt += 1;
-              if (sl == C_SH_SUM) cnt += dh;
-              if (sl == C_SH_MAX) cnt = umax(cnt, dh);
-            }
-          }
-          spc0 = go0 ? pc + 1u : spc0;
-          spc1 = go1 ? pc + 1u : spc1;
-        } else if (ctl & CB(DC_BRA)) {
-          const uint32_t target = a0, rpc = a1;
+        if (ctl & CB(DC_BRA)) {
+          const uint32_t target = hot[14], rpc = hot[15];
           const uint32_t mm0 = (uint32_t)mm, mm1 = (uint32_t)(mm >> 32);
           uint32_t divm = 0;
           if (go0) {
@@ -917,6 +679,259 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             hst |= WAIT1;
           }
         }
+      } else {
+        // ---------------------------------------------------------------- a straight run
+        // This instruction and the ones after it up to the next control instruction or
+        // reconvergence point (the host's run length) issue back to back by the same
+        // warps, without rescheduling: none of them may reach an event (chunk write,
+        // budget) and none may pass the cycle limit.
+        uint32_t n = ctl >> RUN_SHIFT;  // at least 1
+        {
+          const uint32_t room = ev - wi;  // per warp: issues before its next event (at least 1 here)
+          n = umin(n, umin(rl(room, 0) | ~go0, rl(room, 32) | ~go1));
+          if (ballot(iss > a.cyc_safe) & gm) n = 1u;
+        }
+        uint32_t off = pc * (uint32_t)sizeof(DInst);  // byte offset of the current record
+        uint32_t is = iss;
+        u32x16 h = hot;
+        while (true) {
+          const uint32_t c = h[0];
+          KS_ISSUE(is, off / (uint32_t)sizeof(DInst), h[10], h[11]);
+          const uint64_t on64 = mm & ballot(((pbits >> h[12]) & 1u) != h[13]);  // guard
+          if (c & XF_IMM) {
+            uint32_t iv[6];
+            for (int k = 0; k < 6; ++k) iv[k] = *reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
+                prog_b + off + offsetof(DInst, imm) + 4u * k);
+            R.put_imm(ib, iv);
+          }
+          const uint32_t s0 = h[2], s1 = h[3], s2 = h[4], dst = h[5];
+          const uint32_t a0 = h[14], a1 = h[15], a2 = h[1];
+          if (c & CB(DC_FMA)) {
+            uint32_t x0, x1, x2;
+            R.get3(s0, s1, s2, x0, x1, x2);
+            const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
+            const uint32_t cc = (x2 & a1) ^ a2;                  // x2, -x2 or -0.0f
+            R.put_m(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(cc))), on64);
+          } else if (c & CB(DC_IADD)) {
+            uint32_t x0, x1;
+            R.get2(s0, s1, x0, x1);
+            R.put_m(dst, x0 + (x1 ^ a0) + a1, on64);
+          } else if (c & CB(DC_IMAD)) {
+            uint32_t x0, x1, x2;
+            R.get3(s0, s1, s2, x0, x1, x2);
+            R.put_m(dst, x0 * x1 + (x2 & a0), on64);
+          } else if (c & (CB(DC_LDG) | CB(DC_STG))) {
+            // 32-bit global load or store through a 64-bit address register
+            uint32_t blo, bhi;
+            R.get2(s0, s0 + 1u, blo, bhi);
+            const uint64_t A = (((uint64_t)bhi << 32) | blo) + (((uint64_t)a1 << 32) | a0);
+            const uint64_t okm = ballot(((uint32_t)A & 3u) == 0u) & ballot(A < glim4) & on64;
+            const uint32_t is_load = c & CB(DC_LDG);
+            uint32_t v = 0;
+            if (is_load) {
+              if (okm) {  // lanes without a valid access read word 0 of the image and drop it
+                const bool ok = lanes(okm);
+                v = *reinterpret_cast<const uint32_t*>(a.gmem + (ok ? A : 0ull));
+                v = ok ? v : 0u;
+              }
+            } else if (lanes(okm)) {
+              *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
+            }
+            // the accounting does not depend on the loaded value: it runs while the load is in flight
+            const uint64_t faults = on64 & ~okm;
+            KS_COUNT_FAULTS(faults);
+            KS_GLOBAL_ACCOUNT(A, 4u, faults, is_load);
+            if (is_load) R.put_m(dst, v, on64);
+          } else if (c & CB(DC_MOV)) {
+            if (a0) {
+              uint32_t lo, hi;
+              R.get2(s0, s0 + 1u, lo, hi);
+              R.put2_m(dst, lo, hi, on64);
+            } else {
+              R.put_m(dst, R.get(s0), on64);
+            }
+          } else if (c & CB(DC_SELP)) {
+            const bool pr = (pbits >> s2) & 1u;
+            if (a0) {
+              uint32_t xl, xh, yl, yh;
+              R.get2(s0, s0 + 1u, xl, xh);
+              R.get2(s1, s1 + 1u, yl, yh);
+              R.put2_m(dst, pr ? xl : yl, pr ? xh : yh, on64);
+            } else {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              R.put_m(dst, pr ? x0 : x1, on64);
+            }
+          } else if (c & CB(DC_SETP)) {
+            bool lt, eq, gt;
+            if (a0 == DS_F32) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              const float x = __uint_as_float(x0), y = __uint_as_float(x1);
+              lt = x < y;
+              eq = x == y;
+              gt = x > y;  // all false when an input is NaN
+            } else if (a0 <= DS_U32) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              lt = a0 == DS_S32 ? (int32_t)x0 < (int32_t)x1 : x0 < x1;
+              eq = x0 == x1;
+              gt = !lt && !eq;
+            } else {
+              uint32_t xl, xh, yl, yh;
+              R.get2(s0, s0 + 1u, xl, xh);
+              R.get2(s1, s1 + 1u, yl, yh);
+              const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
+              lt = a0 == DS_S64 ? (int64_t)x < (int64_t)y : x < y;
+              eq = x == y;
+              gt = !lt && !eq;
+            }
+            const bool cv = (lt && (a1 & 1u)) || (eq && (a1 & 2u)) || (gt && (a1 & 4u));
+            const uint32_t nb = (pbits & ~(1u << dst)) | ((cv ? 1u : 0u) << dst);
+            pbits = lanes(on64) ? nb : pbits;
+          } else if (c & CB(DC_I64)) {
+            uint64_t r;
+            if (a0 >= DI_WIDE_S) {
+              uint32_t x0, x1;
+              R.get2(s0, s1, x0, x1);
+              r = a0 == DI_WIDE_S ? (uint64_t)((int64_t)(int32_t)x0 * (int64_t)(int32_t)x1)
+                                  : (uint64_t)x0 * (uint64_t)x1;
+            } else {
+              uint32_t xl, xh, yl, yh;
+              R.get2(s0, s0 + 1u, xl, xh);
+              R.get2(s1, s1 + 1u, yl, yh);
+              const uint64_t x = (uint64_t)xl | ((uint64_t)xh << 32), y = (uint64_t)yl | ((uint64_t)yh << 32);
+              if (a0 == DI_ADD) r = x + y;
+              else if (a0 == DI_SUB) r = x - y;
+              else if (a0 == DI_MUL) r = x * y;
+              else {
+                uint32_t zl, zh;
+                R.get2(s2, s2 + 1u, zl, zh);
+                r = x * y + ((uint64_t)zl | ((uint64_t)zh << 32));
+              }
+            }
+            R.put2_m(dst, (uint32_t)r, (uint32_t)(r >> 32), on64);
+          } else if (c & CB_MEM) {
+            const uint32_t is_global = c & CB(DC_MEMG);
+            const uint32_t is_load = c & XF_LOAD;
+            const uint32_t w64 = c & XF_W64;
+            const uint32_t S = w64 ? 8u : 4u;
+            const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
+            const uint64_t off = (uint64_t)a0 | ((uint64_t)a1 << 32);
+            uint64_t base;
+            if (c & XF_A64) {
+              uint32_t lo, hi;
+              R.get2(s0, s0 + 1u, lo, hi);
+              base = (uint64_t)lo | ((uint64_t)hi << 32);
+            } else {
+              base = R.get(s0);
+            }
+            const uint64_t A = base + off;
+            const uint64_t okm = ballot((A & (S - 1u)) == 0 && A <= size && size - A >= S) & on64;
+            if (is_load) {
+              uint32_t lo = 0, hi = 0;
+              if (lanes(okm)) {
+                if (is_global) {
+                  if (w64) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(a.gmem + A);
+                    lo = v.x;
+                    hi = v.y;
+                  } else {
+                    lo = *reinterpret_cast<const uint32_t*>(a.gmem + A);
+                  }
+                } else {
+                  lo = *reinterpret_cast<const uint32_t*>(win + A);
+                  if (w64) hi = *reinterpret_cast<const uint32_t*>(win + A + 4);
+                }
+              }
+              if (w64) R.put2_m(dst, lo, hi, on64);
+              else R.put_m(dst, lo, on64);
+            } else if (lanes(okm)) {
+              if (w64) {
+                uint32_t lo, hi;
+                R.get2(s1, s1 + 1u, lo, hi);
+                if (is_global) {
+                  *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, hi);
+                } else {
+                  *reinterpret_cast<uint32_t*>(win + A) = lo;
+                  *reinterpret_cast<uint32_t*>(win + A + 4) = hi;
+                }
+              } else {
+                const uint32_t lo = R.get(s1);
+                if (is_global) *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
+                else *reinterpret_cast<uint32_t*>(win + A) = lo;
+              }
+            }
+            const uint64_t faults = on64 & ~okm;
+            KS_COUNT_FAULTS(faults);
+            if (is_global) {
+              KS_GLOBAL_ACCOUNT(A, S, faults, is_load);
+            } else {
+              const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
+              const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
+              uint32_t d0 = 1, d1 = 1;
+              bool slow0 = g0 != 0, slow1 = g1 != 0;
+              if (!faults) {
+                // affine fast path for full halves: lanes at A0 + l * d
+                const uint32_t a32 = (uint32_t)A;
+                const uint32_t diff = a32 - prev_in_half(a32, lane);
+                const uint32_t dA = rl(diff, 1), dB = rl(diff, 33);
+                const uint64_t same = ballot(diff == (hl ? dB : dA));
+                if (g0 == 0xFFFFFFFFu && ((uint32_t)same | 1u) == 0xFFFFFFFFu && (dA & 3u) == 0) {
+                  const uint32_t ws = (dA >> 2) & 31u;
+                  d0 = dA == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
+                  slow0 = false;
+                }
+                if (g1 == 0xFFFFFFFFu && ((uint32_t)(same >> 32) | 1u) == 0xFFFFFFFFu && (dB & 3u) == 0) {
+                  const uint32_t ws = (dB >> 2) & 31u;
+                  d1 = dB == 0 ? 1u : (ws == 0 ? 32u : (1u << __builtin_ctz(ws)));
+                  slow1 = false;
+                }
+              }
+              if (slow0) d0 = bank_degree(A, (uint64_t)g0);
+              if (slow1) d1 = bank_degree(A, (uint64_t)g1 << 32);
+              const uint32_t dh = hl ? d1 : d0;
+              if ((hm >> hl) & 1u) {
+                if (sl == C_SH_N) cnt += 1;
+                if (sl == C_SH_SUM) cnt += dh;
+                if (sl == C_SH_MAX) cnt = umax(cnt, dh);
+              }
+            }
+          } else if (c & CB(DC_MOVSP)) {
+            const uint32_t t_lin = my_w * 32u + sl;
+            const uint32_t bx = a.block[0], by = a.block[1];
+            const uint32_t gx = a.grid[0], gy = a.grid[1];
+            uint32_t v;
+            switch (a0) {
+              case KSP_TID_X: v = t_lin % bx; break;
+              case KSP_TID_Y: v = (t_lin / bx) % by; break;
+              case KSP_TID_Z: v = t_lin / (bx * by); break;
+              case KSP_NTID_X: v = a.block[0]; break;
+              case KSP_NTID_Y: v = a.block[1]; break;
+              case KSP_NTID_Z: v = a.block[2]; break;
+              case KSP_CTAID_X: v = blk % gx; break;
+              case KSP_CTAID_Y: v = (blk / gx) % gy; break;
+              case KSP_CTAID_Z: v = blk / (gx * gy); break;
+              case KSP_NCTAID_X: v = a.grid[0]; break;
+              case KSP_NCTAID_Y: v = a.grid[1]; break;
+              case KSP_NCTAID_Z: v = a.grid[2]; break;
+              default: v = sl; break;
+            }
+            R.put_m(dst, v, on64);
+          } else {  // DC_LDP: a uniform value from the launch arguments
+            const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + a0);
+            if (a1) R.put2_m(dst, lo, *reinterpret_cast<const uint32_t*>(a.params + a0 + 4u), on64);
+            else R.put_m(dst, lo, on64);
+          }
+          // the next record (the end sentinel at the latest: a run never includes it)
+          off += (uint32_t)sizeof(DInst);
+          h = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(prog_b + off);
+          is = KS_ISSUE_CYCLE(h);
+          if (--n == 0) break;
+        }
+        const uint32_t p = off / (uint32_t)sizeof(DInst);
+        spc0 = go0 ? p : spc0;
+        spc1 = go1 ? p : spc1;
       }
       if (need & 1u) KS_SETTLE(0, S0, spc0);
       if (need & 2u) KS_SETTLE(1, S1, spc1);
@@ -964,6 +979,18 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
     for (uint32_t l = 0; l < 32u; ++l) {
       ti0 += rl(act, l);
       ti1 += rl(act, 32u + l);
+    }
+    // per-lane analyser shares: lane 32 h + d of cnt holds counter d of warp h
+    {
+      const uint32_t qs[6] = {q_ln, q_ls, q_ll, q_sn, q_ss, q_sl};
+      const uint32_t qd[6] = {C_GLD_N, C_GLD_SEC, C_GLD_LINES, C_GST_N, C_GST_SEC, C_GST_LINES};
+      for (int k = 0; k < 6; ++k) {
+        // read both totals here, with every lane active: a cross-lane read under a
+        // lane condition may see lanes where the sum was never computed
+        const uint32_t t = half_sum(qs[k]);
+        const uint32_t t0 = rl(t, 31), t1 = rl(t, 63);
+        cnt += sl == qd[k] ? (hl ? t1 : t0) : 0u;
+      }
     }
     if (w < W) {
       const uint32_t m_status = (status >> (8u * hl)) & 0xFFu;
@@ -1049,7 +1076,7 @@ int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
 }
 
 size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes) {
-  const size_t sb = (size_t)(wg / 32u) * KS_SB_ENTRIES * 4u;
+  const size_t sb = (size_t)(wg / 32u + 1u) * KS_SB_ENTRIES * 4u;  // the warps' scoreboards and a scratch one
   return sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
 }
 

@@ -944,7 +944,8 @@ void compute_reconvergence(ks_program* P) {
 // ---------------------------------------------------------------------------- device records
 //
 // Lower the parsed records to the interpreter's DInst records (n + 1 of them: a
-// DC_END sentinel after the last instruction).  Immediate source k goes to the
+// DC_END sentinel after the last instruction; then KS_PREFETCH_PAD zero records
+// that the interpreter may read ahead into).  Immediate source k goes to the
 // immediate slots reg_slots + 2k (low) and + 2k + 1 (high); f32 add, sub and mul
 // become one fused multiply-add with constant operands, which rounds exactly as
 // the separate operation does (x + y = fma(x, 1, y), x - y = fma(x, 1, -y),
@@ -952,7 +953,7 @@ void compute_reconvergence(ks_program* P) {
 std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
   const uint32_t n = (uint32_t)P->code.size();
   const uint32_t ib = P->reg_slots;
-  std::vector<DInst> out(n + 1);
+  std::vector<DInst> out(n + 1 + KS_PREFETCH_PAD);
   auto sbo = [](uint8_t sb) -> uint32_t { return (uint32_t)(sb == KS_NO_SB ? KS_SB_ZERO : sb) * 4u; };
   for (uint32_t i = 0; i <= n; ++i) {
     DInst& d = out[i];

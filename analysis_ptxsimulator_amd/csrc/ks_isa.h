@@ -50,6 +50,7 @@ constexpr uint8_t KS_SB_DUMP = 126;      // scoreboard entry written by instruct
 constexpr uint8_t KS_SB_ZERO = 127;      // scoreboard entry that always reads 0 (no source)
 constexpr uint32_t KS_SB_ENTRIES = 129;  // scoreboard words per warp in LDS (odd: warps start in different banks)
 constexpr uint32_t KS_IMM_SLOTS = 6;     // register slots after the program's that hold an instruction's immediates
+constexpr uint32_t KS_PREFETCH_PAD = 4;  // zero records after the end sentinel: reads ahead stay in bounds
 
 struct KsInst {            // 64 bytes
   uint8_t op;              // KOp

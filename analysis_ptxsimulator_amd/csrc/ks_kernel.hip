@@ -696,6 +696,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         u32x16 h = hot;
         while (true) {
           const uint32_t c = h[0];
+          // touch the record two ahead, so that its line is in the scalar cache by then
+          // (the value is consumed only after the next record arrives)
+          const uint32_t pf = *reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
+              prog_b + off + 2u * (uint32_t)sizeof(DInst));
           KS_ISSUE(is, off / (uint32_t)sizeof(DInst), h[10], h[11]);
           const uint64_t on64 = mm & ballot(((pbits >> h[12]) & 1u) != h[13]);  // guard
           if (c & XF_IMM) {
@@ -926,6 +930,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           // the next record (the end sentinel at the latest: a run never includes it)
           off += (uint32_t)sizeof(DInst);
           h = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(prog_b + off);
+          asm volatile("; prefetched %0" : : "s"(pf));
           is = KS_ISSUE_CYCLE(h);
           if (--n == 0) break;
         }

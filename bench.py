@@ -36,9 +36,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_key):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, if it was taken on the current kernel source; else None."""
+def measured_counters(workload_key):
+    """The committed rocprofv3 counter summary of this workload (HBM bytes per
+    launch from FETCH_SIZE/WRITE_SIZE, VALU utilisation), if it was taken on the
+    current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_key)
     if not os.path.exists(p):
         return None
@@ -46,7 +47,7 @@ def measured_traffic(workload_key):
         d = json.load(f)
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
 
 
 def make_workload(name):
@@ -165,7 +166,12 @@ def main():
     alg_bytes = 32 * sectors + 8 * records + (16 + 80) * len(c)
     avg_launch_s = float(np.mean(launch_ms)) / 1000.0
     achieved = alg_bytes / avg_launch_s / 1e9
-    traffic = measured_traffic(args.workload)
+    prof = measured_counters(args.workload)
+    traffic = prof.get("hbm_bytes_per_launch") if prof else None
+    valu = None
+    if prof and "valu_busy" in prof:
+        valu = {"busy": prof["valu_busy"], "lane_util": prof["valu_lane_util"], "salu_busy": prof["salu_busy"],
+                "source": "rocprofv3 counters, profiles/traffic_%s.json" % args.workload}
 
     out = {
         "metric": METRIC,
@@ -191,6 +197,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel": kernel},
+        "valu_utilisation": valu,
     }
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)

@@ -35,12 +35,74 @@ RESERVED_BASE = 56
 RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72}  # register-file VGPRs from RESERVED_BASE on
 
 
+def index_mode_hazards(body: str) -> list:
+    """Places in a kernel body where VGPR index mode is switched on while a load
+    that returns into a VGPR (vector memory or LDS) may still be outstanding.
+
+    On gfx950 such a load's data was observed to land in the wrong register when
+    instructions in index mode ran before it returned.  The check is a forward
+    data flow over the body's branches: a load sets an outstanding bit (vector
+    memory or LDS), `s_waitcnt vmcnt(0)` / `lgkmcnt(0)` clears it, and every
+    `s_set_gpr_idx_on` reached with a bit set is reported as (index, text).  It
+    follows every branch edge, so it may report paths that correlated branch
+    conditions never take; the kernels are written so that it reports none."""
+    insts = []
+    for line in body.split("\n"):
+        t = line.split(";")[0].strip()
+        if t and not (t.startswith(".") and not t.endswith(":")):
+            insts.append(t)
+    labels = {t[:-1]: i for i, t in enumerate(insts) if t.endswith(":")}
+    n = len(insts)
+
+    def successors(i):
+        parts = insts[i].split()
+        op = parts[0]
+        if op == "s_branch":
+            return [labels[parts[1]]]
+        if op.startswith("s_cbranch"):
+            return [labels[parts[1]], i + 1]
+        if op in ("s_endpgm", "s_setpc_b64"):
+            return []
+        return [i + 1] if i + 1 < n else []
+
+    seen = [0] * n
+    visited = [False] * n
+    work = [(0, 0)]
+    found = {}
+    while work:
+        i, st = work.pop()
+        if i >= n or (visited[i] and (seen[i] | st) == seen[i]):
+            continue
+        visited[i] = True
+        seen[i] |= st
+        st = seen[i]
+        t = insts[i]
+        op = "" if t.endswith(":") else t.split()[0]
+        out = st
+        if re.match(r"(global|buffer|flat|scratch)_load", op) or (re.match(r"(global|buffer|flat)_atomic", op) and " glc" in t):
+            out |= 1
+        if re.match(r"ds_(read|load|bpermute|permute|swizzle)", op) or (op.startswith("ds_") and "_rtn" in op):
+            out |= 2
+        if op == "s_waitcnt":
+            if "vmcnt(0)" in t:
+                out &= ~1
+            if "lgkmcnt(0)" in t:
+                out &= ~2
+        if op == "s_set_gpr_idx_on" and st:
+            found[i] = t
+        for j in successors(i):
+            work.append((j, out))
+    return sorted(found.items())
+
+
 def check_device_asm(asm_text: str) -> dict:
     """Check the interpreter kernels' gfx950 assembly; returns per-kernel resources.
 
     Raises RuntimeError when a kernel spills to scratch, when compiler-written
     code (outside inline asm) in a register-file kernel names a VGPR at or above
-    RESERVED_BASE, or when such a kernel's VGPR count does not cover its file."""
+    RESERVED_BASE, when such a kernel's VGPR count does not cover its file, or
+    when VGPR index mode can be switched on while a load is outstanding
+    (index_mode_hazards)."""
     info = {}
     for k in INTERP_KERNELS:
         m = re.search(r"^(_Z\d+%sN2ks6KsArgsE):[^\n]*\n(.*?)^\.Lfunc_end" % k, asm_text, re.S | re.M)
@@ -78,6 +140,10 @@ def check_device_asm(asm_text: str) -> dict:
             if hi >= RESERVED_BASE:
                 raise RuntimeError("%s: compiler-allocated code uses v%d (v%d+ hold the register file)"
                                    % (k, hi, RESERVED_BASE))
+            hz = index_mode_hazards(body)
+            if hz:
+                raise RuntimeError("%s: VGPR index mode switched on while a load may be outstanding: %s"
+                                   % (k, hz[:3]))
     return info
 
 

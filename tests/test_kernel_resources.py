@@ -60,6 +60,30 @@ def test_checker_rejects_compiler_use_of_reserved_vgprs():
             kbuild.check_device_asm(_fake("ks_interp_v64", ok + bad))
 
 
+def test_checker_rejects_index_mode_with_a_load_in_flight():
+    """VGPR index mode must not be switched on while a vector-memory or LDS load
+    may still return into a VGPR; a wait for the counter in between, on every path,
+    makes it legal."""
+    on = ("\t;;#ASMSTART\n\ts_set_gpr_idx_on s2, gpr_idx(SRC0)\n\tv_mov_b32 v3, v%d\n\ts_set_gpr_idx_off\n"
+          "\t;;#ASMEND\n" % kbuild.RESERVED_BASE)
+    vm = "\tglobal_load_dword v4, v[0:1], off\n"
+    ds = "\tds_read_b32 v5, v6\n"
+    good = [vm + "\ts_waitcnt vmcnt(0)\n" + on, ds + "\ts_waitcnt lgkmcnt(0)\n" + on,
+            on + vm + "\ts_waitcnt vmcnt(0)\n",
+            # the load is only on the branch that also waits
+            "\ts_cbranch_scc1 .LB_1\n" + vm + "\ts_waitcnt vmcnt(0)\n.LB_1:\n" + on]
+    bad = [vm + on, ds + on, vm + "\ts_waitcnt lgkmcnt(0)\n" + on,
+           # waits on one path only
+           vm + "\ts_cbranch_scc1 .LB_1\n\ts_waitcnt vmcnt(0)\n.LB_1:\n" + on,
+           # a load late in a loop body reaches the index mode at its head
+           ".LB_0:\n" + on + vm + "\ts_cbranch_scc1 .LB_0\n\ts_waitcnt vmcnt(0)\n"]
+    for b in good:
+        kbuild.check_device_asm(_fake("ks_interp_v64", b + "\ts_endpgm\n"))
+    for b in bad:
+        with pytest.raises(RuntimeError, match="index mode"):
+            kbuild.check_device_asm(_fake("ks_interp_v64", b + "\ts_endpgm\n"))
+
+
 def test_checker_rejects_short_vgpr_count():
     for k, n in kbuild.RF_VGPRS.items():
         kbuild.check_device_asm(_fake(k, "\ts_endpgm\n", vgprs=kbuild.RESERVED_BASE + n))

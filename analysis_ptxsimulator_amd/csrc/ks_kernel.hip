@@ -669,17 +669,38 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           const uint64_t conv = init64 & ~ex64;
           const uint32_t hm = (go0 & 1u) | (go1 & 2u);
           cnt = cnt_add2(cnt, sl, hl, C_BAR, hm, 1u);
-          if (go0) {
-            if ((uint32_t)mm != (uint32_t)conv) status |= KS_ST_BARDIV;
-            S0.pc = pc + 1u;
-            spc0 = INF;
-            hst |= WAIT0;
-          }
-          if (go1) {
-            if ((uint32_t)(mm >> 32) != (uint32_t)(conv >> 32)) status |= KS_ST_BARDIV << 8;
-            S1.pc = pc + 1u;
-            spc1 = INF;
-            hst |= WAIT1;
+          if (go0 && (uint32_t)mm != (uint32_t)conv) status |= KS_ST_BARDIV;
+          if (go1 && (uint32_t)(mm >> 32) != (uint32_t)(conv >> 32)) status |= KS_ST_BARDIV << 8;
+          if ((go0 | (0u - ((hst >> 2) & 1u))) & (go1 | (0u - ((hst >> 3) & 1u)))) {
+            // Every unfinished warp of the wave arrives here together: the wave takes
+            // part in the block's epoch right away (the protocol of the epoch below,
+            // arrival = this issue cycle) and its warps go on after the barrier.
+            const uint32_t slot = epoch % 3u;
+            if (lane == 0) {
+              atomicAdd(&ep_alive[slot], hm == 3u ? 2u : 1u);
+              atomicMax(&ep_max[slot], umax(go0 ? rl(iss, 0) : 0u, go1 ? rl(iss, 32) : 0u));
+            }
+            if (tid == 0) {
+              ep_alive[(epoch + 1u) % 3u] = 0;
+              ep_max[(epoch + 1u) % 3u] = 0;
+            }
+            __syncthreads();
+            const uint32_t release = uni(ep_max[slot]) + a.lat_bar;
+            v_next = gl ? umax(v_next, release) : v_next;
+            ++epoch;
+            if (go0) spc0 = pc + 1u;
+            if (go1) spc1 = pc + 1u;
+          } else {
+            if (go0) {
+              S0.pc = pc + 1u;
+              spc0 = INF;
+              hst |= WAIT0;
+            }
+            if (go1) {
+              S1.pc = pc + 1u;
+              spc1 = INF;
+              hst |= WAIT1;
+            }
           }
         }
       } else {

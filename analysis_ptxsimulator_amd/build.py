@@ -29,23 +29,32 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp
 # The VGPR register-file kernels keep simulated registers in v56 and up, which
 # the compiler must never allocate (they are reserved by amdgpu_num_vgpr), and
 # their VGPR count must cover the file; no interpreter may use scratch memory.
-RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64")
+RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64", "ks_interp_v32_ext", "ks_interp_v64_ext")
 INTERP_KERNELS = RESERVED_VGPR_KERNELS
-RESERVED_BASE = 56
-RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72}  # register-file VGPRs from RESERVED_BASE on
+# first VGPR of each kernel's register file (compiler-allocated code stays below it)
+RESERVED_BASE = {"ks_interp_v32": 56, "ks_interp_v64": 56, "ks_interp_v32_ext": 64, "ks_interp_v64_ext": 64}
+# register-file VGPRs from RESERVED_BASE on
+RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72, "ks_interp_v32_ext": 40, "ks_interp_v64_ext": 72}
+
 
 
 def index_mode_hazards(body: str) -> list:
     """Places in a kernel body where VGPR index mode is switched on while a load
-    that returns into a VGPR (vector memory or LDS) may still be outstanding.
+    that returns into a VGPR (vector memory, scratch or LDS) may still be
+    outstanding.
 
     On gfx950 such a load's data was observed to land in the wrong register when
     instructions in index mode ran before it returned.  The check is a forward
     data flow over the body's branches: a load sets an outstanding bit (vector
     memory or LDS), `s_waitcnt vmcnt(0)` / `lgkmcnt(0)` clears it, and every
-    `s_set_gpr_idx_on` reached with a bit set is reported as (index, text).  It
-    follows every branch edge, so it may report paths that correlated branch
-    conditions never take; the kernels are written so that it reports none."""
+    `s_set_gpr_idx_on` reached with a bit set is reported as (index, text).
+
+    Branches are followed both ways except where the compiler steers control flow
+    with a flag pair it has just set to a constant: `s_mov_b64 s[a:b], 0` or `-1`,
+    then `s_and_b64 vcc, exec, s[a:b]` (vcc = 0 when the pair is 0) or
+    `s_andn2_b64 vcc, exec, s[a:b]` (vcc = 0 when it is -1); a vcc known to be 0
+    decides the next s_cbranch_vccz / s_cbranch_vccnz.  A pair's constant is
+    forgotten at any instruction whose destination names one of its registers."""
     insts = []
     for line in body.split("\n"):
         t = line.split(";")[0].strip()
@@ -53,45 +62,81 @@ def index_mode_hazards(body: str) -> list:
             insts.append(t)
     labels = {t[:-1]: i for i, t in enumerate(insts) if t.endswith(":")}
     n = len(insts)
+    pair_re = re.compile(r"s\[(\d+):(\d+)\]")
 
-    def successors(i):
-        parts = insts[i].split()
+    def dest_regs(t):
+        """Scalar registers named by an instruction's first operand."""
+        parts = t.split(None, 1)
+        if len(parts) < 2:
+            return set()
+        first = parts[1].split(",")[0].strip()
+        m = pair_re.fullmatch(first)
+        if m:
+            return set(range(int(m.group(1)), int(m.group(2)) + 1))
+        m = re.fullmatch(r"s(\d+)", first)
+        if m:
+            return {int(m.group(1))}
+        if first in ("vcc", "vcc_lo", "vcc_hi"):
+            return {"vcc"}
+        return set()
+
+    def step(i, st):
+        """Successor states of instruction i from state st = (bits, consts, vcc0)."""
+        bits, consts, vcc0 = st
+        t = insts[i]
+        if t.endswith(":"):
+            return [(i + 1, st)] if i + 1 < n else []
+        parts = t.split()
         op = parts[0]
+        if re.match(r"(global|buffer|flat|scratch)_load", op) or (re.match(r"(global|buffer|flat)_atomic", op) and " glc" in t):
+            bits |= 1
+        if re.match(r"ds_(read|load|bpermute|permute|swizzle)", op) or (op.startswith("ds_") and "_rtn" in op):
+            bits |= 2
+        if op == "s_waitcnt":
+            if "vmcnt(0)" in t:
+                bits &= ~1
+            if "lgkmcnt(0)" in t:
+                bits &= ~2
+        d = dest_regs(t)
+        new_vcc0 = vcc0 and "vcc" not in d and not op.startswith("v_cmp")
+        if op in ("s_and_b64", "s_andn2_b64") and t.split(None, 1)[1].replace(" ", "").startswith("vcc,exec,"):
+            m = pair_re.search(t.split("exec,", 1)[1])
+            val = dict(consts).get((int(m.group(1)), int(m.group(2)))) if m else None
+            new_vcc0 = (op == "s_and_b64" and val == 0) or (op == "s_andn2_b64" and val == -1)
+        if d:
+            consts = frozenset(c for c in consts if not (set(range(c[0][0], c[0][1] + 1)) & d))
+        if op == "s_mov_b64":
+            m = pair_re.fullmatch(t.split(None, 1)[1].split(",")[0].strip())
+            src = t.split(",", 1)[1].strip()
+            if m and src in ("0", "-1"):
+                consts = consts | {((int(m.group(1)), int(m.group(2))), int(src))}
+        out = (bits, consts, new_vcc0)
         if op == "s_branch":
-            return [labels[parts[1]]]
+            return [(labels[parts[1]], out)]
         if op.startswith("s_cbranch"):
-            return [labels[parts[1]], i + 1]
+            tgt = labels[parts[1]]
+            if op == "s_cbranch_vccz" and vcc0:
+                return [(tgt, out)]
+            if op == "s_cbranch_vccnz" and vcc0:
+                return [(i + 1, out)]
+            return [(tgt, out), (i + 1, out)]
         if op in ("s_endpgm", "s_setpc_b64"):
             return []
-        return [i + 1] if i + 1 < n else []
+        return [(i + 1, out)] if i + 1 < n else []
 
-    seen = [0] * n
-    visited = [False] * n
-    work = [(0, 0)]
+    # states per instruction: a set of (bits, consts, vcc0); small in practice
+    seen = [set() for _ in range(n)]
+    work = [(0, (0, frozenset(), False))]
     found = {}
     while work:
         i, st = work.pop()
-        if i >= n or (visited[i] and (seen[i] | st) == seen[i]):
+        if i >= n or st in seen[i]:
             continue
-        visited[i] = True
-        seen[i] |= st
-        st = seen[i]
+        seen[i].add(st)
         t = insts[i]
-        op = "" if t.endswith(":") else t.split()[0]
-        out = st
-        if re.match(r"(global|buffer|flat|scratch)_load", op) or (re.match(r"(global|buffer|flat)_atomic", op) and " glc" in t):
-            out |= 1
-        if re.match(r"ds_(read|load|bpermute|permute|swizzle)", op) or (op.startswith("ds_") and "_rtn" in op):
-            out |= 2
-        if op == "s_waitcnt":
-            if "vmcnt(0)" in t:
-                out &= ~1
-            if "lgkmcnt(0)" in t:
-                out &= ~2
-        if op == "s_set_gpr_idx_on" and st:
+        if not t.endswith(":") and t.split()[0] == "s_set_gpr_idx_on" and st[0]:
             found[i] = t
-        for j in successors(i):
-            work.append((j, out))
+        work.extend(step(i, st))
     return sorted(found.items())
 
 
@@ -133,13 +178,14 @@ def check_device_asm(asm_text: str) -> dict:
                 for lo, top, single in re.findall(r"\bv(?:\[(\d+):(\d+)\]|(\d+)\b)", line):
                     hi = max(hi, int(top or single))
             info[k]["max_compiler_vgpr"] = hi
-            need = RESERVED_BASE + RF_VGPRS[k]
+            base = RESERVED_BASE[k]
+            need = base + RF_VGPRS[k]
             if info[k]["vgprs"] < need:
                 raise RuntimeError("%s: VGPR count %d does not cover the register file (v%d..v%d)"
-                                   % (k, info[k]["vgprs"], RESERVED_BASE, need - 1))
-            if hi >= RESERVED_BASE:
+                                   % (k, info[k]["vgprs"], base, need - 1))
+            if hi >= base:
                 raise RuntimeError("%s: compiler-allocated code uses v%d (v%d+ hold the register file)"
-                                   % (k, hi, RESERVED_BASE))
+                                   % (k, hi, base))
             hz = index_mode_hazards(body)
             if hz:
                 raise RuntimeError("%s: VGPR index mode switched on while a load may be outstanding: %s"

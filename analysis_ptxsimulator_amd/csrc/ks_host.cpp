@@ -1237,7 +1237,9 @@ ks_status ks_query_layout(const ks_program* p, const ks_config* cfg, ks_layout* 
     out->warps_per_block = (uint32_t)((tpb + 31) / 32);
     out->n_warps = nb * out->warps_per_block;
     out->counters_bytes = out->n_warps * 80;
-    out->slot_bytes = 16 + 8 * (uint64_t)cfg->trace_cap;
+    if (cfg->trace_format != KS_TRACE_BASIC && cfg->trace_format != KS_TRACE_EXTENDED)
+      raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", cfg->trace_format);
+    out->slot_bytes = 16 + (cfg->trace_format == KS_TRACE_EXTENDED ? 16 : 8) * (uint64_t)cfg->trace_cap;
     out->trace_bytes = out->n_warps * out->slot_bytes;
     return KS_OK;
   });
@@ -1336,13 +1338,23 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       a.cyc_safe = span < limit ? (uint32_t)(limit - span) : 0u;
     }
     a.rf_slots = p->reg_slots + KS_IMM_SLOTS;
+    a.ext = st->cfg.trace_format == KS_TRACE_EXTENDED ? 1u : 0u;
+    // %tid.y and %tid.z divide the linear thread index (< 1024) by block sizes (<= 1024):
+    // (t * ceil(2^22 / d)) >> 22 == t / d over that range, with no 32-bit overflow
+    auto recip22 = [](uint64_t d) { return (uint32_t)(((1ull << 22) + d - 1) / d); };
+    a.div_bx = recip22(block.x);
+    a.div_by = recip22(block.y);
+    a.div_bxy = recip22((uint64_t)block.x * block.y);
     if (p->param_bytes) memcpy(a.params, params, p->param_bytes);
     uint64_t warps = nb * a.warps_per_block;
     if (warps > st->max_warps) raise(KS_E_INVALID_ARG, 0, "run needs more warps than the allocation");
     {
-      if (ks_choose_variant(p->reg_slots, a.threads_per_block) == 0)
-        raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots", p->reg_slots);
+      const int variant = ks_choose_variant(p->reg_slots, a.threads_per_block);
+      if (variant == 0) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots", p->reg_slots);
       const uint32_t wg = 64u * ((a.warps_per_block + 1u) / 2u);
+      if (wg > ks_max_block_threads(variant, a.ext != 0))
+        raise(KS_E_UNSUPPORTED, 0, "extended trace records with %u register slots support blocks of up to %u threads",
+              p->reg_slots, ks_max_block_threads(variant, true));
       const size_t need = ks_lds_bytes(wg, p->shared_bytes);
       if (need + 64 > ks_lds_limit())
         raise(KS_E_UNSUPPORTED, 0, "block of %u threads needs %zu bytes of LDS (limit %zu)", a.threads_per_block, need,

@@ -161,6 +161,8 @@ struct KsArgs {
   uint32_t rf_slots;       // register slots per simulated thread, immediate slots included
   uint32_t cyc_safe;       // a run may continue past its first instruction when that one issues
                            // at most at this cycle: RUN_MAX issues cannot then pass the cycle limit
+  uint32_t ext;            // 1: extended 16-byte trace records (KS_TRACE_EXTENDED)
+  uint32_t div_bx, div_by, div_bxy;  // ceil(2^22 / d) for d = block x, y and x * y (special registers)
   uint8_t params[KS_PARAM_MAX];
 };
 

@@ -91,88 +91,84 @@ __device__ __forceinline__ uint32_t s_eq_mask(uint32_t a, uint32_t b) {
 
 // ---------------------------------------------------------------------------- register files
 //
-// RFN = 40 / 72 physical VGPRs v56 .. v56+RFN-1, outside the compiler's
-// allocation, hold the register file: slot s of a lane is VGPR
-// v[56 + s] of that lane.  The kernels carry amdgpu_num_vgpr(28): on targets with
-// the unified VGPR/AGPR file the compiler doubles that figure, so v56 and up are
-// reserved (never allocated).  A figure the launch bound cannot honour is
-// silently ignored, which would hand v56+ back to the allocator; the build checks
-// the assembly for any compiler-written use of them and that the kernel's VGPR
-// count covers the file (the zero() clobber lists make the compiler count it).
+// RFN = 40 / 72 physical VGPRs vBASE .. vBASE+RFN-1, outside the compiler's
+// allocation, hold the register file: slot s of a lane is VGPR v[BASE + s] of
+// that lane.  The kernels carry amdgpu_num_vgpr(BASE / 2): on targets with the
+// unified VGPR/AGPR file the compiler doubles that figure, so vBASE and up are
+// reserved (never allocated).  BASE is 56 for the interpreters of the timed path
+// and 64 for the extended-trace variants, whose record payloads need more
+// compiler registers.  A figure the launch bound cannot honour is silently
+// ignored, which would hand vBASE+ back to the allocator; the build checks the
+// assembly for any compiler-written use of them and that the kernel's VGPR count
+// covers the file (the zero() clobber lists make the compiler count it).
 
-template <int RFN>
+template <int RFN, int BASE>
 struct RegFile;
 
 // VGPR index mode: between s_set_gpr_idx_on and s_set_gpr_idx_off the SRC0 (or
 // DST) VGPR operand of each VALU instruction is offset by the index held in M0;
-// s_set_gpr_idx_idx changes the index without leaving the mode.
-// First six VGPRs of the register file (RF_V0 = slot 0 before indexing).  The
-// build's RESERVED_BASE must name the same register.
-#define KS_RF_V0 "v56"
-#define KS_RF_V1 "v57"
-#define KS_RF_V2 "v58"
-#define KS_RF_V3 "v59"
-#define KS_RF_V4 "v60"
-#define KS_RF_V5 "v61"
-
-#define KS_RF_ASM_ACCESS                                                                           \
+// s_set_gpr_idx_idx changes the index without leaving the mode.  V0 .. V5 name
+// the first six VGPRs of the register file (V0 = slot 0 before indexing); the
+// build's reserved base of each kernel must name the same register.
+#define KS_RF_ASM_ACCESS(V0, V1, V2, V3, V4, V5)                                                                           \
   __device__ __forceinline__ uint32_t get(uint32_t s) const {                                      \
     uint32_t r;                                                                                    \
-    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, " KS_RF_V0                  \
+    asm volatile("s_set_gpr_idx_on %1, gpr_idx(SRC0)\n\tv_mov_b32 %0, " V0                  \
                  "\n\ts_set_gpr_idx_off"                                                          \
                  : "=v"(r) : "s"(s) : "m0");                                                      \
     return r;                                                                                      \
   }                                                                                                \
   __device__ __forceinline__ void get2(uint32_t i0, uint32_t i1, uint32_t& a, uint32_t& b) const {  \
-    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, " KS_RF_V0 "\n\t"          \
-                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, " KS_RF_V0 "\n\ts_set_gpr_idx_off"         \
+    asm volatile("s_set_gpr_idx_on %2, gpr_idx(SRC0)\n\tv_mov_b32 %0, " V0 "\n\t"          \
+                 "s_set_gpr_idx_idx %3\n\tv_mov_b32 %1, " V0 "\n\ts_set_gpr_idx_off"         \
                  : "=&v"(a), "=v"(b) : "s"(i0), "s"(i1) : "m0");                                  \
   }                                                                                                \
   __device__ __forceinline__ void get3(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t& a, uint32_t& b, \
                                        uint32_t& c) const {                                        \
-    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, " KS_RF_V0 "\n\t"          \
-                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, " KS_RF_V0 "\n\t"                          \
-                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, " KS_RF_V0 "\n\ts_set_gpr_idx_off"         \
+    asm volatile("s_set_gpr_idx_on %3, gpr_idx(SRC0)\n\tv_mov_b32 %0, " V0 "\n\t"          \
+                 "s_set_gpr_idx_idx %4\n\tv_mov_b32 %1, " V0 "\n\t"                          \
+                 "s_set_gpr_idx_idx %5\n\tv_mov_b32 %2, " V0 "\n\ts_set_gpr_idx_off"         \
                  : "=&v"(a), "=&v"(b), "=v"(c) : "s"(i0), "s"(i1), "s"(i2) : "m0");               \
   }                                                                                                \
   __device__ __forceinline__ void put(uint32_t s, uint32_t v) const {                              \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 " KS_RF_V0 ", %1"                 \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 " V0 ", %1"                 \
                  "\n\ts_set_gpr_idx_off"                                                          \
                  : : "s"(s), "v"(v) : "m0");                                                      \
   }                                                                                                \
   __device__ __forceinline__ void put2(uint32_t s, uint32_t lo, uint32_t hi) const {               \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 " KS_RF_V0 ", %1\n\t"           \
-                 "v_mov_b32 " KS_RF_V1 ", %2\n\ts_set_gpr_idx_off"                                 \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\tv_mov_b32 " V0 ", %1\n\t"           \
+                 "v_mov_b32 " V1 ", %2\n\ts_set_gpr_idx_off"                                 \
                  : : "s"(s), "v"(lo), "v"(hi) : "m0");                                            \
   }                                                                                                \
   /* slot s of the lanes in m takes v, the other lanes keep their value: SRC0 and DST */          \
   /* are both indexed, so v_cndmask reads the old value and writes the slot under full exec */    \
   __device__ __forceinline__ void put_m(uint32_t s, uint32_t v, uint64_t m) const {                \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(SRC0,DST)\n\tv_cndmask_b32_e64 " KS_RF_V0 ", "      \
-                 KS_RF_V0 ", %1, %2\n\ts_set_gpr_idx_off"                                          \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(SRC0,DST)\n\tv_cndmask_b32_e64 " V0 ", "      \
+                 V0 ", %1, %2\n\ts_set_gpr_idx_off"                                          \
                  : : "s"(s), "v"(v), "s"(m) : "m0");                                              \
   }                                                                                                \
   __device__ __forceinline__ void put2_m(uint32_t s, uint32_t lo, uint32_t hi, uint64_t m) const { \
-    asm volatile("s_set_gpr_idx_on %0, gpr_idx(SRC0,DST)\n\tv_cndmask_b32_e64 " KS_RF_V0 ", "      \
-                 KS_RF_V0 ", %1, %3\n\tv_cndmask_b32_e64 " KS_RF_V1 ", " KS_RF_V1 ", %2, %3\n\t"    \
+    asm volatile("s_set_gpr_idx_on %0, gpr_idx(SRC0,DST)\n\tv_cndmask_b32_e64 " V0 ", "      \
+                 V0 ", %1, %3\n\tv_cndmask_b32_e64 " V1 ", " V1 ", %2, %3\n\t"    \
                  "s_set_gpr_idx_off"                                                               \
                  : : "s"(s), "v"(lo), "v"(hi), "s"(m) : "m0");                                    \
   }                                                                                                \
   __device__ __forceinline__ void put_imm(uint32_t ib, const uint32_t* v) const {                  \
     asm volatile("s_set_gpr_idx_on %0, gpr_idx(DST)\n\t"                                           \
-                 "v_mov_b32 " KS_RF_V0 ", %1\n\tv_mov_b32 " KS_RF_V1 ", %2\n\t"                     \
-                 "v_mov_b32 " KS_RF_V2 ", %3\n\tv_mov_b32 " KS_RF_V3 ", %4\n\t"                     \
-                 "v_mov_b32 " KS_RF_V4 ", %5\n\tv_mov_b32 " KS_RF_V5 ", %6\n\t"                     \
+                 "v_mov_b32 " V0 ", %1\n\tv_mov_b32 " V1 ", %2\n\t"                     \
+                 "v_mov_b32 " V2 ", %3\n\tv_mov_b32 " V3 ", %4\n\t"                     \
+                 "v_mov_b32 " V4 ", %5\n\tv_mov_b32 " V5 ", %6\n\t"                     \
                  "s_set_gpr_idx_off"                                                               \
                  : : "s"(ib), "s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5])     \
                  : "m0");                                                                          \
   }
 
 template <>
-struct RegFile<40> {
-  KS_RF_ASM_ACCESS
+struct RegFile<40, 56> {
+  KS_RF_ASM_ACCESS("v56", "v57", "v58", "v59", "v60", "v61")
   __device__ __forceinline__ static void zero() {
-    asm volatile("v_mov_b32 v56, 0\n\t""v_mov_b32 v57, 0\n\t""v_mov_b32 v58, 0\n\t""v_mov_b32 v59, 0\n\t"
+    asm volatile(
+                 "v_mov_b32 v56, 0\n\t""v_mov_b32 v57, 0\n\t""v_mov_b32 v58, 0\n\t""v_mov_b32 v59, 0\n\t"
                  "v_mov_b32 v60, 0\n\t""v_mov_b32 v61, 0\n\t""v_mov_b32 v62, 0\n\t""v_mov_b32 v63, 0\n\t"
                  "v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t"
                  "v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t"
@@ -192,10 +188,11 @@ struct RegFile<40> {
 };
 
 template <>
-struct RegFile<72> {
-  KS_RF_ASM_ACCESS
+struct RegFile<72, 56> {
+  KS_RF_ASM_ACCESS("v56", "v57", "v58", "v59", "v60", "v61")
   __device__ __forceinline__ static void zero() {
-    asm volatile("v_mov_b32 v56, 0\n\t""v_mov_b32 v57, 0\n\t""v_mov_b32 v58, 0\n\t""v_mov_b32 v59, 0\n\t"
+    asm volatile(
+                 "v_mov_b32 v56, 0\n\t""v_mov_b32 v57, 0\n\t""v_mov_b32 v58, 0\n\t""v_mov_b32 v59, 0\n\t"
                  "v_mov_b32 v60, 0\n\t""v_mov_b32 v61, 0\n\t""v_mov_b32 v62, 0\n\t""v_mov_b32 v63, 0\n\t"
                  "v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t"
                  "v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t"
@@ -223,6 +220,66 @@ struct RegFile<72> {
                  "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111",
                  "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119",
                  "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127");
+  }
+};
+
+template <>
+struct RegFile<40, 64> {
+  KS_RF_ASM_ACCESS("v64", "v65", "v66", "v67", "v68", "v69")
+  __device__ __forceinline__ static void zero() {
+    asm volatile(
+                 "v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t"
+                 "v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t"
+                 "v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t"
+                 "v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t"
+                 "v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t"
+                 "v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t"
+                 "v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t"
+                 "v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t"
+                 "v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t"
+                 "v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t"
+                 :::
+                 "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71",
+                 "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79",
+                 "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87",
+                 "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95",
+                 "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103");
+  }
+};
+
+template <>
+struct RegFile<72, 64> {
+  KS_RF_ASM_ACCESS("v64", "v65", "v66", "v67", "v68", "v69")
+  __device__ __forceinline__ static void zero() {
+    asm volatile(
+                 "v_mov_b32 v64, 0\n\t""v_mov_b32 v65, 0\n\t""v_mov_b32 v66, 0\n\t""v_mov_b32 v67, 0\n\t"
+                 "v_mov_b32 v68, 0\n\t""v_mov_b32 v69, 0\n\t""v_mov_b32 v70, 0\n\t""v_mov_b32 v71, 0\n\t"
+                 "v_mov_b32 v72, 0\n\t""v_mov_b32 v73, 0\n\t""v_mov_b32 v74, 0\n\t""v_mov_b32 v75, 0\n\t"
+                 "v_mov_b32 v76, 0\n\t""v_mov_b32 v77, 0\n\t""v_mov_b32 v78, 0\n\t""v_mov_b32 v79, 0\n\t"
+                 "v_mov_b32 v80, 0\n\t""v_mov_b32 v81, 0\n\t""v_mov_b32 v82, 0\n\t""v_mov_b32 v83, 0\n\t"
+                 "v_mov_b32 v84, 0\n\t""v_mov_b32 v85, 0\n\t""v_mov_b32 v86, 0\n\t""v_mov_b32 v87, 0\n\t"
+                 "v_mov_b32 v88, 0\n\t""v_mov_b32 v89, 0\n\t""v_mov_b32 v90, 0\n\t""v_mov_b32 v91, 0\n\t"
+                 "v_mov_b32 v92, 0\n\t""v_mov_b32 v93, 0\n\t""v_mov_b32 v94, 0\n\t""v_mov_b32 v95, 0\n\t"
+                 "v_mov_b32 v96, 0\n\t""v_mov_b32 v97, 0\n\t""v_mov_b32 v98, 0\n\t""v_mov_b32 v99, 0\n\t"
+                 "v_mov_b32 v100, 0\n\t""v_mov_b32 v101, 0\n\t""v_mov_b32 v102, 0\n\t""v_mov_b32 v103, 0\n\t"
+                 "v_mov_b32 v104, 0\n\t""v_mov_b32 v105, 0\n\t""v_mov_b32 v106, 0\n\t""v_mov_b32 v107, 0\n\t"
+                 "v_mov_b32 v108, 0\n\t""v_mov_b32 v109, 0\n\t""v_mov_b32 v110, 0\n\t""v_mov_b32 v111, 0\n\t"
+                 "v_mov_b32 v112, 0\n\t""v_mov_b32 v113, 0\n\t""v_mov_b32 v114, 0\n\t""v_mov_b32 v115, 0\n\t"
+                 "v_mov_b32 v116, 0\n\t""v_mov_b32 v117, 0\n\t""v_mov_b32 v118, 0\n\t""v_mov_b32 v119, 0\n\t"
+                 "v_mov_b32 v120, 0\n\t""v_mov_b32 v121, 0\n\t""v_mov_b32 v122, 0\n\t""v_mov_b32 v123, 0\n\t"
+                 "v_mov_b32 v124, 0\n\t""v_mov_b32 v125, 0\n\t""v_mov_b32 v126, 0\n\t""v_mov_b32 v127, 0\n\t"
+                 "v_mov_b32 v128, 0\n\t""v_mov_b32 v129, 0\n\t""v_mov_b32 v130, 0\n\t""v_mov_b32 v131, 0\n\t"
+                 "v_mov_b32 v132, 0\n\t""v_mov_b32 v133, 0\n\t""v_mov_b32 v134, 0\n\t""v_mov_b32 v135, 0\n\t"
+                 :::
+                 "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71",
+                 "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79",
+                 "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87",
+                 "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95",
+                 "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103",
+                 "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111",
+                 "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119",
+                 "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127",
+                 "v128", "v129", "v130", "v131", "v132", "v133", "v134", "v135");
   }
 };
 
@@ -335,7 +392,9 @@ __device__ __forceinline__ void stk_push(Stk& S, uint32_t top_mask, uint32_t pc,
 
 // ---------------------------------------------------------------------------- the interpreter
 
-template <int RFN>
+// EXT: extended 16-byte trace records (kind, active mask, payload) written from
+// each step, instead of the staged 8-byte {issue cycle, pc} records.
+template <int RFN, bool EXT>
 __device__ __forceinline__ void interp(const KsArgs& a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ uint32_t ep_max[3], ep_alive[3];
@@ -355,8 +414,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t ib = a.rf_slots - KS_IMM_SLOTS;  // first immediate slot
 
   // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] [shared window]
-  RegFile<RFN> R;
-  RegFile<RFN>::zero();
+  RegFile<RFN, EXT ? 64 : 56> R;
+  RegFile<RFN, EXT ? 64 : 56>::zero();
   uint32_t* const sbw = lds;
   uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
   uint8_t* const win = dump_sb + 4u * KS_SB_ENTRIES;
@@ -402,7 +461,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   uint32_t wi = 0;            // warp: issued warp-instructions
   uint32_t fl = 0;            // warp: trace records written to memory
   // warp: record count at which the next chunk is written (from the records written so far)
-  auto next_flush = [&](uint32_t written) -> uint32_t { return written < cap ? umin(cap, written + 32u) : INF; };
+  auto next_flush = [&](uint32_t written) -> uint32_t {
+    if constexpr (EXT) return INF;  // extended records are written as they are issued
+    return written < cap ? umin(cap, written + 32u) : INF;
+  };
   uint32_t ev = umin(next_flush(0), budget);      // warp: next event (chunk write or budget)
   uint32_t act = 0;           // instructions issued with this lane's thread active (see KS_SET_LIVE)
   uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
@@ -490,7 +552,18 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const uint32_t fn_ = (f_ && prev == 0u) ? 1u : 0u;                            \
       const uint32_t fs_ = (f_ && sid1 != prev) ? 1u : 0u;                          \
       const uint32_t fl_ = (f_ && (prev == 0u || ((sid1 - 1u) >> 2) != ((prev - 1u) >> 2))) ? 1u : 0u; \
-      if (is_load) {                                                                \
+      if constexpr (EXT) {                                                          \
+        /* the per-warp counts of this access go into the record and the counters */ \
+        const uint64_t bs_ = ballot(fs_ != 0u), bl_ = ballot(fl_ != 0u);            \
+        const uint32_t s0_ = popc((uint32_t)bs_), s1_ = popc((uint32_t)(bs_ >> 32)); \
+        const uint32_t l0_ = popc((uint32_t)bl_), l1_ = popc((uint32_t)(bl_ >> 32)); \
+        x_sl0 = s0_ | (l0_ << 8);                                                   \
+        x_sl1 = s1_ | (l1_ << 8);                                                   \
+        /* counters n, sectors, lines of the lane's warp when its half took this path */ \
+        const uint32_t d_ = sl - ((is_load) ? C_GLD_N : C_GST_N);                   \
+        const bool fh_ = hl ? (fast >> 32) != 0 : (uint32_t)fast != 0;              \
+        if (fh_ && d_ < 3u) cnt += d_ == 0 ? 1u : (d_ == 1 ? (hl ? s1_ : s0_) : (hl ? l1_ : l0_)); \
+      } else if (is_load) {                                                         \
         q_ln += fn_;                                                                \
         q_ls += fs_;                                                                \
         q_ll += fl_;                                                                \
@@ -517,6 +590,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const uint32_t d = sl - cn;                                                   \
       const uint32_t eh = hl ? e1 : e0;                                             \
       if (eh && d < 3u) cnt += d == 0 ? 1u : (d == 1 ? (hl ? sec1 : sec0) : (hl ? lin1 : lin0)); \
+      if constexpr (EXT) {                                                          \
+        if (e0) x_sl0 = sec0 | (lin0 << 8);                                         \
+        if (e1) x_sl1 = sec1 | (lin1 << 8);                                         \
+      }                                                                             \
     }                                                                               \
   }
 
@@ -527,12 +604,27 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   // write a scratch scoreboard instead).
 #define KS_ISSUE(is_, p_, sbod_, lat_)                                               \
   {                                                                                 \
-    const bool tr_ = sl == ((wi & 31u) | tnm);                                      \
-    tr_c = tr_ ? (is_) : tr_c;                                                      \
-    tr_p = tr_ ? (p_) : tr_p;                                                       \
+    if constexpr (!EXT) {                                                           \
+      const bool tr_ = sl == ((wi & 31u) | tnm);                                    \
+      tr_c = tr_ ? (is_) : tr_c;                                                    \
+      tr_p = tr_ ? (p_) : tr_p;                                                     \
+    }                                                                               \
     wi += ginc;                                                                     \
     v_next = gl ? (is_) + 1u : v_next;                                              \
     *reinterpret_cast<uint32_t*>(sb_sel + (sbod_)) = (is_) + (lat_);                 \
+  }
+
+  // Extended trace record of the instruction just issued by the warps of gm (after
+  // KS_ISSUE: it is the warp's record wi - 1), written by the first lane of each
+  // issuing half: issue cycle, pc | kind << 16, the warp's live lanes, payload.
+#define KS_EXT_REC(is_, pc_, kind_, pay_)                                            \
+  if constexpr (EXT) {                                                              \
+    const uint32_t k_ = wi - 1u;                                                    \
+    if (gl && sl == 0u && k_ < cap) {                                               \
+      uint2* const r_ = reinterpret_cast<uint2*>(slot_base + 16ull * k_);           \
+      r_[0] = make_uint2((is_), (pc_) | ((uint32_t)(kind_) << 16));                 \
+      r_[1] = make_uint2(hl ? (uint32_t)(mm >> 32) : (uint32_t)mm, (pay_));         \
+    }                                                                               \
   }
 
   // Issue cycle of the instruction whose hot words are h: the later of the warp's
@@ -541,9 +633,6 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 #define KS_ISSUE_CYCLE(h)                                                            \
   umax(umax(v_next, sb_at((h)[6])), umax(umax(sb_at((h)[7]), sb_at((h)[8])), sb_at((h)[9])))
 
-  // value of a 32-bit global load (kept across steps so that a new load does not wait
-  // for an earlier write of the register to retire)
-  uint32_t ld_v = 0;
   uint32_t epoch = 0;
   while (true) {
     // ------------------------------------------------------------------ run both warps until blocked
@@ -652,7 +741,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             KS_SET_LIVE(mask64 & ~ex64);
             cnt = cnt_add2(cnt, sl, hl, C_DIV, divm, 1u);
           }
+          KS_EXT_REC(iss, pc, ((divm >> hl) & 1u) ? KS_EV_DIVERGE : KS_EV_BRANCH, (hl ? (uint32_t)(on64 >> 32) : (uint32_t)on64));
         } else if (ctl & CB(DC_RET)) {
+          KS_EXT_REC(iss, pc, KS_EV_RET, (hl ? (uint32_t)(on64 >> 32) : (uint32_t)on64));
           ex64 |= on64;
           KS_SET_LIVE(mask64 & ~ex64);
           if (go0) {
@@ -666,6 +757,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             need |= (uint32_t)(m64 >> 32) == 0 ? 2u : 0u;
           }
         } else {  // DC_BAR: the issuing warps wait for the block
+          KS_EXT_REC(iss, pc, KS_EV_BARRIER, 0u);
           const uint64_t conv = init64 & ~ex64;
           const uint32_t hm = (go0 & 1u) | (go1 & 2u);
           cnt = cnt_add2(cnt, sl, hl, C_BAR, hm, 1u);
@@ -726,6 +818,11 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               prog_b + off + 2u * (uint32_t)sizeof(DInst));
           KS_ISSUE(is, off / (uint32_t)sizeof(DInst), h[10], h[11]);
           const uint64_t on64 = mm & ballot(((pbits >> h[12]) & 1u) != h[13]);  // guard
+          // extended record of a non-memory instruction: the lanes passing the guard
+          // (memory instructions write theirs after the access is analysed)
+          if constexpr (EXT)
+            if (!(c & (CB(DC_LDG) | CB(DC_STG) | CB_MEM)))
+              KS_EXT_REC(is, off / (uint32_t)sizeof(DInst), KS_EV_OTHER, (hl ? (uint32_t)(on64 >> 32) : (uint32_t)on64));
           if (c & XF_IMM) {
             uint32_t iv[6];
             for (int k = 0; k < 6; ++k) iv[k] = *reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
@@ -755,8 +852,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             const uint64_t A = (((uint64_t)bhi << 32) | blo) + (((uint64_t)a1 << 32) | a0);
             const uint64_t okm = ballot(((uint32_t)A & 3u) == 0u) & ballot(A < glim4) & on64;
             const uint64_t faults = on64 & ~okm;
+            [[maybe_unused]] uint32_t x_sl0 = 0, x_sl1 = 0;  // sectors | lines << 8 of each warp (extended records)
             if (c & CB(DC_LDG)) {
               if (faults) R.put_m(dst, 0u, faults);  // lanes without a valid access read 0
+              // the loaded value; lanes outside okm are never written to the register,
+              // so the register starts with whatever it holds (no write that the load
+              // would have to wait for)
+              uint32_t ld_v;
+              asm volatile("" : "=v"(ld_v));
               if (lanes(okm)) ld_v = *reinterpret_cast<const uint32_t*>(a.gmem + A);
               // The accounting needs only the addresses: it runs while the load is in
               // flight.  Nothing in it uses VGPR index mode, which must stay off while
@@ -769,6 +872,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               if (lanes(okm)) *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
               KS_COUNT_FAULTS(faults);
               KS_GLOBAL_ACCOUNT(A, 4u, faults, false);
+            }
+            if constexpr (EXT) {
+              const uint32_t p0 = x_sl0 | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
+              const uint32_t p1 = x_sl1 | (popc((uint32_t)(on64 >> 32)) << 16) | (popc((uint32_t)(faults >> 32)) << 24);
+              KS_EXT_REC(is, off / (uint32_t)sizeof(DInst), (c & CB(DC_LDG)) ? KS_EV_LD_GLOBAL : KS_EV_ST_GLOBAL,
+                         hl ? p1 : p0);
             }
           } else if (c & CB(DC_MOV)) {
             if (a0) {
@@ -845,7 +954,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             const uint32_t w64 = c & XF_W64;
             const uint32_t S = w64 ? 8u : 4u;
             const uint64_t size = is_global ? a.gmem_bytes : (uint64_t)a.shared_bytes;
-            const uint64_t off = (uint64_t)a0 | ((uint64_t)a1 << 32);
+            const uint64_t aoff = (uint64_t)a0 | ((uint64_t)a1 << 32);  // byte offset of the address
             uint64_t base;
             if (c & XF_A64) {
               uint32_t lo, hi;
@@ -854,7 +963,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             } else {
               base = R.get(s0);
             }
-            const uint64_t A = base + off;
+            const uint64_t A = base + aoff;
             const uint64_t okm = ballot((A & (S - 1u)) == 0 && A <= size && size - A >= S) & on64;
             if (is_load) {
               uint32_t lo = 0, hi = 0;
@@ -892,8 +1001,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             }
             const uint64_t faults = on64 & ~okm;
             KS_COUNT_FAULTS(faults);
+            [[maybe_unused]] uint32_t x_sl0 = 0, x_sl1 = 0;
             if (is_global) {
               KS_GLOBAL_ACCOUNT(A, S, faults, is_load);
+              if constexpr (EXT) {
+                const uint32_t p0 = x_sl0 | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
+                const uint32_t p1 = x_sl1 | (popc((uint32_t)(on64 >> 32)) << 16) | (popc((uint32_t)(faults >> 32)) << 24);
+                KS_EXT_REC(is, off / (uint32_t)sizeof(DInst), is_load ? KS_EV_LD_GLOBAL : KS_EV_ST_GLOBAL, hl ? p1 : p0);
+              }
             } else {
               const uint32_t g0 = (uint32_t)on64, g1 = (uint32_t)(on64 >> 32);
               const uint32_t hm = (g0 ? 1u : 0u) | (g1 ? 2u : 0u);  // warps with participating lanes
@@ -924,16 +1039,28 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
                 if (sl == C_SH_SUM) cnt += dh;
                 if (sl == C_SH_MAX) cnt = umax(cnt, dh);
               }
+              if constexpr (EXT) {
+                const uint32_t p0 = ((hm & 1u) ? d0 : 0u) | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
+                const uint32_t p1 = ((hm & 2u) ? d1 : 0u) | (popc((uint32_t)(on64 >> 32)) << 16) |
+                                    (popc((uint32_t)(faults >> 32)) << 24);
+                KS_EXT_REC(is, off / (uint32_t)sizeof(DInst), is_load ? KS_EV_LD_SHARED : KS_EV_ST_SHARED, hl ? p1 : p0);
+              }
             }
           } else if (c & CB(DC_MOVSP)) {
-            const uint32_t t_lin = my_w * 32u + sl;
+            // t / bx and t / (bx by) as (t * m) >> 22 with m = ceil(2^22 / d) from the
+            // host: exact for t < 1024 and d <= 1024, and cheaper than a division.  The
+            // empty asm keeps these per-lane values here: hoisted out of the loop they
+            // would hold registers for the whole run.
+            uint32_t t_lin = my_w * 32u + sl;
+            asm volatile("" : "+v"(t_lin));
             const uint32_t bx = a.block[0], by = a.block[1];
             const uint32_t gx = a.grid[0], gy = a.grid[1];
+            const uint32_t qx = (t_lin * a.div_bx) >> 22;  // t / bx
             uint32_t v;
             switch (a0) {
-              case KSP_TID_X: v = t_lin % bx; break;
-              case KSP_TID_Y: v = (t_lin / bx) % by; break;
-              case KSP_TID_Z: v = t_lin / (bx * by); break;
+              case KSP_TID_X: v = t_lin - qx * bx; break;
+              case KSP_TID_Y: v = qx - ((qx * a.div_by) >> 22) * by; break;
+              case KSP_TID_Z: v = (t_lin * a.div_bxy) >> 22; break;
               case KSP_NTID_X: v = a.block[0]; break;
               case KSP_NTID_Y: v = a.block[1]; break;
               case KSP_NTID_Z: v = a.block[2]; break;
@@ -946,9 +1073,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               default: v = sl; break;
             }
             R.put_m(dst, v, on64);
-          } else {  // DC_LDP: a uniform value from the launch arguments
-            const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.params + a0);
-            if (a1) R.put2_m(dst, lo, *reinterpret_cast<const uint32_t*>(a.params + a0 + 4u), on64);
+          } else {  // DC_LDP: a uniform value from the launch arguments (scalar loads)
+            typedef const __attribute__((address_space(4))) uint32_t* cword;
+            const uint32_t lo = *(cword)(a.params + a0);
+            if (a1) R.put2_m(dst, lo, *(cword)(a.params + a0 + 4u), on64);
             else R.put_m(dst, lo, on64);
           }
           // the next record (the end sentinel at the latest: a run never includes it)
@@ -1029,9 +1157,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const uint32_t written = umin(wi, cap);
       const uint32_t dropped = wi - written;
       const uint32_t st = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);
-      const uint64_t gw = gw0 + hl;
-      // records staged since the last chunk write
-      if (sl < written - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+      // this lane's warp, recomputed here (kept from the start it would hold two
+      // registers through the whole run)
+      uint32_t hl_e = hl;
+      asm volatile("" : "+v"(hl_e));
+      const uint64_t gw = gw0 + hl_e;
+      // records staged since the last chunk write (extended records are already written)
+      if constexpr (!EXT)
+        if (sl < written - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
       if (sl < 20) {
         uint32_t v;
         switch (sl) {
@@ -1053,7 +1186,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         uint32_t v;
         switch (sl) {
           case 0: v = written; break;
-          case 1: v = 1u | (flags << 8) | ((w & 0xFFFFu) << 16); break;
+          case 1: v = (EXT ? 2u : 1u) | (flags << 8) | ((w & 0xFFFFu) << 16); break;  // version: record format
           case 2: v = dropped; break;
           default: v = 0; break;
         }
@@ -1068,13 +1201,23 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 // Register file in 40 reserved VGPRs (v56..v95): 96 VGPRs, 5 waves per SIMD,
 // blocks up to 1024 threads.
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v32(const KsArgs a) {
-  interp<40>(a);
+  interp<40, false>(a);
 }
 
 // Register file in 72 reserved VGPRs (v56..v127): 128 VGPRs, 4 waves per SIMD,
 // blocks up to 1024 threads.
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v64(const KsArgs a) {
-  interp<72>(a);
+  interp<72, false>(a);
+}
+
+// The same interpreters writing extended 16-byte trace records, with 64 compiler
+// VGPRs and the register file from v64: 104 VGPRs (4 waves per SIMD, blocks up to
+// 1024 threads) and 136 (3 waves per SIMD, so blocks up to 768 threads).
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v32_ext(const KsArgs a) {
+  interp<40, true>(a);
+}
+__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64_ext(const KsArgs a) {
+  interp<72, true>(a);
 }
 
 __global__ void ks_zero_word(uint32_t* out) { *out = 0; }
@@ -1104,6 +1247,8 @@ int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
   return 0;
 }
 
+uint32_t ks_max_block_threads(int variant, bool ext) { return (ext && variant == 64) ? 768u : 1024u; }
+
 size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes) {
   const size_t sb = (size_t)(wg / 32u + 1u) * KS_SB_ENTRIES * 4u;  // the warps' scoreboards and a scratch one
   return sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
@@ -1114,18 +1259,24 @@ hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, 
   const uint32_t wg = 64u * waves;
   const int variant = ks_choose_variant(slots, a.threads_per_block);
   const size_t lds = ks_lds_bytes(wg, a.shared_bytes);
-  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > 1024) return hipErrorInvalidValue;
+  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0))
+    return hipErrorInvalidValue;
   if (a.rf_slots != slots + KS_IMM_SLOTS) return hipErrorInvalidValue;
-  const void* fn = variant == 32 ? (const void*)ks_interp_v32 : (const void*)ks_interp_v64;
-  static bool attr_set[2] = {false, false};
-  const int vi = variant == 32 ? 0 : 1;
+  const int vi = (variant == 32 ? 0 : 1) + (a.ext ? 2 : 0);
+  const void* const fns[4] = {(const void*)ks_interp_v32, (const void*)ks_interp_v64, (const void*)ks_interp_v32_ext,
+                              (const void*)ks_interp_v64_ext};
+  static bool attr_set[4] = {false, false, false, false};
   if (!attr_set[vi]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(ks_lds_limit() - 64));
+    hipError_t e = hipFuncSetAttribute(fns[vi], hipFuncAttributeMaxDynamicSharedMemorySize, (int)(ks_lds_limit() - 64));
     if (e != hipSuccess) return e;
     attr_set[vi] = true;
   }
-  if (variant == 32) hipLaunchKernelGGL(ks_interp_v32, dim3(n_blocks), dim3(wg), lds, s, a);
-  else hipLaunchKernelGGL(ks_interp_v64, dim3(n_blocks), dim3(wg), lds, s, a);
+  switch (vi) {
+    case 0: hipLaunchKernelGGL(ks_interp_v32, dim3(n_blocks), dim3(wg), lds, s, a); break;
+    case 1: hipLaunchKernelGGL(ks_interp_v64, dim3(n_blocks), dim3(wg), lds, s, a); break;
+    case 2: hipLaunchKernelGGL(ks_interp_v32_ext, dim3(n_blocks), dim3(wg), lds, s, a); break;
+    default: hipLaunchKernelGGL(ks_interp_v64_ext, dim3(n_blocks), dim3(wg), lds, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -19,5 +19,9 @@ size_t ks_lds_limit();
 // VGPRs) or 64 (72 reserved VGPRs), immediate slots included; 0 if neither fits.
 int ks_choose_variant(uint32_t slots, uint32_t block_threads);
 
+// Largest block the interpreter variant can run: 1024 threads, except the
+// extended-trace variant with the 72-VGPR file (136 VGPRs: 768 threads).
+uint32_t ks_max_block_threads(int variant, bool ext);
+
 // Dynamic LDS bytes of one workgroup of `wg` lanes (scoreboards and the shared window).
 size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes);

@@ -27,6 +27,13 @@ COUNTER_DTYPE = np.dtype([
 ])
 TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("flags", "u1"),
                                ("warp_in_block", "<u2"), ("records_dropped", "<u8")])
+# trace formats (ks_config.trace_format) and the 16-byte extended record
+KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
+EXT_RECORD_DTYPE = np.dtype([("cycle", "<u4"), ("pc", "<u2"), ("kind", "u1"), ("reserved", "u1"),
+                             ("active", "<u4"), ("payload", "<u4")])
+EV_NAMES = ["other", "ld.global", "st.global", "ld.shared", "st.shared", "branch", "diverge", "barrier", "ret"]
+(KS_EV_OTHER, KS_EV_LD_GLOBAL, KS_EV_ST_GLOBAL, KS_EV_LD_SHARED, KS_EV_ST_SHARED, KS_EV_BRANCH, KS_EV_DIVERGE,
+ KS_EV_BARRIER, KS_EV_RET) = range(9)
 
 
 class KsError(RuntimeError):
@@ -43,7 +50,8 @@ class ks_dim3(ctypes.Structure):
 class ks_config(ctypes.Structure):
     _fields_ = [("max_grid", ks_dim3), ("max_block", ks_dim3), ("gmem_bytes", ctypes.c_uint64),
                 ("trace_cap", ctypes.c_uint32), ("max_warp_instrs", ctypes.c_uint32),
-                ("latency", ctypes.c_uint16 * KS_NLAT)]
+                ("latency", ctypes.c_uint16 * KS_NLAT), ("trace_format", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
 
 
 class ks_program_desc(ctypes.Structure):
@@ -201,13 +209,17 @@ def ks_last_error():
     return lib().ks_last_error().decode(errors="replace")
 
 
-def trace_slots(trace, trace_cap):
-    """Split trace slot bytes into (headers, records[warp, cap, 2])."""
-    slot = 16 + 8 * trace_cap
+def trace_slots(trace, trace_cap, trace_format=KS_TRACE_BASIC):
+    """Split trace slot bytes into (headers, records): records[warp, cap, 2] u32 for
+    the basic format, records[warp, cap] of EXT_RECORD_DTYPE for the extended one."""
+    rec = 16 if trace_format == KS_TRACE_EXTENDED else 8
+    slot = 16 + rec * trace_cap
     t = trace.reshape(-1, slot)
     hdr = t[:, :16].copy().view(TRACE_HEADER_DTYPE).reshape(-1)
-    rec = t[:, 16:].copy().view("<u4").reshape(t.shape[0], trace_cap, 2)
-    return hdr, rec
+    body = t[:, 16:].copy()
+    if trace_format == KS_TRACE_EXTENDED:
+        return hdr, body.view(EXT_RECORD_DTYPE).reshape(t.shape[0], trace_cap)
+    return hdr, body.view("<u4").reshape(t.shape[0], trace_cap, 2)
 
 
 # ---------------------------------------------------------------- device-memory plumbing
@@ -219,7 +231,7 @@ class Session:
     Memory management only; all simulation work happens in ks_run."""
 
     def __init__(self, ptx, grid, block, gmem_bytes, trace_cap=0, max_warp_instrs=0xFFFFFFFF, latency=None,
-                 device="cuda:0", entry=None):
+                 device="cuda:0", entry=None, trace_format=KS_TRACE_BASIC):
         import torch
         self.torch = torch
         self.device = torch.device(device)
@@ -231,6 +243,9 @@ class Session:
         cfg.gmem_bytes = int(gmem_bytes)
         cfg.trace_cap = int(trace_cap)
         cfg.max_warp_instrs = int(max_warp_instrs)
+        cfg.trace_format = int(trace_format)
+        self.trace_format = int(trace_format)
+        self.trace_cap = int(trace_cap)
         if latency is not None:
             lat = list(latency) + [0] * (KS_NLAT - len(latency))
             cfg.latency[:] = lat
@@ -275,6 +290,15 @@ class Session:
 
     def status(self):
         return ks_run_status(self.state, self.stream_ptr())
+
+    def trace_records(self, first=0, n=None):
+        """(headers, records) of the last run's trace slots (see trace_slots)."""
+        return trace_slots(self.read_trace(first, n), self.trace_cap, self.trace_format)
+
+    def kernel_name(self):
+        """Name of the interpreter kernel ks_run launches for this session."""
+        name = ks_interp_kernel(self.prog, self.block)
+        return name + ("_ext" if self.trace_format == KS_TRACE_EXTENDED else "")
 
     def close(self):
         if getattr(self, "state", None):

@@ -10,7 +10,11 @@
  *   - a memory analyser (32-byte sectors and 128-byte lines per global warp
  *     access, the bank-conflict degree over 32 four-byte banks per shared warp
  *     access).
- * It also writes a per-warp trace of {issue cycle, pc} records.
+ * It also writes a per-warp trace: {issue cycle, pc} records, or (extended
+ * format) 16-byte records that add the instruction kind, the active mask and a
+ * per-kind payload (sectors and lines of a global access, bank-conflict degree of
+ * a shared access, the lanes taking a branch).  Extended records for programs of
+ * more than 34 register slots support blocks of up to 768 threads.
  *
  * Sources of the semantics, by page and section:
  *   - KernelScope backend documentation (github.com/briefgaming/kernelscope).
@@ -74,6 +78,32 @@ enum {
   KS_LAT_ST_GLOBAL = 9, KS_LAT_ST_SHARED = 10, KS_LAT_BRA = 11, KS_LAT_BAR = 12, KS_LAT_RET = 13
 };
 
+/* Trace record formats (ks_config.trace_format).  Both follow the IKET page's
+ * per-warp slot: a 16-byte header {u32 records_written, u8 version, u8 flags,
+ * u16 warp_in_block, u64 records_dropped}, then trace_cap fixed-size records;
+ * the header's version byte names the format (1 or 2).
+ *   KS_TRACE_BASIC     8-byte records {u32 issue_cycle, u32 pc}.
+ *   KS_TRACE_EXTENDED  16-byte records {u32 issue_cycle, u16 pc, u8 kind,
+ *                      u8 reserved (0), u32 active, u32 payload}: `active` is the
+ *                      warp's live-lane mask at issue (bit l = lane l), `kind` a
+ *                      KS_EV_* value, and `payload` depends on the kind:
+ *     KS_EV_LD_GLOBAL / KS_EV_ST_GLOBAL: bits 0-7 distinct 32-byte sectors,
+ *         bits 8-15 distinct 128-byte lines, bits 16-23 lanes passing the guard,
+ *         bits 24-31 lanes whose access faulted (all 0 when no lane passes);
+ *     KS_EV_LD_SHARED / KS_EV_ST_SHARED: bits 0-7 bank-conflict degree (0 when
+ *         no lane passes), bits 16-23 lanes passing the guard, bits 24-31 faults;
+ *     KS_EV_BRANCH / KS_EV_DIVERGE: the lanes taking the branch (DIVERGE when the
+ *         warp split: some but not all live lanes take it);
+ *     KS_EV_BARRIER: 0;
+ *     KS_EV_OTHER / KS_EV_RET: the lanes passing the guard.
+ *   Stall cycles are the gaps between consecutive records' issue cycles. */
+#define KS_TRACE_BASIC 0u
+#define KS_TRACE_EXTENDED 1u
+enum {
+  KS_EV_OTHER = 0, KS_EV_LD_GLOBAL = 1, KS_EV_ST_GLOBAL = 2, KS_EV_LD_SHARED = 3, KS_EV_ST_SHARED = 4,
+  KS_EV_BRANCH = 5, KS_EV_DIVERGE = 6, KS_EV_BARRIER = 7, KS_EV_RET = 8
+};
+
 /* Limits of this build. */
 #define KS_MAX_REG_SLOTS 64      /* 32-bit register slots per thread (a 64-bit register takes 2) */
 #define KS_MAX_PREDS 32          /* predicate registers */
@@ -93,6 +123,8 @@ typedef struct {
   uint32_t trace_cap;        /* trace records per warp slot; 0 = headers only */
   uint32_t max_warp_instrs;  /* per-warp issue budget; a warp reaching it stops with KS_ST_BUDGET */
   uint16_t latency[KS_NLAT]; /* cycles per latency class (ks_default_config fills sm_80 values) */
+  uint32_t trace_format;     /* KS_TRACE_BASIC (default) or KS_TRACE_EXTENDED */
+  uint32_t reserved;         /* 0 */
 } ks_config;
 
 typedef struct {
@@ -109,7 +141,7 @@ typedef struct {
   uint32_t reserved;
   uint64_t n_warps;          /* warps of the largest grid: max blocks * warps_per_block */
   uint64_t counters_bytes;   /* n_warps * 80: size of d_counters */
-  uint64_t slot_bytes;       /* 16 + 8 * trace_cap: one trace slot */
+  uint64_t slot_bytes;       /* 16 + 8 * trace_cap (basic) or 16 + 16 * trace_cap (extended): one slot */
   uint64_t trace_bytes;      /* n_warps * slot_bytes: size of d_trace */
 } ks_layout;
 
@@ -141,7 +173,8 @@ ks_status ks_default_config(ks_config* cfg);
 
 /* Sizes of the caller-owned device buffers for runs up to cfg->max_grid x
  * cfg->max_block.  The trace slot size follows the IKET page's per-warp slot
- * (a 16-byte header and fixed 8-byte records, without its 1.15 margin). */
+ * (a 16-byte header and fixed 8- or 16-byte records, without its 1.15 margin).
+ * KS_E_INVALID_ARG for an unknown trace_format. */
 ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layout* out);
 
 /* Bind a program to caller-owned device buffers on the current HIP device:
@@ -161,14 +194,16 @@ ks_status ks_alloc_state(const ks_program* prog, const ks_config* cfg, void* d_g
  * predicates, stacks, scoreboards and shared windows, and rewrites every
  * counter record and trace header of the grid's warps.  Warps are numbered
  * linear block id * warps_per_block + warp in block.
- * Errors: KS_E_INVALID_ARG (shape beyond the allocation, short params), KS_E_HIP. */
+ * Errors: KS_E_INVALID_ARG (shape beyond the allocation, short params),
+ * KS_E_UNSUPPORTED (a block too large for the interpreter variant), KS_E_HIP. */
 ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, size_t params_len,
                  void* stream);
 
 /* Name of the interpreter kernel ks_run launches for this program and block shape,
  * as profilers list it: "ks_interp_v32" (programs of up to 34 register slots: a
  * 40-VGPR register file per lane, six slots of it for immediates) or
- * "ks_interp_v64" (up to 64 slots: a 72-VGPR file).  *name points to a static
+ * "ks_interp_v64" (up to 64 slots: a 72-VGPR file); runs with the extended trace
+ * format launch the same kernel with the suffix "_ext".  *name points to a static
  * string.  Errors: KS_E_INVALID_ARG (NULL arguments, empty or oversized block). */
 ks_status ks_interp_kernel(const ks_program* prog, ks_dim3 block, const char** name);
 

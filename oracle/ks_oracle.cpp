@@ -1065,7 +1065,10 @@ struct Warp {
   std::vector<uint8_t> preds;    // [pred][lane]
   std::vector<uint64_t> ready;   // per value register, then per predicate
   oracle_counters c;
-  std::vector<std::pair<uint32_t, uint32_t>> records;
+  struct Record {
+    uint32_t cycle, pc, kind, active, payload;
+  };
+  std::vector<Record> records;
   uint64_t dropped = 0;
 };
 
@@ -1166,7 +1169,9 @@ struct Sim {
       global_races->first = shared_races->first;
     }
 
-    size_t slot = 16 + 8 * (size_t)cfg->trace_cap;
+    const bool ext = (cfg->flags & ORACLE_FLAG_EXT_TRACE) != 0;
+    const size_t rec = ext ? 16 : 8;
+    size_t slot = 16 + rec * (size_t)cfg->trace_cap;
     for (uint32_t wi = 0; wi < warps_per_block; ++wi) {
       Warp& w = warps[wi];
       w.c.cycles = (uint32_t)(w.prev_issue + 1);
@@ -1175,7 +1180,7 @@ struct Sim {
       out_c[wi] = w.c;
       uint8_t* s = out_trace + slot * wi;
       uint32_t written = (uint32_t)w.records.size();
-      uint8_t version = 1;
+      uint8_t version = ext ? 2 : 1;
       uint8_t flags = (uint8_t)((w.dropped ? 1 : 0) | ((w.c.status & ORACLE_ST_FAULT) ? 2 : 0) |
                                 ((w.c.status & ORACLE_ST_BUDGET) ? 4 : 0) |
                                 ((w.c.status & ORACLE_ST_FINISHED) ? 8 : 0));
@@ -1187,8 +1192,20 @@ struct Sim {
       memcpy(s + 6, &wib, 2);
       memcpy(s + 8, &dropped, 8);
       for (uint32_t k = 0; k < written; ++k) {
-        memcpy(s + 16 + 8 * (size_t)k, &w.records[k].first, 4);
-        memcpy(s + 20 + 8 * (size_t)k, &w.records[k].second, 4);
+        const Warp::Record& r = w.records[k];
+        uint8_t* d = s + 16 + rec * (size_t)k;
+        memcpy(d, &r.cycle, 4);
+        if (!ext) {
+          memcpy(d + 4, &r.pc, 4);
+          continue;
+        }
+        uint16_t pc16 = (uint16_t)r.pc;
+        uint8_t kind = (uint8_t)r.kind, zero = 0;
+        memcpy(d + 4, &pc16, 2);
+        memcpy(d + 6, &kind, 1);
+        memcpy(d + 7, &zero, 1);
+        memcpy(d + 8, &r.active, 4);
+        memcpy(d + 12, &r.payload, 4);
       }
       // records past records_written are left as they were in the caller's buffer
     }
@@ -1233,9 +1250,14 @@ struct Sim {
         w.done = true;
         return;
       }
-      // Issue: trace record, counters.
-      if (w.records.size() < cfg->trace_cap) w.records.push_back({(uint32_t)issue, pc});
-      else w.dropped++;
+      // Issue: trace record (kind and payload filled in below), counters.
+      Warp::Record* rec = nullptr;
+      if (w.records.size() < cfg->trace_cap) {
+        w.records.push_back({(uint32_t)issue, pc, (uint32_t)ORACLE_EV_OTHER, m, 0});
+        rec = &w.records.back();
+      } else {
+        w.dropped++;
+      }
       w.c.warp_instrs++;
       w.c.thread_instrs += (uint64_t)__builtin_popcount(m);
       w.prev_issue = (int64_t)issue;
@@ -1263,6 +1285,7 @@ struct Sim {
       special[SP_NCTAID_Z] = cfg->grid[2];
 
       uint32_t next_pc = pc + 1;
+      uint32_t kind = ORACLE_EV_OTHER, payload = g;
       switch (in.op) {
         case OP_ADD: case OP_SUB: case OP_MUL_LO: case OP_MUL_WIDE: case OP_MAD_LO:
         case OP_FADD: case OP_FSUB: case OP_FMUL: case OP_FFMA:
@@ -1284,11 +1307,20 @@ struct Sim {
             if ((g >> l) & 1) w.vals[(size_t)in.dst.reg * 32 + l] = v;
           break;
         }
-        case OP_LD_GLOBAL: case OP_ST_GLOBAL: case OP_LD_SHARED: case OP_ST_SHARED:
-          memory_access(w, in, g, block_linear, shared, shared_races);
+        case OP_LD_GLOBAL: case OP_ST_GLOBAL: case OP_LD_SHARED: case OP_ST_SHARED: {
+          const MemInfo mi = memory_access(w, in, g, block_linear, shared, shared_races);
+          const bool global = in.op == OP_LD_GLOBAL || in.op == OP_ST_GLOBAL;
+          const bool load = in.op == OP_LD_GLOBAL || in.op == OP_LD_SHARED;
+          kind = global ? (load ? ORACLE_EV_LD_GLOBAL : ORACLE_EV_ST_GLOBAL)
+                        : (load ? ORACLE_EV_LD_SHARED : ORACLE_EV_ST_SHARED);
+          const uint32_t lanes_g = (uint32_t)__builtin_popcount(g);
+          payload = global ? (mi.sectors | (mi.lines << 8) | (lanes_g << 16) | (mi.faults << 24))
+                           : (mi.degree | (lanes_g << 16) | (mi.faults << 24));
           break;
+        }
         case OP_BRA: {
           uint32_t taken = g, not_taken = m & ~g;
+          kind = ORACLE_EV_BRANCH;
           if (not_taken == 0) {
             next_pc = (uint32_t)in.target;
           } else if (taken == 0) {
@@ -1300,6 +1332,7 @@ struct Sim {
             uint32_t tgt = (uint32_t)in.target;
             top.pc = r;
             w.c.diverge_n++;
+            kind = ORACLE_EV_DIVERGE;
             if (tgt != r) w.stack.push_back({tgt, taken, r});
             if (pc + 1 != r) w.stack.push_back({pc + 1, not_taken, r});
             w.c.max_stack_depth = std::max<uint32_t>(w.c.max_stack_depth, (uint32_t)w.stack.size());
@@ -1310,13 +1343,20 @@ struct Sim {
         }
         case OP_RET:
           w.exited |= g;
+          kind = ORACLE_EV_RET;
           break;
         case OP_BAR:
+          kind = ORACLE_EV_BARRIER;
+          payload = 0;
           w.c.barrier_n++;
           if (m != (w.init_mask & ~w.exited)) w.c.status |= ORACLE_ST_BARDIV;
           w.waiting = true;
           w.arrival = issue;
           break;
+      }
+      if (rec) {
+        rec->kind = kind;
+        rec->payload = payload;
       }
       if (next_pc != EXIT_PC) w.stack.back().pc = next_pc;
 
@@ -1366,8 +1406,14 @@ struct Sim {
     w.vals[(size_t)in.dst.reg * 32 + l] = r;
   }
 
-  void memory_access(Warp& w, const Inst& in, uint32_t g, uint64_t block_linear,
-                     std::vector<uint8_t>& shared, RaceLog* shared_races) {
+  // What the analyser found for one warp access (all 0 when no lane passes the guard).
+  struct MemInfo {
+    uint32_t sectors = 0, lines = 0, degree = 0, faults = 0;
+  };
+
+  MemInfo memory_access(Warp& w, const Inst& in, uint32_t g, uint64_t block_linear,
+                        std::vector<uint8_t>& shared, RaceLog* shared_races) {
+    MemInfo mi;
     bool global = in.op == OP_LD_GLOBAL || in.op == OP_ST_GLOBAL;
     bool load = in.op == OP_LD_GLOBAL || in.op == OP_LD_SHARED;
     uint8_t* base = global ? gmem : shared.data();
@@ -1379,7 +1425,7 @@ struct Sim {
       if (in.addr_width == 32) b &= 0xFFFFFFFFull;
       addr[l] = b + (uint64_t)in.addr_off;
     }
-    if (g == 0) return;  // nothing to access or analyse
+    if (g == 0) return mi;  // nothing to access or analyse
     // Analyse.
     if (global) {
       std::set<uint64_t> sectors, lines;
@@ -1391,6 +1437,8 @@ struct Sim {
         lines.insert(first >> 7);
         lines.insert(last >> 7);
       }
+      mi.sectors = (uint32_t)sectors.size();
+      mi.lines = (uint32_t)lines.size();
       if (load) {
         w.c.gld_n++;
         w.c.gld_sectors += (uint32_t)sectors.size();
@@ -1415,6 +1463,7 @@ struct Sim {
         }
         if (count >= 2 && !same) degree = std::max(degree, count);
       }
+      mi.degree = degree;
       w.c.sh_n++;
       w.c.sh_degree_sum += degree;
       w.c.sh_degree_max = std::max(w.c.sh_degree_max, degree);
@@ -1427,6 +1476,7 @@ struct Sim {
       bool ok = valid(a, size, in.size);
       uint64_t tid = block_linear * (uint64_t)threads_per_block + (uint64_t)w.index * 32 + (uint64_t)l;
       if (!ok) {
+        mi.faults++;
         w.c.fault_n++;
         w.c.status |= ORACLE_ST_FAULT;
         if (load) w.vals[(size_t)in.dst.reg * 32 + l] = 0;
@@ -1448,6 +1498,7 @@ struct Sim {
         memcpy(base + a, &v, (size_t)in.size);
       }
     }
+    return mi;
   }
 };
 
@@ -1554,7 +1605,7 @@ int oracle_run(const char* ptx, size_t len, const char* entry, const oracle_cfg*
     sim.gmem_bytes = cfg->gmem_bytes;
     sim.threads_per_block = (uint32_t)tpb;
     sim.warps_per_block = (uint32_t)((tpb + 31) / 32);
-    size_t slot = 16 + 8 * (size_t)cfg->trace_cap;
+    size_t slot = 16 + ((cfg->flags & ORACLE_FLAG_EXT_TRACE) ? 16 : 8) * (size_t)cfg->trace_cap;
     RaceLog races;
     bool check = (cfg->flags & ORACLE_FLAG_CHECK_RACES) != 0;
     if (check) sim.global_races = &races;

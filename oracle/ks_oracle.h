@@ -10,12 +10,16 @@
  *
  * Output layouts (little-endian, identical in meaning to the GPU path's):
  *   per-warp counters: 80 bytes, see struct oracle_counters below;
- *   per-warp trace slot: 16-byte header {u32 records_written, u8 version(=1),
+ *   per-warp trace slot: 16-byte header {u32 records_written, u8 version,
  *   u8 flags, u16 warp_in_block, u64 records_dropped} followed by trace_cap
- *   records of {u32 issue_cycle, u32 pc}.  The slot shape (a fixed header, then
- *   fixed-size records, one slot per warp, overflow counted rather than dropped
- *   silently) follows the per-warp buffer described in "CuTeDSL IKET 浅析"
- *   (zhen8838.github.io/posts/iket.html), section 2, "buffer 是怎么定形的".
+ *   records.  Version 1: 8-byte records {u32 issue_cycle, u32 pc}.  Version 2
+ *   (ORACLE_FLAG_EXT_TRACE): 16-byte records {u32 issue_cycle, u16 pc, u8 kind,
+ *   u8 0, u32 active lanes, u32 payload}, kinds and payloads as listed at
+ *   ORACLE_EV_* below.  The slot shape (a fixed header, then fixed-size records,
+ *   one slot per warp, overflow counted rather than dropped silently; events of
+ *   4/8 bytes without a payload and 16 bytes with one) follows the per-warp buffer
+ *   described in "CuTeDSL IKET 浅析" (zhen8838.github.io/posts/iket.html),
+ *   section 2, "buffer 是怎么定形的".
  */
 #ifndef KS_ORACLE_H
 #define KS_ORACLE_H
@@ -52,6 +56,19 @@ enum {
 #define ORACLE_E_RACE (-7)
 
 #define ORACLE_FLAG_CHECK_RACES 0x1u
+#define ORACLE_FLAG_EXT_TRACE 0x2u   /* 16-byte trace records (version 2) */
+
+/* Record kinds of the 16-byte trace records, and their payloads:
+ *   LD/ST_GLOBAL: sectors | lines << 8 | guard lanes << 16 | faulting lanes << 24
+ *                 (counts; all 0 when no lane passes the guard);
+ *   LD/ST_SHARED: bank-conflict degree (0 when no lane passes) | guard lanes << 16 |
+ *                 faulting lanes << 24;
+ *   BRANCH, DIVERGE (the warp split): mask of the lanes taking the branch;
+ *   BARRIER: 0;  OTHER, RET: mask of the lanes passing the guard. */
+enum {
+  ORACLE_EV_OTHER = 0, ORACLE_EV_LD_GLOBAL = 1, ORACLE_EV_ST_GLOBAL = 2, ORACLE_EV_LD_SHARED = 3,
+  ORACLE_EV_ST_SHARED = 4, ORACLE_EV_BRANCH = 5, ORACLE_EV_DIVERGE = 6, ORACLE_EV_BARRIER = 7, ORACLE_EV_RET = 8
+};
 
 typedef struct {
   uint64_t thread_instrs;   /* sum over issued warp-instructions of popcount(active mask) */
@@ -104,7 +121,8 @@ int oracle_param(const char* ptx, size_t len, const char* entry, uint32_t index,
 void oracle_default_latency(uint16_t out[ORACLE_NLAT]);
 
 /* Simulate.  `gmem` (gmem_bytes) is read and updated in place.  `counters` receives
- * n_out_warps * 80 bytes and `trace` n_out_warps * (16 + 8 * trace_cap) bytes, where
+ * n_out_warps * 80 bytes and `trace` n_out_warps * (16 + R * trace_cap) bytes (R = 8, or 16
+ * with ORACLE_FLAG_EXT_TRACE), where
  * n_out_warps = (n_block_list ? n_block_list : total blocks) * warps_per_block, in
  * block-list (or linear block) order.  Returns ORACLE_OK, an error code, or
  * ORACLE_E_RACE when race checking is on and a race was seen (outputs still written). */

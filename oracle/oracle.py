@@ -29,6 +29,11 @@ assert COUNTER_DTYPE.itemsize == 80
 
 TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("flags", "u1"),
                                ("warp_in_block", "<u2"), ("records_dropped", "<u8")])
+# the 16-byte records of the extended trace format
+EXT_RECORD_DTYPE = np.dtype([("cycle", "<u4"), ("pc", "<u2"), ("kind", "u1"), ("reserved", "u1"),
+                             ("active", "<u4"), ("payload", "<u4")])
+TRACE_BASIC, TRACE_EXTENDED = 0, 1
+FLAG_EXT_TRACE = 2
 
 E_RACE = -7
 
@@ -141,13 +146,14 @@ def _dim3(d):
 
 
 def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFFFFFFF, latency=None,
-        threads=0, blocks=None, check_races=False, entry=None):
+        threads=0, blocks=None, check_races=False, entry=None, trace_format=TRACE_BASIC):
     """Simulate.  `gmem` is a writable uint8 numpy array, updated in place.
 
     Returns (counters, trace, rc): counters is a COUNTER_DTYPE array with one record
-    per simulated warp, trace a uint8 array of (16 + 8 * trace_cap) bytes per warp,
-    rc 0 or E_RACE (race checking only).  `blocks` optionally lists the linear block
-    ids to simulate; outputs follow that order."""
+    per simulated warp, trace a uint8 array of (16 + R * trace_cap) bytes per warp
+    (R = 8, or 16 with trace_format TRACE_EXTENDED), rc 0 or E_RACE (race checking
+    only).  `blocks` optionally lists the linear block ids to simulate; outputs
+    follow that order."""
     assert gmem.dtype == np.uint8 and gmem.flags.c_contiguous and gmem.flags.writeable
     grid, block = _dim3(grid), _dim3(block)
     cfg = _Cfg()
@@ -160,7 +166,8 @@ def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFF
     lat = lat + [0] * (NLAT - len(lat))
     cfg.latency[:] = lat
     cfg.n_threads = threads
-    cfg.flags = 1 if check_races else 0
+    cfg.flags = (1 if check_races else 0) | (FLAG_EXT_TRACE if trace_format == TRACE_EXTENDED else 0)
+    rec = 16 if trace_format == TRACE_EXTENDED else 8
     tpb = block[0] * block[1] * block[2]
     wpb = (tpb + 31) // 32
     if blocks is None:
@@ -173,7 +180,7 @@ def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFF
         cfg.block_list = bl.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
         cfg.n_block_list = nb
     counters = np.zeros(nb * wpb, dtype=COUNTER_DTYPE)
-    trace = np.zeros(nb * wpb * (16 + 8 * trace_cap), dtype=np.uint8)
+    trace = np.zeros(nb * wpb * (16 + rec * trace_cap), dtype=np.uint8)
     pb = bytes(params_bytes)
     pbuf = ctypes.create_string_buffer(pb, max(len(pb), 1))
     err = ctypes.create_string_buffer(1024)
@@ -185,10 +192,14 @@ def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFF
     return counters, trace, rc
 
 
-def trace_slots(trace, trace_cap):
-    """Split a trace buffer into (headers, records[warp, cap, 2]) views."""
-    slot = 16 + 8 * trace_cap
+def trace_slots(trace, trace_cap, trace_format=TRACE_BASIC):
+    """Split a trace buffer into (headers, records): records[warp, cap, 2] u32 for
+    the basic format, records[warp, cap] of EXT_RECORD_DTYPE for the extended one."""
+    rec = 16 if trace_format == TRACE_EXTENDED else 8
+    slot = 16 + rec * trace_cap
     t = trace.reshape(-1, slot)
     hdr = t[:, :16].copy().view(TRACE_HEADER_DTYPE).reshape(-1)
-    rec = t[:, 16:].copy().view("<u4").reshape(t.shape[0], trace_cap, 2)
-    return hdr, rec
+    body = t[:, 16:].copy()
+    if trace_format == TRACE_EXTENDED:
+        return hdr, body.view(EXT_RECORD_DTYPE).reshape(t.shape[0], trace_cap)
+    return hdr, body.view("<u4").reshape(t.shape[0], trace_cap, 2)

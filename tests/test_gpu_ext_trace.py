@@ -1,0 +1,132 @@
+"""GPU: extended 16-byte trace records against the CPU oracle, bit for bit.
+
+The extended format runs the interpreter variants that write {issue cycle, pc,
+kind, active mask, payload} per issued instruction; memory, counters, headers
+and every written record must equal the oracle's, and the basic-format run of
+the same inputs must give the same memory and counters.
+"""
+import numpy as np
+import pytest
+
+from workloads import configs as W
+from workloads import probes as PR
+from workloads import small as S
+from workloads.configs import pack_params
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from analysis_ptxsimulator_amd import ks
+    ks.lib()
+    return ks
+
+
+def _say(msg):
+    print("[gpu] " + msg, flush=True)
+
+
+def gpu_run(K, w, fmt, cap, **kw):
+    _say("%s grid=%s block=%s cap=%d format=%d" % (w.name, w.grid, w.block, cap, fmt))
+    s = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=cap, trace_format=fmt, **kw)
+    try:
+        s.load_gmem(w.gmem)
+        s.run(w.params_bytes)
+        name = s.kernel_name()
+        return s.read_gmem(), s.read_counters(), s.read_trace(), name
+    finally:
+        s.close()
+
+
+def ext_parity(K, O, w, cap=None, **kw):
+    cap = w.trace_cap if cap is None else cap
+    gg, cg, tg, name = gpu_run(K, w, K.KS_TRACE_EXTENDED, cap, **kw)
+    assert name.endswith("_ext")
+    go = w.gmem.copy()
+    okw = {k: v for k, v in kw.items() if k in ("latency", "max_warp_instrs")}
+    co, to, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, go, trace_cap=cap, trace_format=O.TRACE_EXTENDED, **okw)
+    assert np.array_equal(gg, go)
+    for f in co.dtype.names:
+        assert np.array_equal(cg[f], co[f]), f
+    hg, rg = K.trace_slots(tg, cap, K.KS_TRACE_EXTENDED)
+    ho, ro = O.trace_slots(to, cap, O.TRACE_EXTENDED)
+    assert np.array_equal(hg, ho)
+    for i in range(len(ho)):
+        n = int(ho["records_written"][i])
+        assert np.array_equal(rg[i, :n], ro[i, :n]), i
+    # the basic format of the same run: same memory and counters
+    gb, cb, _, _ = gpu_run(K, w, K.KS_TRACE_BASIC, cap, **kw)
+    assert np.array_equal(gb, gg) and np.array_equal(cb, cg)
+
+
+def test_vector_add(K, oracle_mod):
+    ext_parity(K, oracle_mod, W.vector_add())
+
+
+@pytest.mark.parametrize("s", [1, 3, 33])
+def test_strided(K, oracle_mod, s):
+    ext_parity(K, oracle_mod, W.strided_gather(s, n=8192))
+
+
+@pytest.mark.parametrize("n_acc", [1, 8])
+def test_ffma(K, oracle_mod, n_acc):
+    ext_parity(K, oracle_mod, W.ffma_probe(n_acc, iters=6, grid=4, block=256, trace_cap=256))
+
+
+@pytest.mark.parametrize("s", [1, 7, 32])
+def test_bank(K, oracle_mod, s):
+    ext_parity(K, oracle_mod, W.bank_probe(s, iters=4, grid=2, block=1024, trace_cap=64))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_stress(K, oracle_mod, seed):
+    ext_parity(K, oracle_mod, W.random_stress(prog_seed=seed, grid=8, block=256, gmem_bytes=1 << 24,
+                                              trace_cap=1024))
+
+
+def test_random_stress_block_768_and_cap_overflow(K, oracle_mod):
+    """12 waves per workgroup (the largest block of the 64-slot extended variant),
+    and records past the cap dropped and counted; a 1024-thread block is refused."""
+    ext_parity(K, oracle_mod, W.random_stress(prog_seed=2, grid=3, block=768, gmem_bytes=1 << 24, trace_cap=300))
+    w = W.random_stress(prog_seed=2, grid=1, block=1024, gmem_bytes=1 << 22, trace_cap=8)
+    s = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=8, trace_format=K.KS_TRACE_EXTENDED)
+    try:
+        with pytest.raises(K.KsError, match="768"):
+            s.run(w.params_bytes)
+    finally:
+        s.close()
+
+
+@pytest.mark.parametrize("op", ["fma.f32", "mad.s32", "none"])
+def test_probe_chains(K, oracle_mod, op):
+    ext_parity(K, oracle_mod, PR.chain_probe(op, 3, 5, grid=3, block=96, trace_cap=256))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_control_flow_shapes(K, oracle_mod, seed):
+    ptx = S.random_cfg_ptx(seed, loops=seed % 2 == 1)
+    n = 256
+    rng = np.random.default_rng(100 + seed)
+    g = np.zeros(8 * n + 4096, np.uint8)
+    g[:4 * n] = rng.integers(0, 1 << 32, size=n, dtype=np.uint32).view(np.uint8)
+    params = [("param_in", "u64", 0), ("param_out", "u64", 4 * n)]
+    w = W.Workload(name="cfg%d" % seed, ptx=ptx, grid=(2, 1, 1), block=(128, 1, 1), params=params, gmem=g,
+                   trace_cap=512)
+    ext_parity(K, oracle_mod, w, max_warp_instrs=4000)
+
+
+def test_faulting_and_misaligned_lanes(K, oracle_mod):
+    data = 1 << 16
+    gaddr = np.array([0, 2, 30, data + 64] + [0] * 28, np.uint64)
+    guard = np.array([1, 1, 1, 1] + [0] * 28, np.uint32)
+    w = S.addr_probe(gaddr, np.zeros(32, np.uint32), guard, data, block=32)
+    ext_parity(K, oracle_mod, w)
+
+
+def test_budget(K, oracle_mod):
+    ext_parity(K, oracle_mod, W.random_stress(prog_seed=0, grid=2, block=256, gmem_bytes=1 << 22, trace_cap=64),
+               max_warp_instrs=100)

@@ -815,7 +815,7 @@ class Front {
     } else {
       bad_form();
     }
-    in.lat = lat_class;  // class for now; replaced by cycles when a state is allocated
+    in.lat = lat_class;  // the class; its cycles come from the configuration when a state is allocated
     P->code.push_back(d);
   }
 
@@ -1188,6 +1188,31 @@ ks_status ks_param_info(const ks_program* p, uint32_t index, uint32_t* offset, u
   });
 }
 
+ks_status ks_instr_info(const ks_program* p, uint32_t pc, ks_instr_desc* out) {
+  return guarded([&]() -> ks_status {
+    if (!p || !out) raise(KS_E_INVALID_ARG, 0, "NULL argument");
+    if (pc >= p->code.size()) raise(KS_E_INVALID_ARG, 0, "pc %u outside the program (%zu instructions)", pc, p->code.size());
+    const Decoded& d = p->code[pc];
+    const KsInst& in = d.in;
+    memset(out, 0, sizeof *out);
+    out->line = (uint32_t)d.line;
+    out->lat_class = in.lat;
+    switch (in.op) {
+      case KO_LDG32: case KO_LDG64: out->kind = KS_EV_LD_GLOBAL; break;
+      case KO_STG32: case KO_STG64: out->kind = KS_EV_ST_GLOBAL; break;
+      case KO_LDS32: case KO_LDS64: out->kind = KS_EV_LD_SHARED; break;
+      case KO_STS32: case KO_STS64: out->kind = KS_EV_ST_SHARED; break;
+      case KO_BRA: out->kind = KS_EV_BRANCH; break;
+      case KO_BAR: out->kind = KS_EV_BARRIER; break;
+      case KO_RET: out->kind = KS_EV_RET; break;
+      default: out->kind = KS_EV_OTHER; break;
+    }
+    if (out->kind >= KS_EV_LD_GLOBAL && out->kind <= KS_EV_ST_SHARED)
+      out->access_bytes = (in.op == KO_LDG64 || in.op == KO_STG64 || in.op == KO_LDS64 || in.op == KO_STS64) ? 8u : 4u;
+    return KS_OK;
+  });
+}
+
 ks_status ks_ipdom_table(const ks_program* p, uint32_t* out, uint32_t n) {
   return guarded([&]() -> ks_status {
     if (!p || (!out && n)) raise(KS_E_INVALID_ARG, 0, "NULL argument");
@@ -1239,6 +1264,8 @@ ks_status ks_query_layout(const ks_program* p, const ks_config* cfg, ks_layout* 
     out->counters_bytes = out->n_warps * 80;
     if (cfg->trace_format != KS_TRACE_BASIC && cfg->trace_format != KS_TRACE_EXTENDED)
       raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", cfg->trace_format);
+    if (cfg->trace_format == KS_TRACE_EXTENDED && nb > KS_EXT_MAX_BLOCKS)
+      raise(KS_E_UNSUPPORTED, 0, "extended trace records support grids of up to %d blocks", KS_EXT_MAX_BLOCKS);
     out->slot_bytes = 16 + (cfg->trace_format == KS_TRACE_EXTENDED ? 16 : 8) * (uint64_t)cfg->trace_cap;
     out->trace_bytes = out->n_warps * out->slot_bytes;
     return KS_OK;
@@ -1308,6 +1335,8 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       raise(KS_E_INVALID_ARG, 0, "grid/block larger than the allocation");
     if (tpb > KS_MAX_BLOCK_THREADS) raise(KS_E_INVALID_ARG, 0, "more than %d threads per block", KS_MAX_BLOCK_THREADS);
     if (nb > 0x7FFFFFFFull) raise(KS_E_INVALID_ARG, 0, "too many blocks");
+    if (st->cfg.trace_format == KS_TRACE_EXTENDED && nb > KS_EXT_MAX_BLOCKS)
+      raise(KS_E_UNSUPPORTED, 0, "extended trace records support grids of up to %d blocks", KS_EXT_MAX_BLOCKS);
     if (params_len < p->param_bytes || (p->param_bytes && !params)) raise(KS_E_INVALID_ARG, 0, "parameter block shorter than %u bytes", p->param_bytes);
     KsArgs a;
     memset(&a, 0, sizeof a);
@@ -1355,7 +1384,7 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       if (wg > ks_max_block_threads(variant, a.ext != 0))
         raise(KS_E_UNSUPPORTED, 0, "extended trace records with %u register slots support blocks of up to %u threads",
               p->reg_slots, ks_max_block_threads(variant, true));
-      const size_t need = ks_lds_bytes(wg, p->shared_bytes);
+      const size_t need = ks_lds_bytes(wg, p->shared_bytes, a.ext != 0);
       if (need + 64 > ks_lds_limit())
         raise(KS_E_UNSUPPORTED, 0, "block of %u threads needs %zu bytes of LDS (limit %zu)", a.threads_per_block, need,
               ks_lds_limit() - 64);

@@ -15,8 +15,9 @@
 //     so one scalar operation updates both; per-warp values that the lanes use
 //     (next issue cycle, instruction count, trace state) are VGPRs that are
 //     uniform over each warp's 32 lanes; the divergence stack, counters and a
-//     32-record trace staging buffer live in VGPR lanes; the register
-//     scoreboard of each warp is an LDS array;
+//     32-record trace staging buffer live in VGPR lanes (16-byte extended
+//     records: a 32-record ring per warp in LDS); the register scoreboard of
+//     each warp is an LDS array;
 //   * trace flushes, the issue budget and the cycle limit are one per-lane
 //     comparison per step against a precomputed event threshold;
 //   * the analyser counts distinct sectors/lines of monotone addresses with a
@@ -413,15 +414,19 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const __attribute__((address_space(4))) uint8_t* const prog_b = (const __attribute__((address_space(4))) uint8_t*)prog;
   const uint32_t ib = a.rf_slots - KS_IMM_SLOTS;  // first immediate slot
 
-  // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] [shared window]
+  // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] (to 16 bytes)
+  //      [EXT: record ring, 32 x 16 bytes per warp] [shared window]
   RegFile<RFN, EXT ? 64 : 56> R;
   RegFile<RFN, EXT ? 64 : 56>::zero();
   uint32_t* const sbw = lds;
   uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
-  uint8_t* const win = dump_sb + 4u * KS_SB_ENTRIES;
+  const uint32_t sb_words = (WG / 32u + 1u) * KS_SB_ENTRIES;
+  uint8_t* const ring = reinterpret_cast<uint8_t*>(lds) + ((4u * sb_words + 15u) & ~15u);
+  uint8_t* const win = ring + (EXT ? 16u * WG : 0u);
   {
-    const uint32_t words = (WG / 32u + 1u) * KS_SB_ENTRIES + ((a.shared_bytes + 3u) >> 2);
-    for (uint32_t i = tid; i < words; i += WG) lds[i] = 0;
+    for (uint32_t i = tid; i < sb_words; i += WG) lds[i] = 0;
+    uint32_t* const win_w = reinterpret_cast<uint32_t*>(win);
+    for (uint32_t i = tid, n = (a.shared_bytes + 3u) >> 2; i < n; i += WG) win_w[i] = 0;
     if (tid < 3) {
       ep_max[tid] = 0;
       ep_alive[tid] = 0;
@@ -461,15 +466,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   uint32_t wi = 0;            // warp: issued warp-instructions
   uint32_t fl = 0;            // warp: trace records written to memory
   // warp: record count at which the next chunk is written (from the records written so far)
-  auto next_flush = [&](uint32_t written) -> uint32_t {
-    if constexpr (EXT) return INF;  // extended records are written as they are issued
-    return written < cap ? umin(cap, written + 32u) : INF;
-  };
+  auto next_flush = [&](uint32_t written) -> uint32_t { return written < cap ? umin(cap, written + 32u) : INF; };
   uint32_t ev = umin(next_flush(0), budget);      // warp: next event (chunk write or budget)
   uint32_t act = 0;           // instructions issued with this lane's thread active (see KS_SET_LIVE)
   uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
   uint32_t pbits = 0;         // predicate p of this lane's thread in bit p
   uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
+  // EXT: record k of this lane's warp is staged in slot k % 32 of the warp's LDS ring
+  uint8_t* const my_ring = ring + 512u * my_w;
   // global loads / stores: per-lane shares of the access, sector and line counters of
   // the fast analyser path (summed over each warp's lanes at the end)
   uint32_t q_ln = 0, q_ls = 0, q_ll = 0, q_sn = 0, q_ss = 0, q_sl = 0;
@@ -620,12 +624,17 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 #define KS_EXT_REC(is_, pc_, kind_, pay_)                                            \
   if constexpr (EXT) {                                                              \
     const uint32_t k_ = wi - 1u;                                                    \
-    if (gl && sl == 0u && k_ < cap) {                                               \
-      uint2* const r_ = reinterpret_cast<uint2*>(slot_base + 16ull * k_);           \
-      r_[0] = make_uint2((is_), (pc_) | ((uint32_t)(kind_) << 16));                 \
-      r_[1] = make_uint2(hl ? (uint32_t)(mm >> 32) : (uint32_t)mm, (pay_));         \
-    }                                                                               \
+    if (gl && sl == 0u && k_ < cap)                                                 \
+      *reinterpret_cast<uint4*>(my_ring + 16u * (k_ & 31u)) =                       \
+          make_uint4((is_), (pc_) | ((uint32_t)(kind_) << 16),                      \
+                     hl ? (uint32_t)(mm >> 32) : (uint32_t)mm, (pay_));             \
   }
+
+  // A global store whose next index-mode register access may come within a few
+  // instructions (the extended variants' general memory path) waits until the store
+  // has completed, so that it no longer reads its address or data registers then.
+#define KS_EXT_STORE_WAIT()                                                          \
+  if constexpr (EXT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
   // Issue cycle of the instruction whose hot words are h: the later of the warp's
   // previous issue + 1 and the ready cycle of every register source (absent
@@ -673,7 +682,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         const uint64_t om = ballot(iss > CYCLE_LIMIT) & gm & ~bm;
         const uint64_t fm = ballot(wi == next_flush(fl)) & gm & ~om;  // a full chunk (or the cap) to write
         if (lanes(fm)) {
-          if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+          if constexpr (EXT) {
+            if (sl < wi - fl)
+              *reinterpret_cast<uint4*>(slot_base + 16ull * (fl + sl)) = *reinterpret_cast<const uint4*>(my_ring + 16u * sl);
+            KS_EXT_STORE_WAIT();  // the next step's index mode follows soon
+          } else {
+            if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+          }
           fl = wi;
         }
         if (gl) ev = umin(next_flush(fl), budget);
@@ -989,14 +1004,19 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
                 R.get2(s1, s1 + 1u, lo, hi);
                 if (is_global) {
                   *reinterpret_cast<uint2*>(a.gmem + A) = make_uint2(lo, hi);
+                  KS_EXT_STORE_WAIT();
                 } else {
                   *reinterpret_cast<uint32_t*>(win + A) = lo;
                   *reinterpret_cast<uint32_t*>(win + A + 4) = hi;
                 }
               } else {
                 const uint32_t lo = R.get(s1);
-                if (is_global) *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
-                else *reinterpret_cast<uint32_t*>(win + A) = lo;
+                if (is_global) {
+                  *reinterpret_cast<uint32_t*>(a.gmem + A) = lo;
+                  KS_EXT_STORE_WAIT();
+                } else {
+                  *reinterpret_cast<uint32_t*>(win + A) = lo;
+                }
               }
             }
             const uint64_t faults = on64 & ~okm;
@@ -1162,9 +1182,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       uint32_t hl_e = hl;
       asm volatile("" : "+v"(hl_e));
       const uint64_t gw = gw0 + hl_e;
-      // records staged since the last chunk write (extended records are already written)
-      if constexpr (!EXT)
-        if (sl < written - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+      // records staged since the last chunk write
+      if (sl < written - fl) {
+        if constexpr (EXT)
+          *reinterpret_cast<uint4*>(slot_base + 16ull * (fl + sl)) = *reinterpret_cast<const uint4*>(my_ring + 16u * sl);
+        else
+          *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+      }
       if (sl < 20) {
         uint32_t v;
         switch (sl) {
@@ -1249,16 +1273,17 @@ int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
 
 uint32_t ks_max_block_threads(int variant, bool ext) { return (ext && variant == 64) ? 768u : 1024u; }
 
-size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes) {
-  const size_t sb = (size_t)(wg / 32u + 1u) * KS_SB_ENTRIES * 4u;  // the warps' scoreboards and a scratch one
-  return sb + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
+size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes, bool ext) {
+  const size_t sb = ((size_t)(wg / 32u + 1u) * KS_SB_ENTRIES * 4u + 15u) & ~(size_t)15u;  // scoreboards + a scratch one
+  const size_t ring = ext ? (size_t)wg * 16u : 0u;  // 32 staged 16-byte records per warp
+  return sb + ring + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
 }
 
 hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, hipStream_t s) {
   const uint32_t waves = (a.warps_per_block + 1u) / 2u;
   const uint32_t wg = 64u * waves;
   const int variant = ks_choose_variant(slots, a.threads_per_block);
-  const size_t lds = ks_lds_bytes(wg, a.shared_bytes);
+  const size_t lds = ks_lds_bytes(wg, a.shared_bytes, a.ext != 0);
   if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0))
     return hipErrorInvalidValue;
   if (a.rf_slots != slots + KS_IMM_SLOTS) return hipErrorInvalidValue;

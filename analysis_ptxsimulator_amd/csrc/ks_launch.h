@@ -23,5 +23,6 @@ int ks_choose_variant(uint32_t slots, uint32_t block_threads);
 // extended-trace variant with the 72-VGPR file (136 VGPRs: 768 threads).
 uint32_t ks_max_block_threads(int variant, bool ext);
 
-// Dynamic LDS bytes of one workgroup of `wg` lanes (scoreboards and the shared window).
-size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes);
+// Dynamic LDS bytes of one workgroup of `wg` lanes (scoreboards, with `ext` the
+// staging ring of extended trace records, and the shared window).
+size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes, bool ext);

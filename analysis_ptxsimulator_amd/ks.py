@@ -29,6 +29,7 @@ TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("
                                ("warp_in_block", "<u2"), ("records_dropped", "<u8")])
 # trace formats (ks_config.trace_format) and the 16-byte extended record
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
+KS_EXT_MAX_BLOCKS = 32  # largest grid of an extended-record allocation or run
 EXT_RECORD_DTYPE = np.dtype([("cycle", "<u4"), ("pc", "<u2"), ("kind", "u1"), ("reserved", "u1"),
                              ("active", "<u4"), ("payload", "<u4")])
 EV_NAMES = ["other", "ld.global", "st.global", "ld.shared", "st.shared", "branch", "diverge", "barrier", "ret"]
@@ -59,6 +60,11 @@ class ks_program_desc(ctypes.Structure):
                 ("shared_bytes", ctypes.c_uint32), ("reg_slots", ctypes.c_uint32), ("n_preds", ctypes.c_uint32)]
 
 
+class ks_instr_desc(ctypes.Structure):
+    _fields_ = [("line", ctypes.c_uint32), ("kind", ctypes.c_uint32), ("access_bytes", ctypes.c_uint32),
+                ("lat_class", ctypes.c_uint32)]
+
+
 class ks_layout(ctypes.Structure):
     _fields_ = [("warps_per_block", ctypes.c_uint32), ("reserved", ctypes.c_uint32), ("n_warps", ctypes.c_uint64),
                 ("counters_bytes", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64), ("trace_bytes", ctypes.c_uint64)]
@@ -71,6 +77,7 @@ _EXPORTS = {
     "ks_param_info": ([_P, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
                        ctypes.POINTER(ctypes.c_char_p)], ctypes.c_int32),
     "ks_ipdom_table": ([_P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32], ctypes.c_int32),
+    "ks_instr_info": ([_P, ctypes.c_uint32, ctypes.POINTER(ks_instr_desc)], ctypes.c_int32),
     "ks_default_config": ([ctypes.POINTER(ks_config)], ctypes.c_int32),
     "ks_query_layout": ([_P, ctypes.POINTER(ks_config), ctypes.POINTER(ks_layout)], ctypes.c_int32),
     "ks_alloc_state": ([_P, ctypes.POINTER(ks_config), _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int32),
@@ -134,6 +141,12 @@ def ks_param_info(prog, index):
     off, size, name = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_char_p()
     _check(lib().ks_param_info(prog, index, ctypes.byref(off), ctypes.byref(size), ctypes.byref(name)))
     return off.value, size.value, name.value.decode()
+
+
+def ks_instr_info(prog, pc):
+    d = ks_instr_desc()
+    _check(lib().ks_instr_info(prog, pc, ctypes.byref(d)))
+    return {k: getattr(d, k) for k, _ in ks_instr_desc._fields_}
 
 
 def ks_ipdom_table(prog):

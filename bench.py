@@ -157,7 +157,7 @@ def main():
 
     c = s.read_counters()
     status = s.status()
-    kernel = ks.ks_interp_kernel(s.prog, w.block)
+    kernel = s.kernel_name()
     s.close()
     thread_instrs = int(c["thread_instrs"].sum())
     warp_acc = int(c["gld_n"].astype(np.uint64).sum() + c["gst_n"].sum() + c["sh_n"].sum())

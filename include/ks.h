@@ -14,7 +14,8 @@
  * format) 16-byte records that add the instruction kind, the active mask and a
  * per-kind payload (sectors and lines of a global access, bank-conflict degree of
  * a shared access, the lanes taking a branch).  Extended records for programs of
- * more than 34 register slots support blocks of up to 768 threads.
+ * more than 34 register slots support blocks of up to 768 threads, and
+ * extended-record launches hold at most KS_EXT_MAX_BLOCKS blocks.
  *
  * Sources of the semantics, by page and section:
  *   - KernelScope backend documentation (github.com/briefgaming/kernelscope).
@@ -111,6 +112,12 @@ enum {
 #define KS_MAX_PARAM_BYTES 512   /* parameter block */
 #define KS_MAX_SHARED_BYTES 65536 /* simulated shared window per block */
 #define KS_MAX_BLOCK_THREADS 1024
+/* Largest grid (in blocks) of a KS_TRACE_EXTENDED allocation or run: the launch
+ * sizes the extended-record interpreter has been checked at on the GPU.  A
+ * 65536-block extended run faulted and its cause is not found yet, so larger
+ * extended launches are refused (KS_E_UNSUPPORTED); the basic format has no
+ * such limit. */
+#define KS_EXT_MAX_BLOCKS 32
 
 typedef struct ks_program ks_program; /* opaque; created by ks_load_program */
 typedef struct ks_state ks_state;     /* opaque; created by ks_alloc_state */
@@ -160,6 +167,18 @@ ks_status ks_program_info(const ks_program* prog, ks_program_desc* out);
  * are laid out in declaration order, each at its natural alignment. */
 ks_status ks_param_info(const ks_program* prog, uint32_t index, uint32_t* offset, uint32_t* size,
                         const char** name);
+
+typedef struct {
+  uint32_t line;          /* 1-based line of the instruction in the PTX text */
+  uint32_t kind;          /* KS_EV_* kind of its extended trace records (a bra: KS_EV_BRANCH) */
+  uint32_t access_bytes;  /* bytes per lane of a ld/st.global or ld/st.shared (4 or 8), else 0 */
+  uint32_t lat_class;     /* KS_LAT_* class whose latency its destination takes */
+} ks_instr_desc;
+
+/* Host-side description of decoded instruction `pc` (0 <= pc < n_instrs): what the
+ * tools that read trace records (pc -> source line, access width) need.
+ * KS_E_INVALID_ARG for a pc out of range. */
+ks_status ks_instr_info(const ks_program* prog, uint32_t pc, ks_instr_desc* out);
 
 /* Debug: for each instruction, the reconvergence index of a guarded bra (n_instrs
  * meaning "exit"), 0xFFFFFFFF for every other instruction.  `out` holds `n`

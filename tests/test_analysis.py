@@ -1,0 +1,200 @@
+"""Host analysis: occupancy model, hint rules and the trace-event export.
+
+The occupancy model is pinned by the KernelScope page's worked example (sm_80,
+256 threads per block: 32 registers per thread give 64 active warps, 100%; 128
+registers give 25%) and by hand-computed cases for each limiter.  The hint rules
+run over extended trace records of the CPU oracle, on workloads whose memory
+pattern fixes the answer (bank-conflict degree gcd(s, 32), strided sectors
+min(32, 4 s)); the export is checked field by field against the hand-derived
+vector_add trace in tests/golden.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from workloads import configs as W
+from workloads import small as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def A():
+    from analysis_ptxsimulator_amd import analysis, build
+    build.build(force=False)
+    return analysis
+
+
+def ext(O, w, cap=None):
+    cap = w.trace_cap if cap is None else cap
+    g = w.gmem.copy()
+    c, t, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=cap, trace_format=O.TRACE_EXTENDED)
+    return c, O.trace_slots(t, cap, O.TRACE_EXTENDED)
+
+
+def test_occupancy_page_example(A):
+    r = A.occupancy("sm_80", 256, 32)
+    assert r["active_warps_per_sm"] == 64 and r["occupancy_percent"] == 100.0
+    assert r["warps_by_registers"] == 64 and r["warps_by_block_size"] == 64
+    assert r["limiting_factor"] == "registers"
+    r = A.occupancy("sm_80", 256, 128)
+    assert r["active_warps_per_sm"] == 16 and r["occupancy_percent"] == 25.0 and r["limiting_factor"] == "registers"
+
+
+def test_occupancy_limiters_by_hand(A):
+    # 33 registers: 33 * 32 = 1056 -> 1280 per warp (groups of 256); 65536 // 1280 = 51 warps
+    r = A.occupancy("sm_80", 128, 33)
+    assert r["warps_by_registers"] == 51 and r["active_warps_per_sm"] == 51
+    # 48 KiB of shared memory per block: 167936 // 49152 = 3 blocks of 8 warps
+    r = A.occupancy("sm_80", 256, 0, 48 * 1024)
+    assert r["active_warps_per_sm"] == 24 and r["limiting_factor"] == "shared_memory"
+    assert r["occupancy_percent"] == 37.5
+    # 100 bytes of shared memory round up to 256: 65536 // 256 = 256 blocks, capped elsewhere
+    r = A.occupancy("sm_75", 32, 0, 100)
+    assert r["warps_by_shared_memory"] == 256 and r["active_warps_per_sm"] == 16
+    assert r["limiting_factor"] == "block_size"  # 16 blocks per SM of 1 warp
+    # one 1024-thread block fills a T4's 32 warps
+    r = A.occupancy("sm_75", 1024, 16)
+    assert r["active_warps_per_sm"] == 32 and r["occupancy_percent"] == 100.0
+    r = A.occupancy("sm_86", 1024, 0)
+    assert r["active_warps_per_sm"] == 32 and r["limiting_factor"] == "block_size"
+    with pytest.raises(ValueError):
+        A.occupancy("sm_80", 2048, 32)
+
+
+def test_program_occupancy_uses_declared_registers(A):
+    w = W.bank_probe(1, iters=1, grid=1, block=1024)
+    r = A.program_occupancy(w.ptx, 1024)
+    from analysis_ptxsimulator_amd import ks
+    p = ks.ks_load_program(w.ptx)
+    info = ks.ks_program_info(p)
+    ks.ks_program_free(p)
+    assert r == A.occupancy("sm_80", 1024, info["reg_slots"], info["shared_bytes"])
+
+
+@pytest.mark.parametrize("s", [1, 2, 4, 8, 16, 32, 33])
+def test_bank_conflict_hints(A, oracle_mod, s):
+    w = W.bank_probe(s, iters=2, grid=1, block=256, trace_cap=64)
+    _, (hdr, rec) = ext(oracle_mod, w)
+    info = A.ProgramInfo(w.ptx)
+    hs = A.hints(hdr, rec, info, warps_per_block=w.warps_per_block)
+    d = math.gcd(s, 32)
+    per_event = [h for h in hs if "warp" in h and "bank conflict" in h["message"]]
+    # the probe's one global load of v[lane * s] touches min(32, s) lines for 128
+    # requested bytes (one line's worth): below 25% efficiency (critical) past 4 lines
+    scattered = [h for h in hs if "efficiency" in h]
+    assert len(scattered) == (8 if min(32, s) > 4 else 0)
+    assert all(abs(h["efficiency"] - 1.0 / min(32, s)) < 1e-12 for h in scattered)
+    if d == 1:
+        assert per_event == []
+    else:
+        assert len(per_event) == 8 * 4  # 8 warps x (2 stores + 2 loads)
+        assert all(h["message"] == "%d-way bank conflict" % d for h in per_event)
+        assert all(h["severity"] == ("critical" if d >= 8 else "warning") for h in per_event)
+        assert any(h["message"] == "Shared memory bank conflicts (32 events)" for h in hs)
+        assert all(info.text(h["pc"]).startswith(("st.shared", "ld.shared")) for h in per_event)
+
+
+@pytest.mark.parametrize("s", [1, 2, 3, 4, 5, 8, 33])
+def test_global_efficiency_hints(A, oracle_mod, s):
+    w = W.strided_gather(s, n=512)
+    _, (hdr, rec) = ext(oracle_mod, w)
+    info = A.ProgramInfo(w.ptx)
+    hs = A.hints(hdr, rec, info, warps_per_block=w.warps_per_block)
+    # a[i * s]: 32 lanes x 4 bytes fit one line but touch min(32, s) lines
+    eff = 1.0 / min(32, s)
+    crit = [h for h in hs if h.get("severity") == "critical"]
+    if eff < 0.25:
+        assert len(crit) == 16 and all(abs(h["efficiency"] - eff) < 1e-12 for h in crit)
+        assert all(info.text(h["pc"]).startswith("ld.global") for h in crit)
+        assert all(h["message"] == "Poor memory efficiency (%d%%)" % int(eff * 100) for h in crit)
+        assert len(hs) == 16
+    else:
+        # 25-50% is counted as uncoalesced but, as in the rules, gives no hint
+        assert hs == []
+
+
+def test_coalescing_efficiency_page_examples(A, oracle_mod):
+    """The memory-analysis part's three global examples, run through the oracle's
+    extended records: 32 consecutive words (1 line, efficiency 1.0), a 128-byte
+    stride (32 lines, 0.03125) and 32 words from byte 64 (2 lines, 0.5)."""
+    from analysis_ptxsimulator_amd import ks
+    cases = [([i * 4 for i in range(32)], 1, 1.0), ([i * 128 for i in range(32)], 32, 0.03125),
+             ([64 + i * 4 for i in range(32)], 2, 0.5)]
+    gaddr = np.concatenate([np.array(c[0], np.uint64) for c in cases])
+    w = S.addr_probe(gaddr, np.zeros(len(gaddr), np.uint32), np.ones(len(gaddr), np.uint32), 4096, block=96)
+    _, (hdr, rec) = ext(oracle_mod, w)
+    info = A.ProgramInfo(w.ptx)
+    for wi, (_, lines, eff) in enumerate(cases):
+        r = rec[wi, :hdr["records_written"][wi]]
+        probe = [x for x in r if int(x["kind"]) == ks.KS_EV_LD_GLOBAL
+                 and info.desc[int(x["pc"])]["access_bytes"] == 4 and (int(x["payload"]) >> 8) & 0xFF == lines]
+        assert probe, wi
+        got = A.coalescing_efficiency(int(probe[0]["kind"]), probe[0]["payload"], 4)
+        assert got == eff
+    assert A.coalescing_efficiency(ks.KS_EV_OTHER, 0xFFFFFFFF, 4) is None
+
+
+def test_divergence_and_occupancy_hints(A, oracle_mod):
+    # vector_add: warp 31 splits 8 / 24 at the bounds check: ratio 0.25, no warning
+    w = W.vector_add()
+    _, (hdr, rec) = ext(oracle_mod, w)
+    info = A.ProgramInfo(w.ptx)
+    assert A.hints(hdr, rec, info, warps_per_block=w.warps_per_block) == []
+    # lanes splitting evenly on their data: every divergent branch is a warning
+    ptx = S.random_cfg_ptx(3)
+    n = 64
+    g = np.zeros(8 * n + 4096, np.uint8)
+    g[:4 * n] = np.tile(np.array([0, 0xFFFFFFFF], np.uint32), n // 2).view(np.uint8)
+    wk = W.Workload(name="cfg", ptx=ptx, grid=(1, 1, 1), block=(n, 1, 1),
+                    params=[("param_in", "u64", 0), ("param_out", "u64", 4 * n)], gmem=g, trace_cap=256)
+    c, (hdr, rec) = ext(oracle_mod, wk)
+    hs = A.hints(hdr, rec, A.ProgramInfo(ptx), warps_per_block=2)
+    div = [h for h in hs if h["category"] == "divergence" and "warp" in h]
+    n_div = int(c["diverge_n"].sum())
+    assert len(div) <= n_div
+    for h in div:
+        r = rec[h["warp"], h["record"]]
+        act, taken = int(r["active"]), int(r["payload"]) & int(r["active"])
+        assert min(bin(taken).count("1"), bin(act & ~taken).count("1")) / bin(act).count("1") > 0.4
+    if n_div > 3:
+        assert any(h["message"] == "Branch divergence detected (%d events)" % n_div for h in hs)
+    assert [h["severity"] for h in A.hints(hdr[:0], rec[:0], info, A.occupancy("sm_80", 256, 32))] == []
+    # 25%: not below 25 (no critical), below 50 (warning)
+    assert [h["severity"] for h in A.hints(hdr[:0], rec[:0], info, A.occupancy("sm_80", 256, 128))] == ["warning"]
+    assert [h["severity"] for h in A.hints(hdr[:0], rec[:0], info, A.occupancy("sm_80", 256, 200))] == ["critical"]
+    assert [h["severity"] for h in A.hints(hdr[:0], rec[:0], info, A.occupancy("sm_80", 256, 80))] == ["warning"]
+
+
+def test_chrome_trace_export(A, oracle_mod):
+    w = W.vector_add()
+    _, (hdr, rec) = ext(oracle_mod, w)
+    info = A.ProgramInfo(w.ptx)
+    t = json.loads(json.dumps(A.chrome_trace(hdr, rec, info, w.warps_per_block)))
+    gold = json.load(open(os.path.join(GOLDEN, "vector_add_trace.json")))
+    cyc = gold["issue_cycles"]
+    ev = [e for e in t["traceEvents"] if e["ph"] == "X"]
+    assert len(ev) == 32 * 19
+    meta = [e for e in t["traceEvents"] if e["ph"] == "M"]
+    assert sorted({(e["pid"], e["args"]["name"]) for e in meta if e["name"] == "process_name"}) == \
+        [(b, "block %d" % b) for b in range(4)]
+    w0 = [e for e in ev if e["pid"] == 0 and e["tid"] == 0]
+    assert [e["ts"] for e in w0] == cyc
+    assert [e["dur"] for e in w0] == [b - a for a, b in zip(cyc, cyc[1:])] + [1]
+    names = [e["name"] for e in w0]
+    assert names[:4] == ["ld.param.u64"] * 3 + ["ld.param.u32"]
+    assert names[9] == "bra" and names[12] == "ld.global.f32" and names[17] == "st.global.f32" and names[18] == "ret"
+    assert w0[12]["args"]["sectors"] == 4 and w0[12]["args"]["lines"] == 1 and w0[12]["cat"] == "ld.global"
+    w31 = [e for e in ev if e["pid"] == 3 and e["tid"] == 7]
+    assert w31[9]["cat"] == "diverge" and w31[9]["args"]["taken"] == 0xFFFFFF00
+    assert w31[12]["args"]["active"] == "0x000000ff"
+    # the basic 8-byte records export the same timeline, without payloads
+    g = w.gmem.copy()
+    _, tb, _ = oracle_mod.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=w.trace_cap)
+    hb, rb = oracle_mod.trace_slots(tb, w.trace_cap)
+    tbj = A.chrome_trace(hb, rb, info, w.warps_per_block, trace_format=0)
+    evb = [e for e in tbj["traceEvents"] if e["ph"] == "X"]
+    assert [(e["ts"], e["dur"], e["name"]) for e in evb] == [(e["ts"], e["dur"], e["name"]) for e in ev]

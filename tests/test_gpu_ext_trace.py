@@ -130,3 +130,27 @@ def test_faulting_and_misaligned_lanes(K, oracle_mod):
 def test_budget(K, oracle_mod):
     ext_parity(K, oracle_mod, W.random_stress(prog_seed=0, grid=2, block=256, gmem_bytes=1 << 22, trace_cap=64),
                max_warp_instrs=100)
+
+
+@pytest.mark.parametrize("case", ["bank_8", "strided_33", "random_1"])
+def test_host_analysis_on_gpu_records(K, oracle_mod, case):
+    """Hints and the trace-event export computed from the GPU's extended records
+    equal those computed from the oracle's."""
+    from analysis_ptxsimulator_amd import analysis as A
+    kind, arg = case.split("_")
+    if kind == "bank":
+        w = W.bank_probe(int(arg), iters=3, grid=2, block=256, trace_cap=64)
+    elif kind == "strided":
+        w = W.strided_gather(int(arg), n=4096)
+    else:
+        w = W.random_stress(prog_seed=int(arg), grid=2, block=256, gmem_bytes=1 << 22, trace_cap=2048)
+    _, _, tg, _ = gpu_run(K, w, K.KS_TRACE_EXTENDED, w.trace_cap)
+    go = w.gmem.copy()
+    _, to, _ = oracle_mod.run(w.ptx, w.grid, w.block, w.params_bytes, go, trace_cap=w.trace_cap,
+                              trace_format=oracle_mod.TRACE_EXTENDED)
+    info = A.ProgramInfo(w.ptx)
+    occ = A.program_occupancy(w.ptx, w.threads_per_block)
+    hg, rg = K.trace_slots(tg, w.trace_cap, K.KS_TRACE_EXTENDED)
+    ho, ro = oracle_mod.trace_slots(to, w.trace_cap, oracle_mod.TRACE_EXTENDED)
+    assert A.hints(hg, rg, info, occ, w.warps_per_block) == A.hints(ho, ro, info, occ, w.warps_per_block)
+    assert A.chrome_trace(hg, rg, info, w.warps_per_block) == A.chrome_trace(ho, ro, info, w.warps_per_block)

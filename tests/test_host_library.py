@@ -120,6 +120,28 @@ def test_layout_and_default_config(ks):
     ks.ks_program_free(p)
 
 
+def test_extended_layout_and_grid_limit(ks):
+    """Extended slots hold 16-byte records; an extended allocation of more than
+    KS_EXT_MAX_BLOCKS blocks is refused before any device work (the basic format
+    takes any grid)."""
+    p = ks.ks_load_program(W.VECTOR_ADD_PTX)
+    cfg = ks.ks_default_config()
+    cfg.max_block = ks.ks_dim3(256, 1, 1)
+    cfg.trace_cap = 32
+    cfg.trace_format = ks.KS_TRACE_EXTENDED
+    cfg.max_grid = ks.ks_dim3(ks.KS_EXT_MAX_BLOCKS // 2, 2, 1)
+    lay = ks.ks_query_layout(p, cfg)
+    assert lay.slot_bytes == 16 + 16 * 32 and lay.n_warps == 8 * ks.KS_EXT_MAX_BLOCKS
+    cfg.max_grid = ks.ks_dim3(ks.KS_EXT_MAX_BLOCKS + 1, 1, 1)
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_query_layout(p, cfg)
+    assert e.value.code == -2 and "%d blocks" % ks.KS_EXT_MAX_BLOCKS in e.value.msg
+    cfg.trace_format = ks.KS_TRACE_BASIC
+    cfg.max_grid = ks.ks_dim3(65536, 1, 1)
+    assert ks.ks_query_layout(p, cfg).n_warps == 8 * 65536
+    ks.ks_program_free(p)
+
+
 def test_default_latency_matches_oracle(ks, oracle_mod):
     assert list(ks.ks_default_config().latency) == oracle_mod.default_latency()
 
@@ -161,3 +183,26 @@ def test_interp_kernel_choice(ks):
     finally:
         ks.ks_program_free(small)
         ks.ks_program_free(big)
+
+
+def test_instr_info_maps_pcs_to_source_lines(ks):
+    """ks_instr_info: each decoded instruction's PTX line, record kind and access width."""
+    import re as _re
+    ptx = W.VECTOR_ADD_PTX
+    lines = ptx.split("\n")
+    p = ks.ks_load_program(ptx)
+    try:
+        n = ks.ks_program_info(p)["n_instrs"]
+        d = [ks.ks_instr_info(p, pc) for pc in range(n)]
+        with pytest.raises(ks.KsError):
+            ks.ks_instr_info(p, n)
+    finally:
+        ks.ks_program_free(p)
+    texts = [_re.sub(r"^@!?%\w+\s+", "", lines[x["line"] - 1].strip()) for x in d]
+    assert [t.split()[0] for t in texts] == (["ld.param.u64"] * 3 + ["ld.param.u32"] + ["mov.u32"] * 3 +
+                                             ["mad.lo.s32", "setp.ge.s32", "bra", "mul.wide.s32", "add.s64",
+                                              "ld.global.f32", "add.s64", "ld.global.f32", "add.f32", "add.s64",
+                                              "st.global.f32", "ret;"])
+    assert [x["kind"] for x in d] == [0] * 9 + [5, 0, 0, 1, 0, 1, 0, 0, 2, 8]
+    assert [x["access_bytes"] for x in d] == [0] * 12 + [4, 0, 4, 0, 0, 4, 0]
+    assert d[15]["lat_class"] == 2 and d[12]["lat_class"] == 7  # add.f32: FP32; ld.global

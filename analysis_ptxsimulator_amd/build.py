@@ -29,12 +29,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp
 # The VGPR register-file kernels keep simulated registers in v56 and up, which
 # the compiler must never allocate (they are reserved by amdgpu_num_vgpr), and
 # their VGPR count must cover the file; no interpreter may use scratch memory.
-RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64", "ks_interp_v32_ext", "ks_interp_v64_ext")
+RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64", "ks_interp_v32_ext", "ks_interp_v64_ext",
+                         "ks_interp_v32_cache", "ks_interp_v64_cache")
 INTERP_KERNELS = RESERVED_VGPR_KERNELS
 # first VGPR of each kernel's register file (compiler-allocated code stays below it)
-RESERVED_BASE = {"ks_interp_v32": 56, "ks_interp_v64": 56, "ks_interp_v32_ext": 64, "ks_interp_v64_ext": 64}
+RESERVED_BASE = {"ks_interp_v32": 56, "ks_interp_v64": 56, "ks_interp_v32_ext": 64, "ks_interp_v64_ext": 64,
+                 "ks_interp_v32_cache": 64, "ks_interp_v64_cache": 64}
 # register-file VGPRs from RESERVED_BASE on
-RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72, "ks_interp_v32_ext": 40, "ks_interp_v64_ext": 72}
+RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72, "ks_interp_v32_ext": 40, "ks_interp_v64_ext": 72,
+            "ks_interp_v32_cache": 40, "ks_interp_v64_cache": 72}
 
 
 

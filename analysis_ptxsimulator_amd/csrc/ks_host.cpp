@@ -1132,6 +1132,7 @@ struct ks_state {
   void* d_gmem;
   void* d_counters;
   void* d_trace;
+  void* d_cache;              // the cache model's per-warp state (NULL without it)
   uint32_t* d_status;
   uint64_t last_warps = 0;    // warps of the last run (0 = no run yet)
   uint64_t slot_bytes;
@@ -1244,6 +1245,10 @@ ks_status ks_default_config(ks_config* cfg) {
     L[KS_LAT_ST_SHARED] = 23;
     L[KS_LAT_BRA] = 4;
     L[KS_LAT_BAR] = 20;
+    // cache model: the cache latencies of the KernelScope memory-analysis part
+    L[KS_LAT_L1_HIT] = 28;
+    L[KS_LAT_L2_HIT] = 150;
+    L[KS_LAT_DRAM] = 400;
     L[KS_LAT_RET] = 4;
     return KS_OK;
   });
@@ -1266,18 +1271,27 @@ ks_status ks_query_layout(const ks_program* p, const ks_config* cfg, ks_layout* 
       raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", cfg->trace_format);
     if (cfg->trace_format == KS_TRACE_EXTENDED && nb > KS_EXT_MAX_BLOCKS)
       raise(KS_E_UNSUPPORTED, 0, "extended trace records support grids of up to %d blocks", KS_EXT_MAX_BLOCKS);
+    if (cfg->cache_model != KS_CACHE_NONE && cfg->cache_model != KS_CACHE_WARP)
+      raise(KS_E_INVALID_ARG, 0, "unknown cache model %u", cfg->cache_model);
+    if (cfg->cache_model == KS_CACHE_WARP) {
+      if (cfg->trace_format != KS_TRACE_BASIC) raise(KS_E_UNSUPPORTED, 0, "the cache model runs with basic trace records");
+      // valid addresses give line numbers below 2^31: tags (line + 1) fit 32 bits
+      if (cfg->gmem_bytes > (1ull << 38)) raise(KS_E_UNSUPPORTED, 0, "the cache model covers at most 2^38 bytes");
+    }
     out->slot_bytes = 16 + (cfg->trace_format == KS_TRACE_EXTENDED ? 16 : 8) * (uint64_t)cfg->trace_cap;
     out->trace_bytes = out->n_warps * out->slot_bytes;
+    out->cache_bytes = cfg->cache_model == KS_CACHE_WARP ? out->n_warps * (uint64_t)KS_CACHE_WARP_BYTES : 0;
     return KS_OK;
   });
 }
 
 ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem, void* d_counters, void* d_trace,
-                         ks_state** out) {
+                         void* d_cache, ks_state** out) {
   return guarded([&]() -> ks_status {
     if (!p || !cfg || !out) raise(KS_E_INVALID_ARG, 0, "NULL argument");
     *out = nullptr;
     if (!d_gmem || !d_counters || !d_trace) raise(KS_E_INVALID_ARG, 0, "NULL device buffer");
+    if (cfg->cache_model == KS_CACHE_WARP && !d_cache) raise(KS_E_INVALID_ARG, 0, "NULL cache buffer");
     if (p->reg_slots > KS_MAX_REG_SLOTS) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots (limit %d)", p->reg_slots, KS_MAX_REG_SLOTS);
     if (p->n_preds > KS_MAX_PREDS) raise(KS_E_UNSUPPORTED, 0, "program needs %u predicates (limit %d)", p->n_preds, KS_MAX_PREDS);
     if (p->code.empty()) raise(KS_E_INVALID_ARG, 0, "empty program");
@@ -1310,6 +1324,7 @@ ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem
     st->d_gmem = d_gmem;
     st->d_counters = d_counters;
     st->d_trace = d_trace;
+    st->d_cache = cfg->cache_model == KS_CACHE_WARP ? d_cache : nullptr;
     st->d_status = d_status;
     st->slot_bytes = lay.slot_bytes;
     st->max_warps = lay.n_warps;
@@ -1368,6 +1383,11 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
     }
     a.rf_slots = p->reg_slots + KS_IMM_SLOTS;
     a.ext = st->cfg.trace_format == KS_TRACE_EXTENDED ? 1u : 0u;
+    a.cache = (uint8_t*)st->d_cache;
+    a.cache_on = st->d_cache ? 1u : 0u;
+    a.lat_l1 = st->cfg.latency[KS_LAT_L1_HIT];
+    a.lat_l2 = st->cfg.latency[KS_LAT_L2_HIT];
+    a.lat_dram = st->cfg.latency[KS_LAT_DRAM];
     // %tid.y and %tid.z divide the linear thread index (< 1024) by block sizes (<= 1024):
     // (t * ceil(2^22 / d)) >> 22 == t / d over that range, with no 32-bit overflow
     auto recip22 = [](uint64_t d) { return (uint32_t)(((1ull << 22) + d - 1) / d); };
@@ -1381,13 +1401,19 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       const int variant = ks_choose_variant(p->reg_slots, a.threads_per_block);
       if (variant == 0) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots", p->reg_slots);
       const uint32_t wg = 64u * ((a.warps_per_block + 1u) / 2u);
-      if (wg > ks_max_block_threads(variant, a.ext != 0))
-        raise(KS_E_UNSUPPORTED, 0, "extended trace records with %u register slots support blocks of up to %u threads",
+      if (wg > ks_max_block_threads(variant, a.ext != 0 || a.cache_on != 0))
+        raise(KS_E_UNSUPPORTED, 0, "extended trace records or the cache model with %u register slots support blocks of up to %u threads",
               p->reg_slots, ks_max_block_threads(variant, true));
       const size_t need = ks_lds_bytes(wg, p->shared_bytes, a.ext != 0);
       if (need + 64 > ks_lds_limit())
         raise(KS_E_UNSUPPORTED, 0, "block of %u threads needs %zu bytes of LDS (limit %zu)", a.threads_per_block, need,
               ks_lds_limit() - 64);
+    }
+    if (a.cache_on) {
+      // the caches of this run's warps start empty
+      if (!hip_ok(hipMemsetAsync(st->d_cache, 0, warps * (uint64_t)KS_CACHE_WARP_BYTES, (hipStream_t)stream),
+                  "hipMemsetAsync(cache)"))
+        return KS_E_HIP;
     }
     hipError_t e = ks_launch_interp(a, (uint32_t)nb, p->reg_slots, (hipStream_t)stream);
     if (!hip_ok(e, "kernel launch")) return KS_E_HIP;

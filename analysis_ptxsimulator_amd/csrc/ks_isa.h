@@ -162,6 +162,9 @@ struct KsArgs {
   uint32_t cyc_safe;       // a run may continue past its first instruction when that one issues
                            // at most at this cycle: RUN_MAX issues cannot then pass the cycle limit
   uint32_t ext;            // 1: extended 16-byte trace records (KS_TRACE_EXTENDED)
+  uint8_t* cache;          // cache model (KS_CACHE_WARP): KS_CACHE_WARP_BYTES of state per warp
+  uint32_t cache_on;       // 1: the cache model is on
+  uint32_t lat_l1, lat_l2, lat_dram;  // its latencies
   uint32_t div_bx, div_by, div_bxy;  // ceil(2^22 / d) for d = block x, y and x * y (special registers)
   uint8_t params[KS_PARAM_MAX];
 };

@@ -395,7 +395,8 @@ __device__ __forceinline__ void stk_push(Stk& S, uint32_t top_mask, uint32_t pc,
 
 // EXT: extended 16-byte trace records (kind, active mask, payload) written from
 // each step, instead of the staged 8-byte {issue cycle, pc} records.
-template <int RFN, bool EXT>
+// CACHE: the cache-latency model (per-warp direct-mapped L1 and L2 in a.cache).
+template <int RFN, bool EXT, bool CACHE>
 __device__ __forceinline__ void interp(const KsArgs& a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ uint32_t ep_max[3], ep_alive[3];
@@ -416,8 +417,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 
   // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] (to 16 bytes)
   //      [EXT: record ring, 32 x 16 bytes per warp] [shared window]
-  RegFile<RFN, EXT ? 64 : 56> R;
-  RegFile<RFN, EXT ? 64 : 56>::zero();
+  RegFile<RFN, (EXT || CACHE) ? 64 : 56> R;
+  RegFile<RFN, (EXT || CACHE) ? 64 : 56>::zero();
   uint32_t* const sbw = lds;
   uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
   const uint32_t sb_words = (WG / 32u + 1u) * KS_SB_ENTRIES;
@@ -635,6 +636,50 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   // has completed, so that it no longer reads its address or data registers then.
 #define KS_EXT_STORE_WAIT()                                                          \
   if constexpr (EXT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+
+  // Cache-latency model (KernelScope memory analysis: direct-mapped L1 and L2 of
+  // 128-byte lines): the line of the lowest valid guard lane of each warp (okm)
+  // is looked up in that warp's L1, on a miss in its L2, installing it where it
+  // missed; lane 0 of each half does its warp's lookup.  The outcome (0 L1 hit,
+  // 1 L2 hit, 2 miss) is counted in lanes 32 h + 20 + outcome of cnt, and a load's
+  // destination becomes ready after that level's latency (a warp with no valid
+  // lane keeps the ld.global latency its issue wrote).  Valid addresses are below
+  // 2^38 bytes, so line numbers fit 32 bits.
+#define KS_CACHE_ACCESS(A, okm, is_load, sbod_)                                       \
+  if constexpr (CACHE) {                                                            \
+    const uint32_t v0_ = (uint32_t)(okm), v1_ = (uint32_t)((okm) >> 32);            \
+    const uint32_t lnl_ = (uint32_t)((A) >> 7);                                     \
+    const uint32_t line0_ = rl(lnl_, v0_ ? (uint32_t)__builtin_ctz(v0_) : 0u);       \
+    const uint32_t line1_ = rl(lnl_, v1_ ? 32u + (uint32_t)__builtin_ctz(v1_) : 32u); \
+    const uint32_t line_ = hl ? line1_ : line0_;                                    \
+    uint32_t lvl_ = 3u;                                                             \
+    if (sl == 0u && (hl ? v1_ : v0_) != 0u) {                                        \
+      uint32_t* const cw_ = reinterpret_cast<uint32_t*>(a.cache + (gw0 + hl) * (uint64_t)KS_CACHE_WARP_BYTES); \
+      const uint32_t t_ = line_ + 1u;                                               \
+      uint32_t* const e1_ = cw_ + 4u + (line_ & (KS_CACHE_L1_LINES - 1u));          \
+      uint32_t* const e2_ = cw_ + 4u + KS_CACHE_L1_LINES + line_ % KS_CACHE_L2_LINES; \
+      if (*e1_ == t_) {                                                             \
+        lvl_ = 0u;                                                                  \
+      } else {                                                                      \
+        *e1_ = t_;                                                                  \
+        if (*e2_ == t_) {                                                           \
+          lvl_ = 1u;                                                                \
+        } else {                                                                    \
+          *e2_ = t_;                                                                \
+          lvl_ = 2u;                                                                \
+        }                                                                           \
+      }                                                                             \
+    }                                                                               \
+    /* index mode follows soon: the tag stores must be done with their registers */ \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                \
+    const uint32_t my_lv_ = hl ? rl(lvl_, 32) : rl(lvl_, 0);                         \
+    cnt += (my_lv_ < 3u && sl == 20u + my_lv_) ? 1u : 0u;                            \
+    /* the three latencies as values (a select of their fields would address the */ \
+    /* kernel arguments dynamically and copy them to scratch) */                    \
+    const uint32_t c1_ = uni(a.lat_l1), c2_ = uni(a.lat_l2), c3_ = uni(a.lat_dram);  \
+    if ((is_load) && my_lv_ < 3u)                                                   \
+      *reinterpret_cast<uint32_t*>(sb_sel + (sbod_)) = is + (my_lv_ == 0u ? c1_ : (my_lv_ == 1u ? c2_ : c3_)); \
+  }
 
   // Issue cycle of the instruction whose hot words are h: the later of the warp's
   // previous issue + 1 and the ready cycle of every register source (absent
@@ -882,11 +927,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               // lands in the wrong register).
               KS_COUNT_FAULTS(faults);
               KS_GLOBAL_ACCOUNT(A, 4u, faults, true);
+              KS_CACHE_ACCESS(A, okm, true, h[10]);
               R.put_m(dst, ld_v, okm);
             } else {
               if (lanes(okm)) *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
               KS_COUNT_FAULTS(faults);
               KS_GLOBAL_ACCOUNT(A, 4u, faults, false);
+              KS_CACHE_ACCESS(A, okm, false, h[10]);
             }
             if constexpr (EXT) {
               const uint32_t p0 = x_sl0 | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
@@ -1024,6 +1071,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             [[maybe_unused]] uint32_t x_sl0 = 0, x_sl1 = 0;
             if (is_global) {
               KS_GLOBAL_ACCOUNT(A, S, faults, is_load);
+              KS_CACHE_ACCESS(A, okm, is_load, h[10]);
               if constexpr (EXT) {
                 const uint32_t p0 = x_sl0 | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
                 const uint32_t p1 = x_sl1 | (popc((uint32_t)(on64 >> 32)) << 16) | (popc((uint32_t)(faults >> 32)) << 24);
@@ -1145,6 +1193,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 #undef KS_SETTLE
 #undef KS_COUNT_FAULTS
 #undef KS_GLOBAL_ACCOUNT
+#undef KS_CACHE_ACCESS
   act += lanes(m64) ? wi : 0u;
 #undef KS_SET_LIVE
 
@@ -1204,6 +1253,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         }
         reinterpret_cast<uint32_t*>(a.counters + gw * 80u)[sl] = v;
       }
+      if constexpr (CACHE)  // the warp's cache outcome counts: L1 hits, L2 hits, misses
+        if (sl >= 20u && sl < 23u) reinterpret_cast<uint32_t*>(a.cache + gw * (uint64_t)KS_CACHE_WARP_BYTES)[sl - 20u] = cnt;
       if (sl < 4) {
         const uint32_t flags = (dropped ? 1u : 0u) | ((st & KS_ST_FAULT) ? 2u : 0u) |
                                ((st & KS_ST_BUDGET) ? 4u : 0u) | ((st & KS_ST_FINISHED) ? 8u : 0u);
@@ -1225,23 +1276,29 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 // Register file in 40 reserved VGPRs (v56..v95): 96 VGPRs, 5 waves per SIMD,
 // blocks up to 1024 threads.
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v32(const KsArgs a) {
-  interp<40, false>(a);
+  interp<40, false, false>(a);
 }
 
 // Register file in 72 reserved VGPRs (v56..v127): 128 VGPRs, 4 waves per SIMD,
 // blocks up to 1024 threads.
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v64(const KsArgs a) {
-  interp<72, false>(a);
+  interp<72, false, false>(a);
 }
 
 // The same interpreters writing extended 16-byte trace records, with 64 compiler
 // VGPRs and the register file from v64: 104 VGPRs (4 waves per SIMD, blocks up to
 // 1024 threads) and 136 (3 waves per SIMD, so blocks up to 768 threads).
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v32_ext(const KsArgs a) {
-  interp<40, true>(a);
+  interp<40, true, false>(a);
 }
 __global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64_ext(const KsArgs a) {
-  interp<72, true>(a);
+  interp<72, true, false>(a);
+}
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v32_cache(const KsArgs a) {
+  interp<40, false, true>(a);
+}
+__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64_cache(const KsArgs a) {
+  interp<72, false, true>(a);
 }
 
 __global__ void ks_zero_word(uint32_t* out) { *out = 0; }
@@ -1284,13 +1341,15 @@ hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, 
   const uint32_t wg = 64u * waves;
   const int variant = ks_choose_variant(slots, a.threads_per_block);
   const size_t lds = ks_lds_bytes(wg, a.shared_bytes, a.ext != 0);
-  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0))
+  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0 || a.cache_on != 0))
     return hipErrorInvalidValue;
   if (a.rf_slots != slots + KS_IMM_SLOTS) return hipErrorInvalidValue;
-  const int vi = (variant == 32 ? 0 : 1) + (a.ext ? 2 : 0);
-  const void* const fns[4] = {(const void*)ks_interp_v32, (const void*)ks_interp_v64, (const void*)ks_interp_v32_ext,
-                              (const void*)ks_interp_v64_ext};
-  static bool attr_set[4] = {false, false, false, false};
+  if (a.ext && a.cache_on) return hipErrorInvalidValue;
+  const int vi = (variant == 32 ? 0 : 1) + (a.ext ? 2 : 0) + (a.cache_on ? 4 : 0);
+  const void* const fns[6] = {(const void*)ks_interp_v32,     (const void*)ks_interp_v64,
+                              (const void*)ks_interp_v32_ext, (const void*)ks_interp_v64_ext,
+                              (const void*)ks_interp_v32_cache, (const void*)ks_interp_v64_cache};
+  static bool attr_set[6] = {false, false, false, false, false, false};
   if (!attr_set[vi]) {
     hipError_t e = hipFuncSetAttribute(fns[vi], hipFuncAttributeMaxDynamicSharedMemorySize, (int)(ks_lds_limit() - 64));
     if (e != hipSuccess) return e;
@@ -1300,7 +1359,9 @@ hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, 
     case 0: hipLaunchKernelGGL(ks_interp_v32, dim3(n_blocks), dim3(wg), lds, s, a); break;
     case 1: hipLaunchKernelGGL(ks_interp_v64, dim3(n_blocks), dim3(wg), lds, s, a); break;
     case 2: hipLaunchKernelGGL(ks_interp_v32_ext, dim3(n_blocks), dim3(wg), lds, s, a); break;
-    default: hipLaunchKernelGGL(ks_interp_v64_ext, dim3(n_blocks), dim3(wg), lds, s, a); break;
+    case 3: hipLaunchKernelGGL(ks_interp_v64_ext, dim3(n_blocks), dim3(wg), lds, s, a); break;
+    case 4: hipLaunchKernelGGL(ks_interp_v32_cache, dim3(n_blocks), dim3(wg), lds, s, a); break;
+    default: hipLaunchKernelGGL(ks_interp_v64_cache, dim3(n_blocks), dim3(wg), lds, s, a); break;
   }
   return hipGetLastError();
 }

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkscope.so")
 
 KS_OK = 0
-KS_NLAT = 16
+KS_NLAT = 18
 ST_FINISHED, ST_BUDGET, ST_FAULT, ST_TRACE_DROP, ST_BARDIV, ST_CYCLE_OVF = 1, 2, 4, 8, 16, 32
 LAT_LD_GLOBAL, LAT_BAR = 7, 12
 
@@ -30,6 +30,12 @@ TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("
 # trace formats (ks_config.trace_format) and the 16-byte extended record
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
 KS_EXT_MAX_BLOCKS = 32  # largest grid of an extended-record allocation or run
+# cache-latency model (ks_config.cache_model) and its per-warp state in d_cache
+KS_CACHE_NONE, KS_CACHE_WARP = 0, 1
+KS_LAT_L1_HIT, KS_LAT_L2_HIT, KS_LAT_DRAM = 14, 15, 16
+KS_CACHE_L1_LINES, KS_CACHE_L2_LINES = 1024, 49152
+KS_CACHE_WARP_BYTES = 16 + 4 * (KS_CACHE_L1_LINES + KS_CACHE_L2_LINES)
+CACHE_HEADER_DTYPE = np.dtype([("l1_hits", "<u4"), ("l2_hits", "<u4"), ("misses", "<u4"), ("reserved", "<u4")])
 EXT_RECORD_DTYPE = np.dtype([("cycle", "<u4"), ("pc", "<u2"), ("kind", "u1"), ("reserved", "u1"),
                              ("active", "<u4"), ("payload", "<u4")])
 EV_NAMES = ["other", "ld.global", "st.global", "ld.shared", "st.shared", "branch", "diverge", "barrier", "ret"]
@@ -52,7 +58,7 @@ class ks_config(ctypes.Structure):
     _fields_ = [("max_grid", ks_dim3), ("max_block", ks_dim3), ("gmem_bytes", ctypes.c_uint64),
                 ("trace_cap", ctypes.c_uint32), ("max_warp_instrs", ctypes.c_uint32),
                 ("latency", ctypes.c_uint16 * KS_NLAT), ("trace_format", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32)]
+                ("cache_model", ctypes.c_uint32)]
 
 
 class ks_program_desc(ctypes.Structure):
@@ -67,7 +73,8 @@ class ks_instr_desc(ctypes.Structure):
 
 class ks_layout(ctypes.Structure):
     _fields_ = [("warps_per_block", ctypes.c_uint32), ("reserved", ctypes.c_uint32), ("n_warps", ctypes.c_uint64),
-                ("counters_bytes", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64), ("trace_bytes", ctypes.c_uint64)]
+                ("counters_bytes", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64), ("trace_bytes", ctypes.c_uint64),
+                ("cache_bytes", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -80,7 +87,7 @@ _EXPORTS = {
     "ks_instr_info": ([_P, ctypes.c_uint32, ctypes.POINTER(ks_instr_desc)], ctypes.c_int32),
     "ks_default_config": ([ctypes.POINTER(ks_config)], ctypes.c_int32),
     "ks_query_layout": ([_P, ctypes.POINTER(ks_config), ctypes.POINTER(ks_layout)], ctypes.c_int32),
-    "ks_alloc_state": ([_P, ctypes.POINTER(ks_config), _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int32),
+    "ks_alloc_state": ([_P, ctypes.POINTER(ks_config), _P, _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int32),
     "ks_run": ([_P, ks_dim3, ks_dim3, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
     "ks_interp_kernel": ([_P, ks_dim3, ctypes.POINTER(ctypes.c_char_p)], ctypes.c_int32),
     "ks_read_outputs": ([_P, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
@@ -174,9 +181,10 @@ def ks_query_layout(prog, cfg):
     return lay
 
 
-def ks_alloc_state(prog, cfg, d_gmem, d_counters, d_trace):
+def ks_alloc_state(prog, cfg, d_gmem, d_counters, d_trace, d_cache=0):
     out = _P()
-    _check(lib().ks_alloc_state(prog, ctypes.byref(cfg), _P(d_gmem), _P(d_counters), _P(d_trace), ctypes.byref(out)))
+    _check(lib().ks_alloc_state(prog, ctypes.byref(cfg), _P(d_gmem), _P(d_counters), _P(d_trace), _P(d_cache),
+                                ctypes.byref(out)))
     return out
 
 
@@ -244,7 +252,7 @@ class Session:
     Memory management only; all simulation work happens in ks_run."""
 
     def __init__(self, ptx, grid, block, gmem_bytes, trace_cap=0, max_warp_instrs=0xFFFFFFFF, latency=None,
-                 device="cuda:0", entry=None, trace_format=KS_TRACE_BASIC):
+                 device="cuda:0", entry=None, trace_format=KS_TRACE_BASIC, cache_model=KS_CACHE_NONE):
         import torch
         self.torch = torch
         self.device = torch.device(device)
@@ -257,7 +265,9 @@ class Session:
         cfg.trace_cap = int(trace_cap)
         cfg.max_warp_instrs = int(max_warp_instrs)
         cfg.trace_format = int(trace_format)
+        cfg.cache_model = int(cache_model)
         self.trace_format = int(trace_format)
+        self.cache_model = int(cache_model)
         self.trace_cap = int(trace_cap)
         if latency is not None:
             lat = list(latency) + [0] * (KS_NLAT - len(latency))
@@ -269,9 +279,11 @@ class Session:
         self.gmem = torch.empty(max(int(gmem_bytes), 1), dtype=torch.uint8, device=self.device)
         self.counters = torch.empty(max(int(self.layout.counters_bytes), 1), dtype=torch.uint8, device=self.device)
         self.trace = torch.empty(max(int(self.layout.trace_bytes), 1), dtype=torch.uint8, device=self.device)
+        self.cache = (torch.empty(int(self.layout.cache_bytes), dtype=torch.uint8, device=self.device)
+                      if self.layout.cache_bytes else None)
         with torch.cuda.device(self.device):
             self.state = ks_alloc_state(self.prog, cfg, self.gmem.data_ptr(), self.counters.data_ptr(),
-                                        self.trace.data_ptr())
+                                        self.trace.data_ptr(), self.cache.data_ptr() if self.cache is not None else 0)
 
     @property
     def n_warps(self):
@@ -311,7 +323,22 @@ class Session:
     def kernel_name(self):
         """Name of the interpreter kernel ks_run launches for this session."""
         name = ks_interp_kernel(self.prog, self.block)
-        return name + ("_ext" if self.trace_format == KS_TRACE_EXTENDED else "")
+        if self.trace_format == KS_TRACE_EXTENDED:
+            return name + "_ext"
+        return name + ("_cache" if self.cache_model == KS_CACHE_WARP else "")
+
+    def read_cache(self, first=0, n=None):
+        """The cache model's state of warps [first, first + n) after the last run:
+        (headers of CACHE_HEADER_DTYPE, L1 tags [n, 1024], L2 tags [n, 49152]) as u32,
+        a tag being the line number + 1 (0: empty)."""
+        assert self.cache is not None, "the session has no cache model"
+        n = self.last_warps - first if n is None else n
+        self.torch.cuda.synchronize(self.device)
+        raw = self.cache[first * KS_CACHE_WARP_BYTES:(first + n) * KS_CACHE_WARP_BYTES].cpu().numpy()
+        c = raw.reshape(n, KS_CACHE_WARP_BYTES)
+        hdr = c[:, :16].copy().view(CACHE_HEADER_DTYPE).reshape(-1)
+        tags = c[:, 16:].copy().view("<u4")
+        return hdr, tags[:, :KS_CACHE_L1_LINES], tags[:, KS_CACHE_L1_LINES:]
 
     def close(self):
         if getattr(self, "state", None):

@@ -72,12 +72,37 @@ typedef int32_t ks_status;
 #define KS_ST_CYCLE_OVF 0x20u  /* an issue cycle would exceed 2^31 - 1; warp stopped */
 
 /* Latency classes, the indices of ks_config.latency[]. */
-#define KS_NLAT 16
+#define KS_NLAT 18
 enum {
   KS_LAT_INT32 = 0, KS_LAT_INT64 = 1, KS_LAT_FP32 = 2, KS_LAT_SETP = 3, KS_LAT_SELP = 4,
   KS_LAT_MOV = 5, KS_LAT_LD_PARAM = 6, KS_LAT_LD_GLOBAL = 7, KS_LAT_LD_SHARED = 8,
-  KS_LAT_ST_GLOBAL = 9, KS_LAT_ST_SHARED = 10, KS_LAT_BRA = 11, KS_LAT_BAR = 12, KS_LAT_RET = 13
+  KS_LAT_ST_GLOBAL = 9, KS_LAT_ST_SHARED = 10, KS_LAT_BRA = 11, KS_LAT_BAR = 12, KS_LAT_RET = 13,
+  /* ld.global under the cache-latency model: L1 hit, L2 hit, miss in both */
+  KS_LAT_L1_HIT = 14, KS_LAT_L2_HIT = 15, KS_LAT_DRAM = 16
 };
+
+/* Cache-latency model (ks_config.cache_model), after the KernelScope simulator
+ * page's memory-analysis part (its cache parameters and direct-mapped SimpleCache):
+ *   KS_CACHE_NONE  ld.global takes latency[KS_LAT_LD_GLOBAL];
+ *   KS_CACHE_WARP  each warp owns a direct-mapped L1 of KS_CACHE_L1_LINES and L2 of
+ *                  KS_CACHE_L2_LINES 128-byte lines, empty at the start of every
+ *                  run.  A global warp access with at least one valid guard lane
+ *                  looks up the line of its lowest such lane in the L1, on a miss in
+ *                  the L2, installing it where it missed; a load's destination is
+ *                  then ready after latency[KS_LAT_L1_HIT], [KS_LAT_L2_HIT] or
+ *                  [KS_LAT_DRAM].  A load with no valid guard lane touches no cache
+ *                  and takes latency[KS_LAT_LD_GLOBAL].  The caches are private to
+ *                  each warp so that the result does not depend on how the
+ *                  simulated warps interleave (the page has one cache for all).
+ * The state lives in a caller-owned buffer d_cache of KS_CACHE_WARP_BYTES per warp:
+ * {u32 l1_hits, u32 l2_hits, u32 misses, u32 0}, the L1 tags, then the L2 tags, a
+ * tag being the line number + 1 (0: empty set).  Runs with the cache model use the
+ * basic trace format and at most 2^38 bytes of simulated memory. */
+#define KS_CACHE_NONE 0u
+#define KS_CACHE_WARP 1u
+#define KS_CACHE_L1_LINES 1024u
+#define KS_CACHE_L2_LINES 49152u
+#define KS_CACHE_WARP_BYTES (16u + 4u * (KS_CACHE_L1_LINES + KS_CACHE_L2_LINES))
 
 /* Trace record formats (ks_config.trace_format).  Both follow the IKET page's
  * per-warp slot: a 16-byte header {u32 records_written, u8 version, u8 flags,
@@ -131,7 +156,7 @@ typedef struct {
   uint32_t max_warp_instrs;  /* per-warp issue budget; a warp reaching it stops with KS_ST_BUDGET */
   uint16_t latency[KS_NLAT]; /* cycles per latency class (ks_default_config fills sm_80 values) */
   uint32_t trace_format;     /* KS_TRACE_BASIC (default) or KS_TRACE_EXTENDED */
-  uint32_t reserved;         /* 0 */
+  uint32_t cache_model;      /* KS_CACHE_NONE (default) or KS_CACHE_WARP */
 } ks_config;
 
 typedef struct {
@@ -150,6 +175,7 @@ typedef struct {
   uint64_t counters_bytes;   /* n_warps * 80: size of d_counters */
   uint64_t slot_bytes;       /* 16 + 8 * trace_cap (basic) or 16 + 16 * trace_cap (extended): one slot */
   uint64_t trace_bytes;      /* n_warps * slot_bytes: size of d_trace */
+  uint64_t cache_bytes;      /* n_warps * KS_CACHE_WARP_BYTES with the cache model, else 0: size of d_cache */
 } ks_layout;
 
 /* Parse a PTX module and decode the entry `entry` (NULL or "" = the first .entry).
@@ -187,25 +213,30 @@ ks_status ks_ipdom_table(const ks_program* prog, uint32_t* out, uint32_t n);
 
 /* Fill `cfg` with defaults: the sm_80 latency table of the KernelScope latency
  * page (int/fp32 4, ld.global 200, ld.shared 23, ld.param as ld.const 4,
- * bar.sync 20), trace_cap 0, max_warp_instrs 0xFFFFFFFF, max grid/block 1. */
+ * bar.sync 20) and the cache latencies of its memory-analysis part (L1 hit 28,
+ * L2 hit 150, DRAM 400), trace_cap 0, max_warp_instrs 0xFFFFFFFF, max grid/block
+ * 1, basic trace format, no cache model. */
 ks_status ks_default_config(ks_config* cfg);
 
 /* Sizes of the caller-owned device buffers for runs up to cfg->max_grid x
  * cfg->max_block.  The trace slot size follows the IKET page's per-warp slot
  * (a 16-byte header and fixed 8- or 16-byte records, without its 1.15 margin).
- * KS_E_INVALID_ARG for an unknown trace_format. */
+ * KS_E_INVALID_ARG for an unknown trace_format or cache_model; KS_E_UNSUPPORTED
+ * for the cache model with extended records or over more than 2^38 bytes. */
 ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layout* out);
 
 /* Bind a program to caller-owned device buffers on the current HIP device:
  *   d_gmem      cfg->gmem_bytes of simulated global memory (inputs are written here by
  *               the caller; ks_run updates it in place and it persists across runs),
  *   d_counters  layout.counters_bytes: 80-byte per-warp counter records,
- *   d_trace     layout.trace_bytes: per-warp trace slots.
+ *   d_trace     layout.trace_bytes: per-warp trace slots,
+ *   d_cache     layout.cache_bytes: the cache model's per-warp state (NULL
+ *               without the cache model; ks_run clears the run's part first).
  * Uploads the decoded program (latencies baked in from cfg) to a small device
  * buffer owned by the state.  Errors: KS_E_INVALID_ARG (NULL buffers, limits),
  * KS_E_UNSUPPORTED (program beyond this build's limits), KS_E_HIP, KS_E_NOMEM. */
 ks_status ks_alloc_state(const ks_program* prog, const ks_config* cfg, void* d_gmem, void* d_counters,
-                         void* d_trace, ks_state** out);
+                         void* d_trace, void* d_cache, ks_state** out);
 
 /* Launch one simulation of grid x block threads on `stream` (asynchronous).
  * `params` holds `params_len` >= param_bytes bytes of the parameter block (host
@@ -222,7 +253,8 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
  * as profilers list it: "ks_interp_v32" (programs of up to 34 register slots: a
  * 40-VGPR register file per lane, six slots of it for immediates) or
  * "ks_interp_v64" (up to 64 slots: a 72-VGPR file); runs with the extended trace
- * format launch the same kernel with the suffix "_ext".  *name points to a static
+ * format launch the same kernel with the suffix "_ext", runs with the cache model
+ * the one with the suffix "_cache".  *name points to a static
  * string.  Errors: KS_E_INVALID_ARG (NULL arguments, empty or oversized block). */
 ks_status ks_interp_kernel(const ks_program* prog, ks_dim3 block, const char** name);
 

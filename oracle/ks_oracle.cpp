@@ -1070,6 +1070,9 @@ struct Warp {
   };
   std::vector<Record> records;
   uint64_t dropped = 0;
+  // cache-latency model: tag of each set (-1 = empty) and the outcome counts
+  std::vector<int64_t> l1, l2;
+  uint32_t cache_count[3] = {0, 0, 0};  // L1 hits, L2 hits, misses
 };
 
 struct Sim {
@@ -1113,7 +1116,16 @@ struct Sim {
     return a % (uint64_t)s == 0 && a <= size && size - a >= (uint64_t)s;
   }
 
-  void run_block(uint64_t block_linear, oracle_counters* out_c, uint8_t* out_trace) {
+  // One access of the SimpleCache of the cache model: a hit when the line's set
+  // holds that line; a miss installs it.
+  static bool cache_access(std::vector<int64_t>& tags, uint64_t line) {
+    const size_t set = (size_t)(line % tags.size());
+    if (tags[set] == (int64_t)line) return true;
+    tags[set] = (int64_t)line;
+    return false;
+  }
+
+  void run_block(uint64_t block_linear, oracle_counters* out_c, uint8_t* out_trace, uint8_t* out_cache) {
     const Program& P = *p;
     uint32_t gx = cfg->grid[0], gy = cfg->grid[1];
     uint32_t ctaid[3] = {(uint32_t)(block_linear % gx), (uint32_t)((block_linear / gx) % gy),
@@ -1134,6 +1146,10 @@ struct Sim {
       w.ready.assign((size_t)P.n_vals + P.n_preds, 0);
       memset(&w.c, 0, sizeof w.c);
       w.c.max_stack_depth = 1;
+      if (cfg->flags & ORACLE_FLAG_CACHE) {
+        w.l1.assign(ORACLE_CACHE_L1_LINES, -1);
+        w.l2.assign(ORACLE_CACHE_L2_LINES, -1);
+      }
     }
 
     while (true) {
@@ -1208,6 +1224,14 @@ struct Sim {
         memcpy(d + 12, &r.payload, 4);
       }
       // records past records_written are left as they were in the caller's buffer
+      if (cfg->flags & ORACLE_FLAG_CACHE) {
+        uint8_t* cw = out_cache + (size_t)ORACLE_CACHE_WARP_BYTES * wi;
+        const uint32_t head[4] = {w.cache_count[0], w.cache_count[1], w.cache_count[2], 0};
+        memcpy(cw, head, 16);
+        uint32_t* tags = (uint32_t*)(cw + 16);
+        for (uint32_t k = 0; k < ORACLE_CACHE_L1_LINES; ++k) tags[k] = (uint32_t)(w.l1[k] + 1);
+        for (uint32_t k = 0; k < ORACLE_CACHE_L2_LINES; ++k) tags[ORACLE_CACHE_L1_LINES + k] = (uint32_t)(w.l2[k] + 1);
+      }
     }
   }
 
@@ -1286,6 +1310,7 @@ struct Sim {
 
       uint32_t next_pc = pc + 1;
       uint32_t kind = ORACLE_EV_OTHER, payload = g;
+      uint32_t dst_lat = lat(in.lat_class);  // the cache model may change a global load's
       switch (in.op) {
         case OP_ADD: case OP_SUB: case OP_MUL_LO: case OP_MUL_WIDE: case OP_MAD_LO:
         case OP_FADD: case OP_FSUB: case OP_FMUL: case OP_FFMA:
@@ -1309,6 +1334,7 @@ struct Sim {
         }
         case OP_LD_GLOBAL: case OP_ST_GLOBAL: case OP_LD_SHARED: case OP_ST_SHARED: {
           const MemInfo mi = memory_access(w, in, g, block_linear, shared, shared_races);
+          if (in.op == OP_LD_GLOBAL && mi.cache_latency) dst_lat = mi.cache_latency;
           const bool global = in.op == OP_LD_GLOBAL || in.op == OP_ST_GLOBAL;
           const bool load = in.op == OP_LD_GLOBAL || in.op == OP_LD_SHARED;
           kind = global ? (load ? ORACLE_EV_LD_GLOBAL : ORACLE_EV_ST_GLOBAL)
@@ -1365,7 +1391,7 @@ struct Sim {
         case OP_ADD: case OP_SUB: case OP_MUL_LO: case OP_MUL_WIDE: case OP_MAD_LO:
         case OP_FADD: case OP_FSUB: case OP_FMUL: case OP_FFMA:
         case OP_SELP: case OP_MOV: case OP_LD_PARAM: case OP_LD_GLOBAL: case OP_LD_SHARED:
-          w.ready[in.dst.reg] = issue + lat(in.lat_class);
+          w.ready[in.dst.reg] = issue + dst_lat;
           break;
         case OP_SETP:
           w.ready[P.n_vals + in.dst.reg] = issue + lat(in.lat_class);
@@ -1409,6 +1435,7 @@ struct Sim {
   // What the analyser found for one warp access (all 0 when no lane passes the guard).
   struct MemInfo {
     uint32_t sectors = 0, lines = 0, degree = 0, faults = 0;
+    uint32_t cache_latency = 0;  // cache model: latency of the access (0 = no cache access)
   };
 
   MemInfo memory_access(Warp& w, const Inst& in, uint32_t g, uint64_t block_linear,
@@ -1439,6 +1466,19 @@ struct Sim {
       }
       mi.sectors = (uint32_t)sectors.size();
       mi.lines = (uint32_t)lines.size();
+      if (cfg->flags & ORACLE_FLAG_CACHE) {
+        // the representative address: the lowest guard lane whose access is valid
+        for (int l = 0; l < 32; ++l) {
+          if (!((g >> l) & 1) || !valid(addr[l], size, in.size)) continue;
+          const uint64_t line = addr[l] / 128;
+          int level = 2;
+          if (cache_access(w.l1, line)) level = 0;
+          else if (cache_access(w.l2, line)) level = 1;
+          w.cache_count[level]++;
+          mi.cache_latency = lat(level == 0 ? ORACLE_LAT_L1_HIT : level == 1 ? ORACLE_LAT_L2_HIT : ORACLE_LAT_DRAM);
+          break;
+        }
+      }
       if (load) {
         w.c.gld_n++;
         w.c.gld_sectors += (uint32_t)sectors.size();
@@ -1521,6 +1561,10 @@ void default_latency(uint16_t* lat) {
   lat[ORACLE_LAT_BRA] = 4;
   lat[ORACLE_LAT_BAR] = 20;
   lat[ORACLE_LAT_RET] = 4;
+  // cache model (KernelScope memory-analysis part, cache parameters)
+  lat[ORACLE_LAT_L1_HIT] = 28;
+  lat[ORACLE_LAT_L2_HIT] = 150;
+  lat[ORACLE_LAT_DRAM] = 400;
 }
 
 }  // namespace
@@ -1587,6 +1631,9 @@ int oracle_run(const char* ptx, size_t len, const char* entry, const oracle_cfg*
     uint64_t tpb = (uint64_t)cfg->block[0] * cfg->block[1] * cfg->block[2];
     if (tpb > 1024) fail(ORACLE_E_INVALID_ARG, 0, "more than 1024 threads per block");
     if (params_len < p.param_bytes) fail(ORACLE_E_INVALID_ARG, 0, "parameter buffer too short");
+    if ((cfg->flags & ORACLE_FLAG_CACHE) && !cfg->cache) fail(ORACLE_E_INVALID_ARG, 0, "cache model without an output buffer");
+    if ((cfg->flags & ORACLE_FLAG_CACHE) && cfg->gmem_bytes > (1ull << 38))
+      fail(ORACLE_E_UNSUPPORTED, 0, "cache model over more than 2^38 bytes of memory");
     uint64_t n_blocks = (uint64_t)cfg->grid[0] * cfg->grid[1] * cfg->grid[2];
     std::vector<uint64_t> blocks;
     if (cfg->n_block_list) {
@@ -1621,7 +1668,8 @@ int oracle_run(const char* ptx, size_t len, const char* entry, const oracle_cfg*
       try {
         for (uint64_t i = lo; i < hi; ++i) {
           oracle_counters* c = (oracle_counters*)(counters + sizeof(oracle_counters) * sim.warps_per_block * i);
-          sim.run_block(blocks[i], c, trace + slot * sim.warps_per_block * i);
+          uint8_t* cw = cfg->cache ? cfg->cache + (size_t)ORACLE_CACHE_WARP_BYTES * sim.warps_per_block * i : nullptr;
+          sim.run_block(blocks[i], c, trace + slot * sim.warps_per_block * i, cw);
         }
       } catch (const OracleError& e) {
         codes[id] = e.code;

@@ -30,14 +30,16 @@
 extern "C" {
 #endif
 
-#define ORACLE_NLAT 16
+#define ORACLE_NLAT 18
 
 /* Latency classes: index into oracle_cfg.latency[]. */
 enum {
   ORACLE_LAT_INT32 = 0, ORACLE_LAT_INT64 = 1, ORACLE_LAT_FP32 = 2, ORACLE_LAT_SETP = 3,
   ORACLE_LAT_SELP = 4, ORACLE_LAT_MOV = 5, ORACLE_LAT_LD_PARAM = 6, ORACLE_LAT_LD_GLOBAL = 7,
   ORACLE_LAT_LD_SHARED = 8, ORACLE_LAT_ST_GLOBAL = 9, ORACLE_LAT_ST_SHARED = 10,
-  ORACLE_LAT_BRA = 11, ORACLE_LAT_BAR = 12, ORACLE_LAT_RET = 13
+  ORACLE_LAT_BRA = 11, ORACLE_LAT_BAR = 12, ORACLE_LAT_RET = 13,
+  /* ld.global under ORACLE_FLAG_CACHE: L1 hit, L2 hit, miss in both */
+  ORACLE_LAT_L1_HIT = 14, ORACLE_LAT_L2_HIT = 15, ORACLE_LAT_DRAM = 16
 };
 
 /* Per-warp status bits. */
@@ -57,6 +59,20 @@ enum {
 
 #define ORACLE_FLAG_CHECK_RACES 0x1u
 #define ORACLE_FLAG_EXT_TRACE 0x2u   /* 16-byte trace records (version 2) */
+#define ORACLE_FLAG_CACHE 0x4u       /* cache-latency model: per-warp L1 and L2 */
+
+/* Cache-latency model (KernelScope simulator page, memory-analysis part: the cache
+ * parameters and the direct-mapped SimpleCache).  Each warp owns an L1 of 1024 and
+ * an L2 of 49152 direct-mapped 128-byte lines, both empty at the start of a run.
+ * A global warp access with at least one valid guard lane looks up the line of its
+ * lowest such lane: the L1 first, on a miss the L2; a miss installs the line.  A
+ * load's destination is then ready after the L1-hit, L2-hit or DRAM latency; a
+ * load with no valid guard lane takes the ld.global latency and touches no cache.
+ * Output, per warp, ORACLE_CACHE_WARP_BYTES: {u32 l1_hits, u32 l2_hits, u32
+ * misses, u32 0}, then the L1 and the L2 tags as u32 (line number + 1, 0 = empty). */
+#define ORACLE_CACHE_L1_LINES 1024u
+#define ORACLE_CACHE_L2_LINES 49152u
+#define ORACLE_CACHE_WARP_BYTES (16u + 4u * (ORACLE_CACHE_L1_LINES + ORACLE_CACHE_L2_LINES))
 
 /* Record kinds of the 16-byte trace records, and their payloads:
  *   LD/ST_GLOBAL: sectors | lines << 8 | guard lanes << 16 | faulting lanes << 24
@@ -95,6 +111,7 @@ typedef struct {
   uint32_t flags;            /* ORACLE_FLAG_* */
   const uint32_t* block_list; /* optional: linear ids of the blocks to simulate */
   uint64_t n_block_list;      /* 0 = simulate every block of the grid */
+  uint8_t* cache;             /* ORACLE_FLAG_CACHE: n_out_warps * ORACLE_CACHE_WARP_BYTES out */
 } oracle_cfg;
 
 typedef struct {

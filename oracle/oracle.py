@@ -12,9 +12,9 @@ import numpy as np
 
 from . import build as _build
 
-NLAT = 16
+NLAT = 18
 LAT_NAMES = ["int32", "int64", "fp32", "setp", "selp", "mov", "ld_param", "ld_global",
-             "ld_shared", "st_global", "st_shared", "bra", "bar", "ret"]
+             "ld_shared", "st_global", "st_shared", "bra", "bar", "ret", "l1_hit", "l2_hit", "dram"]
 
 ST_FINISHED, ST_BUDGET, ST_FAULT, ST_TRACE_DROP, ST_BARDIV, ST_CYCLE_OVF = 1, 2, 4, 8, 16, 32
 
@@ -34,6 +34,10 @@ EXT_RECORD_DTYPE = np.dtype([("cycle", "<u4"), ("pc", "<u2"), ("kind", "u1"), ("
                              ("active", "<u4"), ("payload", "<u4")])
 TRACE_BASIC, TRACE_EXTENDED = 0, 1
 FLAG_EXT_TRACE = 2
+FLAG_CACHE = 4
+# cache-latency model: per warp {u32 l1_hits, l2_hits, misses, 0}, L1 tags, L2 tags
+CACHE_L1_LINES, CACHE_L2_LINES = 1024, 49152
+CACHE_WARP_BYTES = 16 + 4 * (CACHE_L1_LINES + CACHE_L2_LINES)
 
 E_RACE = -7
 
@@ -50,7 +54,8 @@ class _Cfg(ctypes.Structure):
                 ("gmem_bytes", ctypes.c_uint64), ("trace_cap", ctypes.c_uint32),
                 ("max_warp_instrs", ctypes.c_uint32), ("latency", ctypes.c_uint16 * NLAT),
                 ("n_threads", ctypes.c_uint32), ("flags", ctypes.c_uint32),
-                ("block_list", ctypes.POINTER(ctypes.c_uint32)), ("n_block_list", ctypes.c_uint64)]
+                ("block_list", ctypes.POINTER(ctypes.c_uint32)), ("n_block_list", ctypes.c_uint64),
+                ("cache", ctypes.c_void_p)]
 
 
 class _Info(ctypes.Structure):
@@ -146,14 +151,16 @@ def _dim3(d):
 
 
 def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFFFFFFF, latency=None,
-        threads=0, blocks=None, check_races=False, entry=None, trace_format=TRACE_BASIC):
+        threads=0, blocks=None, check_races=False, entry=None, trace_format=TRACE_BASIC, cache=None):
     """Simulate.  `gmem` is a writable uint8 numpy array, updated in place.
 
     Returns (counters, trace, rc): counters is a COUNTER_DTYPE array with one record
     per simulated warp, trace a uint8 array of (16 + R * trace_cap) bytes per warp
     (R = 8, or 16 with trace_format TRACE_EXTENDED), rc 0 or E_RACE (race checking
     only).  `blocks` optionally lists the linear block ids to simulate; outputs
-    follow that order."""
+    follow that order.  `cache`, a writable uint8 array of CACHE_WARP_BYTES per
+    simulated warp, turns the cache-latency model on and receives its per-warp
+    state."""
     assert gmem.dtype == np.uint8 and gmem.flags.c_contiguous and gmem.flags.writeable
     grid, block = _dim3(grid), _dim3(block)
     cfg = _Cfg()
@@ -167,6 +174,8 @@ def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFF
     cfg.latency[:] = lat
     cfg.n_threads = threads
     cfg.flags = (1 if check_races else 0) | (FLAG_EXT_TRACE if trace_format == TRACE_EXTENDED else 0)
+    if cache is not None:
+        cfg.flags |= FLAG_CACHE
     rec = 16 if trace_format == TRACE_EXTENDED else 8
     tpb = block[0] * block[1] * block[2]
     wpb = (tpb + 31) // 32
@@ -180,6 +189,10 @@ def run(ptx, grid, block, params_bytes, gmem, trace_cap=0, max_warp_instrs=0xFFF
         cfg.block_list = bl.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
         cfg.n_block_list = nb
     counters = np.zeros(nb * wpb, dtype=COUNTER_DTYPE)
+    if cache is not None:
+        assert cache.dtype == np.uint8 and cache.flags.c_contiguous and cache.flags.writeable
+        assert cache.size >= nb * wpb * CACHE_WARP_BYTES
+        cfg.cache = cache.ctypes.data
     trace = np.zeros(nb * wpb * (16 + rec * trace_cap), dtype=np.uint8)
     pb = bytes(params_bytes)
     pbuf = ctypes.create_string_buffer(pb, max(len(pb), 1))
@@ -203,3 +216,15 @@ def trace_slots(trace, trace_cap, trace_format=TRACE_BASIC):
     if trace_format == TRACE_EXTENDED:
         return hdr, body.view(EXT_RECORD_DTYPE).reshape(t.shape[0], trace_cap)
     return hdr, body.view("<u4").reshape(t.shape[0], trace_cap, 2)
+
+
+CACHE_HEADER_DTYPE = np.dtype([("l1_hits", "<u4"), ("l2_hits", "<u4"), ("misses", "<u4"), ("reserved", "<u4")])
+
+
+def cache_state(cache, n_warps):
+    """Split a cache-model buffer into (headers, l1 tags, l2 tags) per warp; a tag is
+    the line number + 1, 0 for an empty set."""
+    c = cache[:n_warps * CACHE_WARP_BYTES].reshape(n_warps, CACHE_WARP_BYTES)
+    hdr = c[:, :16].copy().view(CACHE_HEADER_DTYPE).reshape(-1)
+    tags = c[:, 16:].copy().view("<u4")
+    return hdr, tags[:, :CACHE_L1_LINES], tags[:, CACHE_L1_LINES:]

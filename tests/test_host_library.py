@@ -142,6 +142,41 @@ def test_extended_layout_and_grid_limit(ks):
     ks.ks_program_free(p)
 
 
+def test_cache_model_layout_and_limits(ks, oracle_mod):
+    """The cache model adds KS_CACHE_WARP_BYTES of state per warp (the oracle's
+    layout), refuses extended records and memories above 2^38 bytes, and needs
+    its buffer at allocation; an unknown model is an invalid argument."""
+    p = ks.ks_load_program(W.VECTOR_ADD_PTX)
+    cfg = ks.ks_default_config()
+    assert list(cfg.latency)[14:17] == [28, 150, 400] and cfg.cache_model == ks.KS_CACHE_NONE
+    cfg.max_grid = ks.ks_dim3(4, 1, 1)
+    cfg.max_block = ks.ks_dim3(256, 1, 1)
+    cfg.gmem_bytes = 1 << 20
+    assert ks.ks_query_layout(p, cfg).cache_bytes == 0
+    cfg.cache_model = ks.KS_CACHE_WARP
+    lay = ks.ks_query_layout(p, cfg)
+    assert ks.KS_CACHE_WARP_BYTES == oracle_mod.CACHE_WARP_BYTES == 200720
+    assert lay.cache_bytes == 32 * ks.KS_CACHE_WARP_BYTES
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_alloc_state(p, cfg, 1, 1, 1, 0)
+    assert e.value.code == -3 and "cache buffer" in e.value.msg
+    cfg.gmem_bytes = (1 << 38) + 4096
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_query_layout(p, cfg)
+    assert e.value.code == -2
+    cfg.gmem_bytes = 1 << 20
+    cfg.trace_format = ks.KS_TRACE_EXTENDED
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_query_layout(p, cfg)
+    assert e.value.code == -2 and "basic trace" in e.value.msg
+    cfg.trace_format = ks.KS_TRACE_BASIC
+    cfg.cache_model = 7
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_query_layout(p, cfg)
+    assert e.value.code == -3
+    ks.ks_program_free(p)
+
+
 def test_default_latency_matches_oracle(ks, oracle_mod):
     assert list(ks.ks_default_config().latency) == oracle_mod.default_latency()
 

@@ -1,7 +1,7 @@
 """Resource checks of the gfx950 interpreter kernels (CPU: compile to assembly only).
 
 The VGPR register-file kernels keep simulated registers in VGPRs from a reserved
-base (v56, or v64 for the extended-trace variants) up, outside the compiler's
+base (v56, or v64 for the extended-trace and cache-model variants) up, outside the compiler's
 allocation; if compiler-written code ever touched them, simulated
 register values (and the compiler's own) would be silently corrupted, and if the
 kernel's VGPR count did not cover the file, indexed accesses would reach past
@@ -174,7 +174,7 @@ def test_register_file_names_match_the_reserved_base():
         regs = sorted({int(r) for r in re.findall(r'\bv(\d+)\b', zero)})
         assert regs == list(range(b, b + n)), (n, b)
     for k, base in kbuild.RESERVED_BASE.items():
-        assert base == (64 if k.endswith("_ext") else 56)
+        assert base == (64 if k.endswith(("_ext", "_cache")) else 56)
     # each kernel's register file is the one its VGPR budget reserves: amdgpu_num_vgpr(base / 2)
     for k, base in kbuild.RESERVED_BASE.items():
         m = re.search(r"amdgpu_num_vgpr\((\d+)\)\)\) %s\(" % k, src)

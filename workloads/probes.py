@@ -120,3 +120,57 @@ COUNT_SWEEP_ITERS: Tuple[int, ...] = (32, 128, 512, 2048, 4096, 8192)   # x 32 t
 ACC_SWEEP: Tuple[int, ...] = (1, 2, 4, 8, 16)
 WARP_SWEEP: Tuple[Tuple[int, int], ...] = ((1, 1), (1, 32), (1, 64), (1, 128), (256, 128))
 CONTROL_OPS: Tuple[str, ...] = ("none", "fma.f32", "add.s32", "add.f32")
+
+
+# ---------------------------------------------------------------------------- pointer chase
+#
+# Inputs for the cache-latency model (the KernelScope page's direct-mapped L1 and L2
+# in front of DRAM): a chain of dependent global loads.  Word k of the chain holds
+# the byte offset of word k + 1, so every load's address comes from the previous
+# load and the loads issue one after another.  Nothing here models a cache.
+
+
+def chase_ptx(hops: int) -> str:
+    """Each thread loads its start offset from a per-lane table, follows `hops`
+    links of the chain (ld.global, then mul.wide + add.s64 to form the next
+    address) and stores the last word it read."""
+    assert hops >= 1
+    L = [".version 7.5", ".target sm_80", ".address_size 64", "",
+         ".visible .entry chase(", "    .param .u64 param_base,", "    .param .u64 param_start,",
+         "    .param .u64 param_out", ")", "{",
+         "    .reg .b32 %r<4>;", "    .reg .b64 %rd<8>;", "",
+         "    ld.param.u64 %rd0, [param_base];", "    ld.param.u64 %rd5, [param_start];",
+         "    ld.param.u64 %rd6, [param_out];",
+         "    mov.u32 %r2, %tid.x;", "    mul.wide.u32 %rd3, %r2, 4;", "    add.s64 %rd4, %rd5, %rd3;",
+         "    ld.global.u32 %r1, [%rd4];"]
+    for _ in range(hops):
+        L += ["    mul.wide.u32 %rd2, %r1, 1;", "    add.s64 %rd1, %rd0, %rd2;", "    ld.global.u32 %r1, [%rd1];"]
+    L += ["    add.s64 %rd7, %rd6, %rd3;", "    st.global.u32 [%rd7], %r1;", "    ret;", "}", ""]
+    return "\n".join(L)
+
+
+def chase_probe(cycle, hops: int, starts=None, block: int = 32, grid: int = 1, mem_bytes: int = None,
+                trace_cap: int = 64) -> Workload:
+    """A chase over the byte offsets `cycle` (word at cycle[i] holds cycle[i + 1],
+    the last one cycle[0]); thread %tid.x = t of every block starts at
+    starts[t % len(starts)] (default: every thread at cycle[0]).  The start table
+    and the output, both indexed by %tid.x, follow the chain's region on lines of
+    their own."""
+    cycle = [int(c) for c in cycle]
+    assert all(c % 4 == 0 for c in cycle) and len(set(cycle)) == len(cycle)
+    starts = [cycle[0]] if starts is None else [int(s) for s in starts]
+    nthreads = block * grid
+    off_start = _align(max(cycle) + 4)
+    off_out = _align(off_start + 4 * nthreads)
+    size = _align(off_out + 4 * nthreads) if mem_bytes is None else int(mem_bytes)
+    assert size >= off_out + 4 * nthreads
+    gmem = np.zeros(size, dtype=np.uint8)
+    words = gmem.view("<u4")
+    for i, c in enumerate(cycle):
+        words[c // 4] = cycle[(i + 1) % len(cycle)]
+    words[off_start // 4: off_start // 4 + nthreads] = np.array([starts[t % len(starts)] for t in range(nthreads)],
+                                                                 dtype=np.uint32)
+    return Workload(name="chase", ptx=chase_ptx(hops), grid=(grid, 1, 1), block=(block, 1, 1),
+                    params=[("param_base", "u64", 0), ("param_start", "u64", off_start), ("param_out", "u64", off_out)],
+                    gmem=gmem, trace_cap=trace_cap, outputs={"out": (off_out, nthreads, "<u4")},
+                    meta={"cycle": cycle, "hops": hops, "off_start": off_start, "off_out": off_out})

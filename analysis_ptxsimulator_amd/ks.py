@@ -327,6 +327,14 @@ class Session:
             return name + "_ext"
         return name + ("_cache" if self.cache_model == KS_CACHE_WARP else "")
 
+    def read_cache_headers(self, first=0, n=None):
+        """Only the 16-byte headers (outcome counts) of warps [first, first + n)."""
+        assert self.cache is not None, "the session has no cache model"
+        n = self.last_warps - first if n is None else n
+        v = self.cache[first * KS_CACHE_WARP_BYTES:(first + n) * KS_CACHE_WARP_BYTES].view(n, KS_CACHE_WARP_BYTES)
+        raw = v[:, :16].contiguous().cpu().numpy()
+        return raw.reshape(-1).view(CACHE_HEADER_DTYPE)
+
     def read_cache(self, first=0, n=None):
         """The cache model's state of warps [first, first + n) after the last run:
         (headers of CACHE_HEADER_DTYPE, L1 tags [n, 1024], L2 tags [n, 49152]) as u32,

@@ -76,13 +76,15 @@ def describe(w):
     return "%s: grid %s block %s trace cap %d" % (w.name, w.grid, w.block, w.trace_cap)
 
 
-def cpu_baseline(w, sample_blocks, threads):
+def cpu_baseline(w, sample_blocks, threads, cache_model=False):
     from oracle import oracle as O
     import numpy as np
     blocks = list(range(sample_blocks))
     g = w.gmem  # the sampled blocks only write their own thread-private words
+    cache = np.zeros(sample_blocks * w.warps_per_block * O.CACHE_WARP_BYTES, np.uint8) if cache_model else None
     t0 = time.perf_counter()
-    c, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=w.trace_cap, blocks=blocks, threads=threads)
+    c, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=w.trace_cap, blocks=blocks, threads=threads,
+                    cache=cache)
     dt = time.perf_counter() - t0
     ti = int(c["thread_instrs"].sum())
     return {"value": ti / dt, "unit": "thread-instr/s", "cores": threads, "kind": "oracle",
@@ -118,6 +120,8 @@ def main():
     ap.add_argument("--workload", default="random_stress")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=65536)
+    ap.add_argument("--cache-model", choices=("none", "warp"), default="none",
+                    help="ld.global latency: the fixed table (the timed default) or per-warp L1/L2 caches")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "
@@ -134,7 +138,9 @@ def main():
     if args.workload == "copy":
         return copy_calibration(args, dev)
     w = make_workload(args.workload)
-    s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, device=dev)
+    cache_on = args.cache_model == "warp"
+    s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, device=dev,
+                   cache_model=ks.KS_CACHE_WARP if cache_on else ks.KS_CACHE_NONE)
     s.load_gmem(w.gmem)
     params = w.params_bytes
     stream = torch.cuda.current_stream(dev)
@@ -158,15 +164,25 @@ def main():
     c = s.read_counters()
     status = s.status()
     kernel = s.kernel_name()
+    ch = s.read_cache_headers() if cache_on else None
     s.close()
     thread_instrs = int(c["thread_instrs"].sum())
     warp_acc = int(c["gld_n"].astype(np.uint64).sum() + c["gst_n"].sum() + c["sh_n"].sum())
     sectors = int(c["gld_sectors"].astype(np.uint64).sum() + c["gst_sectors"].sum())
     records = int(np.minimum(c["warp_instrs"], w.trace_cap).astype(np.uint64).sum())
     alg_bytes = 32 * sectors + 8 * records + (16 + 80) * len(c)
+    cache_stats = None
+    if cache_on:
+        # the cache model's own state: every warp's caches cleared per run, a 4-byte L1
+        # tag read per access, on an L1 miss an L1 tag write and an L2 tag read, on an
+        # L2 miss an L2 tag write, and the 16-byte header
+        l1h, l2h, miss = (int(ch[f].astype(np.uint64).sum()) for f in ("l1_hits", "l2_hits", "misses"))
+        alg_bytes += len(c) * ks.KS_CACHE_WARP_BYTES + 4 * (l1h + l2h + miss) + 8 * (l2h + miss) + 4 * miss
+        cache_stats = {"l1_hits": l1h, "l2_hits": l2h, "misses": miss,
+                       "state_bytes": len(c) * ks.KS_CACHE_WARP_BYTES}
     avg_launch_s = float(np.mean(launch_ms)) / 1000.0
     achieved = alg_bytes / avg_launch_s / 1e9
-    prof = measured_counters(args.workload)
+    prof = measured_counters(args.workload + ("_cache" if cache_on else ""))
     traffic = prof.get("hbm_bytes_per_launch") if prof else None
     valu = None
     if prof and "valu_busy" in prof:
@@ -187,7 +203,8 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": describe(w), "threads": w.n_blocks * w.threads_per_block,
-                   "warps": len(c), "parallelism": "single GPU"},
+                   "warps": len(c), "parallelism": "single GPU",
+                   "ld_global_latency": "per-warp L1/L2 cache model" if cache_on else "fixed table"},
         "warp_accesses_per_s": warp_acc / (ms_per_step / 1000.0),
         "thread_instrs_per_step": thread_instrs,
         "warp_accesses_per_step": warp_acc,
@@ -199,9 +216,13 @@ def main():
                      "kernel": kernel},
         "valu_utilisation": valu,
     }
+    if cache_on:
+        out["cache_model"] = cache_stats
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_blocks, w.n_blocks), threads)
+        # the cache model's oracle holds 200 KB of state per warp: a smaller sample
+        sample = min(args.cpu_sample_blocks, w.n_blocks, 1024 if cache_on else w.n_blocks)
+        out["cpu_baseline"] = cpu_baseline(w, sample, threads, cache_on)
     print(json.dumps(out), flush=True)
 
 

@@ -145,3 +145,44 @@ def test_rerun_starts_cold(K, oracle_mod):
     finally:
         s.close()
     assert np.array_equal(c1, c2) and np.array_equal(h1, h2)
+
+
+def test_random_stress_full_size_sampled(K, oracle_mod):
+    """The full 65536 x 256 random-stress launch with the cache model (105 GB of
+    per-warp cache state); the oracle simulates sampled blocks, whose warps'
+    counters, trace slots and cache state must match."""
+    w = W.random_stress(prog_seed=0)
+    blocks = [0, 1, 32767, 65535] + [int(x) for x in np.random.default_rng(7).integers(0, 65536, 4)]
+    cap = w.trace_cap
+    _say("%s full grid=%s cache, sampled blocks %s" % (w.name, w.grid, blocks))
+    s = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=cap, cache_model=K.KS_CACHE_WARP)
+    wpb = w.warps_per_block
+    try:
+        s.load_gmem(w.gmem)
+        s.run(w.params_bytes)
+        cg = s.read_counters()
+        got = []
+        for b in blocks:
+            hg, l1g, l2g = s.read_cache(b * wpb, wpb)
+            tg = s.read_trace(b * wpb, wpb)
+            got.append((hg, l1g, l2g, tg))
+    finally:
+        s.close()
+    go = w.gmem.copy()
+    cache = np.zeros(len(blocks) * wpb * oracle_mod.CACHE_WARP_BYTES, np.uint8)
+    co, to, _ = oracle_mod.run(w.ptx, w.grid, w.block, w.params_bytes, go, trace_cap=cap, blocks=blocks, cache=cache)
+    ho, l1o, l2o = oracle_mod.cache_state(cache, len(blocks) * wpb)
+    slot = 16 + 8 * cap
+    for i, b in enumerate(blocks):
+        sl = slice(i * wpb, (i + 1) * wpb)
+        for f in co.dtype.names:
+            assert np.array_equal(cg[f][b * wpb:(b + 1) * wpb], co[f][sl]), (b, f)
+        hg, l1g, l2g, tg = got[i]
+        assert np.array_equal(hg[["l1_hits", "l2_hits", "misses"]], ho[sl][["l1_hits", "l2_hits", "misses"]]), b
+        assert np.array_equal(l1g, l1o[sl]) and np.array_equal(l2g, l2o[sl]), b
+        hgt, rg = K.trace_slots(tg, cap)
+        hot, ro = oracle_mod.trace_slots(to.reshape(-1, slot)[sl].reshape(-1), cap)
+        assert np.array_equal(hgt, hot), b
+        for k in range(wpb):
+            n = int(hot["records_written"][k])
+            assert np.array_equal(rg[k, :n], ro[k, :n]), (b, k)

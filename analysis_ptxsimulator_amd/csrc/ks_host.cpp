@@ -1088,6 +1088,10 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
     const KsInst& in = P->code[i].in;
     if (in.op == KO_BRA && in.rpc != KS_RPC_EXIT) out[in.rpc].ctl |= XF_FIX;
   }
+  // each record also carries the next one's scoreboard offsets (a straight run reads
+  // them with this record, so the next issue cycle does not wait for the next record)
+  for (uint32_t i = 0; i < n; ++i)
+    for (int k = 0; k < 4; ++k) out[i].nsbo[k] = out[i + 1].sbo[k];
   // straight runs, from the end: the run of a non-control instruction is itself and
   // the instructions after it that may follow it without rescheduling (neither a
   // control instruction, nor a reconvergence point, nor the end sentinel)

@@ -136,7 +136,8 @@ struct DInst {         // 128 bytes; dwords 0-15 are read for every instruction
   uint32_t gmode;      // 0: @p, 1: @!p, 2: unguarded (compared with the predicate bit: on = bit != gmode)
   uint32_t a0, a1;     // class-specific
   uint32_t imm[6];     // immediate slot values: source k at imm[2k] (low) and imm[2k+1] (high)
-  uint32_t pad[10];
+  uint32_t nsbo[4];    // sbo[] of the next record: its issue cycle is read without waiting for it
+  uint32_t pad[6];
 };
 static_assert(sizeof(DInst) == 128, "DInst must be 128 bytes");
 

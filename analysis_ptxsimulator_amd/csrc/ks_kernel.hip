@@ -64,6 +64,7 @@ enum {
 
 typedef const __attribute__((address_space(4))) DInst* cdinst;
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));  // the 16 dwords every instruction reads
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t rl(uint32_t v, uint32_t l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
@@ -876,6 +877,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           // (the value is consumed only after the next record arrives)
           const uint32_t pf = *reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
               prog_b + off + 2u * (uint32_t)sizeof(DInst));
+          // the next record's scoreboard offsets, carried by this one
+          const u32x4 nsbo = *reinterpret_cast<const __attribute__((address_space(4))) u32x4*>(
+              prog_b + off + offsetof(DInst, nsbo));
           KS_ISSUE(is, off / (uint32_t)sizeof(DInst), h[10], h[11]);
           const uint64_t on64 = mm & ballot(((pbits >> h[12]) & 1u) != h[13]);  // guard
           // extended record of a non-memory instruction: the lanes passing the guard
@@ -1147,11 +1151,13 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             if (a1) R.put2_m(dst, lo, *(cword)(a.params + a0 + 4u), on64);
             else R.put_m(dst, lo, on64);
           }
-          // the next record (the end sentinel at the latest: a run never includes it)
+          // the next record (the end sentinel at the latest: a run never includes it),
+          // and its issue cycle: its scoreboard reads go out with the record's load
           off += (uint32_t)sizeof(DInst);
+          const uint32_t r0 = sb_at(nsbo[0]), r1 = sb_at(nsbo[1]), r2 = sb_at(nsbo[2]), r3 = sb_at(nsbo[3]);
           h = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(prog_b + off);
           asm volatile("; prefetched %0" : : "s"(pf));
-          is = KS_ISSUE_CYCLE(h);
+          is = umax(umax(v_next, r0), umax(umax(r1, r2), r3));
           if (--n == 0) break;
         }
         const uint32_t p = off / (uint32_t)sizeof(DInst);

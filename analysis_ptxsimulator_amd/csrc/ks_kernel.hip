@@ -689,6 +689,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   umax(umax(v_next, sb_at((h)[6])), umax(umax(sb_at((h)[7]), sb_at((h)[8])), sb_at((h)[9])))
 
   uint32_t epoch = 0;
+  // kept in a register (the compiler would reload the kernel argument on every pass)
+  uint32_t cyc_safe = a.cyc_safe;
+  asm volatile("" : "+v"(cyc_safe));
   while (true) {
     // ------------------------------------------------------------------ run both warps until blocked
     while (true) {
@@ -866,7 +869,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         {
           const uint32_t room = ev - wi;  // per warp: issues before its next event (at least 1 here)
           n = umin(n, umin(rl(room, 0) | ~go0, rl(room, 32) | ~go1));
-          if (ballot(iss > a.cyc_safe) & gm) n = 1u;
+          if (ballot(iss > cyc_safe) & gm) n = 1u;
         }
         uint32_t off = pc * (uint32_t)sizeof(DInst);  // byte offset of the current record
         uint32_t is = iss;

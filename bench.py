@@ -54,6 +54,8 @@ def make_workload(name):
     from workloads import configs as W
     if name == "random_stress":
         return W.random_stress(prog_seed=0)
+    if name.startswith("random_stress_g"):  # the same program and memory on fewer blocks
+        return W.random_stress(prog_seed=0, grid=int(name[15:]))
     if name == "ffma_dep":
         return W.ffma_probe(n_acc=1)
     if name == "ffma_ind":
@@ -70,9 +72,10 @@ def make_workload(name):
 def describe(w):
     m = w.meta
     if w.name.startswith("random_stress"):
-        return ("random_stress: %d x %d threads (16.8M), %d-instruction PTX program seed %d, %d MiB simulated "
-                "memory seed %d, trace cap %d" % (w.grid[0], w.block[0], m["n_instr"], m["prog_seed"],
-                                                   w.gmem.size >> 20, m["mem_seed"], w.trace_cap))
+        return ("random_stress: %d x %d threads (%.3gM), %d-instruction PTX program seed %d, %d MiB simulated "
+                "memory seed %d, trace cap %d" % (w.grid[0], w.block[0], w.n_blocks * w.threads_per_block / 1e6,
+                                                   m["n_instr"], m["prog_seed"], w.gmem.size >> 20, m["mem_seed"],
+                                                   w.trace_cap))
     return "%s: grid %s block %s trace cap %d" % (w.name, w.grid, w.block, w.trace_cap)
 
 
@@ -122,6 +125,9 @@ def main():
     ap.add_argument("--cpu-sample-blocks", type=int, default=65536)
     ap.add_argument("--cache-model", choices=("none", "warp"), default="none",
                     help="ld.global latency: the fixed table (the timed default) or per-warp L1/L2 caches")
+    ap.add_argument("--trace-format", choices=("basic", "extended"), default="basic",
+                    help="trace records: 8-byte {cycle, pc} (the timed default) or 16-byte with kind, mask and "
+                         "payload (grids of up to 32 blocks, e.g. --workload random_stress_g32)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "
@@ -139,8 +145,10 @@ def main():
         return copy_calibration(args, dev)
     w = make_workload(args.workload)
     cache_on = args.cache_model == "warp"
+    ext = args.trace_format == "extended"
     s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, device=dev,
-                   cache_model=ks.KS_CACHE_WARP if cache_on else ks.KS_CACHE_NONE)
+                   cache_model=ks.KS_CACHE_WARP if cache_on else ks.KS_CACHE_NONE,
+                   trace_format=ks.KS_TRACE_EXTENDED if ext else ks.KS_TRACE_BASIC)
     s.load_gmem(w.gmem)
     params = w.params_bytes
     stream = torch.cuda.current_stream(dev)
@@ -170,7 +178,7 @@ def main():
     warp_acc = int(c["gld_n"].astype(np.uint64).sum() + c["gst_n"].sum() + c["sh_n"].sum())
     sectors = int(c["gld_sectors"].astype(np.uint64).sum() + c["gst_sectors"].sum())
     records = int(np.minimum(c["warp_instrs"], w.trace_cap).astype(np.uint64).sum())
-    alg_bytes = 32 * sectors + 8 * records + (16 + 80) * len(c)
+    alg_bytes = 32 * sectors + (16 if ext else 8) * records + (16 + 80) * len(c)
     cache_stats = None
     if cache_on:
         # the cache model's own state: every warp's caches cleared per run, a 4-byte L1
@@ -182,7 +190,7 @@ def main():
                        "state_bytes": len(c) * ks.KS_CACHE_WARP_BYTES}
     avg_launch_s = float(np.mean(launch_ms)) / 1000.0
     achieved = alg_bytes / avg_launch_s / 1e9
-    prof = measured_counters(args.workload + ("_cache" if cache_on else ""))
+    prof = measured_counters(args.workload + ("_cache" if cache_on else "") + ("_ext" if ext else ""))
     traffic = prof.get("hbm_bytes_per_launch") if prof else None
     valu = None
     if prof and "valu_busy" in prof:
@@ -204,7 +212,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(w), "threads": w.n_blocks * w.threads_per_block,
                    "warps": len(c), "parallelism": "single GPU",
-                   "ld_global_latency": "per-warp L1/L2 cache model" if cache_on else "fixed table"},
+                   "ld_global_latency": "per-warp L1/L2 cache model" if cache_on else "fixed table",
+                   "trace_format": args.trace_format},
         "warp_accesses_per_s": warp_acc / (ms_per_step / 1000.0),
         "thread_instrs_per_step": thread_instrs,
         "warp_accesses_per_step": warp_acc,

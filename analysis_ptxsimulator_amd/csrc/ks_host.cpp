@@ -949,7 +949,8 @@ void compute_reconvergence(ks_program* P) {
 // immediate slots reg_slots + 2k (low) and + 2k + 1 (high); f32 add, sub and mul
 // become one fused multiply-add with constant operands, which rounds exactly as
 // the separate operation does (x + y = fma(x, 1, y), x - y = fma(x, 1, -y),
-// x * y = fma(x, y, -0)); integer add/sub and mul/mad differ only in constants.
+// x * y = fma(x, y, -0)), the constants read from the two slots after the
+// immediates; integer add/sub and mul/mad differ only in constants.
 std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
   const uint32_t n = (uint32_t)P->code.size();
   const uint32_t ib = P->reg_slots;
@@ -1008,25 +1009,19 @@ std::vector<DInst> lower_program(const ks_program* P, const ks_config* cfg) {
         cls = DC_I64;
         d.a0 = in.op == KO_MULWIDE_S ? DI_WIDE_S : DI_WIDE_U;
         break;
-      case KO_FADD: case KO_FSUB:  // fma(x0, 1.0, +-x1): x1 is read as the third operand
+      case KO_FADD: case KO_FSUB:  // fma(x0, 1.0, +-x1): 1.0 from its constant slot, x1 the third operand
         cls = DC_FMA;
-        d.s1 = slot[0];
+        d.s1 = ib + KS_IMM_SLOTS;
         d.s2 = slot[1];
-        d.a0 = 0xFFFFFFFFu;
-        d.a1 = 0xFFFFFFFFu;
         d.a2 = in.op == KO_FSUB ? 0x80000000u : 0u;
         break;
-      case KO_FMUL:  // fma(x0, x1, -0.0)
+      case KO_FMUL:  // fma(x0, x1, -0.0): -0.0 from its constant slot
         cls = DC_FMA;
-        d.s2 = slot[0];
-        d.a0 = 0;
-        d.a1 = 0;
-        d.a2 = 0x80000000u;
+        d.s2 = ib + KS_IMM_SLOTS + 1u;
+        d.a2 = 0;
         break;
       case KO_FFMA:  // fma(x0, x1, x2)
         cls = DC_FMA;
-        d.a0 = 0;
-        d.a1 = 0xFFFFFFFFu;
         d.a2 = 0;
         break;
       case KO_SETP_S32: case KO_SETP_U32: case KO_SETP_F32: case KO_SETP_S64: case KO_SETP_U64: {
@@ -1385,7 +1380,7 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       const uint64_t limit = 0x7FFFFFFFull, span = (uint64_t)RUN_MAX * step;
       a.cyc_safe = span < limit ? (uint32_t)(limit - span) : 0u;
     }
-    a.rf_slots = p->reg_slots + KS_IMM_SLOTS;
+    a.rf_slots = p->reg_slots + KS_IMM_SLOTS + KS_CONST_SLOTS;
     a.ext = st->cfg.trace_format == KS_TRACE_EXTENDED ? 1u : 0u;
     a.cache = (uint8_t*)st->d_cache;
     a.cache_on = st->d_cache ? 1u : 0u;

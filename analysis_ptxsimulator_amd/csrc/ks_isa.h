@@ -50,6 +50,7 @@ constexpr uint8_t KS_SB_DUMP = 126;      // scoreboard entry written by instruct
 constexpr uint8_t KS_SB_ZERO = 127;      // scoreboard entry that always reads 0 (no source)
 constexpr uint32_t KS_SB_ENTRIES = 129;  // scoreboard words per warp in LDS (odd: warps start in different banks)
 constexpr uint32_t KS_IMM_SLOTS = 6;     // register slots after the program's that hold an instruction's immediates
+constexpr uint32_t KS_CONST_SLOTS = 2;   // then two slots holding 1.0f and -0.0f (f32 add/sub and mul operands)
 constexpr uint32_t KS_PREFETCH_PAD = 4;  // zero records after the end sentinel: reads ahead stay in bounds
 
 struct KsInst {            // 64 bytes
@@ -78,7 +79,7 @@ static_assert(sizeof(KsInst) == 64, "KsInst must be 64 bytes");
 // Interpreter classes.  Register-writing classes first (their issue ends with
 // pc + 1), then memory, then control.
 enum DClass : uint32_t {
-  DC_FMA,      // f32 add/sub/mul/fma as one rounding: r = fma(x0, a0 ? 1.0 : x1, (x2 & a1) ^ a2)
+  DC_FMA,      // f32 add/sub/mul/fma as one rounding: r = fma(x0, x1, x2 ^ a2) (1.0 / -0.0 from the constant slots)
   DC_IADD,     // add/sub.{s,u}32: r = x0 + (x1 ^ a0) + a1
   DC_IMAD,     // mul.lo/mad.lo.{s,u}32: r = x0 * x1 + (x2 & a0)
   DC_MOV,      // mov (register or immediate); a0 = 1: 64-bit
@@ -159,7 +160,7 @@ struct KsArgs {
   uint32_t threads_per_block;
   uint32_t warps_per_block;
   uint32_t lat_bar;
-  uint32_t rf_slots;       // register slots per simulated thread, immediate slots included
+  uint32_t rf_slots;       // register slots per simulated thread, immediate and constant slots included
   uint32_t cyc_safe;       // a run may continue past its first instruction when that one issues
                            // at most at this cycle: RUN_MAX issues cannot then pass the cycle limit
   uint32_t ext;            // 1: extended 16-byte trace records (KS_TRACE_EXTENDED)

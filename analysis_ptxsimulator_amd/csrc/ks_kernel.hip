@@ -414,12 +414,15 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t n_instr = a.n_instrs;
   const cdinst prog = (cdinst)(uintptr_t)a.prog;
   const __attribute__((address_space(4))) uint8_t* const prog_b = (const __attribute__((address_space(4))) uint8_t*)prog;
-  const uint32_t ib = a.rf_slots - KS_IMM_SLOTS;  // first immediate slot
+  const uint32_t ib = a.rf_slots - KS_IMM_SLOTS - KS_CONST_SLOTS;  // first immediate slot
 
   // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] (to 16 bytes)
   //      [EXT: record ring, 32 x 16 bytes per warp] [shared window]
   RegFile<RFN, (EXT || CACHE) ? 64 : 56> R;
   RegFile<RFN, (EXT || CACHE) ? 64 : 56>::zero();
+  // the constant slots after the immediates: 1.0f and -0.0f
+  R.put(ib + KS_IMM_SLOTS, 0x3F800000u);
+  R.put(ib + KS_IMM_SLOTS + 1u, 0x80000000u);
   uint32_t* const sbw = lds;
   uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
   const uint32_t sb_words = (WG / 32u + 1u) * KS_SB_ENTRIES;
@@ -901,9 +904,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           if (c & CB(DC_FMA)) {
             uint32_t x0, x1, x2;
             R.get3(s0, s1, s2, x0, x1, x2);
-            const uint32_t b = (a0 & 0x3F800000u) | (~a0 & x1);  // 1.0f or x1
-            const uint32_t cc = (x2 & a1) ^ a2;                  // x2, -x2 or -0.0f
-            R.put_m(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(b), __uint_as_float(cc))), on64);
+            R.put_m(dst, canon_bits(__builtin_fmaf(__uint_as_float(x0), __uint_as_float(x1), __uint_as_float(x2 ^ a2))),
+                    on64);
           } else if (c & CB(DC_IADD)) {
             uint32_t x0, x1;
             R.get2(s0, s1, x0, x1);
@@ -1331,7 +1333,7 @@ size_t ks_lds_limit() {
 // 32 (40-VGPR file) or 64 (72-VGPR file); 0 if it fits neither.
 int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
   (void)block_threads;  // both variants run blocks of up to 1024 threads
-  const uint32_t total = slots + KS_IMM_SLOTS;
+  const uint32_t total = slots + KS_IMM_SLOTS + KS_CONST_SLOTS;
   if (total <= 40) return 32;
   if (total <= 72) return 64;
   return 0;
@@ -1352,7 +1354,7 @@ hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, 
   const size_t lds = ks_lds_bytes(wg, a.shared_bytes, a.ext != 0);
   if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0 || a.cache_on != 0))
     return hipErrorInvalidValue;
-  if (a.rf_slots != slots + KS_IMM_SLOTS) return hipErrorInvalidValue;
+  if (a.rf_slots != slots + KS_IMM_SLOTS + KS_CONST_SLOTS) return hipErrorInvalidValue;
   if (a.ext && a.cache_on) return hipErrorInvalidValue;
   const int vi = (variant == 32 ? 0 : 1) + (a.ext ? 2 : 0) + (a.cache_on ? 4 : 0);
   const void* const fns[6] = {(const void*)ks_interp_v32,     (const void*)ks_interp_v64,

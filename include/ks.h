@@ -14,7 +14,7 @@
  * format) 16-byte records that add the instruction kind, the active mask and a
  * per-kind payload (sectors and lines of a global access, bank-conflict degree of
  * a shared access, the lanes taking a branch).  Extended records for programs of
- * more than 34 register slots support blocks of up to 768 threads, and
+ * more than 32 register slots support blocks of up to 768 threads, and
  * extended-record launches hold at most KS_EXT_MAX_BLOCKS blocks.
  *
  * Sources of the semantics, by page and section:
@@ -250,9 +250,10 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
                  void* stream);
 
 /* Name of the interpreter kernel ks_run launches for this program and block shape,
- * as profilers list it: "ks_interp_v32" (programs of up to 34 register slots: a
- * 40-VGPR register file per lane, six slots of it for immediates) or
- * "ks_interp_v64" (up to 64 slots: a 72-VGPR file); runs with the extended trace
+ * as profilers list it: "ks_interp_v32" (programs of up to 32 register slots: a
+ * 40-VGPR register file per lane, six slots of it for immediates and two for the
+ * constants 1.0f and -0.0f) or "ks_interp_v64" (up to 64 slots: a 72-VGPR
+ * file); runs with the extended trace
  * format launch the same kernel with the suffix "_ext", runs with the cache model
  * the one with the suffix "_cache".  *name points to a static
  * string.  Errors: KS_E_INVALID_ARG (NULL arguments, empty or oversized block). */

@@ -202,12 +202,18 @@ def test_program_limits(ks):
 
 
 def test_interp_kernel_choice(ks):
-    """Register-file variant: 40 reserved VGPRs when the program needs at most 34
-    slots (six more hold immediates), else 72; blocks of up to 1024 threads."""
+    """Register-file variant: 40 reserved VGPRs when the program needs at most 32
+    slots (six more hold immediates, two the f32 constants), else 72; blocks of up
+    to 1024 threads."""
     small = ks.ks_load_program(W.vector_add().ptx)
     big = ks.ks_load_program(W.random_stress(prog_seed=0, grid=4, gmem_bytes=1 << 20).ptx)
+    edge = {n: ks.ks_load_program(S.HEADER + ".visible .entry k()\n{\n    .reg .b32 %%r<%d>;\n"
+                                   "    mov.u32 %%r%d, 1;\n    ret;\n}\n" % (n, n - 1)) for n in (32, 33, 64)}
     try:
-        assert ks.ks_program_info(small)["reg_slots"] <= 34
+        assert ks.ks_program_info(small)["reg_slots"] <= 32
+        assert ks.ks_interp_kernel(edge[32], (32,)) == "ks_interp_v32"
+        assert ks.ks_interp_kernel(edge[33], (32,)) == "ks_interp_v64"
+        assert ks.ks_interp_kernel(edge[64], (32,)) == "ks_interp_v64"
         assert ks.ks_program_info(big)["reg_slots"] == 64
         for block in ((32,), (256,), (1024,), (32, 32)):
             assert ks.ks_interp_kernel(small, block) == "ks_interp_v32"
@@ -218,6 +224,8 @@ def test_interp_kernel_choice(ks):
     finally:
         ks.ks_program_free(small)
         ks.ks_program_free(big)
+        for p in edge.values():
+            ks.ks_program_free(p)
 
 
 def test_instr_info_maps_pcs_to_source_lines(ks):

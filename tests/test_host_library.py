@@ -249,3 +249,14 @@ def test_instr_info_maps_pcs_to_source_lines(ks):
     assert [x["kind"] for x in d] == [0] * 9 + [5, 0, 0, 1, 0, 1, 0, 0, 2, 8]
     assert [x["access_bytes"] for x in d] == [0] * 12 + [4, 0, 4, 0, 0, 4, 0]
     assert d[15]["lat_class"] == 2 and d[12]["lat_class"] == 7  # add.f32: FP32; ld.global
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says why,
+    before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -549,7 +549,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const bool on_ = lanes(on64);                                                 \
       /* sector id + 1 on guard lanes, 0 elsewhere; prev: the largest over the earlier lanes of the half */ \
       const uint32_t sid1 = on_ ? (uint32_t)((A) >> 5) + 1u : 0u;                   \
-      const uint32_t prev = prev_in_half(half_prefix_max(sid1), lane);              \
+      /* with every lane on, the previous lane's id is that largest id wherever */  \
+      /* the ids do not decrease, and the other halves are found by the same test */ \
+      uint32_t pm_ = sid1;                                                          \
+      if (on64 != ~0ull) {                                                          \
+        pm_ = half_prefix_max(sid1);                                                \
+        asm volatile("" : "+v"(pm_)); /* a branch, not a select of both arms */     \
+      }                                                                             \
+      const uint32_t prev = prev_in_half(pm_, lane);                                \
       uint64_t fast = on64;                                                         \
       const uint64_t nonmono = ballot(sid1 < prev) & on64;                          \
       if (nonmono) {                                                                \

@@ -669,11 +669,14 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const uint32_t t_ = line_ + 1u;                                               \
       uint32_t* const e1_ = cw_ + 4u + (line_ & (KS_CACHE_L1_LINES - 1u));          \
       uint32_t* const e2_ = cw_ + 4u + KS_CACHE_L1_LINES + line_ % KS_CACHE_L2_LINES; \
-      if (*e1_ == t_) {                                                             \
+      /* both tags in one memory round trip (the two arrays never overlap) */        \
+      uint32_t o1_ = *e1_, o2_ = *e2_;                                              \
+      asm volatile("" : "+v"(o1_), "+v"(o2_)); /* keeps the L2 load ahead of the branch */ \
+      if (o1_ == t_) {                                                              \
         lvl_ = 0u;                                                                  \
       } else {                                                                      \
         *e1_ = t_;                                                                  \
-        if (*e2_ == t_) {                                                           \
+        if (o2_ == t_) {                                                            \
           lvl_ = 1u;                                                                \
         } else {                                                                    \
           *e2_ = t_;                                                                \

@@ -131,7 +131,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "
-              "(blocks never communicate; see the sharding note in DESIGN.md). Run with --gpus 1.",
+              "(blocks never communicate, so a launch would shard by block ranges, one range per GPU). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1169,8 +1169,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           // the next record (the end sentinel at the latest: a run never includes it),
           // and its issue cycle: its scoreboard reads go out with the record's load
           off += (uint32_t)sizeof(DInst);
+          const u32x16 hn = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(prog_b + off);
+          asm volatile("" :: "s"(off));  // the record's load goes out ahead of the scoreboard reads
           const uint32_t r0 = sb_at(nsbo[0]), r1 = sb_at(nsbo[1]), r2 = sb_at(nsbo[2]), r3 = sb_at(nsbo[3]);
-          h = *reinterpret_cast<const __attribute__((address_space(4))) u32x16*>(prog_b + off);
+          h = hn;
           asm volatile("; prefetched %0" : : "s"(pf));
           is = umax(umax(v_next, r0), umax(umax(r1, r2), r3));
           if (--n == 0) break;

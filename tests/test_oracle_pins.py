@@ -152,6 +152,73 @@ def test_count_sweep_exactly_affine(oracle_mod, n_acc, slope):
     assert slope / 32 == (4.0 if n_acc == 1 else 35 / 32)
 
 
+def test_barrier_release_hand_derived(oracle_mod):
+    """bar.sync release = latest arrival of the waiting warps + lat(bar.sync), and a
+    warp that finished without reaching the barrier does not hold it: issue cycles
+    derived by hand (tests/golden/barrier_trace.json)."""
+    with open(os.path.join(GOLDEN, "barrier_trace.json")) as f:
+        gold = json.load(f)
+    g = np.zeros(64, np.uint8)
+    c, t, _ = oracle_mod.run(gold["ptx"], 1, gold["block"], pack_params([("param_out", "u64", 0)]), g,
+                             trace_cap=16)
+    hdr, rec = oracle_mod.trace_slots(t, 16)
+    for w in range(3):
+        pcs, cyc = gold["pcs"][str(w)], gold["issue_cycles"][str(w)]
+        n = len(pcs)
+        assert hdr[w]["records_written"] == n
+        assert rec[w, :n, 1].tolist() == pcs, (w, rec[w, :n].tolist())
+        assert rec[w, :n, 0].tolist() == cyc, (w, rec[w, :n].tolist())
+        assert c["cycles"][w] == gold["cycles"][str(w)]
+        assert c["barrier_n"][w] == gold["barrier_n"][str(w)]
+        assert c["warp_instrs"][w] == n and c["stall_cycles"][w] == c["cycles"][w] - n
+    assert (c["status"] == oracle_mod.ST_FINISHED).all() and (c["diverge_n"] == 0).all()
+
+
+def _barrier_chain_ptx(k, slow_warp):
+    body = []
+    for j in range(k):
+        body += ["    @%%p1 bra $L__b%d;" % j, "    ld.global.u32 %r2, [%rd1];", "    add.s32 %r3, %r3, %r2;",
+                 "$L__b%d:" % j, "    bar.sync 0;"]
+    cmp = "ge" if slow_warp == 0 else "lt"
+    return S.HEADER + """.visible .entry barchain(.param .u64 param_out)
+{
+    .reg .pred %%p<2>;
+    .reg .b32 %%r<4>;
+    .reg .b64 %%rd<2>;
+    ld.param.u64 %%rd1, [param_out];
+    mov.u32 %%r1, %%tid.x;
+    setp.%s.u32 %%p1, %%r1, 32;
+%s
+    ret;
+}
+""" % (cmp, "\n".join(body))
+
+
+@pytest.mark.parametrize("slow_warp", [0, 1])
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 20])
+def test_barrier_chain_closed_form(oracle_mod, k, slow_warp):
+    """k barriers, one warp running a 200-cycle load before each: both warps finish
+    at cycles = 10 + 222 k (hand-derived in tests/golden/barrier_trace.json,
+    'chain'), whichever warp is the slow one."""
+    with open(os.path.join(GOLDEN, "barrier_trace.json")) as f:
+        gold = json.load(f)["chain"]
+    g = np.zeros(64, np.uint8)
+    c, t, _ = oracle_mod.run(_barrier_chain_ptx(k, slow_warp), 1, gold["block"],
+                             pack_params([("param_out", "u64", 0)]), g, trace_cap=8 * k + 8)
+    assert c["cycles"].tolist() == [gold["cycles_at_zero"] + gold["cycles_per_barrier"] * k] * 2
+    assert c["barrier_n"].tolist() == [k, k]
+    fast = 1 - slow_warp
+    assert c["warp_instrs"][slow_warp] == 4 * k + 4 and c["warp_instrs"][fast] == 2 * k + 4
+    # iteration j's bra (pc 3 + 4 j) issues at t_j = 9 + 222 j in both warps, and
+    # the final ret at 9 + 222 k
+    _, rec = oracle_mod.trace_slots(t, 8 * k + 8)
+    for w in range(2):
+        n = int(c["warp_instrs"][w])
+        at = {int(p): int(cy) for cy, p in rec[w, :n].tolist()}
+        assert [at[3 + 4 * j] for j in range(k)] == [9 + 222 * j for j in range(k)]
+        assert rec[w, n - 1].tolist() == [9 + 222 * k, 3 + 4 * k]
+
+
 def test_ffma_probe_values(oracle_mod):
     """Probe outputs equal the scalar reference (exact IEEE fma) for a few threads."""
     for n_acc in (1, 8):

@@ -1188,6 +1188,20 @@ ks_status ks_param_info(const ks_program* p, uint32_t index, uint32_t* offset, u
   });
 }
 
+ks_status ks_param_offset(const ks_program* p, const char* name, uint32_t* offset, uint32_t* size) {
+  return guarded([&]() -> ks_status {
+    if (!p || !name) raise(KS_E_INVALID_ARG, 0, "NULL argument");
+    for (const auto& prm : p->params) {
+      if (prm.name == name) {
+        if (offset) *offset = prm.offset;
+        if (size) *size = prm.size;
+        return KS_OK;
+      }
+    }
+    raise(KS_E_INVALID_ARG, 0, "no parameter named '%s'", name);
+  });
+}
+
 ks_status ks_instr_info(const ks_program* p, uint32_t pc, ks_instr_desc* out) {
   return guarded([&]() -> ks_status {
     if (!p || !out) raise(KS_E_INVALID_ARG, 0, "NULL argument");

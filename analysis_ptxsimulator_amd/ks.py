@@ -83,6 +83,8 @@ _EXPORTS = {
     "ks_program_info": ([_P, ctypes.POINTER(ks_program_desc)], ctypes.c_int32),
     "ks_param_info": ([_P, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
                        ctypes.POINTER(ctypes.c_char_p)], ctypes.c_int32),
+    "ks_param_offset": ([_P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)],
+                        ctypes.c_int32),
     "ks_ipdom_table": ([_P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_uint32], ctypes.c_int32),
     "ks_instr_info": ([_P, ctypes.c_uint32, ctypes.POINTER(ks_instr_desc)], ctypes.c_int32),
     "ks_default_config": ([ctypes.POINTER(ks_config)], ctypes.c_int32),
@@ -148,6 +150,12 @@ def ks_param_info(prog, index):
     off, size, name = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_char_p()
     _check(lib().ks_param_info(prog, index, ctypes.byref(off), ctypes.byref(size), ctypes.byref(name)))
     return off.value, size.value, name.value.decode()
+
+
+def ks_param_offset(prog, name):
+    off, size = ctypes.c_uint32(), ctypes.c_uint32()
+    _check(lib().ks_param_offset(prog, name.encode(), ctypes.byref(off), ctypes.byref(size)))
+    return off.value, size.value
 
 
 def ks_instr_info(prog, pc):

@@ -179,20 +179,40 @@ typedef struct {
 } ks_layout;
 
 /* Parse a PTX module and decode the entry `entry` (NULL or "" = the first .entry).
- * `ptx` holds `len` bytes of text.  On success *out owns the decoded program.
- * The accepted subset and its meaning are those of the KernelScope parser and
- * simulator pages, restricted as described in the repository's design notes.
+ * `ptx` holds `len` bytes of text (not necessarily NUL-terminated; the library
+ * keeps no pointer to it).  On success *out owns the decoded program, to be
+ * released with ks_program_free.
+ * Defined by: the KernelScope page's "ptx/parser.py, ptx/models.py" part (the
+ * module, kernel, parameter and instruction grammar, predicate guards) and its
+ * "simulator/engine.py" part, load_kernel (the first kernel is taken, directives
+ * are dropped, and instructions are numbered in listing order: the pc).  Branch
+ * reconvergence points are computed here too (the SIMT stack entry of that part
+ * holds one); they are immediate post-dominators.
  * Errors: KS_E_PARSE (message "line N: ..."), KS_E_UNSUPPORTED, KS_E_INVALID_ARG. */
 ks_status ks_load_program(const char* ptx, size_t len, const char* entry, ks_program** out);
 
-/* Shape of a decoded program. */
+/* Shape of a decoded program: instruction count, parameter block, shared window,
+ * register slots and predicates.  Writes *out; no ownership changes.
+ * Defined by: the KernelScope page's "ptx/parser.py, ptx/models.py" part (a
+ * parsed kernel's params, registers and instructions).  KS_E_INVALID_ARG for NULL. */
 ks_status ks_program_info(const ks_program* prog, ks_program_desc* out);
 
 /* Parameter `index` (declaration order): byte offset in the parameter block, size
  * in bytes, and its name (points into `prog`, valid while prog lives).  Parameters
- * are laid out in declaration order, each at its natural alignment. */
+ * are laid out in declaration order, each at its natural alignment (the pages give
+ * no layout; this is the reading the oracle uses too).  Any output pointer may be
+ * NULL.  Defined by: the KernelScope page's "ptx/parser.py, ptx/models.py" part
+ * (the kernel's .param list).  KS_E_INVALID_ARG for an index out of range. */
 ks_status ks_param_info(const ks_program* prog, uint32_t index, uint32_t* offset, uint32_t* size,
                         const char** name);
+
+/* The parameter named `name` (a NUL-terminated string, as declared in the .entry's
+ * parameter list): its byte offset in the parameter block ks_run takes, and its
+ * size in bytes.  `offset` or `size` may be NULL.  The same layout as
+ * ks_param_info.  Defined by: the KernelScope page's "ptx/parser.py,
+ * ptx/models.py" part (parameters by name, as ld.param [name] reads them).
+ * Errors: KS_E_INVALID_ARG for NULL prog/name or no parameter of that name. */
+ks_status ks_param_offset(const ks_program* prog, const char* name, uint32_t* offset, uint32_t* size);
 
 typedef struct {
   uint32_t line;          /* 1-based line of the instruction in the PTX text */
@@ -202,30 +222,45 @@ typedef struct {
 } ks_instr_desc;
 
 /* Host-side description of decoded instruction `pc` (0 <= pc < n_instrs): what the
- * tools that read trace records (pc -> source line, access width) need.
- * KS_E_INVALID_ARG for a pc out of range. */
+ * tools that read trace records (pc -> source line, access width) need.  Writes
+ * *out.  Defined by: the KernelScope page's "ptx/parser.py, ptx/models.py" part
+ * (each instruction keeps its source line, used to place hints and highlight
+ * code) and its "simulator/models.py" part (the trace event names the
+ * instruction it comes from).  KS_E_INVALID_ARG for NULL or a pc out of range. */
 ks_status ks_instr_info(const ks_program* prog, uint32_t pc, ks_instr_desc* out);
 
 /* Debug: for each instruction, the reconvergence index of a guarded bra (n_instrs
- * meaning "exit"), 0xFFFFFFFF for every other instruction.  `out` holds `n`
- * entries; the first min(n, n_instrs) are written. */
+ * meaning "exit"), 0xFFFFFFFF for every other instruction.  `out` (host memory)
+ * holds `n` entries; the first min(n, n_instrs) are written.  Defined by: the
+ * KernelScope page's "simulator/engine.py, simulator/models.py" part (the SIMT
+ * stack entry's reconvergence point), read as the immediate post-dominator.
+ * KS_E_INVALID_ARG for NULL arguments. */
 ks_status ks_ipdom_table(const ks_program* prog, uint32_t* out, uint32_t n);
 
-/* Fill `cfg` with defaults: the sm_80 latency table of the KernelScope latency
- * page (int/fp32 4, ld.global 200, ld.shared 23, ld.param as ld.const 4,
- * bar.sync 20) and the cache latencies of its memory-analysis part (L1 hit 28,
- * L2 hit 150, DRAM 400), trace_cap 0, max_warp_instrs 0xFFFFFFFF, max grid/block
- * 1, basic trace format, no cache model. */
+/* Fill `cfg` with defaults: the sm_80 latency table of the KernelScope page's
+ * "latency/model.py" part (int/fp32 4, ld.global 200, ld.shared 23, ld.param as
+ * ld.const 4, bar.sync 20) and the cache latencies of its memory-analysis part
+ * (L1 hit 28, L2 hit 150, DRAM 400), trace_cap 0, max_warp_instrs 0xFFFFFFFF
+ * (the simulator's run(max_steps) cap, per warp), max grid/block 1, basic trace
+ * format, no cache model.  KS_E_INVALID_ARG for NULL. */
 ks_status ks_default_config(ks_config* cfg);
 
 /* Sizes of the caller-owned device buffers for runs up to cfg->max_grid x
- * cfg->max_block.  The trace slot size follows the IKET page's per-warp slot
- * (a 16-byte header and fixed 8- or 16-byte records, without its 1.15 margin).
- * KS_E_INVALID_ARG for an unknown trace_format or cache_model; KS_E_UNSUPPORTED
- * for the cache model with extended records or over more than 2^38 bytes. */
+ * cfg->max_block, written to *out.  Defined by: the IKET page, section 2 ("buffer
+ * 是怎么定形的"): the buffer is sized once the launch's grid and block are known,
+ * one slot per warp (warps per block = ceil(threads / 32)), a slot being a
+ * 16-byte header plus the per-warp record cap times the record size (8 bytes, or
+ * 16 with a payload); the 1.15 margin is dropped because records past the cap are
+ * counted, not stored.  KS_E_INVALID_ARG for an unknown trace_format or
+ * cache_model; KS_E_UNSUPPORTED for the cache model with extended records or over
+ * more than 2^38 bytes, or extended records beyond KS_EXT_MAX_BLOCKS blocks. */
 ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layout* out);
 
-/* Bind a program to caller-owned device buffers on the current HIP device:
+/* Bind a program to caller-owned device buffers on the current HIP device.
+ * Defined by: the KernelScope page's "simulator/engine.py" part (PtxSimulator(config)
+ * with load_kernel: a simulator instance holds one program and its launch
+ * configuration) and the IKET page, section 2 (the trace buffer is allocated per
+ * launch shape and handed to the kernel by its base address).  Buffers:
  *   d_gmem      cfg->gmem_bytes of simulated global memory (inputs are written here by
  *               the caller; ks_run updates it in place and it persists across runs),
  *   d_counters  layout.counters_bytes: 80-byte per-warp counter records,
@@ -239,6 +274,11 @@ ks_status ks_alloc_state(const ks_program* prog, const ks_config* cfg, void* d_g
                          void* d_trace, void* d_cache, ks_state** out);
 
 /* Launch one simulation of grid x block threads on `stream` (asynchronous).
+ * Defined by: the KernelScope page's "simulator/engine.py" part, run() (step every
+ * warp of every block until all have finished or the step cap is reached; here
+ * the cap is cfg->max_warp_instrs per warp) and its "simulator/models.py" part
+ * (warps, active masks, the SIMT stack, barriers); the trace base pointer is a
+ * launch argument as on the IKET page, section 2.
  * `params` holds `params_len` >= param_bytes bytes of the parameter block (host
  * memory; copied into the launch arguments).  Each run re-initialises registers,
  * predicates, stacks, scoreboards and shared windows, and rewrites every
@@ -260,21 +300,35 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
 ks_status ks_interp_kernel(const ks_program* prog, ks_dim3 block, const char** name);
 
 /* Copy n bytes of simulated global memory at byte offset sim_addr to host memory
- * (after the work queued on `stream`).  KS_E_INVALID_ARG if out of range. */
+ * `host` (caller-owned, >= n bytes), after the work queued on `stream`; returns
+ * when the copy is done.  Defined by: the KernelScope page's "simulator/models.py"
+ * part (the simulated global memory the kernel's st.global writes).
+ * KS_E_INVALID_ARG if out of range or NULL, KS_E_HIP if the copy fails. */
 ks_status ks_read_outputs(ks_state* st, uint64_t sim_addr, void* host, size_t n, void* stream);
 
 /* Copy the counter records of warps [first_warp, first_warp + n_warps) of the last
- * run to `host` (n >= 80 * n_warps bytes).  KS_E_STATE before any run. */
+ * run to `host` (caller-owned, n >= 80 * n_warps bytes); returns when done.
+ * Defined by: the KernelScope page's "simulator/models.py" part (per-warp
+ * statistics: instructions, cycles, stalls) and its memory-analysis part (per
+ * access transactions, sectors and bank-conflict degree), summed per warp.
+ * KS_E_STATE before any run; KS_E_INVALID_ARG for a range outside the last run. */
 ks_status ks_read_counters(ks_state* st, uint64_t first_warp, uint64_t n_warps, void* host, size_t n,
                            void* stream);
 
 /* Copy the trace slots of warps [first_warp, first_warp + n_warps) of the last run
- * to `host` (n >= slot_bytes * n_warps).  Record bytes past a slot's
- * records_written are unspecified.  KS_E_STATE before any run. */
+ * to `host` (caller-owned, n >= slot_bytes * n_warps); returns when done.  Record
+ * bytes past a slot's records_written are unspecified.  Defined by: the IKET
+ * page, section 2 (per-warp slots) and section 3 (after the kernel finishes the
+ * buffer is copied back to the host for post-processing).  KS_E_STATE before any
+ * run; KS_E_INVALID_ARG for a range outside the last run. */
 ks_status ks_read_trace(ks_state* st, uint64_t first_warp, uint64_t n_warps, void* host, size_t n,
                         void* stream);
 
-/* OR of the status bits of every warp of the last run (reduced on the GPU). */
+/* OR of the status bits of every warp of the last run (reduced on the GPU into a
+ * small device word the state owns), written to *or_bits.  Defined by: the IKET
+ * page, section 2 (overflow is reported, never silently dropped) and the
+ * KernelScope page's "simulator/engine.py" part (a run ends when every warp has
+ * finished or the step cap is reached).  KS_E_STATE before any run. */
 ks_status ks_run_status(ks_state* st, uint32_t* or_bits, void* stream);
 
 /* Release a state (and its device copy of the program) or a program.  NULL is a no-op. */

@@ -54,7 +54,16 @@ def test_program_shape_matches_oracle(ks, oracle_mod):
         assert info["n_preds"] == o["n_preds"]
         for i, (name, off, size) in enumerate(oracle_mod.params(ptx)):
             assert ks.ks_param_info(p, i) == (off, size, name)
+            assert ks.ks_param_offset(p, name) == (off, size)
         ks.ks_program_free(p)
+
+
+def test_param_offset_unknown_name_is_an_error(ks):
+    p = ks.ks_load_program(W.VECTOR_ADD_PTX)
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_param_offset(p, "no_such_param")
+    assert e.value.code == -3 and "no_such_param" in e.value.msg
+    ks.ks_program_free(p)
 
 
 def test_random_stress_uses_64_slots(ks):

@@ -12,7 +12,14 @@ Prints one JSON line (rank 0).  `roofline` prices the interpreter kernel's
 algorithmic bytes (32 B per counted sector + 8 B per written trace record +
 16 B header and 80 B counters per warp) per launch against MI355X's 8 TB/s HBM;
 the launch duration comes from HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`hbm_measured` prices the rocprofv3 FETCH_SIZE/WRITE_SIZE bytes of the same
+kernel (from the committed counter summary, when it was taken on the current
+kernel source) the same way.  `launch_ms` gives min, median, mean, max, std, p5
+and p95 of the per-launch HIP-event times, whose raw values go to a CSV file; a
+plain 1 GiB device copy is timed in the same run as the achievable ceiling.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+(with every host thread, and on one thread over 1/64 of that sample), and
+reports whether its counter records equal the GPU's.
 """
 import argparse
 import hashlib
@@ -79,21 +86,82 @@ def describe(w):
     return "%s: grid %s block %s trace cap %d" % (w.name, w.grid, w.block, w.trace_cap)
 
 
-def cpu_baseline(w, sample_blocks, threads, cache_model=False):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, sample_blocks, threads, cache_model=False, gpu_counters=None):
+    """The oracle, as it stands, on blocks [0, sample_blocks) with `threads` host
+    threads, then on one thread over the first 1/64 of them.  With the GPU's
+    counter records of the same run, reports whether the oracle's are identical."""
     from oracle import oracle as O
     import numpy as np
-    blocks = list(range(sample_blocks))
-    g = w.gmem  # the sampled blocks only write their own thread-private words
-    cache = np.zeros(sample_blocks * w.warps_per_block * O.CACHE_WARP_BYTES, np.uint8) if cache_model else None
-    t0 = time.perf_counter()
-    c, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=w.trace_cap, blocks=blocks, threads=threads,
-                    cache=cache)
-    dt = time.perf_counter() - t0
+
+    def timed(nb, nthreads):
+        g = w.gmem  # the sampled blocks only write their own thread-private words
+        cache = np.zeros(nb * w.warps_per_block * O.CACHE_WARP_BYTES, np.uint8) if cache_model else None
+        t0 = time.perf_counter()
+        c, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g, trace_cap=w.trace_cap, blocks=list(range(nb)),
+                        threads=nthreads, cache=cache)
+        return c, time.perf_counter() - t0
+
+    c, dt = timed(sample_blocks, threads)
     ti = int(c["thread_instrs"].sum())
-    return {"value": ti / dt, "unit": "thread-instr/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d blocks (%d thread-instructions) of the same workload, %.2f s wall"
-                      % (sample_blocks, w.n_blocks, ti, dt),
-            "warp_accesses_per_s": int((c["gld_n"].astype(np.uint64) + c["gst_n"] + c["sh_n"]).sum()) / dt}
+    out = {"value": ti / dt, "unit": "thread-instr/s", "cores": threads, "kind": "oracle",
+           "sample": "%d of %d blocks (%d thread-instructions) of the same workload, %.2f s wall"
+                     % (sample_blocks, w.n_blocks, ti, dt),
+           "warp_accesses_per_s": int((c["gld_n"].astype(np.uint64) + c["gst_n"] + c["sh_n"]).sum()) / dt,
+           "cpu_model": cpu_model()}
+    if gpu_counters is not None:
+        out["counters_equal_gpu"] = bool(np.array_equal(c, gpu_counters[:len(c)]))
+    nb1 = max(1, sample_blocks // 64)
+    c1, dt1 = timed(nb1, 1)
+    out["single_thread"] = {"value": int(c1["thread_instrs"].sum()) / dt1, "unit": "thread-instr/s",
+                            "sample": "%d blocks (1/64 of the sample), %.2f s wall" % (nb1, dt1)}
+    return out
+
+
+def launch_stats(launch_ms):
+    import numpy as np
+    a = np.asarray(launch_ms, dtype=np.float64)
+    return {"min": float(a.min()), "median": float(np.median(a)), "mean": float(a.mean()), "max": float(a.max()),
+            "std": float(a.std(ddof=1)) if a.size > 1 else 0.0, "p5": float(np.percentile(a, 5)),
+            "p95": float(np.percentile(a, 95)), "n": int(a.size)}
+
+
+def write_csv(path, launch_ms):
+    d = os.path.dirname(path)
+    if d:
+        os.makedirs(d, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("launch,ms\n")
+        for k, v in enumerate(launch_ms):
+            f.write("%d,%.6f\n" % (k, v))
+
+
+def copy_ceiling(dev, reps=5):
+    """GB/s (bytes read + written) of a plain 1 GiB device-to-device copy."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / dt / 1e9
 
 
 def copy_calibration(args, dev):
@@ -118,8 +186,9 @@ def copy_calibration(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--csv", default=None, help="raw per-launch times (default gpurun_out/launch_ms_<workload>.csv)")
     ap.add_argument("--workload", default="random_stress")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=65536)
@@ -192,6 +261,9 @@ def main():
     achieved = alg_bytes / avg_launch_s / 1e9
     prof = measured_counters(args.workload + ("_cache" if cache_on else "") + ("_ext" if ext else ""))
     traffic = prof.get("hbm_bytes_per_launch") if prof else None
+    csv_path = args.csv or os.path.join("gpurun_out", "launch_ms_%s.csv" % args.workload)
+    write_csv(csv_path, launch_ms)
+    copy_gbs = copy_ceiling(dev)
     valu = None
     if prof and "valu_busy" in prof:
         valu = {"busy": prof["valu_busy"], "lane_util": prof["valu_lane_util"], "salu_busy": prof["salu_busy"],
@@ -218,11 +290,19 @@ def main():
         "thread_instrs_per_step": thread_instrs,
         "warp_accesses_per_step": warp_acc,
         "run_status_bits": status,
-        "launch_ms": {"min": min(launch_ms), "median": float(np.median(launch_ms)), "max": max(launch_ms)},
+        "launch_ms": dict(launch_stats(launch_ms), csv=csv_path),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel": kernel},
+        # the benchmark spec's own measure: rocprofv3 HBM bytes (FETCH_SIZE x 2 + WRITE_SIZE,
+        # scaled by a plain copy) per launch over the mean launch time; null when the
+        # committed counters were taken on another kernel source
+        "hbm_measured": ({"GBps": traffic / avg_launch_s / 1e9, "frac": traffic / avg_launch_s / 1e9 / HBM_PEAK_GBS,
+                          "bytes_per_launch": traffic,
+                          "source": "rocprofv3 FETCH_SIZE/WRITE_SIZE, profiles/traffic_%s.json" % args.workload}
+                         if traffic else None),
+        "copy_ceiling_GBps": copy_gbs,
         "valu_utilisation": valu,
     }
     if cache_on:
@@ -231,7 +311,7 @@ def main():
         threads = min(16, os.cpu_count() or 1)
         # the cache model's oracle holds 200 KB of state per warp: a smaller sample
         sample = min(args.cpu_sample_blocks, w.n_blocks, 1024 if cache_on else w.n_blocks)
-        out["cpu_baseline"] = cpu_baseline(w, sample, threads, cache_on)
+        out["cpu_baseline"] = cpu_baseline(w, sample, threads, cache_on, gpu_counters=c)
     print(json.dumps(out), flush=True)
 
 

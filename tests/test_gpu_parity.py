@@ -81,7 +81,7 @@ def compare_traces(K, tg, to, cap, where=""):
                                  (where, wi, k, rg[wi, k].tolist(), ro[wi, k].tolist()))
 
 
-def full_parity(K, O, w, trace_cap=None, **kw):
+def full_parity(K, O, w, trace_cap=None, oracle_threads=0, **kw):
     cap = w.trace_cap if trace_cap is None else trace_cap
     gg, cg, tg, st = gpu_run(K, w, trace_cap=cap, **kw)
     okw = {}
@@ -89,6 +89,8 @@ def full_parity(K, O, w, trace_cap=None, **kw):
         okw["max_warp_instrs"] = kw["max_warp_instrs"]
     if "latency" in kw:
         okw["latency"] = kw["latency"]
+    if oracle_threads:
+        okw["threads"] = oracle_threads
     go, co, to = oracle_run(O, w, trace_cap=cap, **okw)
     if not np.array_equal(gg, go):
         bad = np.nonzero(gg != go)[0]
@@ -322,19 +324,82 @@ def test_ffma_full_size(K, oracle_mod, n_acc):
     assert (cg["cycles"] > per_iter * 4096).all() and (cg["cycles"] < per_iter * 4096 + 2000).all()
 
 
-@pytest.mark.parametrize("s", [1, 2, 3, 8, 16, 31, 32])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s", list(range(1, 33)))
 def test_bank_full_size(K, oracle_mod, s):
+    """The full 256 x 1024 bank probe at every word stride: all memory, every
+    counter record and every trace record against the oracle's full grid."""
     w = W.bank_probe(s)
-    cg, _ = sampled_parity(K, oracle_mod, w, [0, 255], [(w.outputs["out"][0], 4, 0)])
+    cg = full_parity(K, oracle_mod, w, oracle_threads=_host_threads())
     assert (cg["sh_degree_max"] == math.gcd(s, 32)).all()
     assert (cg["sh_degree_sum"] == 2048 * math.gcd(s, 32)).all()
 
 
+def _host_threads():
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def compare_records_masked(rg, ro, n, where):
+    """Basic records [warps, cap, 2] of both sides over each warp's first n[w]."""
+    cap = ro.shape[1]
+    live = np.arange(cap)[None, :] < n.astype(np.int64)[:, None]
+    if np.array_equal(np.where(live[:, :, None], rg, 0), np.where(live[:, :, None], ro, 0)):
+        return
+    diff = (rg != ro).any(axis=2) & live
+    wi, k = (int(x[0]) for x in np.nonzero(diff))
+    raise AssertionError("%s warp %d record %d: gpu %s oracle %s" % (where, wi, k, rg[wi, k].tolist(),
+                                                                     ro[wi, k].tolist()))
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_random_stress_full_size(K, oracle_mod, seed):
+    """The timed configuration, 65536 x 256 threads over 1 GiB, on the whole grid:
+    the oracle simulates every block (in chunks of 8192 blocks, its memory image
+    carried from chunk to chunk: blocks never communicate), and every byte of
+    simulated memory (the W1 and W4 output regions included), all 524288 counter
+    records, every trace header and every written trace record must agree."""
     w = W.random_stress(prog_seed=seed)
-    nt = w.n_blocks * w.threads_per_block
-    blocks = [0, 1, 32767, 65535] + [int(x) for x in np.random.default_rng(100 + seed).integers(0, 65536, 4)]
-    w1, w4 = w.outputs["w1"][0], w.outputs["w4"][0]
-    # W1 words j at w1 + 4 gtid + 4 j nt; W4 words at w4 + 16 gtid + 4 j
-    sampled_parity(K, oracle_mod, w, blocks, [(w1, 4, 4 * nt), (w4, 16, 0)])
+    cap = w.trace_cap
+    slot = 16 + 8 * cap
+    wpb = w.warps_per_block
+    s = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=cap)
+    try:
+        _say("random_stress seed %d: full grid %s x %s on the GPU" % (seed, w.grid, w.block))
+        s.load_gmem(w.gmem)
+        # the kernel never writes a slot past its records_written records: with the
+        # buffer cleared first, each slot must equal the oracle's (zero-filled) byte
+        # for byte
+        s.trace.zero_()
+        s.run(w.params_bytes)
+        gg = s.read_gmem()
+        cg = s.read_counters()
+        st = s.status()
+        go = w.gmem.copy()
+        chunk = 8192
+        threads = _host_threads()
+        for b0 in range(0, w.n_blocks, chunk):
+            blocks = list(range(b0, min(w.n_blocks, b0 + chunk)))
+            co, to, _ = oracle_mod.run(w.ptx, w.grid, w.block, w.params_bytes, go, trace_cap=cap, blocks=blocks,
+                                       threads=threads)
+            wlo, nw = b0 * wpb, len(blocks) * wpb
+            where = "random_stress seed %d blocks %d-%d" % (seed, blocks[0], blocks[-1])
+            compare_counters(cg[wlo:wlo + nw], co, where)
+            tg = s.read_trace(wlo, nw)
+            if not np.array_equal(tg, to):
+                hg, rg = K.trace_slots(tg, cap)
+                ho, ro = K.trace_slots(to, cap)
+                for f in ho.dtype.names:
+                    assert np.array_equal(hg[f], ho[f]), "%s trace header %s differs" % (where, f)
+                compare_records_masked(rg, ro, ho["records_written"], where)
+                raise AssertionError("%s: bytes past records_written were written" % where)
+            del tg, to
+            _say("%s: counters, headers and records equal" % where)
+        if not np.array_equal(gg, go):
+            bad = np.nonzero(gg != go)[0]
+            raise AssertionError("random_stress seed %d: %d memory bytes differ, first at %d" % (seed, bad.size, bad[0]))
+        assert st == int(np.bitwise_or.reduce(cg["status"]))
+        _say("random_stress seed %d: all 1 GiB of memory equal, status %#x" % (seed, st))
+    finally:
+        s.close()

@@ -635,6 +635,20 @@ def test_race_checker(oracle_mod):
     assert g[:4].view("<u4")[0] == 31
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_stress_full_programs_are_race_free(oracle_mod, seed):
+    """The 2000-instruction stress programs (the parity set, seeds 0-2) at 64 x 256
+    threads: the race checker finds no byte that two threads access with an
+    order-dependent outcome (two writes of different values, or a read and a write
+    of another value), over the whole run for global memory and within one barrier
+    interval for shared memory, so results do not depend on the order warps run in."""
+    w = W.random_stress(prog_seed=seed, grid=64, gmem_bytes=1 << 26)
+    _, c, _, rc = run(oracle_mod, w, trace_cap=4, check_races=True, threads=8)
+    assert rc == 0
+    assert (c["status"] & oracle_mod.ST_FINISHED).all()
+    assert int(c["barrier_n"].max()) > 50 and int(c["gst_n"].sum()) > 0
+
+
 def test_block_subset_equals_full_run(oracle_mod):
     w = W.strided_gather(2, n=4096)
     g_full, c_full, t_full, _ = run(oracle_mod, w)

@@ -30,6 +30,7 @@ TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("
 # trace formats (ks_config.trace_format) and the 16-byte extended record
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
 KS_EXT_MAX_BLOCKS = 32  # largest grid of an extended-record allocation or run
+KS_EXT64_MAX_BLOCK_THREADS = 256  # largest block of an extended run of a program of > 32 slots
 # cache-latency model (ks_config.cache_model) and its per-warp state in d_cache
 KS_CACHE_NONE, KS_CACHE_WARP = 0, 1
 KS_LAT_L1_HIT, KS_LAT_L2_HIT, KS_LAT_DRAM = 14, 15, 16

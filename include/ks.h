@@ -14,8 +14,8 @@
  * format) 16-byte records that add the instruction kind, the active mask and a
  * per-kind payload (sectors and lines of a global access, bank-conflict degree of
  * a shared access, the lanes taking a branch).  Extended records for programs of
- * more than 32 register slots support blocks of up to 768 threads, and
- * extended-record launches hold at most KS_EXT_MAX_BLOCKS blocks.
+ * more than 32 register slots support blocks of up to KS_EXT64_MAX_BLOCK_THREADS
+ * threads, and extended-record launches hold at most KS_EXT_MAX_BLOCKS blocks.
  *
  * Sources of the semantics, by page and section:
  *   - KernelScope backend documentation (github.com/briefgaming/kernelscope).
@@ -143,6 +143,11 @@ enum {
  * extended launches are refused (KS_E_UNSUPPORTED); the basic format has no
  * such limit. */
 #define KS_EXT_MAX_BLOCKS 32
+/* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run of a program of
+ * more than 32 register slots.  Extended runs of such programs with 768-thread
+ * blocks (three waves per SIMD) gave wrong counters on the GPU now and then, with
+ * no cause found yet, so larger blocks are refused (KS_E_UNSUPPORTED). */
+#define KS_EXT64_MAX_BLOCK_THREADS 256
 
 typedef struct ks_program ks_program; /* opaque; created by ks_load_program */
 typedef struct ks_state ks_state;     /* opaque; created by ks_alloc_state */

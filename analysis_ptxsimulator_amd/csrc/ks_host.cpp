@@ -1136,6 +1136,8 @@ struct ks_state {
   uint64_t last_warps = 0;    // warps of the last run (0 = no run yet)
   uint64_t slot_bytes;
   uint64_t max_warps;
+  bool in_scratch = false;    // program and status word live in the library's static scratch
+  uint64_t generation = 0;    // its binding generation on `device` (in_scratch only)
 };
 
 // ---------------------------------------------------------------------------- ABI
@@ -1350,16 +1352,67 @@ ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem
   });
 }
 
+ks_status ks_alloc_state_static(const ks_program* p, const ks_config* cfg, void* d_gmem, void* d_counters,
+                                void* d_trace, void* d_cache, ks_state** out) {
+  return guarded([&]() -> ks_status {
+    if (!p || !cfg || !out) raise(KS_E_INVALID_ARG, 0, "NULL argument");
+    *out = nullptr;
+    if (!d_gmem || !d_counters || !d_trace) raise(KS_E_INVALID_ARG, 0, "NULL device buffer");
+    if (cfg->cache_model == KS_CACHE_WARP && !d_cache) raise(KS_E_INVALID_ARG, 0, "NULL cache buffer");
+    if (p->reg_slots > KS_MAX_REG_SLOTS) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots (limit %d)", p->reg_slots, KS_MAX_REG_SLOTS);
+    if (p->n_preds > KS_MAX_PREDS) raise(KS_E_UNSUPPORTED, 0, "program needs %u predicates (limit %d)", p->n_preds, KS_MAX_PREDS);
+    if (p->code.empty()) raise(KS_E_INVALID_ARG, 0, "empty program");
+    if (p->code.size() > KS_STATIC_MAX_INSTRS)
+      raise(KS_E_UNSUPPORTED, 0, "program of %zu instructions exceeds the static scratch (at most %d instructions)",
+            p->code.size(), KS_STATIC_MAX_INSTRS);
+    ks_layout lay;
+    ks_status s = ks_query_layout(p, cfg, &lay);
+    if (s != KS_OK) return s;
+    int dev = -1;
+    if (!hip_ok(hipGetDevice(&dev), "hipGetDevice")) return KS_E_HIP;
+    hipDeviceProp_t prop;
+    if (!hip_ok(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties")) return KS_E_HIP;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) raise(KS_E_HIP, 0, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    const std::vector<DInst> table = lower_program(p, cfg);
+    DInst* d_prog = nullptr;
+    uint32_t* d_status = nullptr;
+    uint64_t gen = 0;
+    if (!hip_ok(ks_static_scratch(dev, &d_prog, &d_status, &gen), "static scratch address")) return KS_E_HIP;
+    if (!hip_ok(hipMemcpy(d_prog, table.data(), table.size() * sizeof(DInst), hipMemcpyHostToDevice), "hipMemcpy(program)"))
+      return KS_E_HIP;
+    ks_state* st = new ks_state();
+    st->prog = p;
+    st->cfg = *cfg;
+    st->device = dev;
+    st->d_prog = d_prog;
+    st->d_gmem = d_gmem;
+    st->d_counters = d_counters;
+    st->d_trace = d_trace;
+    st->d_cache = cfg->cache_model == KS_CACHE_WARP ? d_cache : nullptr;
+    st->d_status = d_status;
+    st->slot_bytes = lay.slot_bytes;
+    st->max_warps = lay.n_warps;
+    st->in_scratch = true;
+    st->generation = gen;
+    *out = st;
+    return KS_OK;
+  });
+}
+
 void ks_state_free(ks_state* st) {
   if (!st) return;
-  (void)hipFree(st->d_prog);
-  (void)hipFree(st->d_status);
+  if (!st->in_scratch) {
+    (void)hipFree(st->d_prog);
+    (void)hipFree(st->d_status);
+  }
   delete st;
 }
 
 ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, size_t params_len, void* stream) {
   return guarded([&]() -> ks_status {
     if (!st) raise(KS_E_INVALID_ARG, 0, "NULL state");
+    if (st->in_scratch && ks_static_generation(st->device) != st->generation)
+      raise(KS_E_STATE, 0, "another static state was bound on device %d since this one: its program is gone", st->device);
     const ks_program* p = st->prog;
     if (!grid.x || !grid.y || !grid.z || !block.x || !block.y || !block.z) raise(KS_E_INVALID_ARG, 0, "zero grid or block dimension");
     uint64_t tpb = dim_count(block), nb = dim_count(grid);

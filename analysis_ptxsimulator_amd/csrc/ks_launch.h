@@ -27,3 +27,12 @@ uint32_t ks_max_block_threads(int variant, bool ext);
 // Dynamic LDS bytes of one workgroup of `wg` lanes (scoreboards, with `ext` the
 // staging ring of extended trace records, and the shared window).
 size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes, bool ext);
+
+// The library's static scratch on device `dev` (the current device), for states
+// that must not allocate: where the decoded program and the status word go.  The
+// first call on a device looks the array's address up (hipGetSymbolAddress); each
+// call starts a new binding generation on that device, returned in *generation.
+hipError_t ks_static_scratch(int dev, ks::DInst** prog, uint32_t** status, uint64_t* generation);
+
+// The latest binding generation of device `dev` (0 before any static binding).
+uint64_t ks_static_generation(int dev);

@@ -30,6 +30,7 @@ TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("
 # trace formats (ks_config.trace_format) and the 16-byte extended record
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
 KS_EXT_MAX_BLOCKS = 32  # largest grid of an extended-record allocation or run
+KS_STATIC_MAX_INSTRS = 8187  # largest program a ks_alloc_state_static binding holds
 KS_EXT64_MAX_BLOCK_THREADS = 256  # largest block of an extended run of a program of > 32 slots
 # cache-latency model (ks_config.cache_model) and its per-warp state in d_cache
 KS_CACHE_NONE, KS_CACHE_WARP = 0, 1
@@ -91,6 +92,7 @@ _EXPORTS = {
     "ks_default_config": ([ctypes.POINTER(ks_config)], ctypes.c_int32),
     "ks_query_layout": ([_P, ctypes.POINTER(ks_config), ctypes.POINTER(ks_layout)], ctypes.c_int32),
     "ks_alloc_state": ([_P, ctypes.POINTER(ks_config), _P, _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int32),
+    "ks_alloc_state_static": ([_P, ctypes.POINTER(ks_config), _P, _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int32),
     "ks_run": ([_P, ks_dim3, ks_dim3, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
     "ks_interp_kernel": ([_P, ks_dim3, ctypes.POINTER(ctypes.c_char_p)], ctypes.c_int32),
     "ks_read_outputs": ([_P, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
@@ -194,6 +196,13 @@ def ks_alloc_state(prog, cfg, d_gmem, d_counters, d_trace, d_cache=0):
     out = _P()
     _check(lib().ks_alloc_state(prog, ctypes.byref(cfg), _P(d_gmem), _P(d_counters), _P(d_trace), _P(d_cache),
                                 ctypes.byref(out)))
+    return out
+
+
+def ks_alloc_state_static(prog, cfg, d_gmem, d_counters, d_trace, d_cache=0):
+    out = _P()
+    _check(lib().ks_alloc_state_static(prog, ctypes.byref(cfg), _P(d_gmem), _P(d_counters), _P(d_trace),
+                                       _P(d_cache), ctypes.byref(out)))
     return out
 
 

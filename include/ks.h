@@ -148,6 +148,10 @@ enum {
  * blocks (three waves per SIMD) gave wrong counters on the GPU now and then, with
  * no cause found yet, so larger blocks are refused (KS_E_UNSUPPORTED). */
 #define KS_EXT64_MAX_BLOCK_THREADS 256
+/* Largest program (decoded instructions) a state bound by ks_alloc_state_static can
+ * hold: the library's static device scratch is (KS_STATIC_MAX_INSTRS + 5) 128-byte
+ * records plus 256 bytes, 1 MiB + 256 bytes per GPU. */
+#define KS_STATIC_MAX_INSTRS 8187
 
 typedef struct ks_program ks_program; /* opaque; created by ks_load_program */
 typedef struct ks_state ks_state;     /* opaque; created by ks_alloc_state */
@@ -277,6 +281,24 @@ ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layou
  * KS_E_UNSUPPORTED (program beyond this build's limits), KS_E_HIP, KS_E_NOMEM. */
 ks_status ks_alloc_state(const ks_program* prog, const ks_config* cfg, void* d_gmem, void* d_counters,
                          void* d_trace, void* d_cache, ks_state** out);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ks_alloc_state without
+ * any device allocation.  The decoded program and the status word of
+ * ks_run_status go into a static scratch array the library holds on each GPU
+ * (1 MiB + 256 bytes, kept until the process ends) instead of memory of the
+ * state's own; the caller-owned buffers are as for ks_alloc_state.  The program is
+ * copied in synchronously (hipMemcpy) by this call; nothing else is allocated on
+ * the device, and ks_run, ks_run_status, ks_read_* and ks_state_free work on the
+ * returned state as on any other (ks_state_free releases no device memory).
+ * Sharing: every static state on a GPU shares that GPU's scratch, which holds the
+ * program of the latest binding.  A ks_run of a static state bound before the
+ * latest one on its device fails with KS_E_STATE; work of two static states that
+ * overlaps on one GPU (other streams, other host threads) races.
+ * Errors: KS_E_UNSUPPORTED for a program of more than KS_STATIC_MAX_INSTRS
+ * instructions, otherwise those of ks_alloc_state (never KS_E_NOMEM). */
+ks_status ks_alloc_state_static(const ks_program* prog, const ks_config* cfg, void* d_gmem, void* d_counters,
+                                void* d_trace, void* d_cache, ks_state** out);
 
 /* Launch one simulation of grid x block threads on `stream` (asynchronous).
  * Defined by: the KernelScope page's "simulator/engine.py" part, run() (step every

@@ -175,6 +175,22 @@ def test_extended_64_slot_block_limit(ks):
     ks.ks_program_free(q)
 
 
+def test_static_binding_refuses_programs_beyond_its_scratch(ks):
+    """ks_alloc_state_static holds at most KS_STATIC_MAX_INSTRS decoded
+    instructions; a longer program is refused before any device work."""
+    from workloads.randprog import random_program
+    ptx = random_program(0, n_instr=ks.KS_STATIC_MAX_INSTRS + 100, n_threads=256)[0]
+    p = ks.ks_load_program(ptx)
+    assert ks.ks_program_info(p)["n_instrs"] > ks.KS_STATIC_MAX_INSTRS
+    cfg = ks.ks_default_config()
+    cfg.max_block = ks.ks_dim3(256, 1, 1)
+    cfg.gmem_bytes = 1 << 20
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_alloc_state_static(p, cfg, 1, 2, 3)  # dummy buffers: refused before they are used
+    assert e.value.code == -2 and "%d instructions" % ks.KS_STATIC_MAX_INSTRS in e.value.msg
+    ks.ks_program_free(p)
+
+
 def test_cache_model_layout_and_limits(ks, oracle_mod):
     """The cache model adds KS_CACHE_WARP_BYTES of state per warp (the oracle's
     layout), refuses extended records and memories above 2^38 bytes, and needs

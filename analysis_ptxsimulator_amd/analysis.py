@@ -125,8 +125,10 @@ def decode_payload(kind, payload):
     return {"guard_lanes": p}
 
 
-def _popc(x):
-    return bin(int(x)).count("1")
+def _popc32(x):
+    """Per-element population count of a uint32 array."""
+    x = np.asarray(x, dtype=np.uint32)
+    return np.unpackbits(x.view(np.uint8).reshape(x.shape + (4,)), axis=-1).sum(axis=-1, dtype=np.int64)
 
 
 def coalescing_efficiency(kind, payload, access_bytes):
@@ -141,102 +143,162 @@ def coalescing_efficiency(kind, payload, access_bytes):
     return min(1.0, ((f["lanes"] * access_bytes + 127) // 128) / f["lines"])
 
 
-def hints(headers, records, info, occupancy_result=None, warps_per_block=1):
-    """The hint rules over extended trace records (one slot per warp).  Per-event
-    hints carry the warp, the record index, the pc and the source line.
+# Thresholds of the hint rules (KernelScope "hints/analyzer.py" part): a shared access
+# whose conflict degree reaches 8 is critical, above 1 a warning; a global access
+# below 25% efficiency is critical, below 50% uncoalesced (counted, no event hint);
+# a divergent branch whose divergence ratio exceeds 40% is a warning; more than 5
+# conflicting shared accesses or more than 3 divergent branches add a summary
+# warning; occupancy below 25% is critical, below 50% a warning.
+RULES = dict(degree_critical=8, efficiency_critical=0.25, efficiency_uncoalesced=0.5, divergence_ratio=0.4,
+             conflicts_summary=5, divergent_summary=3, occupancy_critical=25.0, occupancy_warning=50.0)
 
-    The efficiency of a global access is the coalescing analysis's: the fewest
-    128-byte lines its requested bytes could take (guard lanes x access bytes,
-    rounded up to whole lines) over the lines it touches, at most 1.  Accesses
-    between 25% and 50% are counted as uncoalesced but, as in the rules, produce
-    no hint.  Reading (the rules use a ratio they do not define): the divergence
-    ratio of a divergent branch = lanes on the smaller side / active lanes (0.5
-    for an even split)."""
+
+def hint_table(headers, records, info):
+    """The per-record measures the hint rules look at, over every written extended
+    record at once (numpy arrays over [warp, record] positions).
+
+    Returns a dict of flat arrays for the records that trip a rule: `warp`,
+    `record`, `pc`, `rule` (0 shared conflict, 1 scattered global access, 2 split
+    branch), `value` (conflict degree, coalescing efficiency or divergence ratio),
+    plus the totals `conflicts` (shared accesses with a degree above 1),
+    `uncoalesced` (global accesses at 25-50% efficiency) and `divergent`
+    (divergent branches).
+
+    Efficiency of a global access: the fewest 128-byte lines its requested bytes
+    need (guard lanes x access bytes, rounded up to whole lines) over the lines it
+    touches, at most 1.  Divergence ratio (the rules use it without defining it;
+    reading): lanes on the smaller side of the split over the live lanes."""
+    n_w = len(headers)
+    cap = records.shape[1] if records.ndim == 2 else 0
+    written = np.asarray(headers["records_written"], dtype=np.int64).reshape(n_w)
+    # the 16-byte records as four words: cycle, pc | kind << 16, active, payload
+    words = np.ascontiguousarray(records).view(np.uint32).reshape(n_w, cap, 4)
+    pk = words[:, :, 1]
+    kind = (pk >> 16) & 0xFF
+    live = np.arange(cap, dtype=np.int64)[None, :] < written[:, None]
+    kind = np.where(live, kind, 0xFF)  # unwritten positions take a kind no rule looks at
+    pay = words[:, :, 3]
+    deg = pay & 0xFF
+    conflict = ((kind == ks.KS_EV_LD_SHARED) | (kind == ks.KS_EV_ST_SHARED)) & (deg > 1)
+    glob = ((kind == ks.KS_EV_LD_GLOBAL) | (kind == ks.KS_EV_ST_GLOBAL)) & (((pay >> 8) & 0xFF) > 0)
+    div = kind == ks.KS_EV_DIVERGE
+    acc = np.array([d["access_bytes"] for d in info.desc] + [0], dtype=np.int64)
+
+    # efficiency of the global accesses
+    g_w, g_k = np.nonzero(glob)
+    gp = pay[g_w, g_k].astype(np.int64)
+    gpc = np.minimum((pk[g_w, g_k] & 0xFFFF).astype(np.int64), len(acc) - 1)
+    g_eff = np.minimum(1.0, ((((gp >> 16) & 0xFF) * acc[gpc] + 127) // 128) / ((gp >> 8) & 0xFF))
+    g_bad = g_eff < RULES["efficiency_critical"]
+    uncoalesced = int(((g_eff >= RULES["efficiency_critical"]) & (g_eff < RULES["efficiency_uncoalesced"])).sum())
+
+    # divergence ratio of the divergent branches
+    d_w, d_k = np.nonzero(div)
+    d_act = words[d_w, d_k, 2]
+    d_tak = pay[d_w, d_k] & d_act
+    d_ratio = np.minimum(_popc32(d_tak), _popc32(d_act & ~d_tak)) / np.maximum(1, _popc32(d_act))
+    d_bad = d_ratio > RULES["divergence_ratio"]
+
+    c_w, c_k = np.nonzero(conflict)
+    w_i = np.concatenate([c_w, g_w[g_bad], d_w[d_bad]])
+    k_i = np.concatenate([c_k, g_k[g_bad], d_k[d_bad]])
+    rule = np.concatenate([np.zeros(len(c_w), np.int64), np.ones(int(g_bad.sum()), np.int64),
+                           np.full(int(d_bad.sum()), 2, np.int64)])
+    value = np.concatenate([deg[c_w, c_k].astype(np.float64), g_eff[g_bad], d_ratio[d_bad]])
+    order = np.lexsort((k_i, w_i))  # warp order, then record order
+    w_i, k_i, rule, value = w_i[order], k_i[order], rule[order], value[order]
+    return {"warp": w_i, "record": k_i, "pc": (pk[w_i, k_i] & 0xFFFF).astype(np.int64), "rule": rule, "value": value,
+            "conflicts": int(len(c_w)), "uncoalesced": uncoalesced, "divergent": int(len(d_w))}
+
+
+def hints(headers, records, info, occupancy_result=None, warps_per_block=1):
+    """Performance hints over extended trace records (one slot per warp), from the
+    rule table of hint_table: one hint per record that trips a rule (with its warp,
+    block, record index, pc and source line), then the summary and occupancy hints."""
+    t = hint_table(headers, records, info)
+    lines = [d["line"] for d in info.desc]
     out = []
-    n_conflict = n_uncoalesced = n_divergent = 0
-    for w in range(len(headers)):
-        n = int(headers["records_written"][w])
-        for k in range(n):
-            r = records[w, k]
-            kind, pc = int(r["kind"]), int(r["pc"])
-            where = {"warp": w, "block": w // warps_per_block, "record": k, "pc": pc,
-                     "source_line": info.desc[pc]["line"]}
-            f = decode_payload(kind, r["payload"])
-            if kind in (ks.KS_EV_LD_SHARED, ks.KS_EV_ST_SHARED) and f["degree"] > 1:
-                n_conflict += 1
-                sev = "critical" if f["degree"] >= 8 else "warning"
-                out.append(dict(category="memory", severity=sev, message="%d-way bank conflict" % f["degree"],
-                                detail="Severe bank conflict causing serialized access" if sev == "critical"
-                                else "Bank conflict reducing throughput", **where))
-            elif kind in (ks.KS_EV_LD_GLOBAL, ks.KS_EV_ST_GLOBAL) and f["lines"]:
-                eff = coalescing_efficiency(kind, r["payload"], info.desc[pc]["access_bytes"])
-                if eff < 0.25:
-                    out.append(dict(category="memory", severity="critical",
-                                    message="Poor memory efficiency (%d%%)" % int(eff * 100),
-                                    detail="Scattered access causing many transactions", efficiency=eff, **where))
-                elif eff < 0.5:
-                    n_uncoalesced += 1
-            elif kind == ks.KS_EV_DIVERGE:
-                n_divergent += 1
-                act, taken = int(r["active"]), f["taken"] & int(r["active"])
-                ratio = min(_popc(taken), _popc(act & ~taken)) / max(1, _popc(act))
-                if ratio > 0.4:
-                    out.append(dict(category="divergence", severity="warning",
-                                    message="High divergence (%d%%)" % int(ratio * 100),
-                                    detail="Significant warp divergence at this branch", ratio=ratio, **where))
-    if n_conflict > 5:
+    for w, k, pc, rule, v in zip(t["warp"].tolist(), t["record"].tolist(), t["pc"].tolist(), t["rule"].tolist(),
+                                 t["value"].tolist()):
+        where = {"warp": w, "block": w // warps_per_block, "record": k, "pc": pc, "source_line": lines[pc]}
+        if rule == 0:
+            d = int(v)
+            if d >= RULES["degree_critical"]:
+                out.append(dict(category="memory", severity="critical", message="shared bank-conflict degree %d" % d,
+                                detail="at least %d lanes wait on one bank: this access runs as %d serial passes"
+                                % (RULES["degree_critical"], d), degree=d, **where))
+            else:
+                out.append(dict(category="memory", severity="warning", message="shared bank-conflict degree %d" % d,
+                                detail="lanes share a bank at different addresses: %d passes instead of one" % d,
+                                degree=d, **where))
+        elif rule == 1:
+            out.append(dict(category="memory", severity="critical",
+                            message="global access at %d%% coalescing efficiency" % int(v * 100),
+                            detail="its bytes are spread over far more 128-byte lines than they fill",
+                            efficiency=v, **where))
+        else:
+            out.append(dict(category="divergence", severity="warning",
+                            message="branch splits the warp, %d%% of lanes on the smaller side" % int(v * 100),
+                            detail="the two sides of this branch run one after the other", ratio=v, **where))
+    if t["conflicts"] > RULES["conflicts_summary"]:
         out.append(dict(category="memory", severity="warning",
-                        message="Shared memory bank conflicts (%d events)" % n_conflict,
-                        detail="Consider padding arrays or restructuring access patterns"))
-    if n_divergent > 3:
+                        message="%d shared accesses with bank conflicts" % t["conflicts"],
+                        detail="lay shared arrays out (padding, a different index) so that a warp's lanes "
+                               "fall in distinct banks"))
+    if t["divergent"] > RULES["divergent_summary"]:
         out.append(dict(category="divergence", severity="warning",
-                        message="Branch divergence detected (%d events)" % n_divergent,
-                        detail="Consider restructuring conditionals or using predication"))
+                        message="%d branches split their warp" % t["divergent"],
+                        detail="keep branch conditions uniform across a warp, or turn short branches into selects"))
     if occupancy_result:
         occ, lim = occupancy_result["occupancy_percent"], occupancy_result["limiting_factor"]
-        if occ < 25:
-            out.append(dict(category="occupancy", severity="critical", message="Very low occupancy (%g%%)" % occ,
-                            detail="Limited by %s. Consider reducing resource usage." % lim))
-        elif occ < 50:
-            out.append(dict(category="occupancy", severity="warning", message="Low occupancy (%g%%)" % occ,
-                            detail="Limited by %s." % lim))
+        lim = lim.replace("_", " ")
+        if occ < RULES["occupancy_critical"]:
+            out.append(dict(category="occupancy", severity="critical", message="occupancy %g%%, under a quarter" % occ,
+                            detail="%s bound the resident warps; ask for less of them per thread or per block"
+                                   % lim))
+        elif occ < RULES["occupancy_warning"]:
+            out.append(dict(category="occupancy", severity="warning", message="occupancy %g%%, under half" % occ,
+                            detail="%s bound the resident warps" % lim))
     return out
 
 
-def chrome_trace(headers, records, info, warps_per_block, trace_format=ks.KS_TRACE_EXTENDED):
-    """Trace-event JSON of the per-warp slots: one process per block, one thread per
-    warp, one complete event per issued instruction from its issue cycle to the
-    warp's next issue (1 cycle for the last).  Time unit: one simulated cycle."""
-    ev = []
-    for w in range(len(headers)):
-        n = int(headers["records_written"][w])
-        if n == 0:
-            continue
-        b, wib = w // warps_per_block, w % warps_per_block
-        if wib == 0:
-            ev.append({"ph": "M", "name": "process_name", "pid": b, "tid": 0, "args": {"name": "block %d" % b}})
-        ev.append({"ph": "M", "name": "thread_name", "pid": b, "tid": wib, "args": {"name": "warp %d" % wib}})
-        if trace_format == ks.KS_TRACE_EXTENDED:
-            cyc = records[w, :n]["cycle"].astype(np.int64)
-            pcs = records[w, :n]["pc"].astype(np.int64)
-        else:
-            cyc = records[w, :n, 0].astype(np.int64)
-            pcs = records[w, :n, 1].astype(np.int64)
-        for k in range(n):
-            pc = int(pcs[k])
-            dur = int(cyc[k + 1] - cyc[k]) if k + 1 < n else 1
-            args = {"pc": pc, "line": info.desc[pc]["line"], "text": info.text(pc)}
-            cat = "issue"
-            if trace_format == ks.KS_TRACE_EXTENDED:
-                r = records[w, k]
-                kind = int(r["kind"])
-                cat = ks.EV_NAMES[kind]
-                args["active"] = "0x%08x" % int(r["active"])
-                args.update(decode_payload(kind, r["payload"]))
-            ev.append({"ph": "X", "name": info.mnemonic(pc), "cat": cat, "pid": b, "tid": wib,
-                       "ts": int(cyc[k]), "dur": dur, "args": args})
-    return {"traceEvents": ev, "displayTimeUnit": "ns",
-            "otherData": {"time_unit": "simulated cycle", "source": "libkscope per-warp trace slots"}}
+def _slot_bytes(headers, records, trace_format):
+    """Headers and records back in the slot layout of ks_read_trace (one row per warp)."""
+    n_w = len(headers)
+    h = np.ascontiguousarray(headers).view(np.uint8).reshape(n_w, 16)
+    r = np.ascontiguousarray(records).view(np.uint8).reshape(n_w, -1)
+    raw = np.empty((n_w, 16 + r.shape[1]), dtype=np.uint8)
+    raw[:, :16] = h
+    raw[:, 16:] = r
+    return raw
+
+
+def write_chrome_trace(path, headers, records, info, warps_per_block, trace_format=ks.KS_TRACE_EXTENDED,
+                       first_warp=0):
+    """Write the per-warp slots as a trace-event JSON file (Chrome / Perfetto): one
+    process per block, one thread per warp, one complete event per issued instruction
+    from its issue cycle to the warp's next issue (1 cycle for the last); time unit
+    one simulated cycle.  The libkscope writer does the formatting; this side only
+    supplies each pc's name and source line.  Returns the number of instruction events."""
+    names = [json.dumps(info.mnemonic(pc)) for pc in range(len(info.desc))]
+    args = ['"pc":%d,"line":%d,"text":%s' % (pc, d["line"], json.dumps(info.text(pc))) for pc, d in enumerate(info.desc)]
+    raw = _slot_bytes(headers, records, trace_format)
+    return ks.ks_write_trace_events(raw, len(headers), raw.shape[1], trace_format, first_warp, warps_per_block,
+                                    names, args, path)
+
+
+def chrome_trace(headers, records, info, warps_per_block, trace_format=ks.KS_TRACE_EXTENDED, first_warp=0):
+    """The document write_chrome_trace writes, parsed into a dict (for small traces)."""
+    import os
+    import tempfile
+    fd, path = tempfile.mkstemp(suffix=".json")
+    os.close(fd)
+    try:
+        write_chrome_trace(path, headers, records, info, warps_per_block, trace_format, first_warp)
+        with open(path) as f:
+            return json.load(f)
+    finally:
+        os.unlink(path)
 
 
 def main(argv=None):
@@ -282,8 +344,7 @@ def main(argv=None):
                       "hints": [h for h in hs if "warp" not in h] + [h for h in hs if "warp" in h][:20],
                       "n_event_hints": sum(1 for h in hs if "warp" in h)}, indent=1))
     if args.out:
-        with open(args.out, "w") as f:
-            json.dump(chrome_trace(hdr[: args.warps], rec[: args.warps], info, w.warps_per_block), f)
+        write_chrome_trace(args.out, hdr[: args.warps], rec[: args.warps], info, w.warps_per_block)
 
 
 if __name__ == "__main__":

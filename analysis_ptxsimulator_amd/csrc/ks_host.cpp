@@ -1547,6 +1547,160 @@ ks_status ks_read_trace(ks_state* st, uint64_t first_warp, uint64_t n_warps, voi
   });
 }
 
+// ---------------------------------------------------------------------------- trace-event export
+
+namespace {
+
+// Buffered text output with integer formatting of its own (the export writes some
+// hundred million numbers for a large slice).
+struct JsonOut {
+  FILE* f;
+  std::string buf;
+  explicit JsonOut(FILE* fp) : f(fp) { buf.reserve(1u << 23); }
+  void put(const char* s) { buf.append(s); }
+  void put(const char* s, size_t n) { buf.append(s, n); }
+  void num(uint64_t v) {
+    char t[24];
+    int n = 0;
+    do {
+      t[n++] = (char)('0' + v % 10u);
+      v /= 10u;
+    } while (v);
+    while (n) buf.push_back(t[--n]);
+  }
+  void hex8(uint32_t v) {
+    static const char* d = "0123456789abcdef";
+    for (int k = 7; k >= 0; --k) buf.push_back(d[(v >> (4 * k)) & 15u]);
+  }
+  bool flush(bool force) {
+    if (!force && buf.size() < (1u << 22)) return true;
+    const bool ok = fwrite(buf.data(), 1, buf.size(), f) == buf.size();
+    buf.clear();
+    return ok;
+  }
+};
+
+const char* const kEvNames[9] = {"other", "ld.global", "st.global", "ld.shared", "st.shared", "branch", "diverge", "barrier", "ret"};
+
+}  // namespace
+
+ks_status ks_write_trace_events(const void* trace, uint64_t n_warps, uint64_t slot_bytes, uint32_t trace_format,
+                                uint64_t first_warp, uint32_t warps_per_block, uint32_t n_pcs,
+                                const char* const* pc_names, const char* const* pc_args, const char* path,
+                                uint64_t* n_events) {
+  return guarded([&]() -> ks_status {
+    if ((!trace && n_warps) || !path || (n_pcs && (!pc_names || !pc_args)) || !warps_per_block)
+      raise(KS_E_INVALID_ARG, 0, "NULL argument or zero warps per block");
+    if (trace_format != KS_TRACE_BASIC && trace_format != KS_TRACE_EXTENDED)
+      raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", trace_format);
+    const uint64_t rec = trace_format == KS_TRACE_EXTENDED ? 16u : 8u;
+    if (slot_bytes < 16u || (slot_bytes - 16u) % rec) raise(KS_E_INVALID_ARG, 0, "slot of %llu bytes", (unsigned long long)slot_bytes);
+    const uint64_t cap = (slot_bytes - 16u) / rec;
+    FILE* f = fopen(path, "wb");
+    if (!f) raise(KS_E_INVALID_ARG, 0, "cannot open %s", path);
+    JsonOut o(f);
+    uint64_t events = 0;
+    bool first = true, ok = true;
+    o.put("{\"traceEvents\":[");
+    const uint8_t* base = static_cast<const uint8_t*>(trace);
+    for (uint64_t wl = 0; wl < n_warps && ok; ++wl) {
+      const uint8_t* slot = base + wl * slot_bytes;
+      uint32_t written;
+      memcpy(&written, slot, 4);
+      if (written > cap) {
+        fclose(f);
+        raise(KS_E_INVALID_ARG, 0, "warp %llu: %u records in a slot of %llu", (unsigned long long)(first_warp + wl), written,
+              (unsigned long long)cap);
+      }
+      if (!written) continue;
+      const uint64_t w = first_warp + wl;
+      const uint64_t b = w / warps_per_block, wib = w % warps_per_block;
+      if (wib == 0) {
+        o.put(first ? "" : ",");
+        o.put("{\"ph\":\"M\",\"name\":\"process_name\",\"pid\":");
+        o.num(b);
+        o.put(",\"tid\":0,\"args\":{\"name\":\"block ");
+        o.num(b);
+        o.put("\"}}");
+        first = false;
+      }
+      o.put(first ? "" : ",");
+      o.put("{\"ph\":\"M\",\"name\":\"thread_name\",\"pid\":");
+      o.num(b);
+      o.put(",\"tid\":");
+      o.num(wib);
+      o.put(",\"args\":{\"name\":\"warp ");
+      o.num(wib);
+      o.put("\"}}");
+      first = false;
+      const uint8_t* r = slot + 16;
+      for (uint32_t k = 0; k < written; ++k, r += rec) {
+        uint32_t cyc, pc, kind = 0, active = 0, pay = 0, next = 0;
+        memcpy(&cyc, r, 4);
+        if (trace_format == KS_TRACE_EXTENDED) {
+          uint32_t w1;
+          memcpy(&w1, r + 4, 4);
+          pc = w1 & 0xFFFFu;
+          kind = (w1 >> 16) & 0xFFu;
+          memcpy(&active, r + 8, 4);
+          memcpy(&pay, r + 12, 4);
+        } else {
+          memcpy(&pc, r + 4, 4);
+        }
+        if (pc >= n_pcs || kind > KS_EV_RET) {
+          fclose(f);
+          raise(KS_E_INVALID_ARG, 0, "warp %llu record %u: pc %u / kind %u outside the program", (unsigned long long)w, k, pc, kind);
+        }
+        if (k + 1 < written) memcpy(&next, r + rec, 4);
+        const uint64_t dur = k + 1 < written ? (uint64_t)next - cyc : 1u;
+        o.put(",{\"ph\":\"X\",\"name\":");
+        o.put(pc_names[pc]);
+        o.put(",\"cat\":\"");
+        o.put(trace_format == KS_TRACE_EXTENDED ? kEvNames[kind] : "issue");
+        o.put("\",\"pid\":");
+        o.num(b);
+        o.put(",\"tid\":");
+        o.num(wib);
+        o.put(",\"ts\":");
+        o.num(cyc);
+        o.put(",\"dur\":");
+        o.num(dur);
+        o.put(",\"args\":{");
+        o.put(pc_args[pc]);
+        if (trace_format == KS_TRACE_EXTENDED) {
+          o.put(",\"active\":\"0x");
+          o.hex8(active);
+          o.put("\"");
+          if (kind == KS_EV_LD_GLOBAL || kind == KS_EV_ST_GLOBAL) {
+            o.put(",\"sectors\":"); o.num(pay & 0xFFu);
+            o.put(",\"lines\":"); o.num((pay >> 8) & 0xFFu);
+            o.put(",\"lanes\":"); o.num((pay >> 16) & 0xFFu);
+            o.put(",\"faults\":"); o.num(pay >> 24);
+          } else if (kind == KS_EV_LD_SHARED || kind == KS_EV_ST_SHARED) {
+            o.put(",\"degree\":"); o.num(pay & 0xFFu);
+            o.put(",\"lanes\":"); o.num((pay >> 16) & 0xFFu);
+            o.put(",\"faults\":"); o.num(pay >> 24);
+          } else if (kind == KS_EV_BRANCH || kind == KS_EV_DIVERGE) {
+            o.put(",\"taken\":"); o.num(pay);
+          } else if (kind != KS_EV_BARRIER) {
+            o.put(",\"guard_lanes\":"); o.num(pay);
+          }
+        }
+        o.put("}}");
+        ++events;
+        ok = o.flush(false);
+      }
+    }
+    o.put("],\"displayTimeUnit\":\"ns\",\"otherData\":{\"time_unit\":\"simulated cycle\","
+          "\"source\":\"libkscope per-warp trace slots\"}}");
+    ok = ok && o.flush(true);
+    ok = (fclose(f) == 0) && ok;
+    if (!ok) raise(KS_E_INVALID_ARG, 0, "writing %s failed", path);
+    if (n_events) *n_events = events;
+    return KS_OK;
+  });
+}
+
 ks_status ks_run_status(ks_state* st, uint32_t* or_bits, void* stream) {
   return guarded([&]() -> ks_status {
     if (!st || !or_bits) raise(KS_E_INVALID_ARG, 0, "NULL argument");

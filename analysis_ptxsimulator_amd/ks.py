@@ -99,6 +99,10 @@ _EXPORTS = {
     "ks_read_counters": ([_P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
     "ks_read_trace": ([_P, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, _P], ctypes.c_int32),
     "ks_run_status": ([_P, ctypes.POINTER(ctypes.c_uint32), _P], ctypes.c_int32),
+    "ks_write_trace_events": ([ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64,
+                               ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_char_p),
+                               ctypes.POINTER(ctypes.c_char_p), ctypes.c_char_p, ctypes.POINTER(ctypes.c_uint64)],
+                              ctypes.c_int32),
     "ks_state_free": ([_P], None),
     "ks_program_free": ([_P], None),
     "ks_last_error": ([], ctypes.c_char_p),
@@ -234,6 +238,23 @@ def ks_run_status(state, stream=0):
     v = ctypes.c_uint32()
     _check(lib().ks_run_status(state, ctypes.byref(v), _P(stream)))
     return v.value
+
+
+def ks_write_trace_events(trace, n_warps, slot_bytes, trace_format, first_warp, warps_per_block, pc_names,
+                          pc_args, path):
+    """trace: a C-contiguous host buffer (numpy) of n_warps slots; pc_names / pc_args:
+    lists of str (JSON fragments).  Returns the number of instruction events."""
+    t = np.ascontiguousarray(trace)
+    assert t.nbytes >= n_warps * slot_bytes, "trace buffer smaller than its slots"
+    n = len(pc_names)
+    assert len(pc_args) == n
+    names = (ctypes.c_char_p * max(n, 1))(*[x.encode() for x in pc_names])
+    args = (ctypes.c_char_p * max(n, 1))(*[x.encode() for x in pc_args])
+    out = ctypes.c_uint64()
+    _check(lib().ks_write_trace_events(t.ctypes.data_as(ctypes.c_void_p), n_warps, slot_bytes, trace_format,
+                                       first_warp, warps_per_block, n, names, args, os.fsencode(path),
+                                       ctypes.byref(out)))
+    return out.value
 
 
 def ks_state_free(state):

@@ -358,6 +358,26 @@ ks_status ks_read_trace(ks_state* st, uint64_t first_warp, uint64_t n_warps, voi
  * finished or the step cap is reached).  KS_E_STATE before any run. */
 ks_status ks_run_status(ks_state* st, uint32_t* or_bits, void* stream);
 
+/* Host-side export (no device work): write the trace slots of warps [first_warp,
+ * first_warp + n_warps) -- `trace` holds them as ks_read_trace returns them,
+ * slot_bytes each, in trace_format -- as a Chrome / Perfetto trace-event JSON file
+ * at `path`: one process per block, one thread per warp (warps_per_block warps per
+ * block), one complete event per record from its issue cycle to the warp's next
+ * issue (1 cycle for the last), time unit one simulated cycle.  Extended records
+ * add the record's active mask and its payload fields (sectors, lines, lanes and
+ * faults; degree; taken; guard_lanes) to the event's args.  pc_names[pc] and
+ * pc_args[pc] (pc < n_pcs) are inserted verbatim: a JSON string for the event name
+ * and the leading JSON members of its args (for example "pc":4,"line":12).
+ * *n_events (may be NULL) receives the number of instruction events.  Defined by:
+ * the IKET page, sections 3 and 5 (post-processing of the per-warp buffer into a
+ * Perfetto timeline).  Errors: KS_E_INVALID_ARG for NULL arguments, a slot size
+ * that does not fit the format, a record whose pc or kind is outside the program,
+ * or a file that cannot be written. */
+ks_status ks_write_trace_events(const void* trace, uint64_t n_warps, uint64_t slot_bytes, uint32_t trace_format,
+                                uint64_t first_warp, uint32_t warps_per_block, uint32_t n_pcs,
+                                const char* const* pc_names, const char* const* pc_args, const char* path,
+                                uint64_t* n_events);
+
 /* Release a state (and its device copy of the program) or a program.  NULL is a no-op. */
 void ks_state_free(ks_state* st);
 void ks_program_free(ks_program* prog);

@@ -82,7 +82,7 @@ def test_bank_conflict_hints(A, oracle_mod, s):
     info = A.ProgramInfo(w.ptx)
     hs = A.hints(hdr, rec, info, warps_per_block=w.warps_per_block)
     d = math.gcd(s, 32)
-    per_event = [h for h in hs if "warp" in h and "bank conflict" in h["message"]]
+    per_event = [h for h in hs if "warp" in h and "bank-conflict degree" in h["message"]]
     # the probe's one global load of v[lane * s] touches min(32, s) lines for 128
     # requested bytes (one line's worth): below 25% efficiency (critical) past 4 lines
     scattered = [h for h in hs if "efficiency" in h]
@@ -92,9 +92,9 @@ def test_bank_conflict_hints(A, oracle_mod, s):
         assert per_event == []
     else:
         assert len(per_event) == 8 * 4  # 8 warps x (2 stores + 2 loads)
-        assert all(h["message"] == "%d-way bank conflict" % d for h in per_event)
+        assert all(h["message"] == "shared bank-conflict degree %d" % d and h["degree"] == d for h in per_event)
         assert all(h["severity"] == ("critical" if d >= 8 else "warning") for h in per_event)
-        assert any(h["message"] == "Shared memory bank conflicts (32 events)" for h in hs)
+        assert any(h["message"] == "32 shared accesses with bank conflicts" for h in hs)
         assert all(info.text(h["pc"]).startswith(("st.shared", "ld.shared")) for h in per_event)
 
 
@@ -110,7 +110,7 @@ def test_global_efficiency_hints(A, oracle_mod, s):
     if eff < 0.25:
         assert len(crit) == 16 and all(abs(h["efficiency"] - eff) < 1e-12 for h in crit)
         assert all(info.text(h["pc"]).startswith("ld.global") for h in crit)
-        assert all(h["message"] == "Poor memory efficiency (%d%%)" % int(eff * 100) for h in crit)
+        assert all(h["message"] == "global access at %d%% coalescing efficiency" % int(eff * 100) for h in crit)
         assert len(hs) == 16
     else:
         # 25-50% is counted as uncoalesced but, as in the rules, gives no hint
@@ -161,7 +161,7 @@ def test_divergence_and_occupancy_hints(A, oracle_mod):
         act, taken = int(r["active"]), int(r["payload"]) & int(r["active"])
         assert min(bin(taken).count("1"), bin(act & ~taken).count("1")) / bin(act).count("1") > 0.4
     if n_div > 3:
-        assert any(h["message"] == "Branch divergence detected (%d events)" % n_div for h in hs)
+        assert any(h["message"] == "%d branches split their warp" % n_div for h in hs)
     assert [h["severity"] for h in A.hints(hdr[:0], rec[:0], info, A.occupancy("sm_80", 256, 32))] == []
     # 25%: not below 25 (no critical), below 50 (warning)
     assert [h["severity"] for h in A.hints(hdr[:0], rec[:0], info, A.occupancy("sm_80", 256, 128))] == ["warning"]
@@ -198,3 +198,105 @@ def test_chrome_trace_export(A, oracle_mod):
     tbj = A.chrome_trace(hb, rb, info, w.warps_per_block, trace_format=0)
     evb = [e for e in tbj["traceEvents"] if e["ph"] == "X"]
     assert [(e["ts"], e["dur"], e["name"]) for e in evb] == [(e["ts"], e["dur"], e["name"]) for e in ev]
+
+
+def _random_ext(O, seed=4, grid=2, block=64, cap=512):
+    w = W.random_stress(prog_seed=seed, grid=grid, block=block, gmem_bytes=1 << 16, n_instr=300, trace_cap=cap)
+    _, (hdr, rec) = ext(O, w)
+    return w, hdr, rec
+
+
+@pytest.mark.parametrize("seed", [4, 11])
+def test_hint_table_matches_a_record_by_record_pass(A, oracle_mod, seed):
+    """The array pass of hint_table against the rules applied to one record at a
+    time (pure Python over the decoded fields)."""
+    from analysis_ptxsimulator_amd import ks
+    w, hdr, rec = _random_ext(oracle_mod, seed)
+    info = A.ProgramInfo(w.ptx)
+    t = A.hint_table(hdr, rec, info)
+    want, conflicts, unco, divergent = [], 0, 0, 0
+    popc = lambda x: bin(x & 0xFFFFFFFF).count("1")
+    for wi in range(len(hdr)):
+        for k in range(int(hdr["records_written"][wi])):
+            r = rec[wi, k]
+            kind, pc, act, pay = int(r["kind"]), int(r["pc"]), int(r["active"]), int(r["payload"])
+            if kind in (ks.KS_EV_LD_SHARED, ks.KS_EV_ST_SHARED) and (pay & 0xFF) > 1:
+                conflicts += 1
+                want.append((wi, k, pc, 0, float(pay & 0xFF)))
+            elif kind in (ks.KS_EV_LD_GLOBAL, ks.KS_EV_ST_GLOBAL) and (pay >> 8) & 0xFF:
+                lanes, lines = (pay >> 16) & 0xFF, (pay >> 8) & 0xFF
+                eff = min(1.0, -(-lanes * info.desc[pc]["access_bytes"] // 128) / lines)
+                if eff < 0.25:
+                    want.append((wi, k, pc, 1, eff))
+                elif eff < 0.5:
+                    unco += 1
+            elif kind == ks.KS_EV_DIVERGE:
+                divergent += 1
+                tk = pay & act
+                ratio = min(popc(tk), popc(act & ~tk)) / max(1, popc(act))
+                if ratio > 0.4:
+                    want.append((wi, k, pc, 2, ratio))
+    got = list(zip(t["warp"].tolist(), t["record"].tolist(), t["pc"].tolist(), t["rule"].tolist(),
+                   t["value"].tolist()))
+    assert got == want
+    assert (t["conflicts"], t["uncoalesced"], t["divergent"]) == (conflicts, unco, divergent)
+    assert len(want) > 0 and t["conflicts"] + t["divergent"] > 0
+
+
+def test_trace_export_matches_the_records(A, oracle_mod):
+    """Every field of every event of the native export against the records it
+    came from: block/warp metadata before each warp's events, durations to the
+    warp's next issue, payload fields by kind."""
+    from analysis_ptxsimulator_amd import ks
+    w, hdr, rec = _random_ext(oracle_mod, 7, grid=3, block=96)
+    info = A.ProgramInfo(w.ptx)
+    wpb = w.warps_per_block
+    t = A.chrome_trace(hdr, rec, info, wpb)
+    want = []
+    for wi in range(len(hdr)):
+        n = int(hdr["records_written"][wi])
+        if not n:
+            continue
+        b, wib = wi // wpb, wi % wpb
+        if wib == 0:
+            want.append({"ph": "M", "name": "process_name", "pid": b, "tid": 0, "args": {"name": "block %d" % b}})
+        want.append({"ph": "M", "name": "thread_name", "pid": b, "tid": wib, "args": {"name": "warp %d" % wib}})
+        for k in range(n):
+            r = rec[wi, k]
+            pc, kind, act, pay = int(r["pc"]), int(r["kind"]), int(r["active"]), int(r["payload"])
+            cyc = int(r["cycle"])
+            dur = int(rec[wi, k + 1]["cycle"]) - cyc if k + 1 < n else 1
+            args = {"pc": pc, "line": info.desc[pc]["line"], "text": info.text(pc), "active": "0x%08x" % act}
+            if kind in (ks.KS_EV_LD_GLOBAL, ks.KS_EV_ST_GLOBAL):
+                args.update(sectors=pay & 0xFF, lines=(pay >> 8) & 0xFF, lanes=(pay >> 16) & 0xFF, faults=pay >> 24)
+            elif kind in (ks.KS_EV_LD_SHARED, ks.KS_EV_ST_SHARED):
+                args.update(degree=pay & 0xFF, lanes=(pay >> 16) & 0xFF, faults=pay >> 24)
+            elif kind in (ks.KS_EV_BRANCH, ks.KS_EV_DIVERGE):
+                args.update(taken=pay)
+            elif kind != ks.KS_EV_BARRIER:
+                args.update(guard_lanes=pay)
+            want.append({"ph": "X", "name": info.mnemonic(pc), "cat": ks.EV_NAMES[kind], "pid": b, "tid": wib,
+                         "ts": cyc, "dur": dur, "args": args})
+    assert t["traceEvents"] == want
+    assert t["otherData"]["time_unit"] == "simulated cycle"
+    # a slice of warps keeps its global numbering
+    t2 = A.chrome_trace(hdr[wpb:], rec[wpb:], info, wpb, first_warp=wpb)
+    assert t2["traceEvents"] == [e for e in want if e["pid"] >= 1]
+
+
+def test_trace_export_rejects_records_outside_the_program(A, oracle_mod, tmp_path):
+    from analysis_ptxsimulator_amd import ks
+    w, hdr, rec = _random_ext(oracle_mod, 7)
+    info = A.ProgramInfo(w.ptx)
+    bad = rec.copy()
+    bad[0, 0]["pc"] = len(info.desc)
+    with pytest.raises(ks.KsError, match="outside the program"):
+        A.write_chrome_trace(str(tmp_path / "t.json"), hdr, bad, info, w.warps_per_block)
+    h2 = hdr.copy()
+    h2["records_written"][0] = rec.shape[1] + 1
+    with pytest.raises(ks.KsError, match="records in a slot"):
+        A.write_chrome_trace(str(tmp_path / "t.json"), h2, rec, info, w.warps_per_block)
+    with pytest.raises(ks.KsError, match="cannot open"):
+        A.write_chrome_trace(str(tmp_path / "no" / "t.json"), hdr, rec, info, w.warps_per_block)
+    n = A.write_chrome_trace(str(tmp_path / "t.json"), hdr, rec, info, w.warps_per_block)
+    assert n == int(hdr["records_written"].sum())

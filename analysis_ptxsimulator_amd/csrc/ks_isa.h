@@ -49,6 +49,11 @@ constexpr uint32_t KS_SB_PRED_BASE = 64; // scoreboard index of predicate p = 64
 constexpr uint8_t KS_SB_DUMP = 126;      // scoreboard entry written by instructions without a destination
 constexpr uint8_t KS_SB_ZERO = 127;      // scoreboard entry that always reads 0 (no source)
 constexpr uint32_t KS_SB_ENTRIES = 129;  // scoreboard words per warp in LDS (odd: warps start in different banks)
+// LDS words per warp of the basic-record interpreters: the 129 scoreboard words, a
+// pad word, then a ring of 32 staged {issue cycle, pc} trace records (record k in
+// slot k % 32) from word KS_SB_RING on; 194 is not a multiple of the 32 banks.
+constexpr uint32_t KS_SB_STRIDE = 194;
+constexpr uint32_t KS_SB_RING = 130;
 constexpr uint32_t KS_IMM_SLOTS = 6;     // register slots after the program's that hold an instruction's immediates
 constexpr uint32_t KS_CONST_SLOTS = 2;   // then two slots holding 1.0f and -0.0f (f32 add/sub and mul operands)
 constexpr uint32_t KS_PREFETCH_PAD = 4;  // zero records after the end sentinel: reads ahead stay in bounds

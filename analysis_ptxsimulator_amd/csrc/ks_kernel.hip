@@ -90,6 +90,12 @@ __device__ __forceinline__ uint32_t s_eq_mask(uint32_t a, uint32_t b) {
   asm("s_cmp_eq_u32 %1, %2\n\ts_cselect_b32 %0, -1, 0" : "=s"(r) : "s"(a), "s"(b) : "scc");
   return r;
 }
+// a == 0 ? ~0 : 0, the same way.
+__device__ __forceinline__ uint32_t s_zero_mask(uint32_t a) {
+  uint32_t r;
+  asm("s_cmp_eq_u32 %1, 0\n\ts_cselect_b32 %0, -1, 0" : "=s"(r) : "s"(a) : "scc");
+  return r;
+}
 
 // ---------------------------------------------------------------------------- register files
 //
@@ -424,8 +430,10 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   R.put(ib + KS_IMM_SLOTS, 0x3F800000u);
   R.put(ib + KS_IMM_SLOTS + 1u, 0x80000000u);
   uint32_t* const sbw = lds;
-  uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * KS_SB_ENTRIES);
-  const uint32_t sb_words = (WG / 32u + 1u) * KS_SB_ENTRIES;
+  // words per warp: the scoreboard, and with basic records the staging ring after it
+  constexpr uint32_t SBS = EXT ? KS_SB_ENTRIES : KS_SB_STRIDE;
+  uint8_t* const dump_sb = reinterpret_cast<uint8_t*>(sbw + (WG / 32u) * SBS);
+  const uint32_t sb_words = (WG / 32u + 1u) * SBS;
   uint8_t* const ring = reinterpret_cast<uint8_t*>(lds) + ((4u * sb_words + 15u) & ~15u);
   uint8_t* const win = ring + (EXT ? 16u * WG : 0u);
   {
@@ -443,7 +451,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   // sector ids + 1 of valid accesses fit 32 bits (and stay non-zero)
   const uint32_t small_gmem = a.gmem_bytes <= (1ull << 37) - 64u ? 1u : 0u;
   const uint64_t glim4 = a.gmem_bytes >= 4 ? a.gmem_bytes - 3u : 0u;   // a 4-byte access at A is inside iff A < glim4
-  uint8_t* const my_sb = reinterpret_cast<uint8_t*>(sbw + my_w * KS_SB_ENTRIES);  // this lane's warp's scoreboard
+  uint8_t* const my_sb = reinterpret_cast<uint8_t*>(sbw + my_w * SBS);  // this lane's warp's scoreboard
   auto sb_at = [&](uint32_t off) -> uint32_t& { return *reinterpret_cast<uint32_t*>(my_sb + off); };
 
   // per-warp scalar state (warp 2w = half 0, warp 2w+1 = half 1)
@@ -476,7 +484,11 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   uint32_t act = 0;           // instructions issued with this lane's thread active (see KS_SET_LIVE)
   uint32_t cnt = 0;           // counter d of the lane's warp in lane 32 h + d
   uint32_t pbits = 0;         // predicate p of this lane's thread in bit p
-  uint32_t tr_c = 0, tr_p = 0;  // trace staging: record k of a warp in its lane k % 32
+  // basic records: record k of a warp is staged in slot k % 32 of the ring after its
+  // scoreboard; lane l of the warp writes slot l to memory (chunks start at multiples of 32)
+  auto staged = [&]() -> uint2 {
+    return *reinterpret_cast<const uint2*>(my_sb + 4u * KS_SB_RING + 8u * sl);
+  };
   // EXT: record k of this lane's warp is staged in slot k % 32 of the warp's LDS ring
   uint8_t* const my_ring = ring + 512u * my_w;
   // global loads / stores: per-lane shares of the access, sector and line counters of
@@ -614,16 +626,16 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   }
 
   // Issue of one instruction by the warps of gm, written as per-lane selects so
-  // that exec stays full: lane wi % 32 of each issuing warp stages the trace record
-  // (issue cycle, pc); the issue count and the next issue cycle advance; the
-  // destination's scoreboard entry gets its ready cycle (the other warp's lanes
-  // write a scratch scoreboard instead).
+  // that exec stays full: the trace record (issue cycle, pc) goes into slot wi % 32
+  // of each issuing warp's staging ring; the issue count and the next issue cycle
+  // advance; the destination's scoreboard entry gets its ready cycle (the other
+  // warp's lanes write a scratch scoreboard and ring instead).
 #define KS_ISSUE(is_, p_, sbod_, lat_)                                               \
   {                                                                                 \
     if constexpr (!EXT) {                                                           \
-      const bool tr_ = sl == ((wi & 31u) | tnm);                                    \
-      tr_c = tr_ ? (is_) : tr_c;                                                    \
-      tr_p = tr_ ? (p_) : tr_p;                                                     \
+      uint32_t* const tq_ = reinterpret_cast<uint32_t*>(sb_sel + 4u * KS_SB_RING + ((wi & 31u) << 3)); \
+      tq_[0] = (is_);                                                               \
+      tq_[1] = (p_);                                                                \
     }                                                                               \
     wi += ginc;                                                                     \
     v_next = gl ? (is_) + 1u : v_next;                                              \
@@ -724,7 +736,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           need = (go0 & 1u) | (go1 & 2u);
           ex64 |= m64 & gm;  // lanes that get past the last instruction exit, at no cost
         } else {
-          need = (S0.rpc == pc ? go0 & 1u : 0u) | (S1.rpc == pc ? go1 & 2u : 0u);
+          need = (s_eq_mask(uni(S0.rpc), pc) & go0 & 1u) | (s_eq_mask(uni(S1.rpc), pc) & go1 & 2u);
         }
         if (need & 1u) S0.pc = pc;
         if (need & 2u) S1.pc = pc;
@@ -733,7 +745,6 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       // per-step selects of the issuing lanes
       const bool gl = lanes(gm);
       const uint32_t ginc = gl ? 1u : 0u;   // issue count step
-      const uint32_t tnm = gl ? 0u : 64u;   // trace lane offset (64: no lane matches)
       uint8_t* const sb_sel = gl ? my_sb : dump_sb;
       const uint64_t mm = m64 & gm;        // live lanes of the issuing warps
       if (need) {
@@ -749,7 +760,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               *reinterpret_cast<uint4*>(slot_base + 16ull * (fl + sl)) = *reinterpret_cast<const uint4*>(my_ring + 16u * sl);
             KS_EXT_STORE_WAIT();  // the next step's index mode follows soon
           } else {
-            if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+            if (sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = staged();
           }
           fl = wi;
         }
@@ -826,12 +837,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
           if (go0) {
             spc0 = pc + 1u;
             S0.pc = pc + 1u;
-            need |= (uint32_t)m64 == 0 ? 1u : 0u;  // every lane has exited: pop
+            need |= s_zero_mask((uint32_t)m64) & 1u;  // every lane has exited: pop
           }
           if (go1) {
             spc1 = pc + 1u;
             S1.pc = pc + 1u;
-            need |= (uint32_t)(m64 >> 32) == 0 ? 2u : 0u;
+            need |= s_zero_mask((uint32_t)(m64 >> 32)) & 2u;
           }
         } else {  // DC_BAR: the issuing warps wait for the block
           KS_EXT_REC(iss, pc, KS_EV_BARRIER, 0u);
@@ -1180,6 +1191,17 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         const uint32_t p = off / (uint32_t)sizeof(DInst);
         spc0 = go0 ? p : spc0;
         spc1 = go1 ? p : spc1;
+        if constexpr (!EXT) {
+          // a run that stopped for a full trace chunk writes it here
+          const uint64_t fm = ballot(wi == ev) & ballot(wi == next_flush(fl)) & gm;
+          if (fm) {
+            if (lanes(fm) && sl < wi - fl) *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = staged();
+            if (lanes(fm)) {
+              fl = wi;
+              ev = umin(next_flush(fl), budget);
+            }
+          }
+        }
       }
       if (need & 1u) KS_SETTLE(0, S0, spc0);
       if (need & 2u) KS_SETTLE(1, S1, spc1);
@@ -1259,7 +1281,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
         if constexpr (EXT)
           *reinterpret_cast<uint4*>(slot_base + 16ull * (fl + sl)) = *reinterpret_cast<const uint4*>(my_ring + 16u * sl);
         else
-          *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = make_uint2(tr_c, tr_p);
+          *reinterpret_cast<uint2*>(slot_base + 8ull * (fl + sl)) = staged();
       }
       if (sl < 20) {
         uint32_t v;
@@ -1354,7 +1376,8 @@ int ks_choose_variant(uint32_t slots, uint32_t block_threads) {
 uint32_t ks_max_block_threads(int variant, bool ext) { return (ext && variant == 64) ? 768u : 1024u; }
 
 size_t ks_lds_bytes(uint32_t wg, uint32_t shared_bytes, bool ext) {
-  const size_t sb = ((size_t)(wg / 32u + 1u) * KS_SB_ENTRIES * 4u + 15u) & ~(size_t)15u;  // scoreboards + a scratch one
+  // scoreboards (+ staging rings) of the warps and a scratch one
+  const size_t sb = ((size_t)(wg / 32u + 1u) * (ext ? KS_SB_ENTRIES : KS_SB_STRIDE) * 4u + 15u) & ~(size_t)15u;
   const size_t ring = ext ? (size_t)wg * 16u : 0u;  // 32 staged 16-byte records per warp
   return sb + ring + (((size_t)shared_bytes + 15u) & ~(size_t)15u);
 }

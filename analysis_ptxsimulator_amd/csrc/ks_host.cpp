@@ -1593,6 +1593,8 @@ ks_status ks_write_trace_events(const void* trace, uint64_t n_warps, uint64_t sl
       raise(KS_E_INVALID_ARG, 0, "NULL argument or zero warps per block");
     if (trace_format != KS_TRACE_BASIC && trace_format != KS_TRACE_EXTENDED)
       raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", trace_format);
+    for (uint32_t k = 0; k < n_pcs; ++k)
+      if (!pc_names[k] || !pc_args[k]) raise(KS_E_INVALID_ARG, 0, "NULL name or args fragment of pc %u", k);
     const uint64_t rec = trace_format == KS_TRACE_EXTENDED ? 16u : 8u;
     if (slot_bytes < 16u || (slot_bytes - 16u) % rec) raise(KS_E_INVALID_ARG, 0, "slot of %llu bytes", (unsigned long long)slot_bytes);
     const uint64_t cap = (slot_bytes - 16u) / rec;

@@ -370,7 +370,8 @@ ks_status ks_run_status(ks_state* st, uint32_t* or_bits, void* stream);
  * and the leading JSON members of its args (for example "pc":4,"line":12).
  * *n_events (may be NULL) receives the number of instruction events.  Defined by:
  * the IKET page, sections 3 and 5 (post-processing of the per-warp buffer into a
- * Perfetto timeline).  Errors: KS_E_INVALID_ARG for NULL arguments, a slot size
+ * Perfetto timeline).  Errors: KS_E_INVALID_ARG for NULL arguments (a NULL
+ * fragment included), a slot size
  * that does not fit the format, a record whose pc or kind is outside the program,
  * or a file that cannot be written. */
 ks_status ks_write_trace_events(const void* trace, uint64_t n_warps, uint64_t slot_bytes, uint32_t trace_format,

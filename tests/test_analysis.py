@@ -8,6 +8,7 @@ pattern fixes the answer (bank-conflict degree gcd(s, 32), strided sectors
 min(32, 4 s)); the export is checked field by field against the hand-derived
 vector_add trace in tests/golden.
 """
+import ctypes
 import json
 import math
 import os
@@ -298,5 +299,12 @@ def test_trace_export_rejects_records_outside_the_program(A, oracle_mod, tmp_pat
         A.write_chrome_trace(str(tmp_path / "t.json"), h2, rec, info, w.warps_per_block)
     with pytest.raises(ks.KsError, match="cannot open"):
         A.write_chrome_trace(str(tmp_path / "no" / "t.json"), hdr, rec, info, w.warps_per_block)
+    raw = A._slot_bytes(hdr, rec, ks.KS_TRACE_EXTENDED)
+    names = (ctypes.c_char_p * len(info.desc))(*([b'"x"'] * (len(info.desc) - 1) + [None]))
+    args = (ctypes.c_char_p * len(info.desc))(*([b'"pc":0'] * len(info.desc)))
+    rc = ks.lib().ks_write_trace_events(raw.ctypes.data_as(ctypes.c_void_p), len(hdr), raw.shape[1],
+                                        ks.KS_TRACE_EXTENDED, 0, w.warps_per_block, len(info.desc), names, args,
+                                        str(tmp_path / "t.json").encode(), None)
+    assert rc == -3 and b"NULL name" in ks.lib().ks_last_error()  # KS_E_INVALID_ARG
     n = A.write_chrome_trace(str(tmp_path / "t.json"), hdr, rec, info, w.warps_per_block)
     assert n == int(hdr["records_written"].sum())

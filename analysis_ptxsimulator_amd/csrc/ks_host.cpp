@@ -1284,8 +1284,6 @@ ks_status ks_query_layout(const ks_program* p, const ks_config* cfg, ks_layout* 
     out->counters_bytes = out->n_warps * 80;
     if (cfg->trace_format != KS_TRACE_BASIC && cfg->trace_format != KS_TRACE_EXTENDED)
       raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", cfg->trace_format);
-    if (cfg->trace_format == KS_TRACE_EXTENDED && nb > KS_EXT_MAX_BLOCKS)
-      raise(KS_E_UNSUPPORTED, 0, "extended trace records support grids of up to %d blocks", KS_EXT_MAX_BLOCKS);
     if (cfg->trace_format == KS_TRACE_EXTENDED && ks_choose_variant(p->reg_slots, (uint32_t)tpb) == 64 &&
         tpb > KS_EXT64_MAX_BLOCK_THREADS)
       raise(KS_E_UNSUPPORTED, 0, "extended trace records of programs with %u register slots support blocks of up to %d threads",
@@ -1420,8 +1418,6 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       raise(KS_E_INVALID_ARG, 0, "grid/block larger than the allocation");
     if (tpb > KS_MAX_BLOCK_THREADS) raise(KS_E_INVALID_ARG, 0, "more than %d threads per block", KS_MAX_BLOCK_THREADS);
     if (nb > 0x7FFFFFFFull) raise(KS_E_INVALID_ARG, 0, "too many blocks");
-    if (st->cfg.trace_format == KS_TRACE_EXTENDED && nb > KS_EXT_MAX_BLOCKS)
-      raise(KS_E_UNSUPPORTED, 0, "extended trace records support grids of up to %d blocks", KS_EXT_MAX_BLOCKS);
     if (st->cfg.trace_format == KS_TRACE_EXTENDED && ks_choose_variant(p->reg_slots, (uint32_t)tpb) == 64 &&
         tpb > KS_EXT64_MAX_BLOCK_THREADS)
       raise(KS_E_UNSUPPORTED, 0, "extended trace records of programs with %u register slots support blocks of up to %d threads",
@@ -1489,8 +1485,14 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
                   "hipMemsetAsync(cache)"))
         return KS_E_HIP;
     }
-    hipError_t e = ks_launch_interp(a, (uint32_t)nb, p->reg_slots, (hipStream_t)stream);
-    if (!hip_ok(e, "kernel launch")) return KS_E_HIP;
+    // Extended records run as launches of at most KS_EXT_MAX_BLOCKS blocks, one after
+    // another on the stream; a basic or cache-model run is one launch.
+    const uint64_t chunk = a.ext ? (uint64_t)KS_EXT_MAX_BLOCKS : nb;
+    for (uint64_t b0 = 0; b0 < nb; b0 += chunk) {
+      a.block_base = (uint32_t)b0;
+      hipError_t e = ks_launch_interp(a, (uint32_t)std::min<uint64_t>(chunk, nb - b0), p->reg_slots, (hipStream_t)stream);
+      if (!hip_ok(e, "kernel launch")) return KS_E_HIP;
+    }
     st->last_warps = warps;
     return KS_OK;
   });

@@ -173,6 +173,7 @@ struct KsArgs {
   uint32_t cache_on;       // 1: the cache model is on
   uint32_t lat_l1, lat_l2, lat_dram;  // its latencies
   uint32_t div_bx, div_by, div_bxy;  // ceil(2^22 / d) for d = block x, y and x * y (special registers)
+  uint32_t block_base;     // block id of the launch's first workgroup (launches over part of a grid)
   uint8_t params[KS_PARAM_MAX];
 };
 

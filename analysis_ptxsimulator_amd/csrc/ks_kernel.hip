@@ -414,7 +414,7 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   const uint32_t wave = uni(tid >> 6);  // wave-uniform: keeps every per-warp value scalar
   const uint32_t hl = lane >> 5;
   const uint32_t sl = lane & 31u;
-  const uint32_t blk = blockIdx.x;
+  const uint32_t blk = blockIdx.x + (EXT ? a.block_base : 0u);  // extended-record grids run in parts
   const uint32_t W = a.warps_per_block;
   const uint32_t T = a.threads_per_block;
   const uint32_t n_instr = a.n_instrs;

@@ -29,7 +29,7 @@ TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("
                                ("warp_in_block", "<u2"), ("records_dropped", "<u8")])
 # trace formats (ks_config.trace_format) and the 16-byte extended record
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
-KS_EXT_MAX_BLOCKS = 32  # largest grid of an extended-record allocation or run
+KS_EXT_MAX_BLOCKS = 32  # blocks per launch of an extended-record run (ks_run chunks larger grids)
 KS_STATIC_MAX_INSTRS = 8187  # largest program a ks_alloc_state_static binding holds
 KS_EXT64_MAX_BLOCK_THREADS = 256  # largest block of an extended run of a program of > 32 slots
 # cache-latency model (ks_config.cache_model) and its per-warp state in d_cache

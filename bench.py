@@ -196,7 +196,7 @@ def main():
                     help="ld.global latency: the fixed table (the timed default) or per-warp L1/L2 caches")
     ap.add_argument("--trace-format", choices=("basic", "extended"), default="basic",
                     help="trace records: 8-byte {cycle, pc} (the timed default) or 16-byte with kind, mask and "
-                         "payload (grids of up to 32 blocks, e.g. --workload random_stress_g32)")
+                         "payload (launched 32 blocks at a time, e.g. --workload random_stress_g32)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this simulator's hot path is a single-GPU kernel "

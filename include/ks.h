@@ -15,7 +15,8 @@
  * per-kind payload (sectors and lines of a global access, bank-conflict degree of
  * a shared access, the lanes taking a branch).  Extended records for programs of
  * more than 32 register slots support blocks of up to KS_EXT64_MAX_BLOCK_THREADS
- * threads, and extended-record launches hold at most KS_EXT_MAX_BLOCKS blocks.
+ * threads, and ks_run covers an extended-record grid with launches of at most
+ * KS_EXT_MAX_BLOCKS blocks each.
  *
  * Sources of the semantics, by page and section:
  *   - KernelScope backend documentation (github.com/briefgaming/kernelscope).
@@ -137,11 +138,11 @@ enum {
 #define KS_MAX_PARAM_BYTES 512   /* parameter block */
 #define KS_MAX_SHARED_BYTES 65536 /* simulated shared window per block */
 #define KS_MAX_BLOCK_THREADS 1024
-/* Largest grid (in blocks) of a KS_TRACE_EXTENDED allocation or run: the launch
- * sizes the extended-record interpreter has been checked at on the GPU.  A
- * 65536-block extended run faulted and its cause is not found yet, so larger
- * extended launches are refused (KS_E_UNSUPPORTED); the basic format has no
- * such limit. */
+/* Blocks per launch of a KS_TRACE_EXTENDED run: ks_run covers a larger grid with
+ * consecutive launches of this many blocks on the caller's stream (the last one
+ * shorter), each of a size the extended-record interpreter has been checked at on
+ * the GPU.  A single 65536-block extended launch faulted, with the cause not yet
+ * found, and is never made.  Basic and cache-model runs are one launch. */
 #define KS_EXT_MAX_BLOCKS 32
 /* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run of a program of
  * more than 32 register slots.  Extended runs of such programs with 768-thread
@@ -262,7 +263,7 @@ ks_status ks_default_config(ks_config* cfg);
  * 16 with a payload); the 1.15 margin is dropped because records past the cap are
  * counted, not stored.  KS_E_INVALID_ARG for an unknown trace_format or
  * cache_model; KS_E_UNSUPPORTED for the cache model with extended records or over
- * more than 2^38 bytes, or extended records beyond KS_EXT_MAX_BLOCKS blocks. */
+ * more than 2^38 bytes. */
 ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layout* out);
 
 /* Bind a program to caller-owned device buffers on the current HIP device.
@@ -310,7 +311,9 @@ ks_status ks_alloc_state_static(const ks_program* prog, const ks_config* cfg, vo
  * memory; copied into the launch arguments).  Each run re-initialises registers,
  * predicates, stacks, scoreboards and shared windows, and rewrites every
  * counter record and trace header of the grid's warps.  Warps are numbered
- * linear block id * warps_per_block + warp in block.
+ * linear block id * warps_per_block + warp in block.  With extended records the
+ * grid is launched KS_EXT_MAX_BLOCKS blocks at a time (blocks share nothing but
+ * simulated global memory, whose accesses by different blocks must not race).
  * Errors: KS_E_INVALID_ARG (shape beyond the allocation, short params),
  * KS_E_UNSUPPORTED (a block too large for the interpreter variant), KS_E_HIP. */
 ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, size_t params_len,

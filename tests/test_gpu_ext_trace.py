@@ -104,12 +104,63 @@ def test_random_stress_block_768(K, oracle_mod):
     ext_parity(K, oracle_mod, W.random_stress(prog_seed=2, grid=3, block=768, gmem_bytes=1 << 24, trace_cap=300))
 
 
-@pytest.mark.skip(reason="refused by the library: the 65536 x 256 extended-record launch faulted on the GPU "
-                         "(memory aperture violation) and its cause is not found, so extended grids above "
-                         "KS_EXT_MAX_BLOCKS = 32 blocks are refused")
+def test_random_stress_chunked_launches(K, oracle_mod):
+    """A grid above KS_EXT_MAX_BLOCKS runs as consecutive launches of that many
+    blocks (here 32 + 32 + 16): every byte equal to the oracle's."""
+    ext_parity(K, oracle_mod, W.random_stress(prog_seed=1, grid=80, block=256, gmem_bytes=1 << 24, trace_cap=512))
+
+
 def test_random_stress_full_grid_extended(K, oracle_mod):
+    """The whole 65536 x 256 grid with extended records (2048 launches of 32 blocks;
+    the 17.2 GB of slots reach far past 4 GiB): memory and every counter record
+    equal the basic-format run of the same inputs, every header agrees with its
+    warp's issue count, and the records of sampled blocks (the first, the last
+    and blocks whose slots lie past 4 GiB) equal the oracle's."""
     w = W.random_stress(prog_seed=0)
-    gpu_run(K, w, K.KS_TRACE_EXTENDED, w.trace_cap)
+    cap = w.trace_cap
+    _say("full grid, basic format")
+    sb = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=cap)
+    try:
+        sb.load_gmem(w.gmem)
+        sb.run(w.params_bytes)
+        gb, cb = sb.read_gmem(), sb.read_counters()
+    finally:
+        sb.close()
+    _say("full grid, extended format")
+    se = K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=cap, trace_format=K.KS_TRACE_EXTENDED)
+    try:
+        se.load_gmem(w.gmem)
+        se.run(w.params_bytes)
+        assert se.kernel_name() == "ks_interp_v64_ext"
+        assert np.array_equal(se.read_gmem(), gb)
+        ce = se.read_counters()
+        assert np.array_equal(ce, cb)
+        wpb = w.warps_per_block
+        slot = 16 + 16 * cap
+        hdr = np.empty(len(ce), dtype=K.TRACE_HEADER_DTYPE)
+        step = 8192  # warps per read: headers only are checked over the whole grid
+        for w0 in range(0, len(ce), step):
+            h, _ = K.trace_slots(se.read_trace(w0, min(step, len(ce) - w0)), cap, K.KS_TRACE_EXTENDED)
+            hdr[w0:w0 + len(h)] = h
+        wi = ce["warp_instrs"].astype(np.int64)
+        assert np.array_equal(hdr["records_written"], np.minimum(wi, cap))
+        assert np.array_equal(hdr["records_dropped"].astype(np.int64), wi - np.minimum(wi, cap))
+        assert (hdr["version"] == 2).all()
+        blocks = [0, 16383, 16384, 40000, 65535]  # slots of block 16384 on start past 4 GiB
+        assert 16384 * wpb * slot >= 1 << 32
+        go = w.gmem.copy()
+        co, to, _ = oracle_mod.run(w.ptx, w.grid, w.block, w.params_bytes, go, trace_cap=cap, blocks=blocks,
+                                   trace_format=oracle_mod.TRACE_EXTENDED)
+        ho, ro = oracle_mod.trace_slots(to, cap, oracle_mod.TRACE_EXTENDED)
+        for j, b in enumerate(blocks):
+            hg, rg = K.trace_slots(se.read_trace(b * wpb, wpb), cap, K.KS_TRACE_EXTENDED)
+            assert np.array_equal(hg, ho[j * wpb:(j + 1) * wpb]), b
+            for i in range(wpb):
+                n = int(hg["records_written"][i])
+                assert np.array_equal(rg[i, :n], ro[j * wpb + i, :n]), (b, i)
+            assert np.array_equal(ce[b * wpb:(b + 1) * wpb], co[j * wpb:(j + 1) * wpb]), b
+    finally:
+        se.close()
 
 
 @pytest.mark.parametrize("op", ["fma.f32", "mad.s32", "none"])

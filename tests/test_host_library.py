@@ -129,10 +129,9 @@ def test_layout_and_default_config(ks):
     ks.ks_program_free(p)
 
 
-def test_extended_layout_and_grid_limit(ks):
-    """Extended slots hold 16-byte records; an extended allocation of more than
-    KS_EXT_MAX_BLOCKS blocks is refused before any device work (the basic format
-    takes any grid)."""
+def test_extended_layout_any_grid(ks):
+    """Extended slots hold 16-byte records, for a grid of any size (ks_run launches
+    it KS_EXT_MAX_BLOCKS blocks at a time); the basic format likewise."""
     p = ks.ks_load_program(W.VECTOR_ADD_PTX)
     cfg = ks.ks_default_config()
     cfg.max_block = ks.ks_dim3(256, 1, 1)
@@ -141,12 +140,10 @@ def test_extended_layout_and_grid_limit(ks):
     cfg.max_grid = ks.ks_dim3(ks.KS_EXT_MAX_BLOCKS // 2, 2, 1)
     lay = ks.ks_query_layout(p, cfg)
     assert lay.slot_bytes == 16 + 16 * 32 and lay.n_warps == 8 * ks.KS_EXT_MAX_BLOCKS
-    cfg.max_grid = ks.ks_dim3(ks.KS_EXT_MAX_BLOCKS + 1, 1, 1)
-    with pytest.raises(ks.KsError) as e:
-        ks.ks_query_layout(p, cfg)
-    assert e.value.code == -2 and "%d blocks" % ks.KS_EXT_MAX_BLOCKS in e.value.msg
-    cfg.trace_format = ks.KS_TRACE_BASIC
     cfg.max_grid = ks.ks_dim3(65536, 1, 1)
+    lay = ks.ks_query_layout(p, cfg)
+    assert lay.n_warps == 8 * 65536 and lay.trace_bytes == 8 * 65536 * (16 + 16 * 32)
+    cfg.trace_format = ks.KS_TRACE_BASIC
     assert ks.ks_query_layout(p, cfg).n_warps == 8 * 65536
     ks.ks_program_free(p)
 

@@ -376,7 +376,8 @@ ks_status ks_run_status(ks_state* st, uint32_t* or_bits, void* stream);
  * Perfetto timeline).  Errors: KS_E_INVALID_ARG for NULL arguments (a NULL
  * fragment included), a slot size
  * that does not fit the format, a record whose pc or kind is outside the program,
- * or a file that cannot be written. */
+ * or a file that cannot be written (a file opened before the error is left
+ * partly written). */
 ks_status ks_write_trace_events(const void* trace, uint64_t n_warps, uint64_t slot_bytes, uint32_t trace_format,
                                 uint64_t first_warp, uint32_t warps_per_block, uint32_t n_pcs,
                                 const char* const* pc_names, const char* const* pc_args, const char* path,

@@ -295,7 +295,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel": kernel},
-        # the benchmark spec's own measure: rocprofv3 HBM bytes (FETCH_SIZE x 2 + WRITE_SIZE,
+        # HBM bandwidth as rocprofv3 measures it: FETCH_SIZE x 2 + WRITE_SIZE bytes (each
         # scaled by a plain copy) per launch over the mean launch time; null when the
         # committed counters were taken on another kernel source
         "hbm_measured": ({"GBps": traffic / avg_launch_s / 1e9, "frac": traffic / avg_launch_s / 1e9 / HBM_PEAK_GBS,

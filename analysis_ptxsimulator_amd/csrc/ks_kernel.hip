@@ -668,30 +668,40 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   // destination becomes ready after that level's latency (a warp with no valid
   // lane keeps the ld.global latency its issue wrote).  Valid addresses are below
   // 2^38 bytes, so line numbers fit 32 bits.
-#define KS_CACHE_ACCESS(A, okm, is_load, sbod_)                                       \
+#define KS_CACHE_ISSUE(A, okm)                                                        \
+  [[maybe_unused]] uint32_t cline_ = 0, co1_ = 0, co2_ = 0, cvalid_ = 0;            \
   if constexpr (CACHE) {                                                            \
     const uint32_t v0_ = (uint32_t)(okm), v1_ = (uint32_t)((okm) >> 32);            \
     const uint32_t lnl_ = (uint32_t)((A) >> 7);                                     \
     const uint32_t line0_ = rl(lnl_, v0_ ? (uint32_t)__builtin_ctz(v0_) : 0u);       \
     const uint32_t line1_ = rl(lnl_, v1_ ? 32u + (uint32_t)__builtin_ctz(v1_) : 32u); \
-    const uint32_t line_ = hl ? line1_ : line0_;                                    \
-    uint32_t lvl_ = 3u;                                                             \
-    if (sl == 0u && (hl ? v1_ : v0_) != 0u) {                                        \
-      uint32_t* const cw_ = reinterpret_cast<uint32_t*>(a.cache + (gw0 + hl) * (uint64_t)KS_CACHE_WARP_BYTES); \
-      const uint32_t t_ = line_ + 1u;                                               \
-      uint32_t* const e1_ = cw_ + 4u + (line_ & (KS_CACHE_L1_LINES - 1u));          \
-      uint32_t* const e2_ = cw_ + 4u + KS_CACHE_L1_LINES + line_ % KS_CACHE_L2_LINES; \
+    cline_ = hl ? line1_ : line0_;                                                  \
+    cvalid_ = (sl == 0u && (hl ? v1_ : v0_) != 0u) ? 1u : 0u;                        \
+    if (cvalid_) {                                                                  \
+      const uint32_t* const cw_ =                                                   \
+          reinterpret_cast<const uint32_t*>(a.cache + (gw0 + hl) * (uint64_t)KS_CACHE_WARP_BYTES); \
       /* both tags in one memory round trip (the two arrays never overlap) */        \
-      uint32_t o1_ = *e1_, o2_ = *e2_;                                              \
-      asm volatile("" : "+v"(o1_), "+v"(o2_)); /* keeps the L2 load ahead of the branch */ \
-      if (o1_ == t_) {                                                              \
+      co1_ = cw_[4u + (cline_ & (KS_CACHE_L1_LINES - 1u))];                         \
+      co2_ = cw_[4u + KS_CACHE_L1_LINES + cline_ % KS_CACHE_L2_LINES];              \
+    }                                                                               \
+  }
+
+  // The lookup itself, once the tags of KS_CACHE_ISSUE are needed: a hit in L1, else
+  // install there and look in L2, else install there too.
+#define KS_CACHE_FINISH(is_load, sbod_)                                               \
+  if constexpr (CACHE) {                                                            \
+    uint32_t lvl_ = 3u;                                                             \
+    if (cvalid_) {                                                                  \
+      uint32_t* const cw_ = reinterpret_cast<uint32_t*>(a.cache + (gw0 + hl) * (uint64_t)KS_CACHE_WARP_BYTES); \
+      const uint32_t t_ = cline_ + 1u;                                              \
+      if (co1_ == t_) {                                                             \
         lvl_ = 0u;                                                                  \
       } else {                                                                      \
-        *e1_ = t_;                                                                  \
-        if (o2_ == t_) {                                                            \
+        cw_[4u + (cline_ & (KS_CACHE_L1_LINES - 1u))] = t_;                         \
+        if (co2_ == t_) {                                                           \
           lvl_ = 1u;                                                                \
         } else {                                                                    \
-          *e2_ = t_;                                                                \
+          cw_[4u + KS_CACHE_L1_LINES + cline_ % KS_CACHE_L2_LINES] = t_;            \
           lvl_ = 2u;                                                                \
         }                                                                           \
       }                                                                             \
@@ -951,19 +961,21 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               uint32_t ld_v;
               asm volatile("" : "=v"(ld_v));
               if (lanes(okm)) ld_v = *reinterpret_cast<const uint32_t*>(a.gmem + A);
-              // The accounting needs only the addresses: it runs while the load is in
-              // flight.  Nothing in it uses VGPR index mode, which must stay off while
-              // a load that returns into a VGPR is outstanding (a loaded value then
-              // lands in the wrong register).
+              // The accounting needs only the addresses: it runs while the load (and
+              // the cache model's tag loads) are in flight.  Nothing in it uses VGPR
+              // index mode, which must stay off while a load that returns into a VGPR
+              // is outstanding (a loaded value then lands in the wrong register).
+              KS_CACHE_ISSUE(A, okm);
               KS_COUNT_FAULTS(faults);
               KS_GLOBAL_ACCOUNT(A, 4u, faults, true);
-              KS_CACHE_ACCESS(A, okm, true, h[10]);
+              KS_CACHE_FINISH(true, h[10]);
               R.put_m(dst, ld_v, okm);
             } else {
               if (lanes(okm)) *reinterpret_cast<uint32_t*>(a.gmem + A) = R.get(s1);
+              KS_CACHE_ISSUE(A, okm);
               KS_COUNT_FAULTS(faults);
               KS_GLOBAL_ACCOUNT(A, 4u, faults, false);
-              KS_CACHE_ACCESS(A, okm, false, h[10]);
+              KS_CACHE_FINISH(false, h[10]);
             }
             if constexpr (EXT) {
               const uint32_t p0 = x_sl0 | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
@@ -1100,8 +1112,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
             KS_COUNT_FAULTS(faults);
             [[maybe_unused]] uint32_t x_sl0 = 0, x_sl1 = 0;
             if (is_global) {
+              KS_CACHE_ISSUE(A, okm);
               KS_GLOBAL_ACCOUNT(A, S, faults, is_load);
-              KS_CACHE_ACCESS(A, okm, is_load, h[10]);
+              KS_CACHE_FINISH(is_load, h[10]);
               if constexpr (EXT) {
                 const uint32_t p0 = x_sl0 | (popc((uint32_t)on64) << 16) | (popc((uint32_t)faults) << 24);
                 const uint32_t p1 = x_sl1 | (popc((uint32_t)(on64 >> 32)) << 16) | (popc((uint32_t)(faults >> 32)) << 24);
@@ -1238,7 +1251,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 #undef KS_SETTLE
 #undef KS_COUNT_FAULTS
 #undef KS_GLOBAL_ACCOUNT
-#undef KS_CACHE_ACCESS
+#undef KS_CACHE_ISSUE
+#undef KS_CACHE_FINISH
   act += lanes(m64) ? wi : 0u;
 #undef KS_SET_LIVE
 

@@ -48,6 +48,12 @@ constexpr uint16_t KS_RPC_EXIT = 0xFFFF;
 constexpr uint32_t KS_SB_PRED_BASE = 64; // scoreboard index of predicate p = 64 + p
 constexpr uint8_t KS_SB_DUMP = 126;      // scoreboard entry written by instructions without a destination
 constexpr uint8_t KS_SB_ZERO = 127;      // scoreboard entry that always reads 0 (no source)
+// Two scoreboard words no instruction names (registers use 0-63, predicates 64-95):
+// at each barrier release a warp keeps its issue count and its next issue cycle
+// from before the release there, so that a warp whose last issue was the bar.sync
+// reports cycles = that issue + 1 however late the release.
+constexpr uint8_t KS_SB_BAR_WI = 124;
+constexpr uint8_t KS_SB_BAR_NEXT = 125;
 constexpr uint32_t KS_SB_ENTRIES = 129;  // scoreboard words per warp in LDS (odd: warps start in different banks)
 // LDS words per warp of the basic-record interpreters: the 129 scoreboard words, a
 // pad word, then a ring of 32 staged {issue cycle, pc} trace records (record k in

@@ -874,6 +874,9 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
               ep_alive[(epoch + 1u) % 3u] = 0;
               ep_max[(epoch + 1u) % 3u] = 0;
             }
+            // the issue count and next issue cycle from before the release
+            *reinterpret_cast<uint32_t*>(sb_sel + 4u * KS_SB_BAR_WI) = wi;
+            *reinterpret_cast<uint32_t*>(sb_sel + 4u * KS_SB_BAR_NEXT) = v_next;
             __syncthreads();
             const uint32_t release = uni(ep_max[slot]) + a.lat_bar;
             v_next = gl ? umax(v_next, release) : v_next;
@@ -1236,6 +1239,12 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       ep_alive[(epoch + 1u) % 3u] = 0;
       ep_max[(epoch + 1u) % 3u] = 0;
     }
+    {
+      // a waiting warp's issue count and next issue cycle from before the release
+      uint8_t* const sbr = ((hst >> hl) & 1u) ? my_sb : dump_sb;
+      *reinterpret_cast<uint32_t*>(sbr + 4u * KS_SB_BAR_WI) = wi;
+      *reinterpret_cast<uint32_t*>(sbr + 4u * KS_SB_BAR_NEXT) = v_next;
+    }
     __syncthreads();
     const uint32_t alive_all = uni(ep_alive[slot]);
     if (alive_all == 0) break;
@@ -1281,7 +1290,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
       const uint32_t m_status = (status >> (8u * hl)) & 0xFFu;
       const uint32_t m_depth = hl ? S1.md : S0.md;
       const uint64_t m_ti = hl ? ti1 : ti0;
-      const uint32_t cycles = v_next;
+      // last issue + 1: a release after the warp's last issue (a bar.sync) does not count
+      const uint32_t cycles = wi == sb_at(4u * KS_SB_BAR_WI) ? sb_at(4u * KS_SB_BAR_NEXT) : v_next;
       const uint32_t written = umin(wi, cap);
       const uint32_t dropped = wi - written;
       const uint32_t st = m_status | (dropped ? KS_ST_TRACE_DROP : 0u);

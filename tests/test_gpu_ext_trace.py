@@ -104,6 +104,12 @@ def test_random_stress_block_768(K, oracle_mod):
     ext_parity(K, oracle_mod, W.random_stress(prog_seed=2, grid=3, block=768, gmem_bytes=1 << 24, trace_cap=300))
 
 
+def test_budget_stop_at_a_barrier(K, oracle_mod):
+    """Warps whose budget ends exactly at a bar.sync report cycles = that issue + 1."""
+    w = W.random_stress(prog_seed=989, grid=30, block=64, gmem_bytes=1 << 22, trace_cap=33, n_instr=1106)
+    ext_parity(K, oracle_mod, w, max_warp_instrs=777)
+
+
 def test_random_stress_chunked_launches(K, oracle_mod):
     """A grid above KS_EXT_MAX_BLOCKS runs as consecutive launches of that many
     blocks (here 32 + 32 + 16): every byte equal to the oracle's."""

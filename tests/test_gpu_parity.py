@@ -290,6 +290,41 @@ $L__skip:
     assert (cg["status"][:6] & K.ST_BARDIV).all() and not (cg["status"][6] & K.ST_BARDIV)
 
 
+def test_last_issue_a_barrier(K, oracle_mod):
+    """cycles = last issue + 1 also when a warp's last issue is a bar.sync whose
+    release comes later: here the fast warp of each block reaches the barrier at
+    cycle 9 and the program ends there, while the slow warp waits for a global
+    load first (the release, at 234, raises no issue of the fast warp)."""
+    ptx = S.HEADER + """.visible .entry bar_end(.param .u64 param_in)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<4>;
+    .reg .b64 %rd<3>;
+    mov.u32 %r0, %tid.x;
+    setp.lt.u32 %p0, %r0, 32;
+    @!%p0 bra JOIN;
+    ld.param.u64 %rd0, [param_in];
+    ld.global.u32 %r1, [%rd0];
+    add.s32 %r2, %r1, 1;
+JOIN:
+    bar.sync 0;
+}
+"""
+    w = W.Workload(name="bar_end", ptx=ptx, grid=(2, 1, 1), block=(64, 1, 1), params=[("param_in", "u64", 0)],
+                   gmem=np.zeros(64, np.uint8), trace_cap=16)
+    cg = full_parity(K, oracle_mod, w)
+    assert cg["cycles"].tolist() == [215, 10, 215, 10]
+
+
+def test_budget_stop_at_a_barrier(K, oracle_mod):
+    """Warps that reach their issue budget exactly at a bar.sync: the release that
+    follows is not part of their cycles (a randomised case that found the
+    difference: some warps' 777th issue is a barrier)."""
+    w = W.random_stress(prog_seed=989, grid=30, block=64, gmem_bytes=1 << 22, trace_cap=33, n_instr=1106)
+    cg = full_parity(K, oracle_mod, w, max_warp_instrs=777)
+    assert ((cg["status"] & K.ST_BUDGET) != 0).sum() > 0
+
+
 def test_runs_are_deterministic_and_rerunnable(K, oracle_mod):
     w = W.random_stress(prog_seed=1, grid=16, block=256, gmem_bytes=1 << 24, trace_cap=256)
     outs = gpu_run(K, w, runs=2)

@@ -152,6 +152,39 @@ def test_count_sweep_exactly_affine(oracle_mod, n_acc, slope):
     assert slope / 32 == (4.0 if n_acc == 1 else 35 / 32)
 
 
+def test_cycles_end_at_the_last_issue_not_at_a_later_release(oracle_mod):
+    """cycles = last issue + 1 (the cycle model's definition), also for a warp
+    whose last issue is a bar.sync released later.  Worked by hand with the
+    default latencies (mov, setp and add 4, ld.param 4, ld.global 200, bar.sync
+    20): the warp of threads 0-31 issues mov 0, setp 4, bra 8, ld.param 9,
+    ld.global 13, add 213, bar.sync 214 (cycles 215); the warp of threads 32-63
+    branches straight to the barrier: mov 0, setp 4, bra 8, bar.sync 9 (cycles
+    10).  The release at 214 + 20 = 234 comes after both warps' last issue: the
+    program ends at the barrier."""
+    ptx = S.HEADER + """.visible .entry bar_end(.param .u64 param_in)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<4>;
+    .reg .b64 %rd<3>;
+    mov.u32 %r0, %tid.x;
+    setp.lt.u32 %p0, %r0, 32;
+    @!%p0 bra JOIN;
+    ld.param.u64 %rd0, [param_in];
+    ld.global.u32 %r1, [%rd0];
+    add.s32 %r2, %r1, 1;
+JOIN:
+    bar.sync 0;
+}
+"""
+    g = np.zeros(64, np.uint8)
+    c, t, _ = oracle_mod.run(ptx, (2, 1, 1), (64, 1, 1), np.zeros(8, np.uint8).tobytes(), g, trace_cap=16)
+    h, r = oracle_mod.trace_slots(t, 16)
+    assert c["cycles"].tolist() == [215, 10, 215, 10]
+    assert c["warp_instrs"].tolist() == [7, 4, 7, 4]
+    assert [int(x) for x in r[0, :7, 0]] == [0, 4, 8, 9, 13, 213, 214]
+    assert [int(x) for x in r[1, :4, 0]] == [0, 4, 8, 9] and [int(x) for x in r[1, :4, 1]] == [0, 1, 2, 6]
+
+
 def test_barrier_release_hand_derived(oracle_mod):
     """bar.sync release = latest arrival of the waiting warps + lat(bar.sync), and a
     warp that finished without reaching the barrier does not hold it: issue cycles

@@ -188,7 +188,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--csv", default=None, help="raw per-launch times (default gpurun_out/launch_ms_<workload>.csv)")
+    ap.add_argument("--csv", default=None,
+                    help="raw per-launch times (default $KS_BENCH_OUT/launch_ms_<workload>.csv, KS_BENCH_OUT "
+                         "defaulting to bench_out)")
     ap.add_argument("--workload", default="random_stress")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=65536)
@@ -261,7 +263,7 @@ def main():
     achieved = alg_bytes / avg_launch_s / 1e9
     prof = measured_counters(args.workload + ("_cache" if cache_on else "") + ("_ext" if ext else ""))
     traffic = prof.get("hbm_bytes_per_launch") if prof else None
-    csv_path = args.csv or os.path.join("gpurun_out", "launch_ms_%s.csv" % args.workload)
+    csv_path = args.csv or os.path.join(os.environ.get("KS_BENCH_OUT", "bench_out"), "launch_ms_%s.csv" % args.workload)
     write_csv(csv_path, launch_ms)
     copy_gbs = copy_ceiling(dev)
     valu = None

@@ -14,7 +14,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkscope.so")
-SOURCES = [os.path.join(CSRC, "ks_host.cpp"), os.path.join(CSRC, "ks_kernel.hip"), os.path.join(CSRC, "ks_scratch.hip")]
+SOURCES = [os.path.join(CSRC, "ks_host.cpp"), os.path.join(CSRC, "ks_kernel.hip"), os.path.join(CSRC, "ks_scratch.hip"),
+           os.path.join(CSRC, "ks_clear.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Uniform branches (all of the interpreter's dispatch) need no structurizing: the

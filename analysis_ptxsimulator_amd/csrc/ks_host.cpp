@@ -1309,6 +1309,8 @@ ks_status ks_alloc_state(const ks_program* p, const ks_config* cfg, void* d_gmem
     *out = nullptr;
     if (!d_gmem || !d_counters || !d_trace) raise(KS_E_INVALID_ARG, 0, "NULL device buffer");
     if (cfg->cache_model == KS_CACHE_WARP && !d_cache) raise(KS_E_INVALID_ARG, 0, "NULL cache buffer");
+    if (cfg->cache_model == KS_CACHE_WARP && ((uintptr_t)d_cache & 15u))
+      raise(KS_E_INVALID_ARG, 0, "cache buffer not 16-byte aligned");
     if (p->reg_slots > KS_MAX_REG_SLOTS) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots (limit %d)", p->reg_slots, KS_MAX_REG_SLOTS);
     if (p->n_preds > KS_MAX_PREDS) raise(KS_E_UNSUPPORTED, 0, "program needs %u predicates (limit %d)", p->n_preds, KS_MAX_PREDS);
     if (p->code.empty()) raise(KS_E_INVALID_ARG, 0, "empty program");
@@ -1357,6 +1359,8 @@ ks_status ks_alloc_state_static(const ks_program* p, const ks_config* cfg, void*
     *out = nullptr;
     if (!d_gmem || !d_counters || !d_trace) raise(KS_E_INVALID_ARG, 0, "NULL device buffer");
     if (cfg->cache_model == KS_CACHE_WARP && !d_cache) raise(KS_E_INVALID_ARG, 0, "NULL cache buffer");
+    if (cfg->cache_model == KS_CACHE_WARP && ((uintptr_t)d_cache & 15u))
+      raise(KS_E_INVALID_ARG, 0, "cache buffer not 16-byte aligned");
     if (p->reg_slots > KS_MAX_REG_SLOTS) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots (limit %d)", p->reg_slots, KS_MAX_REG_SLOTS);
     if (p->n_preds > KS_MAX_PREDS) raise(KS_E_UNSUPPORTED, 0, "program needs %u predicates (limit %d)", p->n_preds, KS_MAX_PREDS);
     if (p->code.empty()) raise(KS_E_INVALID_ARG, 0, "empty program");
@@ -1481,8 +1485,8 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
     }
     if (a.cache_on) {
       // the caches of this run's warps start empty
-      if (!hip_ok(hipMemsetAsync(st->d_cache, 0, warps * (uint64_t)KS_CACHE_WARP_BYTES, (hipStream_t)stream),
-                  "hipMemsetAsync(cache)"))
+      if (!hip_ok(ks_launch_clear(st->d_cache, warps * (uint64_t)KS_CACHE_WARP_BYTES, (hipStream_t)stream),
+                  "clearing the cache state"))
         return KS_E_HIP;
     }
     // Extended records run as launches of at most KS_EXT_MAX_BLOCKS blocks, one after

@@ -9,6 +9,9 @@
 // slots plus the immediate slots).
 hipError_t ks_launch_interp(const ks::KsArgs& a, uint32_t n_blocks, uint32_t slots, hipStream_t s);
 
+// Zeroes `bytes` (a multiple of 16) at the 16-byte aligned device address p.
+hipError_t ks_launch_clear(void* p, uint64_t bytes, hipStream_t s);
+
 // OR of the status words of `n_warps` counter records into *d_out.
 hipError_t ks_launch_status_or(const void* counters, uint64_t n_warps, uint32_t* d_out, hipStream_t s);
 

@@ -275,8 +275,9 @@ ks_status ks_query_layout(const ks_program* prog, const ks_config* cfg, ks_layou
  *               the caller; ks_run updates it in place and it persists across runs),
  *   d_counters  layout.counters_bytes: 80-byte per-warp counter records,
  *   d_trace     layout.trace_bytes: per-warp trace slots,
- *   d_cache     layout.cache_bytes: the cache model's per-warp state (NULL
- *               without the cache model; ks_run clears the run's part first).
+ *   d_cache     layout.cache_bytes: the cache model's per-warp state, 16-byte
+ *               aligned (NULL without the cache model; each ks_run first clears
+ *               the state of its grid's warps with a kernel of its own).
  * Uploads the decoded program (latencies baked in from cfg) to a small device
  * buffer owned by the state.  Errors: KS_E_INVALID_ARG (NULL buffers, limits),
  * KS_E_UNSUPPORTED (program beyond this build's limits), KS_E_HIP, KS_E_NOMEM. */
@@ -309,8 +310,8 @@ ks_status ks_alloc_state_static(const ks_program* prog, const ks_config* cfg, vo
  * launch argument as on the IKET page, section 2.
  * `params` holds `params_len` >= param_bytes bytes of the parameter block (host
  * memory; copied into the launch arguments).  Each run re-initialises registers,
- * predicates, stacks, scoreboards and shared windows, and rewrites every
- * counter record and trace header of the grid's warps.  Warps are numbered
+ * predicates, stacks, scoreboards, shared windows and (with the cache model) the
+ * caches, and rewrites every counter record and trace header of the grid's warps.  Warps are numbered
  * linear block id * warps_per_block + warp in block.  With extended records the
  * grid is launched KS_EXT_MAX_BLOCKS blocks at a time (blocks share nothing but
  * simulated global memory, whose accesses by different blocks must not race).

@@ -191,7 +191,7 @@ def test_static_binding_refuses_programs_beyond_its_scratch(ks):
 def test_cache_model_layout_and_limits(ks, oracle_mod):
     """The cache model adds KS_CACHE_WARP_BYTES of state per warp (the oracle's
     layout), refuses extended records and memories above 2^38 bytes, and needs
-    its buffer at allocation; an unknown model is an invalid argument."""
+    its 16-byte aligned buffer at allocation; an unknown model is an invalid argument."""
     p = ks.ks_load_program(W.VECTOR_ADD_PTX)
     cfg = ks.ks_default_config()
     assert list(cfg.latency)[14:17] == [28, 150, 400] and cfg.cache_model == ks.KS_CACHE_NONE
@@ -206,6 +206,9 @@ def test_cache_model_layout_and_limits(ks, oracle_mod):
     with pytest.raises(ks.KsError) as e:
         ks.ks_alloc_state(p, cfg, 1, 1, 1, 0)
     assert e.value.code == -3 and "cache buffer" in e.value.msg
+    with pytest.raises(ks.KsError) as e:  # the kernel clears the state with 16-byte stores
+        ks.ks_alloc_state(p, cfg, 1, 1, 1, 4104)
+    assert e.value.code == -3 and "16-byte aligned" in e.value.msg
     cfg.gmem_bytes = (1 << 38) + 4096
     with pytest.raises(ks.KsError) as e:
         ks.ks_query_layout(p, cfg)

@@ -35,7 +35,7 @@ RESERVED_VGPR_KERNELS = ("ks_interp_v32", "ks_interp_v64", "ks_interp_v32_ext", 
 INTERP_KERNELS = RESERVED_VGPR_KERNELS
 # first VGPR of each kernel's register file (compiler-allocated code stays below it)
 RESERVED_BASE = {"ks_interp_v32": 56, "ks_interp_v64": 56, "ks_interp_v32_ext": 64, "ks_interp_v64_ext": 64,
-                 "ks_interp_v32_cache": 64, "ks_interp_v64_cache": 64}
+                 "ks_interp_v32_cache": 56, "ks_interp_v64_cache": 56}
 # register-file VGPRs from RESERVED_BASE on
 RF_VGPRS = {"ks_interp_v32": 40, "ks_interp_v64": 72, "ks_interp_v32_ext": 40, "ks_interp_v64_ext": 72,
             "ks_interp_v32_cache": 40, "ks_interp_v64_cache": 72}

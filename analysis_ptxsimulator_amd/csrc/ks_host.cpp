@@ -1475,8 +1475,8 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       const int variant = ks_choose_variant(p->reg_slots, a.threads_per_block);
       if (variant == 0) raise(KS_E_UNSUPPORTED, 0, "program needs %u register slots", p->reg_slots);
       const uint32_t wg = 64u * ((a.warps_per_block + 1u) / 2u);
-      if (wg > ks_max_block_threads(variant, a.ext != 0 || a.cache_on != 0))
-        raise(KS_E_UNSUPPORTED, 0, "extended trace records or the cache model with %u register slots support blocks of up to %u threads",
+      if (wg > ks_max_block_threads(variant, a.ext != 0))
+        raise(KS_E_UNSUPPORTED, 0, "extended trace records with %u register slots support blocks of up to %u threads",
               p->reg_slots, ks_max_block_threads(variant, true));
       const size_t need = ks_lds_bytes(wg, p->shared_bytes, a.ext != 0);
       if (need + 64 > ks_lds_limit())

@@ -103,9 +103,8 @@ __device__ __forceinline__ uint32_t s_zero_mask(uint32_t a) {
 // allocation, hold the register file: slot s of a lane is VGPR v[BASE + s] of
 // that lane.  The kernels carry amdgpu_num_vgpr(BASE / 2): on targets with the
 // unified VGPR/AGPR file the compiler doubles that figure, so vBASE and up are
-// reserved (never allocated).  BASE is 56 for the interpreters of the timed path
-// and 64 for the extended-trace variants, whose record payloads need more
-// compiler registers.  A figure the launch bound cannot honour is silently
+// reserved (never allocated).  BASE is 56, except for the extended-trace
+// variants (64), whose record payloads need more compiler registers.  A figure the launch bound cannot honour is silently
 // ignored, which would hand vBASE+ back to the allocator; the build checks the
 // assembly for any compiler-written use of them and that the kernel's VGPR count
 // covers the file (the zero() clobber lists make the compiler count it).
@@ -424,8 +423,8 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
 
   // LDS: [scoreboard, 129 words per warp] [scratch scoreboard, 129 words] (to 16 bytes)
   //      [EXT: record ring, 32 x 16 bytes per warp] [shared window]
-  RegFile<RFN, (EXT || CACHE) ? 64 : 56> R;
-  RegFile<RFN, (EXT || CACHE) ? 64 : 56>::zero();
+  RegFile<RFN, EXT ? 64 : 56> R;
+  RegFile<RFN, EXT ? 64 : 56>::zero();
   // the constant slots after the immediates: 1.0f and -0.0f
   R.put(ib + KS_IMM_SLOTS, 0x3F800000u);
   R.put(ib + KS_IMM_SLOTS + 1u, 0x80000000u);
@@ -1363,10 +1362,10 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_
 __global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64_ext(const KsArgs a) {
   interp<72, true, false>(a);
 }
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v32_cache(const KsArgs a) {
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v32_cache(const KsArgs a) {
   interp<40, false, true>(a);
 }
-__global__ void __launch_bounds__(768) __attribute__((amdgpu_num_vgpr(32))) ks_interp_v64_cache(const KsArgs a) {
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_num_vgpr(28))) ks_interp_v64_cache(const KsArgs a) {
   interp<72, false, true>(a);
 }
 
@@ -1411,7 +1410,7 @@ hipError_t ks_launch_interp(const KsArgs& a, uint32_t n_blocks, uint32_t slots, 
   const uint32_t wg = 64u * waves;
   const int variant = ks_choose_variant(slots, a.threads_per_block);
   const size_t lds = ks_lds_bytes(wg, a.shared_bytes, a.ext != 0);
-  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0 || a.cache_on != 0))
+  if (variant == 0 || lds + 64 > ks_lds_limit() || wg > ks_max_block_threads(variant, a.ext != 0))
     return hipErrorInvalidValue;
   if (a.rf_slots != slots + KS_IMM_SLOTS + KS_CONST_SLOTS) return hipErrorInvalidValue;
   if (a.ext && a.cache_on) return hipErrorInvalidValue;

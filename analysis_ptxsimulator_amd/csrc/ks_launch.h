@@ -23,8 +23,8 @@ size_t ks_lds_limit();
 int ks_choose_variant(uint32_t slots, uint32_t block_threads);
 
 // Largest block the interpreter variant can run: 1024 threads, except the
-// extended-trace and cache-model variants with the 72-VGPR file (136 VGPRs: 768
-// threads); `ext` selects those variants.
+// extended-trace variant with the 72-VGPR file (136 VGPRs: 768 threads); `ext`
+// selects the extended-trace variants.
 uint32_t ks_max_block_threads(int variant, bool ext);
 
 // Dynamic LDS bytes of one workgroup of `wg` lanes (scoreboards, with `ext` the

@@ -174,7 +174,7 @@ def test_register_file_names_match_the_reserved_base():
         regs = sorted({int(r) for r in re.findall(r'\bv(\d+)\b', zero)})
         assert regs == list(range(b, b + n)), (n, b)
     for k, base in kbuild.RESERVED_BASE.items():
-        assert base == (64 if k.endswith(("_ext", "_cache")) else 56)
+        assert base == (64 if k.endswith("_ext") else 56)
     # each kernel's register file is the one its VGPR budget reserves: amdgpu_num_vgpr(base / 2)
     for k, base in kbuild.RESERVED_BASE.items():
         m = re.search(r"amdgpu_num_vgpr\((\d+)\)\)\) %s\(" % k, src)

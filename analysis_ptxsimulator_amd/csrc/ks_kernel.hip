@@ -104,10 +104,11 @@ __device__ __forceinline__ uint32_t s_zero_mask(uint32_t a) {
 // that lane.  The kernels carry amdgpu_num_vgpr(BASE / 2): on targets with the
 // unified VGPR/AGPR file the compiler doubles that figure, so vBASE and up are
 // reserved (never allocated).  BASE is 56, except for the extended-trace
-// variants (64), whose record payloads need more compiler registers.  A figure the launch bound cannot honour is silently
-// ignored, which would hand vBASE+ back to the allocator; the build checks the
-// assembly for any compiler-written use of them and that the kernel's VGPR count
-// covers the file (the zero() clobber lists make the compiler count it).
+// variants (64), whose record payloads need more compiler registers.  A figure
+// the launch bound cannot honour is silently ignored, which would hand vBASE+
+// back to the allocator; the build checks the assembly for any compiler-written
+// use of them and that the kernel's VGPR count covers the file (the zero()
+// clobber lists make the compiler count it).
 
 template <int RFN, int BASE>
 struct RegFile;

@@ -186,6 +186,15 @@ def test_control_flow_shapes(K, oracle_mod, seed):
     full_parity(K, oracle_mod, w)
 
 
+def test_single_ret_program(K, oracle_mod):
+    """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
+    warp and a one-lane warp per block."""
+    w = W.Workload(name="ret_only", ptx=S.HEADER + ".visible .entry k()\n{\n    ret;\n}\n", grid=(3, 1, 1),
+                   block=(33, 1, 1), params=[], gmem=np.zeros(64, np.uint8), trace_cap=4)
+    cg = full_parity(K, oracle_mod, w)
+    assert list(cg["thread_instrs"]) == [32, 1] * 3 and (cg["cycles"] == 1).all()
+
+
 def test_staircase_depth_63(K, oracle_mod):
     g = np.zeros(4096, np.uint8)
     w = W.Workload(name="staircase", ptx=S.staircase_ptx(31), grid=(2, 1, 1), block=(96, 1, 1),

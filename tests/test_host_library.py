@@ -129,6 +129,27 @@ def test_layout_and_default_config(ks):
     ks.ks_program_free(p)
 
 
+def test_zero_or_oversized_shapes_are_invalid(ks):
+    """A grid or block with a zero dimension, or a block of more than 1024 threads,
+    is an invalid argument when the buffers are sized (an empty launch is refused,
+    not run as a no-op)."""
+    p = ks.ks_load_program(W.VECTOR_ADD_PTX)
+    cfg = ks.ks_default_config()
+    cfg.gmem_bytes = 1 << 16
+    for g, b in (((0, 1, 1), (32, 1, 1)), ((1, 0, 1), (32, 1, 1)), ((1, 1, 0), (32, 1, 1)),
+                 ((1, 1, 1), (0, 1, 1)), ((1, 1, 1), (32, 0, 1)), ((1, 1, 1), (32, 1, 0)),
+                 ((1, 1, 1), (1025, 1, 1)), ((1, 1, 1), (32, 32, 2))):
+        cfg.max_grid = ks.ks_dim3(*g)
+        cfg.max_block = ks.ks_dim3(*b)
+        with pytest.raises(ks.KsError) as e:
+            ks.ks_query_layout(p, cfg)
+        assert e.value.code == -3, (g, b)
+    cfg.max_grid = ks.ks_dim3(1, 1, 1)
+    cfg.max_block = ks.ks_dim3(1024, 1, 1)
+    assert ks.ks_query_layout(p, cfg).warps_per_block == 32
+    ks.ks_program_free(p)
+
+
 def test_extended_layout_any_grid(ks):
     """Extended slots hold 16-byte records, for a grid of any size (ks_run launches
     it KS_EXT_MAX_BLOCKS blocks at a time); the basic format likewise."""

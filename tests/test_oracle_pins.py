@@ -700,3 +700,19 @@ def test_thread_count_does_not_change_results(oracle_mod):
     g1, c1, t1, _ = run(oracle_mod, w, threads=1)
     g8, c8, t8, _ = run(oracle_mod, w, threads=8)
     assert np.array_equal(g1, g8) and np.array_equal(c1, c8) and np.array_equal(t1, t8)
+
+
+def test_single_ret_program(oracle_mod):
+    """The smallest program, a lone ret, on 33-thread blocks (a full warp and a
+    one-lane warp): each warp issues once, at cycle 0, with its live lanes, then
+    finishes; cycles = last issue + 1 = 1, stack depth 1, nothing else counted."""
+    ptx = S.HEADER + ".visible .entry k()\n{\n    ret;\n}\n"
+    co, to, _ = oracle_mod.run(ptx, (3, 1, 1), (33, 1, 1), b"", np.zeros(64, np.uint8), trace_cap=4)
+    assert list(co["thread_instrs"]) == [32, 1] * 3
+    assert (co["warp_instrs"] == 1).all() and (co["cycles"] == 1).all() and (co["stall_cycles"] == 0).all()
+    assert (co["status"] == 1).all() and (co["max_stack_depth"] == 1).all()
+    for f in ("gld_n", "gst_n", "sh_n", "diverge_n", "barrier_n", "fault_n"):
+        assert (co[f] == 0).all(), f
+    hs, rs = oracle_mod.trace_slots(to, 4)
+    assert (hs["records_written"] == 1).all() and list(hs["warp_in_block"]) == [0, 1] * 3
+    assert (rs[:, 0] == 0).all()  # issue cycle 0, pc 0

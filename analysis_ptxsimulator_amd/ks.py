@@ -27,6 +27,9 @@ COUNTER_DTYPE = np.dtype([
 ])
 TRACE_HEADER_DTYPE = np.dtype([("records_written", "<u4"), ("version", "u1"), ("flags", "u1"),
                                ("warp_in_block", "<u2"), ("records_dropped", "<u8")])
+# program and launch limits (include/ks.h)
+KS_MAX_REG_SLOTS, KS_MAX_PREDS, KS_MAX_INSTRS = 64, 32, 65535
+KS_MAX_PARAM_BYTES, KS_MAX_SHARED_BYTES, KS_MAX_BLOCK_THREADS = 512, 65536, 1024
 # trace formats (ks_config.trace_format) and the 16-byte extended record
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
 KS_EXT_MAX_BLOCKS = 32  # blocks per launch of an extended-record run (ks_run chunks larger grids)

@@ -42,6 +42,19 @@ def _all_programs():
     return progs
 
 
+def test_binding_constants_match_the_header(ks):
+    """Every integer constant include/ks.h defines that the Python binding mirrors
+    has the header's value."""
+    src = open(os.path.join(ROOT, "include", "ks.h")).read()
+    seen = 0
+    for name, val in re.findall(r"^#define (KS_\w+)\s+\(?(-?(?:0x[0-9A-Fa-f]+|\d+))u?\)?\s*(?:/\*.*)?$", src, re.M):
+        if hasattr(ks, name):
+            assert getattr(ks, name) == int(val, 0), name
+            seen += 1
+    assert ks.KS_CACHE_WARP_BYTES == 16 + 4 * (ks.KS_CACHE_L1_LINES + ks.KS_CACHE_L2_LINES)
+    assert seen >= 15
+
+
 def test_program_shape_matches_oracle(ks, oracle_mod):
     for ptx in _all_programs():
         p = ks.ks_load_program(ptx)
@@ -269,6 +282,15 @@ def test_program_limits(ks):
         ks.ks_alloc_state(p, cfg, 1, 1, 1)
     assert e.value.code == -2 and "register slots" in e.value.msg
     ks.ks_program_free(p)
+    # pcs are 16-bit in the stack entries and extended records: at most KS_MAX_INSTRS
+    body = lambda n: S.HEADER + ".visible .entry k()\n{\n    .reg .b32 %r<2>;\n" + "    mov.u32 %r1, 1;\n" * (n - 1) + \
+        "    ret;\n}\n"
+    p = ks.ks_load_program(body(ks.KS_MAX_INSTRS))
+    assert ks.ks_program_info(p)["n_instrs"] == ks.KS_MAX_INSTRS
+    ks.ks_program_free(p)
+    with pytest.raises(ks.KsError) as e:
+        ks.ks_load_program(body(ks.KS_MAX_INSTRS + 1))
+    assert e.value.code == -2 and "instructions" in e.value.msg
 
 
 def test_interp_kernel_choice(ks):

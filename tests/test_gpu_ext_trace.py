@@ -97,6 +97,13 @@ def test_random_stress_cap_overflow(K, oracle_mod):
         K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=8, trace_format=K.KS_TRACE_EXTENDED)
 
 
+def test_long_program(K, oracle_mod):
+    """A 32000-instruction random program: pcs above 2^14 in the 16-bit record
+    field, and a 1024-record cap against about 31000 issues per warp."""
+    ext_parity(K, oracle_mod, W.random_stress(prog_seed=7, grid=2, block=64, gmem_bytes=1 << 22, trace_cap=1024,
+                                              n_instr=32000))
+
+
 @pytest.mark.skip(reason="refused by the library: extended records of a 64-slot program on 768-thread blocks "
                          "gave wrong gst_lines counters in one of three GPU runs (memory and the other counters "
                          "equal); the cause is not found, so such runs are refused above 256 threads per block")

@@ -186,6 +186,15 @@ def test_control_flow_shapes(K, oracle_mod, seed):
     full_parity(K, oracle_mod, w)
 
 
+def test_long_program(K, oracle_mod):
+    """A 32000-instruction random program: records read from 4 MB into the decoded
+    table, the two-ahead prefetch near its end, and about 31000 issues per warp
+    against a 1024-record cap (the rest counted as dropped)."""
+    w = W.random_stress(prog_seed=7, grid=2, block=64, gmem_bytes=1 << 22, trace_cap=1024, n_instr=32000)
+    cg = full_parity(K, oracle_mod, w, oracle_threads=_host_threads())
+    assert (cg["warp_instrs"] > 30000).all()
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

@@ -195,6 +195,23 @@ def test_long_program(K, oracle_mod):
     assert (cg["warp_instrs"] > 30000).all()
 
 
+def test_largest_shared_window(K, oracle_mod):
+    """A 65536-byte shared window (the largest a program may declare) used at its
+    edges, past its end and misaligned, on 256-thread blocks; where the device's
+    LDS cannot hold it beside the scoreboards the run must be refused instead."""
+    import struct
+    w = W.Workload(name="shared_edges", ptx=S.shared_edges_ptx(), grid=(2, 1, 1), block=(256, 1, 1),
+                   params=[("param_out", "u64", 0)], gmem=np.zeros(2 * 256 * 32, np.uint8), trace_cap=64)
+    assert w.params_bytes == struct.pack("<Q", 0)
+    try:
+        cg = full_parity(K, oracle_mod, w)
+    except K.KsError as e:  # scoreboards, staging rings and a 64 KiB window beyond the device's LDS
+        assert e.code == -2 and "LDS" in e.msg, e
+        _say("shared_edges refused: %s" % e.msg)
+        return
+    assert (cg["fault_n"] == 64).all() and (cg["sh_n"] == 8).all()
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

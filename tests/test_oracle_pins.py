@@ -716,3 +716,23 @@ def test_single_ret_program(oracle_mod):
     hs, rs = oracle_mod.trace_slots(to, 4)
     assert (hs["records_written"] == 1).all() and list(hs["warp_in_block"]) == [0, 1] * 3
     assert (rs[:, 0] == 0).all()  # issue cycle 0, pc 0
+
+
+def test_largest_shared_window_edges(oracle_mod):
+    """The 65536-byte shared window at its edges (workloads.small.shared_edges_ptx):
+    values written before a barrier by other warps are read back at the first and
+    last KiB, the last word and the last 8 bytes as one 64-bit load; the word just
+    past the end and a misaligned word fault and read 0 (fault_n 2 x 32 per warp);
+    every access is stride 1 or a broadcast, so each has bank degree 1."""
+    import struct
+    g = np.zeros(2 * 256 * 32, np.uint8)
+    co, _, _ = oracle_mod.run(S.shared_edges_ptx(), (2, 1, 1), (256, 1, 1), struct.pack("<Q", 0), g, trace_cap=64)
+    out = g.view(np.uint32).reshape(512, 8)
+    t = np.arange(512) % 256
+    nb = np.where(t == 255, 0, t + 1)
+    assert (out[:, 0] == nb + 1).all() and (out[:, 1] == nb + 7).all() and (out[:, 2] == 262).all()
+    assert (out[:, 3] == 0).all() and (out[:, 4] == 0).all() and (out[:, 5] == 0).all()
+    assert (out[:, 6] == 261).all() and (out[:, 7] == 262).all()
+    assert (co["fault_n"] == 64).all() and (co["sh_n"] == 8).all()
+    assert (co["sh_degree_sum"] == 8).all() and (co["sh_degree_max"] == 1).all()
+    assert (co["status"] == 5).all()  # finished, fault

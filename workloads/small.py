@@ -250,3 +250,60 @@ def random_cfg_ptx(seed: int, n_instr: int = 24, loops: bool = False, with_ret: 
         L.append("$L__b%d:" % n_instr)
     L += ["    add.s64 %rd5, %rd2, %rd3;", "    st.global.u32 [%rd5], %r6;", "    ret;", "}"]
     return "\n".join(L) + "\n"
+
+
+def shared_edges_ptx() -> str:
+    """The largest shared window (65536 bytes) at its edges, on 256-thread blocks.
+    Thread t stores t + 1 at word t and t + 7 at word 16128 + t (the last KiB),
+    then, after a barrier, loads its neighbour's two words (neighbour t + 1, or 0
+    for t = 255), the window's last word, one word past the end and a misaligned
+    word (both fault and read 0), and the last 8 bytes as one 64-bit load.  The
+    results go to out[32 t + 0, 4, 8, 12, 16] (u32) and out[32 t + 24] (u64)."""
+    return HEADER + """\
+.visible .entry shared_edges(
+    .param .u64 param_out
+)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<20>;
+    .reg .b64 %rd<6>;
+    .shared .align 8 .b8 smem[65536];
+
+    ld.param.u64 %rd1, [param_out];
+    mov.u32 %r1, %tid.x;
+    mov.u32 %r2, smem;
+    mul.lo.s32 %r3, %r1, 4;
+    add.s32 %r4, %r2, %r3;
+    add.s32 %r5, %r4, 64512;
+    add.s32 %r6, %r1, 1;
+    add.s32 %r7, %r1, 7;
+    st.shared.u32 [%r4], %r6;
+    st.shared.u32 [%r5], %r7;
+    bar.sync 0;
+    setp.eq.u32 %p1, %r1, 255;
+    add.s32 %r8, %r1, 1;
+    mov.u32 %r9, 0;
+    selp.b32 %r8, %r9, %r8, %p1;
+    mul.lo.s32 %r10, %r8, 4;
+    add.s32 %r11, %r2, %r10;
+    ld.shared.u32 %r12, [%r11];
+    add.s32 %r13, %r11, 64512;
+    ld.shared.u32 %r14, [%r13];
+    ld.shared.u32 %r15, [%r2+65532];
+    ld.shared.u32 %r16, [%r2+65536];
+    ld.shared.u32 %r17, [%r2+2];
+    ld.shared.u64 %rd2, [%r2+65528];
+    mov.u32 %r18, %ctaid.x;
+    mov.u32 %r19, %ntid.x;
+    mad.lo.s32 %r18, %r18, %r19, %r1;
+    mul.wide.u32 %rd3, %r18, 32;
+    add.s64 %rd4, %rd1, %rd3;
+    st.global.u32 [%rd4], %r12;
+    st.global.u32 [%rd4+4], %r14;
+    st.global.u32 [%rd4+8], %r15;
+    st.global.u32 [%rd4+12], %r16;
+    st.global.u32 [%rd4+16], %r17;
+    st.global.u64 [%rd4+24], %rd2;
+    ret;
+}
+"""

@@ -212,6 +212,26 @@ def test_largest_shared_window(K, oracle_mod):
     assert (cg["fault_n"] == 64).all() and (cg["sh_n"] == 8).all()
 
 
+@pytest.mark.parametrize("budget", [0, 1])
+def test_budget_zero_and_one(K, oracle_mod, budget):
+    """An issue budget of 0 stops every warp before its first issue (nothing
+    issued, cycles 0, status BUDGET); a budget of 1 lets each warp issue once."""
+    cg = full_parity(K, oracle_mod, W.random_stress(prog_seed=3, grid=3, block=96, gmem_bytes=1 << 22, trace_cap=8),
+                     max_warp_instrs=budget)
+    assert (cg["warp_instrs"] == budget).all() and (cg["status"] & 2).all()
+
+
+def test_memory_too_small_for_every_access(K, oracle_mod):
+    """vector_add over a 4096-byte simulated memory: b and c lie past its end, so
+    every access to them faults (loads read 0, stores are dropped) and is still
+    analysed, while a stays in range."""
+    w = W.vector_add()
+    w = W.Workload(name="vector_add_small_mem", ptx=w.ptx, grid=w.grid, block=w.block, params=w.params,
+                   gmem=w.gmem[:4096].copy(), trace_cap=w.trace_cap)
+    cg = full_parity(K, oracle_mod, w)
+    assert (cg["fault_n"] > 0).all() and (cg["status"] & 4).all()
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

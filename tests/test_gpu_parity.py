@@ -232,6 +232,18 @@ def test_memory_too_small_for_every_access(K, oracle_mod):
     assert (cg["fault_n"] > 0).all() and (cg["status"] & 4).all()
 
 
+def test_latency_class_of_every_producer(K, oracle_mod):
+    """Every destination-writing form of the subset, each followed by a consumer of
+    its result, under a latency table of distinct values per class: the GPU's
+    issue cycles must equal the oracle's, which its pins fix per class."""
+    lat = [101 + 10 * k for k in range(14)] + [28, 150, 400, 0]
+    g = np.zeros(4096, np.uint8)
+    g[64:72] = np.arange(1, 9, dtype=np.uint8)
+    w = W.Workload(name="latency_classes", ptx=S.latency_classes_ptx(), grid=(2, 1, 1), block=(40, 1, 1),
+                   params=[("param_p", "u64", 64), ("param_q", "u32", 9)], gmem=g, trace_cap=128)
+    full_parity(K, oracle_mod, w, latency=lat)
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

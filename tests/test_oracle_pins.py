@@ -736,3 +736,25 @@ def test_largest_shared_window_edges(oracle_mod):
     assert (co["fault_n"] == 64).all() and (co["sh_n"] == 8).all()
     assert (co["sh_degree_sum"] == 8).all() and (co["sh_degree_max"] == 1).all()
     assert (co["status"] == 5).all()  # finished, fault
+
+
+def test_latency_class_of_every_producer(oracle_mod):
+    """Each producer of workloads.small.LATENCY_PAIRS (every destination-writing
+    form of the subset) is followed by a consumer of its result.  With a latency
+    table of distinct values (101 + 10 k for class k), a producer issues one cycle
+    after the previous consumer (its sources are long ready) and its consumer
+    exactly its class's latency later, so a form put in the wrong class fails."""
+    import struct
+    lat = [101 + 10 * k for k in range(14)] + [28, 150, 400, 0]
+    g = np.zeros(4096, np.uint8)
+    co, to, _ = oracle_mod.run(S.latency_classes_ptx(), (1, 1, 1), (32, 1, 1), struct.pack("<QI", 64, 0), g,
+                               trace_cap=128, latency=lat)
+    hs, rs = oracle_mod.trace_slots(to, 128)
+    iss = rs[0, :int(hs["records_written"][0]), 0].astype(np.int64)
+    assert co["status"][0] == 1 and co["fault_n"][0] == 0
+    first = 10  # the prologue's five producer/consumer pairs
+    for k, (prod, cls, _) in enumerate(S.LATENCY_PAIRS):
+        i = first + 2 * k
+        assert iss[i] - iss[i - 1] == 1, prod
+        assert iss[i + 1] - iss[i] == lat[oracle_mod.LAT_NAMES.index(cls)], (prod, cls)
+    assert len(iss) == first + 2 * len(S.LATENCY_PAIRS) + 1  # and the ret

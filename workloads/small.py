@@ -307,3 +307,50 @@ def shared_edges_ptx() -> str:
     ret;
 }
 """
+
+
+# Producer/consumer pairs of latency_classes_ptx: (producer, latency class of the
+# producer, consumer reading the producer's destination).
+LATENCY_PAIRS = [
+    ("add.s32 %r3, %r1, %r2;", "int32", "add.s32 %r11, %r3, 0;"),
+    ("sub.s32 %r3, %r1, %r2;", "int32", "add.s32 %r11, %r3, 0;"),
+    ("mul.lo.s32 %r3, %r1, %r2;", "int32", "add.s32 %r11, %r3, 0;"),
+    ("mad.lo.s32 %r3, %r1, %r2, %r1;", "int32", "add.s32 %r11, %r3, 0;"),
+    ("add.s64 %rd2, %rd1, %rd1;", "int64", "add.s64 %rd10, %rd2, 0;"),
+    ("sub.s64 %rd2, %rd1, %rd1;", "int64", "add.s64 %rd10, %rd2, 0;"),
+    ("mul.lo.s64 %rd2, %rd1, %rd1;", "int64", "add.s64 %rd10, %rd2, 0;"),
+    ("mad.lo.s64 %rd2, %rd1, %rd1, %rd1;", "int64", "add.s64 %rd10, %rd2, 0;"),
+    ("mul.wide.s32 %rd2, %r1, %r2;", "int32", "add.s64 %rd10, %rd2, 0;"),  # 32-bit operands
+    ("mul.wide.u32 %rd2, %r1, %r2;", "int32", "add.s64 %rd10, %rd2, 0;"),
+    ("add.f32 %f2, %f1, %f1;", "fp32", "add.f32 %f10, %f2, %f2;"),
+    ("sub.f32 %f2, %f1, %f1;", "fp32", "add.f32 %f10, %f2, %f2;"),
+    ("mul.f32 %f2, %f1, %f1;", "fp32", "add.f32 %f10, %f2, %f2;"),
+    ("fma.rn.f32 %f2, %f1, %f1, %f1;", "fp32", "add.f32 %f10, %f2, %f2;"),
+    ("setp.lt.s32 %p1, %r1, %r2;", "setp", "selp.b32 %r12, %r1, %r2, %p1;"),
+    ("setp.gt.f32 %p1, %f1, %f1;", "setp", "selp.b32 %r12, %r1, %r2, %p1;"),
+    ("setp.eq.u64 %p1, %rd1, %rd1;", "setp", "selp.b32 %r12, %r1, %r2, %p1;"),
+    ("selp.b32 %r3, %r1, %r2, %p1;", "selp", "add.s32 %r11, %r3, 0;"),
+    ("mov.u32 %r3, %r1;", "mov", "add.s32 %r11, %r3, 0;"),
+    ("mov.u32 %r3, 12345;", "mov", "add.s32 %r11, %r3, 0;"),
+    ("mov.u32 %r3, %tid.x;", "mov", "add.s32 %r11, %r3, 0;"),
+    ("mov.u32 %r4, sm;", "mov", "add.s32 %r11, %r4, 0;"),
+    ("ld.param.u32 %r3, [param_q];", "ld_param", "add.s32 %r11, %r3, 0;"),
+    ("ld.global.u32 %r3, [%rd1];", "ld_global", "add.s32 %r11, %r3, 0;"),
+    ("ld.global.u64 %rd2, [%rd1];", "ld_global", "add.s64 %rd10, %rd2, 0;"),
+    ("ld.shared.u32 %r3, [%r4];", "ld_shared", "add.s32 %r11, %r3, 0;"),
+]
+
+
+def latency_classes_ptx() -> str:
+    """A prologue that makes the pairs' sources ready (each followed by a consumer),
+    then LATENCY_PAIRS in order, then ret.  Every producer reads only registers
+    whose values are long ready, and every consumer reads its producer's result."""
+    pro = ["ld.param.u64 %rd1, [param_p];", "add.s64 %rd9, %rd1, 0;",
+           "mov.u32 %r1, 7;", "add.s32 %r9, %r1, 0;",
+           "mov.u32 %r2, 3;", "add.s32 %r9, %r2, 0;",
+           "mov.f32 %f1, 0f3F800000;", "add.f32 %f9, %f1, %f1;",
+           "setp.ne.s32 %p1, %r1, %r2;", "selp.b32 %r9, %r1, %r2, %p1;"]
+    body = [x for p, _, c in LATENCY_PAIRS for x in (p, c)]
+    return HEADER + (".visible .entry latency_classes(\n    .param .u64 param_p,\n    .param .u32 param_q\n)\n{\n"
+                     "    .reg .pred %p<2>;\n    .reg .b32 %r<13>;\n    .reg .b64 %rd<11>;\n    .reg .f32 %f<11>;\n"
+                     "    .shared .align 8 .b8 sm[64];\n") + "".join("    %s\n" % x for x in pro + body + ["ret;"]) + "}\n"

@@ -740,7 +740,8 @@ def test_largest_shared_window_edges(oracle_mod):
 
 def test_latency_class_of_every_producer(oracle_mod):
     """Each producer of workloads.small.LATENCY_PAIRS (every destination-writing
-    form of the subset) is followed by a consumer of its result.  With a latency
+    form of the subset) is followed by a consumer of its result: as an operand,
+    a guard, a store's value or address, or a load's address.  With a latency
     table of distinct values (101 + 10 k for class k), a producer issues one cycle
     after the previous consumer (its sources are long ready) and its consumer
     exactly its class's latency later, so a form put in the wrong class fails."""
@@ -752,7 +753,7 @@ def test_latency_class_of_every_producer(oracle_mod):
     hs, rs = oracle_mod.trace_slots(to, 128)
     iss = rs[0, :int(hs["records_written"][0]), 0].astype(np.int64)
     assert co["status"][0] == 1 and co["fault_n"][0] == 0
-    first = 10  # the prologue's five producer/consumer pairs
+    first = 12  # the prologue's six producer/consumer pairs
     for k, (prod, cls, _) in enumerate(S.LATENCY_PAIRS):
         i = first + 2 * k
         assert iss[i] - iss[i - 1] == 1, prod

@@ -338,18 +338,26 @@ LATENCY_PAIRS = [
     ("ld.global.u32 %r3, [%rd1];", "ld_global", "add.s32 %r11, %r3, 0;"),
     ("ld.global.u64 %rd2, [%rd1];", "ld_global", "add.s64 %rd10, %rd2, 0;"),
     ("ld.shared.u32 %r3, [%r4];", "ld_shared", "add.s32 %r11, %r3, 0;"),
+    # the issue rule's sources: a guard, a store's value and address, a load's address
+    ("setp.lt.s32 %p1, %r1, %r2;", "setp", "@%p1 add.s32 %r11, %r1, 0;"),
+    ("add.s32 %r3, %r1, %r2;", "int32", "st.shared.u32 [%r4], %r3;"),
+    ("mov.u32 %r5, sm;", "mov", "st.shared.u32 [%r5], %r1;"),
+    ("add.s64 %rd3, %rd1, 0;", "int64", "ld.global.u32 %r11, [%rd3];"),
+    # an instruction no lane passes the guard of still sets its destination's ready cycle
+    ("@%p0 add.s32 %r3, %r1, %r2;", "int32", "add.s32 %r11, %r3, 0;"),
 ]
 
 
 def latency_classes_ptx() -> str:
-    """A prologue that makes the pairs' sources ready (each followed by a consumer),
-    then LATENCY_PAIRS in order, then ret.  Every producer reads only registers
+    """A prologue that makes the pairs' sources ready (each followed by a consumer;
+    %p0 is false and %p1 true), then LATENCY_PAIRS in order, then ret.  Every producer reads only registers
     whose values are long ready, and every consumer reads its producer's result."""
     pro = ["ld.param.u64 %rd1, [param_p];", "add.s64 %rd9, %rd1, 0;",
            "mov.u32 %r1, 7;", "add.s32 %r9, %r1, 0;",
            "mov.u32 %r2, 3;", "add.s32 %r9, %r2, 0;",
            "mov.f32 %f1, 0f3F800000;", "add.f32 %f9, %f1, %f1;",
-           "setp.ne.s32 %p1, %r1, %r2;", "selp.b32 %r9, %r1, %r2, %p1;"]
+           "setp.ne.s32 %p1, %r1, %r2;", "selp.b32 %r9, %r1, %r2, %p1;",
+           "setp.eq.s32 %p0, %r1, %r2;", "selp.b32 %r9, %r1, %r2, %p0;"]
     body = [x for p, _, c in LATENCY_PAIRS for x in (p, c)]
     return HEADER + (".visible .entry latency_classes(\n    .param .u64 param_p,\n    .param .u32 param_q\n)\n{\n"
                      "    .reg .pred %p<2>;\n    .reg .b32 %r<13>;\n    .reg .b64 %rd<11>;\n    .reg .f32 %f<11>;\n"

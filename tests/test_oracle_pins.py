@@ -716,6 +716,12 @@ def test_single_ret_program(oracle_mod):
     hs, rs = oracle_mod.trace_slots(to, 4)
     assert (hs["records_written"] == 1).all() and list(hs["warp_in_block"]) == [0, 1] * 3
     assert (rs[:, 0] == 0).all()  # issue cycle 0, pc 0
+    assert (hs["flags"] == 8).all()  # finished
+    # a budget of 0 stops every warp before its one issue: status and flag BUDGET, nothing written
+    co, to, _ = oracle_mod.run(ptx, (3, 1, 1), (33, 1, 1), b"", np.zeros(64, np.uint8), trace_cap=4, max_warp_instrs=0)
+    hs, _ = oracle_mod.trace_slots(to, 4)
+    assert (co["status"] == 2).all() and (co["warp_instrs"] == 0).all() and (co["cycles"] == 0).all()
+    assert (hs["flags"] == 4).all() and (hs["records_written"] == 0).all()
 
 
 def test_largest_shared_window_edges(oracle_mod):
@@ -726,7 +732,9 @@ def test_largest_shared_window_edges(oracle_mod):
     every access is stride 1 or a broadcast, so each has bank degree 1."""
     import struct
     g = np.zeros(2 * 256 * 32, np.uint8)
-    co, _, _ = oracle_mod.run(S.shared_edges_ptx(), (2, 1, 1), (256, 1, 1), struct.pack("<Q", 0), g, trace_cap=64)
+    co, to, _ = oracle_mod.run(S.shared_edges_ptx(), (2, 1, 1), (256, 1, 1), struct.pack("<Q", 0), g, trace_cap=64)
+    hs, _ = oracle_mod.trace_slots(to, 64)
+    assert (hs["flags"] == 2 | 8).all()  # fault, finished
     out = g.view(np.uint32).reshape(512, 8)
     t = np.arange(512) % 256
     nb = np.where(t == 255, 0, t + 1)

@@ -80,10 +80,10 @@ def occupancy(arch, threads_per_block, registers_per_thread, shared_bytes_per_bl
             "warps_by_registers": by_regs, "warps_by_shared_memory": by_smem, "warps_by_block_size": by_block}
 
 
-def program_occupancy(ptx, block_threads, arch="sm_80"):
+def program_occupancy(ptx, block_threads, arch="sm_80", entry=None):
     """Occupancy of a simulated program: its declared 32-bit register slots per
     thread (a 64-bit register counts two) and its .shared bytes per block."""
-    prog = ks.ks_load_program(ptx)
+    prog = ks.ks_load_program(ptx, entry)
     try:
         info = ks.ks_program_info(prog)
     finally:
@@ -94,9 +94,9 @@ def program_occupancy(ptx, block_threads, arch="sm_80"):
 class ProgramInfo:
     """pc -> (source line, text, access bytes) of a program, from ks_instr_info."""
 
-    def __init__(self, ptx):
+    def __init__(self, ptx, entry=None):
         self.lines = ptx.split("\n")
-        prog = ks.ks_load_program(ptx)
+        prog = ks.ks_load_program(ptx, entry)
         try:
             n = ks.ks_program_info(prog)["n_instrs"]
             self.desc = [ks.ks_instr_info(prog, pc) for pc in range(n)]
@@ -301,9 +301,53 @@ def chrome_trace(headers, records, info, warps_per_block, trace_format=ks.KS_TRA
         os.unlink(path)
 
 
+def param_block(ptx, values, entry=None):
+    """The parameter block of the program's entry holding `values` (a dict from
+    parameter name to an int, or a float for a 4-byte parameter stored as binary32);
+    a pointer parameter's value is a byte offset into simulated memory, and a
+    parameter not named is 0.  The layout is the library's own (ks_param_info, in
+    declaration order at natural alignment), so it is what ks_run reads.  An unknown
+    name or a value that does not fit its parameter is a ValueError."""
+    import struct
+    prog = ks.ks_load_program(ptx, entry)
+    try:
+        info = ks.ks_program_info(prog)
+        buf = bytearray(info["param_bytes"])
+        names = set()
+        for i in range(info["n_params"]):
+            off, size, name = ks.ks_param_info(prog, i)
+            names.add(name)
+            v = values.get(name, 0)
+            if isinstance(v, float):
+                if size != 4:
+                    raise ValueError("parameter %s has %d bytes: a float needs 4" % (name, size))
+                raw = struct.pack("<f", v)
+            else:
+                v = int(v)
+                if not -(1 << (8 * size - 1)) <= v < (1 << (8 * size)):
+                    raise ValueError("value %d does not fit the %d-byte parameter %s" % (v, size, name))
+                raw = (v & ((1 << (8 * size)) - 1)).to_bytes(size, "little")
+            buf[off:off + size] = raw
+        unknown = sorted(set(values) - names)
+        if unknown:
+            raise ValueError("no parameter named %s (the entry has %s)" % (", ".join(unknown), ", ".join(sorted(names))))
+        return bytes(buf)
+    finally:
+        ks.ks_program_free(prog)
+
+
+def _dims(text):
+    d = [int(x) for x in text.split(",")]
+    if not 1 <= len(d) <= 3:
+        raise SystemExit("a grid or block is 1 to 3 comma-separated sizes: %s" % text)
+    return tuple(d + [1] * (3 - len(d)))
+
+
 def main(argv=None):
     """Run a workload on the GPU with extended records and report occupancy, hints
-    and (with --out) a Chrome/Perfetto trace of its first warps."""
+    and (with --out) a Chrome/Perfetto trace of its first warps.  The workload is a
+    built-in one, or a PTX file with its launch shape, parameters and initial
+    simulated memory (--ptx, --grid, --block, --param, --gmem, --gmem-bytes)."""
     import argparse
     import os
     import sys
@@ -312,12 +356,39 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="vector_add",
                     help="vector_add | strided_<s> | bank_<s> | ffma_<acc> | random_<seed>")
+    ap.add_argument("--ptx", default=None, help="simulate this PTX file instead of a built-in workload")
+    ap.add_argument("--entry", default=None, help="the .entry to simulate (default: the first)")
+    ap.add_argument("--grid", default="1", help="grid size x[,y[,z]] (with --ptx)")
+    ap.add_argument("--block", default="32", help="block size x[,y[,z]] (with --ptx)")
+    ap.add_argument("--param", action="append", default=[],
+                    help="name=value, repeatable (with --ptx); a pointer is a byte offset into simulated memory, "
+                         "a value with a '.' a float")
+    ap.add_argument("--gmem", default=None, help="initial simulated memory: a raw byte file (with --ptx)")
+    ap.add_argument("--gmem-bytes", type=int, default=None,
+                    help="simulated memory size (with --ptx; default the --gmem file's size, else 1 MiB)")
+    ap.add_argument("--trace-cap", type=int, default=1024, help="records per warp (with --ptx)")
     ap.add_argument("--arch", default="sm_80")
     ap.add_argument("--out", default=None, help="write the trace-event JSON here")
     ap.add_argument("--warps", type=int, default=64, help="warps exported to the timeline")
     args = ap.parse_args(argv)
     name = args.workload
-    if name == "vector_add":
+    if args.ptx:
+        ptx = open(args.ptx).read()
+        values = {}
+        for kv in args.param:
+            k, _, v = kv.partition("=")
+            values[k.strip()] = float(v) if "." in v else int(v, 0)
+        image = np.fromfile(args.gmem, np.uint8) if args.gmem else np.zeros(0, np.uint8)
+        size = args.gmem_bytes or (image.size if image.size else 1 << 20)
+        if image.size > size:
+            raise SystemExit("the --gmem file holds %d bytes, more than --gmem-bytes %d" % (image.size, size))
+        gmem = np.zeros(size, np.uint8)
+        gmem[:image.size] = image
+        grid, block = _dims(args.grid), _dims(args.block)
+        w = W.Workload(name=os.path.basename(args.ptx), ptx=ptx, grid=grid, block=block, params=[], gmem=gmem,
+                       trace_cap=args.trace_cap)
+        pbytes = param_block(ptx, values, args.entry)
+    elif name == "vector_add":
         w = W.vector_add()
     elif name.startswith("strided_"):
         w = W.strided_gather(int(name[8:]), n=8192)
@@ -329,16 +400,19 @@ def main(argv=None):
         w = W.random_stress(prog_seed=int(name[7:]), grid=16, block=256, gmem_bytes=1 << 24, trace_cap=2048)
     else:
         raise SystemExit("unknown workload %s" % name)
-    s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, trace_format=ks.KS_TRACE_EXTENDED)
+    if not args.ptx:
+        pbytes = w.params_bytes
+    s = ks.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=w.trace_cap, trace_format=ks.KS_TRACE_EXTENDED,
+                   entry=args.entry)
     try:
         s.load_gmem(w.gmem)
-        s.run(w.params_bytes)
+        s.run(pbytes)
         hdr, rec = s.trace_records()
         kernel = s.kernel_name()
     finally:
         s.close()
-    info = ProgramInfo(w.ptx)
-    occ = program_occupancy(w.ptx, w.threads_per_block, args.arch)
+    info = ProgramInfo(w.ptx, args.entry)
+    occ = program_occupancy(w.ptx, w.threads_per_block, args.arch, args.entry)
     hs = hints(hdr, rec, info, occ, w.warps_per_block)
     print(json.dumps({"workload": w.name, "kernel": kernel, "occupancy": occ,
                       "hints": [h for h in hs if "warp" not in h] + [h for h in hs if "warp" in h][:20],

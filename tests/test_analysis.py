@@ -308,3 +308,21 @@ def test_trace_export_rejects_records_outside_the_program(A, oracle_mod, tmp_pat
     assert rc == -3 and b"NULL name" in ks.lib().ks_last_error()  # KS_E_INVALID_ARG
     n = A.write_chrome_trace(str(tmp_path / "t.json"), hdr, rec, info, w.warps_per_block)
     assert n == int(hdr["records_written"].sum())
+
+
+def test_param_block_uses_the_library_layout(A):
+    """param_block packs named values at the offsets the library reads: vector_add's
+    block equals the workload's own packing; floats are binary32; unnamed
+    parameters are 0; an unknown name or an oversized value is refused."""
+    import struct
+    vals = {"param_a": 0, "param_b": 4096, "param_c": 8192, "param_n": 1000}
+    assert A.param_block(W.VECTOR_ADD_PTX, vals) == W.vector_add().params_bytes
+    b = A.param_block(W.VECTOR_ADD_PTX, {"param_c": 0x1234, "param_n": 1.5})
+    assert b[16:24] == (0x1234).to_bytes(8, "little") and b[24:28] == struct.pack("<f", 1.5) and b[:16] == bytes(16)
+    assert A.param_block(W.VECTOR_ADD_PTX, {"param_n": -1})[24:28] == b"\xff\xff\xff\xff"
+    with pytest.raises(ValueError, match="no parameter named param_x"):
+        A.param_block(W.VECTOR_ADD_PTX, {"param_x": 1})
+    with pytest.raises(ValueError, match="does not fit"):
+        A.param_block(W.VECTOR_ADD_PTX, {"param_n": 1 << 32})
+    with pytest.raises(ValueError, match="a float needs 4"):
+        A.param_block(W.VECTOR_ADD_PTX, {"param_a": 0.5})

@@ -229,3 +229,28 @@ def test_host_analysis_on_gpu_records(K, oracle_mod, case):
     ho, ro = oracle_mod.trace_slots(to, w.trace_cap, oracle_mod.TRACE_EXTENDED)
     assert A.hints(hg, rg, info, occ, w.warps_per_block) == A.hints(ho, ro, info, occ, w.warps_per_block)
     assert A.chrome_trace(hg, rg, info, w.warps_per_block) == A.chrome_trace(ho, ro, info, w.warps_per_block)
+
+
+def test_analysis_command_on_a_ptx_file(K, oracle_mod, tmp_path, capsys):
+    """The analysis command on a user's PTX file: vector_add with its launch shape,
+    parameters and memory image given on the command line reports the same hints
+    as the built-in vector_add workload, and writes its trace-event file."""
+    import json
+    from analysis_ptxsimulator_amd import analysis as A
+    w = W.vector_add()
+    ptx = tmp_path / "vadd.ptx"
+    ptx.write_text(w.ptx)
+    img = tmp_path / "mem.bin"
+    w.gmem.tofile(str(img))
+    out = tmp_path / "trace.json"
+    A.main(["--ptx", str(ptx), "--grid", "4", "--block", "256", "--gmem", str(img), "--trace-cap", "32",
+            "--param", "param_a=0", "--param", "param_b=4096", "--param", "param_c=0x2000", "--param", "param_n=1000",
+            "--out", str(out)])
+    got = json.loads(capsys.readouterr().out)
+    A.main(["--workload", "vector_add"])
+    ref = json.loads(capsys.readouterr().out)
+    assert got["workload"] == "vadd.ptx" and got["kernel"] == ref["kernel"]
+    assert got["occupancy"] == ref["occupancy"] and got["hints"] == ref["hints"]
+    assert got["n_event_hints"] == ref["n_event_hints"]
+    events = json.load(open(out))
+    assert len(events["traceEvents"]) > 32

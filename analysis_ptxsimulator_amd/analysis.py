@@ -369,6 +369,7 @@ def main(argv=None):
     ap.add_argument("--trace-cap", type=int, default=1024, help="records per warp (with --ptx)")
     ap.add_argument("--arch", default="sm_80")
     ap.add_argument("--out", default=None, help="write the trace-event JSON here")
+    ap.add_argument("--dump-gmem", default=None, help="write the simulated memory after the run here (raw bytes)")
     ap.add_argument("--warps", type=int, default=64, help="warps exported to the timeline")
     args = ap.parse_args(argv)
     name = args.workload
@@ -409,12 +410,21 @@ def main(argv=None):
         s.run(pbytes)
         hdr, rec = s.trace_records()
         kernel = s.kernel_name()
+        cnt = s.read_counters()
+        if args.dump_gmem:
+            s.read_gmem().tofile(args.dump_gmem)
     finally:
         s.close()
     info = ProgramInfo(w.ptx, args.entry)
     occ = program_occupancy(w.ptx, w.threads_per_block, args.arch, args.entry)
     hs = hints(hdr, rec, info, occ, w.warps_per_block)
-    print(json.dumps({"workload": w.name, "kernel": kernel, "occupancy": occ,
+    totals = {f: int(cnt[f].sum()) for f in ("thread_instrs", "warp_instrs", "gld_n", "gld_sectors", "gld_lines",
+                                               "gst_n", "gst_sectors", "gst_lines", "sh_n", "sh_degree_sum",
+                                               "diverge_n", "barrier_n", "fault_n")}
+    totals.update({"warps": int(len(cnt)), "max_cycles": int(cnt["cycles"].max()) if len(cnt) else 0,
+                   "max_stack_depth": int(cnt["max_stack_depth"].max()) if len(cnt) else 0,
+                   "status_or": int(np.bitwise_or.reduce(cnt["status"])) if len(cnt) else 0})
+    print(json.dumps({"workload": w.name, "kernel": kernel, "occupancy": occ, "counters": totals,
                       "hints": [h for h in hs if "warp" not in h] + [h for h in hs if "warp" in h][:20],
                       "n_event_hints": sum(1 for h in hs if "warp" in h)}, indent=1))
     if args.out:

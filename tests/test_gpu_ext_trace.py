@@ -245,8 +245,12 @@ def test_analysis_command_on_a_ptx_file(K, oracle_mod, tmp_path, capsys):
     out = tmp_path / "trace.json"
     A.main(["--ptx", str(ptx), "--grid", "4", "--block", "256", "--gmem", str(img), "--trace-cap", "32",
             "--param", "param_a=0", "--param", "param_b=4096", "--param", "param_c=0x2000", "--param", "param_n=1000",
-            "--out", str(out)])
+            "--out", str(out), "--dump-gmem", str(tmp_path / "after.bin")])
     got = json.loads(capsys.readouterr().out)
+    c = np.fromfile(str(tmp_path / "after.bin"), np.uint8)[0x2000:0x2000 + 4000].view(np.float32)
+    a, b = w.gmem[:4000].view(np.float32), w.gmem[4096:8096].view(np.float32)
+    assert np.array_equal(c, a + b)  # the memory after the run: c = a + b
+    assert got["counters"]["thread_instrs"] == 19264 and got["counters"]["max_cycles"] == 239
     A.main(["--workload", "vector_add"])
     ref = json.loads(capsys.readouterr().out)
     assert got["workload"] == "vadd.ptx" and got["kernel"] == ref["kernel"]

@@ -361,8 +361,8 @@ def main(argv=None):
     ap.add_argument("--grid", default="1", help="grid size x[,y[,z]] (with --ptx)")
     ap.add_argument("--block", default="32", help="block size x[,y[,z]] (with --ptx)")
     ap.add_argument("--param", action="append", default=[],
-                    help="name=value, repeatable (with --ptx); a pointer is a byte offset into simulated memory, "
-                         "a value with a '.' a float")
+                    help="name=value, repeatable (with --ptx); a pointer is a byte offset into simulated memory; "
+                         "a value that is not an integer (0x.. allowed) is read as a float")
     ap.add_argument("--gmem", default=None, help="initial simulated memory: a raw byte file (with --ptx)")
     ap.add_argument("--gmem-bytes", type=int, default=None,
                     help="simulated memory size (with --ptx; default the --gmem file's size, else 1 MiB)")
@@ -377,8 +377,16 @@ def main(argv=None):
         ptx = open(args.ptx).read()
         values = {}
         for kv in args.param:
-            k, _, v = kv.partition("=")
-            values[k.strip()] = float(v) if "." in v else int(v, 0)
+            k, sep, v = kv.partition("=")
+            if not sep:
+                raise SystemExit("--param takes name=value: %s" % kv)
+            try:
+                values[k.strip()] = int(v, 0)
+            except ValueError:
+                try:
+                    values[k.strip()] = float(v)
+                except ValueError:
+                    raise SystemExit("--param %s: %r is neither an integer nor a float" % (k, v))
         image = np.fromfile(args.gmem, np.uint8) if args.gmem else np.zeros(0, np.uint8)
         size = args.gmem_bytes or (image.size if image.size else 1 << 20)
         if image.size > size:

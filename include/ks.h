@@ -311,8 +311,8 @@ ks_status ks_alloc_state_static(const ks_program* prog, const ks_config* cfg, vo
  * `params` holds `params_len` >= param_bytes bytes of the parameter block (host
  * memory; copied into the launch arguments).  Each run re-initialises registers,
  * predicates, stacks, scoreboards, shared windows and (with the cache model) the
- * caches, and rewrites every counter record and trace header of the grid's warps.  Warps are numbered
- * linear block id * warps_per_block + warp in block.  With extended records the
+ * caches, and rewrites every counter record and trace header of the grid's
+ * warps.  Warps are numbered linear block id * warps_per_block + warp in block.  With extended records the
  * grid is launched KS_EXT_MAX_BLOCKS blocks at a time (blocks share nothing but
  * simulated global memory, whose accesses by different blocks must not race).
  * Errors: KS_E_INVALID_ARG (shape beyond the allocation, short params),

@@ -244,6 +244,21 @@ def test_latency_class_of_every_producer(K, oracle_mod):
     full_parity(K, oracle_mod, w, latency=lat)
 
 
+@pytest.mark.parametrize("block", [64, 256, 1024])
+def test_block_reduce(K, oracle_mod, block):
+    """A shared-memory tree reduction: barriers between its steps, divergence that
+    narrows inside warp 0, stride-1 shared accesses, one output per block."""
+    grid = 24
+    data = np.random.default_rng(block).integers(0, 1 << 32, size=grid * block, dtype=np.uint32)
+    out = 4 * grid * block
+    g = np.zeros(out + 4 * grid, np.uint8)
+    g[:out] = data.view(np.uint8)
+    w = W.Workload(name="block_reduce_%d" % block, ptx=S.block_reduce_ptx(block), grid=(grid, 1, 1),
+                   block=(block, 1, 1), params=[("param_in", "u64", 0), ("param_out", "u64", out)], gmem=g,
+                   trace_cap=64)
+    full_parity(K, oracle_mod, w)
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

@@ -767,3 +767,26 @@ def test_latency_class_of_every_producer(oracle_mod):
         assert iss[i] - iss[i - 1] == 1, prod
         assert iss[i + 1] - iss[i] == lat[oracle_mod.LAT_NAMES.index(cls)], (prod, cls)
     assert len(iss) == first + 2 * len(S.LATENCY_PAIRS) + 1  # and the ret
+
+
+@pytest.mark.parametrize("block", [64, 256, 1024])
+def test_block_reduce_closed_form(oracle_mod, block):
+    """The shared-memory tree reduction (workloads.small.block_reduce_ptx): each
+    block's output is the wrapping sum of its inputs; only warp 0 diverges, at the
+    five steps with s < 32 and at the final t == 0 branch; every thread passes
+    1 + log2(block) barriers; every shared access has bank degree 1 (stride 1)."""
+    import struct
+    grid = 8
+    data = np.random.default_rng(11).integers(0, 1 << 32, size=grid * block, dtype=np.uint32)
+    out = 4 * grid * block
+    g = np.zeros(out + 4 * grid, np.uint8)
+    g[:out] = data.view(np.uint8)
+    co, _, _ = oracle_mod.run(S.block_reduce_ptx(block), (grid, 1, 1), (block, 1, 1), struct.pack("<QQ", 0, out), g,
+                              trace_cap=0)
+    exp = (data.reshape(grid, block).astype(np.uint64).sum(axis=1) % (1 << 32)).astype(np.uint32)
+    assert np.array_equal(g[out:].view(np.uint32), exp)
+    wpb = block // 32
+    warp0 = (np.arange(len(co)) % wpb) == 0
+    assert (co["diverge_n"][warp0] == 6).all() and (co["diverge_n"][~warp0] == 0).all()
+    assert (co["barrier_n"] == 1 + int(np.log2(block))).all()
+    assert (co["sh_degree_max"] == 1).all() and (co["fault_n"] == 0).all()

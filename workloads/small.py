@@ -362,3 +362,32 @@ def latency_classes_ptx() -> str:
     return HEADER + (".visible .entry latency_classes(\n    .param .u64 param_p,\n    .param .u32 param_q\n)\n{\n"
                      "    .reg .pred %p<2>;\n    .reg .b32 %r<13>;\n    .reg .b64 %rd<11>;\n    .reg .f32 %f<11>;\n"
                      "    .shared .align 8 .b8 sm[64];\n") + "".join("    %s\n" % x for x in pro + body + ["ret;"]) + "}\n"
+
+
+def block_reduce_ptx(block: int = 256) -> str:
+    """A shared-memory tree reduction of u32 words over `block` (a power of two)
+    threads: thread t loads in[gid] into sm[t]; then, for s = block/2 .. 1, the
+    threads t < s add sm[t + s] into sm[t] behind a branch (divergent once s < 32)
+    and every thread meets at a bar.sync; thread 0 stores sm[0] to out[blockid].
+    The steps are unrolled (the subset has no shifts)."""
+    assert block & (block - 1) == 0 and 2 <= block <= 1024
+    L = [HEADER + ".visible .entry block_reduce(\n    .param .u64 param_in,\n    .param .u64 param_out\n)\n{",
+         "    .reg .pred %p<2>;", "    .reg .b32 %r<12>;", "    .reg .b64 %rd<8>;",
+         "    .shared .align 4 .b8 sm[%d];" % (4 * block),
+         "    ld.param.u64 %rd1, [param_in];", "    ld.param.u64 %rd2, [param_out];",
+         "    mov.u32 %r1, %tid.x;", "    mov.u32 %r2, %ctaid.x;", "    mov.u32 %r3, %ntid.x;",
+         "    mad.lo.s32 %r4, %r2, %r3, %r1;", "    mul.wide.u32 %rd3, %r4, 4;", "    add.s64 %rd4, %rd1, %rd3;",
+         "    ld.global.u32 %r5, [%rd4];", "    mov.u32 %r6, sm;", "    mul.lo.s32 %r7, %r1, 4;",
+         "    add.s32 %r8, %r6, %r7;", "    st.shared.u32 [%r8], %r5;", "    bar.sync 0;"]
+    s, k = block // 2, 0
+    while s >= 1:
+        L += ["    setp.ge.u32 %%p1, %%r1, %d;" % s, "    @%%p1 bra $L__s%d;" % k,
+              "    ld.shared.u32 %%r9, [%%r8+%d];" % (4 * s), "    ld.shared.u32 %r10, [%r8];",
+              "    add.s32 %r10, %r10, %r9;", "    st.shared.u32 [%r8], %r10;",
+              "$L__s%d:" % k, "    bar.sync 0;"]
+        s //= 2
+        k += 1
+    L += ["    setp.ne.u32 %p1, %r1, 0;", "    @%p1 bra $L__end;", "    ld.shared.u32 %r11, [%r6];",
+          "    mul.wide.u32 %rd5, %r2, 4;", "    add.s64 %rd6, %rd2, %rd5;", "    st.global.u32 [%rd6], %r11;",
+          "$L__end:", "    ret;", "}"]
+    return "\n".join(L) + "\n"

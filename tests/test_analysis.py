@@ -326,3 +326,25 @@ def test_param_block_uses_the_library_layout(A):
         A.param_block(W.VECTOR_ADD_PTX, {"param_n": 1 << 32})
     with pytest.raises(ValueError, match="a float needs 4"):
         A.param_block(W.VECTOR_ADD_PTX, {"param_a": 0.5})
+
+
+@pytest.mark.parametrize("pad", [0, 1])
+def test_transpose_bank_conflict_hint(A, oracle_mod, pad):
+    """On the shared-tile transpose the hint rules flag the unpadded tile's column
+    load (degree 32, critical) in every warp, and nothing once the tile is padded."""
+    gx = 2
+    n = 32 * gx
+    g = np.zeros(8 * n * n, np.uint8)
+    g[:4 * n * n] = np.arange(n * n, dtype=np.uint32).view(np.uint8)
+    w = W.Workload(name="tile_transpose", ptx=S.tile_transpose_ptx(pad), grid=(gx, gx, 1), block=(32, 32, 1),
+                   params=[("param_in", "u64", 0), ("param_out", "u64", 4 * n * n)], gmem=g, trace_cap=64)
+    _, (hdr, rec) = ext(oracle_mod, w)
+    info = A.ProgramInfo(w.ptx)
+    hs = A.hints(hdr, rec, info, warps_per_block=w.warps_per_block)
+    per_event = [h for h in hs if "warp" in h and "bank-conflict degree" in h["message"]]
+    if pad:
+        assert per_event == []
+    else:
+        assert len(per_event) == w.n_warps
+        assert all(h["degree"] == 32 and h["severity"] == "critical" for h in per_event)
+        assert all(info.text(h["pc"]).startswith("ld.shared") for h in per_event)

@@ -259,6 +259,21 @@ def test_block_reduce(K, oracle_mod, block):
     full_parity(K, oracle_mod, w)
 
 
+@pytest.mark.parametrize("pad", [0, 1])
+def test_tile_transpose(K, oracle_mod, pad):
+    """A shared-tile transpose on 32 x 32 blocks over a 4 x 4 grid, with 32-way bank
+    conflicts on the unpadded tile's column loads and none on the padded one."""
+    gx = 4
+    n = 32 * gx
+    g = np.zeros(8 * n * n, np.uint8)
+    g[:4 * n * n] = np.random.default_rng(pad).integers(0, 1 << 32, size=n * n, dtype=np.uint32).view(np.uint8)
+    w = W.Workload(name="tile_transpose_pad%d" % pad, ptx=S.tile_transpose_ptx(pad), grid=(gx, gx, 1),
+                   block=(32, 32, 1), params=[("param_in", "u64", 0), ("param_out", "u64", 4 * n * n)], gmem=g,
+                   trace_cap=64)
+    cg = full_parity(K, oracle_mod, w)
+    assert (cg["sh_degree_max"] == (32 if pad == 0 else 1)).all()
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

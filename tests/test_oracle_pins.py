@@ -790,3 +790,26 @@ def test_block_reduce_closed_form(oracle_mod, block):
     assert (co["diverge_n"][warp0] == 6).all() and (co["diverge_n"][~warp0] == 0).all()
     assert (co["barrier_n"] == 1 + int(np.log2(block))).all()
     assert (co["sh_degree_max"] == 1).all() and (co["fault_n"] == 0).all()
+
+
+@pytest.mark.parametrize("pad", [0, 1])
+def test_tile_transpose_closed_form(oracle_mod, pad):
+    """The shared-tile transpose (workloads.small.tile_transpose_ptx): out is the
+    exact transpose; the tile's row store is stride 1 (degree 1) and its column
+    load is stride 32 + pad words, degree 32 without padding and 1 with it; both
+    global sides stay coalesced (4 sectors, 1 line per warp access)."""
+    import struct
+    gx = 3
+    n = 32 * gx
+    data = np.random.default_rng(5).integers(0, 1 << 32, size=n * n, dtype=np.uint32)
+    g = np.zeros(8 * n * n, np.uint8)
+    g[:4 * n * n] = data.view(np.uint8)
+    co, _, _ = oracle_mod.run(S.tile_transpose_ptx(pad), (gx, gx, 1), (32, 32, 1),
+                              struct.pack("<QQ", 0, 4 * n * n), g, trace_cap=0)
+    assert np.array_equal(g[4 * n * n:].view(np.uint32).reshape(n, n), data.reshape(n, n).T)
+    assert (co["sh_n"] == 2).all()
+    assert (co["sh_degree_max"] == (32 if pad == 0 else 1)).all()
+    assert (co["sh_degree_sum"] == (33 if pad == 0 else 2)).all()
+    for f in ("gld_sectors", "gst_sectors"):
+        assert (co[f] == 4).all(), f
+    assert (co["gld_lines"] == 1).all() and (co["gst_lines"] == 1).all()

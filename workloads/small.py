@@ -391,3 +391,54 @@ def block_reduce_ptx(block: int = 256) -> str:
           "    mul.wide.u32 %rd5, %r2, 4;", "    add.s64 %rd6, %rd2, %rd5;", "    st.global.u32 [%rd6], %r11;",
           "$L__end:", "    ret;", "}"]
     return "\n".join(L) + "\n"
+
+
+def tile_transpose_ptx(pad: int = 0) -> str:
+    """out = in transposed, for an n x n u32 matrix (n = 32 * grid.x, grid square)
+    through a 32 x (32 + pad) shared tile, on 32 x 32 blocks: thread (x, y) of block
+    (bx, by) stores in[32 by + y][32 bx + x] at tile[y][x] (a row: stride 1), meets
+    the others at a bar.sync, and writes tile[x][y] (a column: stride 32 + pad
+    words, so 32-way bank conflicts when pad = 0, none when pad = 1) to
+    out[32 bx + y][32 by + x]."""
+    row = 32 + pad
+    return HEADER + """\
+.visible .entry tile_transpose(
+    .param .u64 param_in,
+    .param .u64 param_out
+)
+{
+    .reg .b32 %%r<20>;
+    .reg .b64 %%rd<8>;
+    .shared .align 4 .b8 tile[%d];
+
+    ld.param.u64 %%rd1, [param_in];
+    ld.param.u64 %%rd2, [param_out];
+    mov.u32 %%r1, %%tid.x;
+    mov.u32 %%r2, %%tid.y;
+    mov.u32 %%r3, %%ctaid.x;
+    mov.u32 %%r4, %%ctaid.y;
+    mov.u32 %%r5, %%nctaid.x;
+    mul.lo.s32 %%r6, %%r5, 32;
+    mad.lo.s32 %%r7, %%r4, 32, %%r2;
+    mad.lo.s32 %%r8, %%r3, 32, %%r1;
+    mad.lo.s32 %%r9, %%r7, %%r6, %%r8;
+    mul.wide.u32 %%rd3, %%r9, 4;
+    add.s64 %%rd4, %%rd1, %%rd3;
+    ld.global.u32 %%r10, [%%rd4];
+    mov.u32 %%r11, tile;
+    mad.lo.s32 %%r12, %%r2, %d, %%r1;
+    mad.lo.s32 %%r13, %%r12, 4, %%r11;
+    st.shared.u32 [%%r13], %%r10;
+    bar.sync 0;
+    mad.lo.s32 %%r14, %%r1, %d, %%r2;
+    mad.lo.s32 %%r15, %%r14, 4, %%r11;
+    ld.shared.u32 %%r16, [%%r15];
+    mad.lo.s32 %%r17, %%r3, 32, %%r2;
+    mad.lo.s32 %%r18, %%r4, 32, %%r1;
+    mad.lo.s32 %%r19, %%r17, %%r6, %%r18;
+    mul.wide.u32 %%rd5, %%r19, 4;
+    add.s64 %%rd6, %%rd2, %%rd5;
+    st.global.u32 [%%rd6], %%r16;
+    ret;
+}
+""" % (4 * 32 * row, row, row)

@@ -274,6 +274,20 @@ def test_tile_transpose(K, oracle_mod, pad):
     assert (cg["sh_degree_max"] == (32 if pad == 0 else 1)).all()
 
 
+def test_stencil3(K, oracle_mod):
+    """A 3-point stencil over a ragged n: branches at both ends and past n, loads
+    that straddle 128-byte lines."""
+    n, block = 100003, 256
+    data = np.random.default_rng(17).integers(0, 1 << 32, size=n, dtype=np.uint32)
+    off = (4 * n + 4095) // 4096 * 4096
+    g = np.zeros(off + 4 * n, np.uint8)
+    g[:4 * n] = data.view(np.uint8)
+    w = W.Workload(name="stencil3", ptx=S.stencil3_ptx(), grid=((n + block - 1) // block, 1, 1), block=(block, 1, 1),
+                   params=[("param_in", "u64", 0), ("param_out", "u64", off), ("param_n", "u32", n)], gmem=g,
+                   trace_cap=32)
+    full_parity(K, oracle_mod, w)
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

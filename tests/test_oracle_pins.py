@@ -813,3 +813,30 @@ def test_tile_transpose_closed_form(oracle_mod, pad):
     for f in ("gld_sectors", "gst_sectors"):
         assert (co[f] == 4).all(), f
     assert (co["gld_lines"] == 1).all() and (co["gst_lines"] == 1).all()
+
+
+def test_stencil3_closed_form(oracle_mod):
+    """The 3-point stencil (workloads.small.stencil3_ptx) over n = 1000 on 128-thread
+    blocks: out = in[i-1] + in[i] + in[i+1] inside, in[i] at the ends.  An interior
+    warp's three loads cover 4 + 5 + 5 sectors and 1 + 2 + 2 lines (the shifted
+    loads straddle a 128-byte line), its store 4 sectors in 1 line; warp 0 leaves
+    lane 0 out of the shifted loads (13 sectors, 4 lines, one divergence); the last
+    warp, with 8 live threads of which the last is an end, counts 4 sectors, 4 lines
+    and two divergences."""
+    import struct
+    n, block = 1000, 128
+    data = np.random.default_rng(3).integers(0, 1 << 32, size=n, dtype=np.uint32)
+    off = 8192
+    g = np.zeros(off + 4 * n, np.uint8)
+    g[:4 * n] = data.view(np.uint8)
+    co, _, _ = oracle_mod.run(S.stencil3_ptx(), ((n + block - 1) // block, 1, 1), (block, 1, 1),
+                              struct.pack("<QQI", 0, off, n), g, trace_cap=0)
+    d = data.astype(np.uint64)
+    exp = d.copy()
+    exp[1:-1] = (d[:-2] + d[1:-1] + d[2:]) % (1 << 32)
+    assert np.array_equal(g[off:].view(np.uint32), exp.astype(np.uint32))
+    row = lambda k: tuple(int(co[f][k]) for f in ("gld_n", "gld_sectors", "gld_lines", "gst_n", "gst_sectors",
+                                                  "gst_lines", "diverge_n"))
+    assert row(0) == (3, 13, 4, 1, 4, 1, 1)
+    assert all(row(k) == (3, 14, 5, 1, 4, 1, 0) for k in range(1, 31))
+    assert row(31) == (3, 4, 4, 1, 1, 1, 2)

@@ -442,3 +442,49 @@ def tile_transpose_ptx(pad: int = 0) -> str:
     ret;
 }
 """ % (4 * 32 * row, row, row)
+
+
+def stencil3_ptx() -> str:
+    """out[i] = in[i-1] + in[i] + in[i+1] (u32, wrapping) for 0 < i < n-1 and
+    out[i] = in[i] at the two ends, one thread per i (threads at i >= n do
+    nothing).  The boundary threads take a branch of their own, and the shifted
+    loads straddle 128-byte lines."""
+    return HEADER + """\
+.visible .entry stencil3(
+    .param .u64 param_in,
+    .param .u64 param_out,
+    .param .u32 param_n
+)
+{
+    .reg .pred %p<3>;
+    .reg .b32 %r<12>;
+    .reg .b64 %rd<8>;
+
+    ld.param.u64 %rd1, [param_in];
+    ld.param.u64 %rd2, [param_out];
+    ld.param.u32 %r1, [param_n];
+    mov.u32 %r2, %tid.x;
+    mov.u32 %r3, %ctaid.x;
+    mov.u32 %r4, %ntid.x;
+    mad.lo.s32 %r5, %r3, %r4, %r2;
+    setp.ge.u32 %p1, %r5, %r1;
+    @%p1 bra $L__done;
+    mul.wide.u32 %rd3, %r5, 4;
+    add.s64 %rd4, %rd1, %rd3;
+    add.s64 %rd5, %rd2, %rd3;
+    ld.global.u32 %r6, [%rd4];
+    add.s32 %r7, %r1, -1;
+    setp.eq.u32 %p1, %r5, 0;
+    setp.eq.u32 %p2, %r5, %r7;
+    @%p1 bra $L__edge;
+    @%p2 bra $L__edge;
+    ld.global.u32 %r8, [%rd4+-4];
+    ld.global.u32 %r9, [%rd4+4];
+    add.s32 %r10, %r8, %r6;
+    add.s32 %r6, %r10, %r9;
+$L__edge:
+    st.global.u32 [%rd5], %r6;
+$L__done:
+    ret;
+}
+"""

@@ -288,6 +288,22 @@ def test_stencil3(K, oracle_mod):
     full_parity(K, oracle_mod, w)
 
 
+def test_lcg64(K, oracle_mod):
+    """64-bit integer forms in a loop (mad/mul/add/sub.u64, 64-bit setp and selp,
+    u64 loads and stores) over 6080 threads (the program has no bounds check, so
+    the grid covers the arrays exactly: extra threads would write into the flags
+    and race with their owners)."""
+    nt, block = 6080, 160
+    seeds = np.random.default_rng(21).integers(0, 1 << 64, size=nt, dtype=np.uint64)
+    so, oo, fo = 0, 8 * nt, 32 * nt
+    g = np.zeros(fo + 4 * nt, np.uint8)
+    g[:8 * nt] = seeds.view(np.uint8)
+    w = W.Workload(name="lcg64", ptx=S.lcg64_ptx(), grid=((nt + block - 1) // block, 1, 1), block=(block, 1, 1),
+                   params=[("param_seeds", "u64", so), ("param_out", "u64", oo), ("param_flags", "u64", fo)],
+                   gmem=g, trace_cap=64)
+    full_parity(K, oracle_mod, w)
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

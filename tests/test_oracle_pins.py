@@ -840,3 +840,57 @@ def test_stencil3_closed_form(oracle_mod):
     assert row(0) == (3, 13, 4, 1, 4, 1, 1)
     assert all(row(k) == (3, 14, 5, 1, 4, 1, 0) for k in range(1, 31))
     assert row(31) == (3, 4, 4, 1, 1, 1, 2)
+
+
+def test_lcg64_against_numpy(oracle_mod):
+    """64-bit integer forms (workloads.small.lcg64_ptx): mad.lo.u64 iterated in a
+    loop, mul.lo/add/sub.u64, unsigned and signed 64-bit setp, selp.b64 and u64
+    loads and stores equal numpy's wrapping uint64 arithmetic; the signed and
+    unsigned compares disagree on part of the threads, so both are exercised."""
+    import struct
+    nt, block = 512, 128
+    seeds = np.random.default_rng(9).integers(0, 1 << 63, size=nt, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+    so, oo, fo = 0, 8 * nt, 32 * nt
+    g = np.zeros(fo + 4 * nt, np.uint8)
+    g[:8 * nt] = seeds.view(np.uint8)
+    oracle_mod.run(S.lcg64_ptx(), (nt // block, 1, 1), (block, 1, 1), struct.pack("<QQQ", so, oo, fo), g, trace_cap=0)
+    a, c = np.uint64(6364136223846793005), np.uint64(1442695040888963407)
+    with np.errstate(over="ignore"):
+        x = seeds.copy()
+        for _ in range(37):
+            x = x * a + c
+        y = x * x + x - c
+    out = g[oo:fo].view(np.uint64).reshape(nt, 3)
+    assert np.array_equal(out[:, 0], x) and np.array_equal(out[:, 1], y)
+    assert np.array_equal(out[:, 2], np.where(x < y, x, y))
+    s = (x.view(np.int64) < y.view(np.int64)).astype(np.uint32)
+    assert np.array_equal(g[fo:].view(np.uint32), s)
+    assert (s != (x < y)).any()
+
+
+def test_extra_workloads_are_race_free(oracle_mod):
+    """The race checker passes the reduction, transpose, stencil, 64-bit and
+    shared-edge programs at the shapes their tests use, and catches the 64-bit
+    program on a grid larger than its arrays (its extra threads write the flags of
+    others: the case the GPU parity test must avoid).  (The latency-class program
+    has every thread store one and the same value to one shared word, a race the
+    checker reports but whose result cannot depend on the order.)"""
+    import struct
+    z = lambda n: np.zeros(n, np.uint8)
+    cases = [
+        (S.block_reduce_ptx(256), (4, 1, 1), (256, 1, 1), struct.pack("<QQ", 0, 4096), z(4096 + 16)),
+        (S.tile_transpose_ptx(0), (2, 2, 1), (32, 32, 1), struct.pack("<QQ", 0, 16384), z(32768)),
+        (S.tile_transpose_ptx(1), (2, 2, 1), (32, 32, 1), struct.pack("<QQ", 0, 16384), z(32768)),
+        (S.stencil3_ptx(), (4, 1, 1), (128, 1, 1), struct.pack("<QQI", 0, 4096, 500), z(8192)),
+        (S.lcg64_ptx(4), (2, 1, 1), (160, 1, 1), struct.pack("<QQQ", 0, 2560, 10240), z(10240 + 1280)),
+        (S.shared_edges_ptx(), (1, 1, 1), (256, 1, 1), struct.pack("<Q", 0), z(8192)),
+    ]
+    for ptx, grid, block, params, g in cases:
+        _, _, rc = oracle_mod.run(ptx, grid, block, params, g, check_races=True)
+        assert rc == 0, ptx.split("(")[0][-40:]
+    # 300 threads' arrays on a 320-thread grid: threads 300..319 write over flags 0..119
+    nt = 300
+    g = z(32 * nt + 4 * nt)
+    _, _, rc = oracle_mod.run(S.lcg64_ptx(4), (2, 1, 1), (160, 1, 1), struct.pack("<QQQ", 0, 8 * nt, 32 * nt), g,
+                              check_races=True)
+    assert rc == oracle_mod.E_RACE

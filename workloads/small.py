@@ -488,3 +488,58 @@ $L__done:
     ret;
 }
 """
+
+
+def lcg64_ptx(iters: int = 37) -> str:
+    """64-bit integer work per thread: x = seeds[gid] (u64), then `iters` times
+    x = x * A + C (mad.lo.u64, A = 6364136223846793005, C = 1442695040888963407);
+    then y = x * x + x - C, z = (x < y unsigned) ? x : y, s = (x < y signed) ? 1 : 0;
+    out[3 gid .. 3 gid + 2] = x, y, z (u64) and flags[gid] = s (u32).  There is no
+    bounds check: the grid must cover the arrays exactly."""
+    return HEADER + """\
+.visible .entry lcg64(
+    .param .u64 param_seeds,
+    .param .u64 param_out,
+    .param .u64 param_flags
+)
+{
+    .reg .pred %%p<3>;
+    .reg .b32 %%r<8>;
+    .reg .b64 %%rd<16>;
+
+    ld.param.u64 %%rd1, [param_seeds];
+    ld.param.u64 %%rd2, [param_out];
+    ld.param.u64 %%rd3, [param_flags];
+    mov.u32 %%r1, %%tid.x;
+    mov.u32 %%r2, %%ctaid.x;
+    mov.u32 %%r3, %%ntid.x;
+    mad.lo.s32 %%r4, %%r2, %%r3, %%r1;
+    mul.wide.u32 %%rd4, %%r4, 8;
+    add.s64 %%rd5, %%rd1, %%rd4;
+    ld.global.u64 %%rd6, [%%rd5];
+    mov.u64 %%rd7, 6364136223846793005;
+    mov.u64 %%rd8, 1442695040888963407;
+    mov.u32 %%r5, 0;
+$L__loop:
+    mad.lo.u64 %%rd6, %%rd6, %%rd7, %%rd8;
+    add.s32 %%r5, %%r5, 1;
+    setp.lt.s32 %%p1, %%r5, %d;
+    @%%p1 bra $L__loop;
+    mul.lo.u64 %%rd9, %%rd6, %%rd6;
+    add.u64 %%rd9, %%rd9, %%rd6;
+    sub.u64 %%rd9, %%rd9, %%rd8;
+    setp.lt.u64 %%p1, %%rd6, %%rd9;
+    selp.b64 %%rd10, %%rd6, %%rd9, %%p1;
+    setp.lt.s64 %%p2, %%rd6, %%rd9;
+    selp.b32 %%r6, 1, 0, %%p2;
+    mul.wide.u32 %%rd11, %%r4, 24;
+    add.s64 %%rd12, %%rd2, %%rd11;
+    st.global.u64 [%%rd12], %%rd6;
+    st.global.u64 [%%rd12+8], %%rd9;
+    st.global.u64 [%%rd12+16], %%rd10;
+    mul.wide.u32 %%rd13, %%r4, 4;
+    add.s64 %%rd14, %%rd3, %%rd13;
+    st.global.u32 [%%rd14], %%r6;
+    ret;
+}
+""" % iters

@@ -304,6 +304,17 @@ def test_lcg64(K, oracle_mod):
     full_parity(K, oracle_mod, w)
 
 
+def test_setp_forms(K, oracle_mod):
+    """The unsigned setp mnemonics, eq/ne on .bN, 64-bit compares and the .u32
+    multiply forms over 8192 threads with equal and adjacent input pairs."""
+    nt = 8192
+    a, b, c, d, offs, g = S.setp_forms_inputs(nt, 31)
+    w = W.Workload(name="setp_forms", ptx=S.setp_forms_ptx(), grid=(nt // 256, 1, 1), block=(256, 1, 1),
+                   params=[(n, "u64", o) for n, o in zip(("param_a", "param_b", "param_c", "param_d", "param_out"),
+                                                           offs)], gmem=g, trace_cap=32)
+    full_parity(K, oracle_mod, w)
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

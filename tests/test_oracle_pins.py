@@ -894,3 +894,24 @@ def test_extra_workloads_are_race_free(oracle_mod):
     _, _, rc = oracle_mod.run(S.lcg64_ptx(4), (2, 1, 1), (160, 1, 1), struct.pack("<QQQ", 0, 8 * nt, 32 * nt), g,
                               check_races=True)
     assert rc == oracle_mod.E_RACE
+
+
+def test_setp_forms_against_numpy(oracle_mod):
+    """The unsigned setp mnemonics (lo ls hi hs), eq/ne on .b32 and .b64, 64-bit
+    unsigned compares and the .u32 forms of mul.lo and mad.lo, one flag bit per
+    comparison (workloads.small.setp_forms_ptx), against numpy over inputs with
+    equal and adjacent pairs; every bit is set for some threads and clear for others."""
+    import struct
+    nt = 1024
+    a, b, c, d, offs, g = S.setp_forms_inputs(nt, 4)
+    oracle_mod.run(S.setp_forms_ptx(), (nt // 256, 1, 1), (256, 1, 1), struct.pack("<5Q", *offs), g, trace_cap=0)
+    out = offs[4]
+    sa, sb = a.view(np.int32), b.view(np.int32)
+    bits = [a < b, a <= b, a > b, a >= b, a == b, a != b, c < d, c >= d, c == d, c != d, sa <= sb, a >= b]
+    assert len(bits) == len(S.SETP_FORMS)
+    exp = sum(e.astype(np.uint32) << k for k, e in enumerate(bits)).astype(np.uint32)
+    assert np.array_equal(g[out:out + 4 * nt].view(np.uint32), exp)
+    assert all(0 < e.mean() < 1 for e in bits)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(g[out + 65536:out + 65536 + 4 * nt].view(np.uint32), a * b)
+        assert np.array_equal(g[out + 131072:out + 131072 + 4 * nt].view(np.uint32), a * b + a)

@@ -543,3 +543,59 @@ $L__loop:
     ret;
 }
 """ % iters
+
+
+# (setp form, operands): the comparisons of setp_forms_ptx, result bit k of flags[i]
+SETP_FORMS = [("setp.lo.u32", "%r1, %r2"), ("setp.ls.u32", "%r1, %r2"), ("setp.hi.u32", "%r1, %r2"),
+              ("setp.hs.u32", "%r1, %r2"), ("setp.eq.b32", "%r1, %r2"), ("setp.ne.b32", "%r1, %r2"),
+              ("setp.lo.u64", "%rd7, %rd8"), ("setp.hs.u64", "%rd7, %rd8"), ("setp.eq.b64", "%rd7, %rd8"),
+              ("setp.ne.b64", "%rd7, %rd8"), ("setp.le.s32", "%r1, %r2"), ("setp.ge.u32", "%r1, %r2")]
+
+
+def setp_forms_ptx() -> str:
+    """Per thread i: a = A[i], b = B[i] (u32) and c = C[i], d = D[i] (u64); flags[i]
+    gets bit k set when comparison k of SETP_FORMS holds; prod[i] = a * b
+    (mul.lo.u32) and fma[i] = a * b + a (mad.lo.u32).  Arrays: A, B at 4 i, C, D at
+    8 i from their bases; flags at out + 4 i, prod at out + 65536 + 4 i, fma at
+    out + 131072 + 4 i."""
+    L = [HEADER + ".visible .entry setp_forms(\n    .param .u64 param_a,\n    .param .u64 param_b,\n"
+         "    .param .u64 param_c,\n    .param .u64 param_d,\n    .param .u64 param_out\n)\n{",
+         "    .reg .pred %p<2>;", "    .reg .b32 %r<12>;", "    .reg .b64 %rd<16>;",
+         "    ld.param.u64 %rd1, [param_a];", "    ld.param.u64 %rd2, [param_b];",
+         "    ld.param.u64 %rd3, [param_c];", "    ld.param.u64 %rd4, [param_d];",
+         "    ld.param.u64 %rd5, [param_out];",
+         "    mov.u32 %r3, %tid.x;", "    mov.u32 %r4, %ctaid.x;", "    mov.u32 %r5, %ntid.x;",
+         "    mad.lo.u32 %r6, %r4, %r5, %r3;", "    mul.wide.u32 %rd6, %r6, 4;", "    mul.wide.u32 %rd9, %r6, 8;",
+         "    add.s64 %rd10, %rd1, %rd6;", "    ld.global.u32 %r1, [%rd10];",
+         "    add.s64 %rd10, %rd2, %rd6;", "    ld.global.u32 %r2, [%rd10];",
+         "    add.s64 %rd10, %rd3, %rd9;", "    ld.global.u64 %rd7, [%rd10];",
+         "    add.s64 %rd10, %rd4, %rd9;", "    ld.global.u64 %rd8, [%rd10];",
+         "    mov.u32 %r7, 0;"]
+    for k, (form, ops) in enumerate(SETP_FORMS):
+        L += ["    %s %%p1, %s;" % (form, ops), "    selp.b32 %%r8, %d, 0, %%p1;" % (1 << k),
+              "    add.s32 %r7, %r7, %r8;"]
+    L += ["    mul.lo.u32 %r9, %r1, %r2;", "    mad.lo.u32 %r10, %r1, %r2, %r1;",
+          "    add.s64 %rd11, %rd5, %rd6;", "    st.global.u32 [%rd11], %r7;",
+          "    add.s64 %rd13, %rd5, 65536;", "    add.s64 %rd14, %rd13, %rd6;",
+          "    st.global.u32 [%rd14], %r9;", "    add.s64 %rd15, %rd14, 65536;", "    st.global.u32 [%rd15], %r10;",
+          "    ret;", "}"]
+    return "\n".join(L) + "\n"
+
+
+def setp_forms_inputs(nt: int, seed: int):
+    """Seeded inputs of setp_forms_ptx for nt threads: u32 a, b with every fourth
+    pair equal and every eighth (from 1) adjacent, u64 c, d with every third pair
+    equal; returns (a, b, c, d, the five parameter offsets, the memory image)."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 1 << 32, size=nt, dtype=np.uint32)
+    b = rng.integers(0, 1 << 32, size=nt, dtype=np.uint32)
+    b[::4] = a[::4]
+    b[1::8] = a[1::8] + np.uint32(1)
+    c = rng.integers(0, 1 << 64, size=nt, dtype=np.uint64)
+    d = rng.integers(0, 1 << 64, size=nt, dtype=np.uint64)
+    d[::3] = c[::3]
+    offs = (0, 8 * nt, 16 * nt, 32 * nt, 48 * nt)
+    g = np.zeros(offs[4] + 3 * 65536, np.uint8)
+    for arr, o in zip((a, b, c, d), offs):
+        g[o:o + arr.nbytes] = arr.view(np.uint8)
+    return a, b, c, d, offs, g

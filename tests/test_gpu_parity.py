@@ -315,6 +315,19 @@ def test_setp_forms(K, oracle_mod):
     full_parity(K, oracle_mod, w)
 
 
+def test_f32_setp(K, oracle_mod):
+    """setp.*.f32 and selp.f32 over the f32 edge values and random patterns."""
+    ops = S.f32_operands(16384, 13)[:, :2].copy()
+    n = len(ops)
+    out = 8 * n + 4096
+    g = np.zeros(out + 65536 + 4 * n, np.uint8)
+    g[:8 * n] = ops.reshape(-1).view(np.uint8)
+    w = W.Workload(name="f32_setp", ptx=S.f32_setp_ptx(), grid=((n + 255) // 256, 1, 1), block=(256, 1, 1),
+                   params=[("param_in", "u64", 0), ("param_out", "u64", out), ("param_n", "u32", n)], gmem=g,
+                   trace_cap=16)
+    full_parity(K, oracle_mod, w)
+
+
 def test_single_ret_program(K, oracle_mod):
     """The smallest program (a lone ret, no parameters) on 33-thread blocks: a full
     warp and a one-lane warp per block."""

@@ -915,3 +915,27 @@ def test_setp_forms_against_numpy(oracle_mod):
     with np.errstate(over="ignore"):
         assert np.array_equal(g[out + 65536:out + 65536 + 4 * nt].view(np.uint32), a * b)
         assert np.array_equal(g[out + 131072:out + 131072 + 4 * nt].view(np.uint32), a * b + a)
+
+
+def test_f32_setp_against_numpy(oracle_mod):
+    """setp.{eq,ne,lt,le,gt,ge}.f32 and selp.f32 (workloads.small.f32_setp_ptx) over
+    the edge-value crossing (NaN, +-0, +-inf, subnormals, extremes) and random
+    patterns, against numpy's comparisons with the ordered reading: every
+    comparison, ne included, is false when an operand is NaN; +0 == -0."""
+    import struct
+    ops = S.f32_operands(4096, 7)[:, :2].copy()
+    n = len(ops)
+    out = 8 * n + 4096
+    g = np.zeros(out + 65536 + 4 * n, np.uint8)
+    g[:8 * n] = ops.reshape(-1).view(np.uint8)
+    oracle_mod.run(S.f32_setp_ptx(), ((n + 255) // 256, 1, 1), (256, 1, 1), struct.pack("<QQI", 0, out, n), g,
+                   trace_cap=0)
+    a, b = ops[:, 0].view(np.float32), ops[:, 1].view(np.float32)
+    nan = np.isnan(a) | np.isnan(b)
+    assert nan.any() and ((a == 0) & (b == 0) & (ops[:, 0] != ops[:, 1])).any()  # NaNs and +0 vs -0 occur
+    with np.errstate(invalid="ignore"):
+        bits = [a == b, (a != b) & ~nan, a < b, a <= b, a > b, a >= b]
+        pick = np.where(a < b, ops[:, 0], ops[:, 1])
+    exp = sum(e.astype(np.uint32) << k for k, e in enumerate(bits)).astype(np.uint32)
+    assert np.array_equal(g[out:out + 4 * n].view(np.uint32), exp)
+    assert np.array_equal(g[out + 65536:out + 65536 + 4 * n].view(np.uint32), pick)

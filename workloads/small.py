@@ -599,3 +599,28 @@ def setp_forms_inputs(nt: int, seed: int):
     for arr, o in zip((a, b, c, d), offs):
         g[o:o + arr.nbytes] = arr.view(np.uint8)
     return a, b, c, d, offs, g
+
+
+F32_SETP = ["eq", "ne", "lt", "le", "gt", "ge"]
+
+
+def f32_setp_ptx() -> str:
+    """Per thread i: a, b = in[2 i], in[2 i + 1] (f32 bit patterns); flags[i] gets
+    bit k set when setp.<F32_SETP[k]>.f32 a, b holds (ordered: false whenever an
+    operand is NaN), and pick[i] = selp.f32 of a or b on a < b.  flags at out + 4 i,
+    pick at out + 65536 + 4 i; threads at i >= n do nothing."""
+    L = [HEADER + ".visible .entry f32_setp(\n    .param .u64 param_in,\n    .param .u64 param_out,\n"
+         "    .param .u32 param_n\n)\n{",
+         "    .reg .pred %p<3>;", "    .reg .b32 %r<10>;", "    .reg .f32 %f<4>;", "    .reg .b64 %rd<8>;",
+         "    ld.param.u64 %rd1, [param_in];", "    ld.param.u64 %rd2, [param_out];", "    ld.param.u32 %r1, [param_n];",
+         "    mov.u32 %r2, %tid.x;", "    mov.u32 %r3, %ctaid.x;", "    mov.u32 %r4, %ntid.x;",
+         "    mad.lo.s32 %r5, %r3, %r4, %r2;", "    setp.ge.u32 %p2, %r5, %r1;", "    @%p2 bra $L__done;",
+         "    mul.wide.u32 %rd3, %r5, 8;", "    add.s64 %rd4, %rd1, %rd3;",
+         "    ld.global.f32 %f1, [%rd4];", "    ld.global.f32 %f2, [%rd4+4];", "    mov.u32 %r6, 0;"]
+    for k, cmp in enumerate(F32_SETP):
+        L += ["    setp.%s.f32 %%p1, %%f1, %%f2;" % cmp, "    selp.b32 %%r7, %d, 0, %%p1;" % (1 << k),
+              "    add.s32 %r6, %r6, %r7;"]
+    L += ["    setp.lt.f32 %p1, %f1, %f2;", "    selp.f32 %f3, %f1, %f2, %p1;",
+          "    mul.wide.u32 %rd5, %r5, 4;", "    add.s64 %rd6, %rd2, %rd5;", "    st.global.u32 [%rd6], %r6;",
+          "    add.s64 %rd7, %rd6, 65536;", "    st.global.f32 [%rd7], %f3;", "$L__done:", "    ret;", "}"]
+    return "\n".join(L) + "\n"

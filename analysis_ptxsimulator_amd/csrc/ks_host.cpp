@@ -56,6 +56,7 @@ struct Tok {
   TokKind kind;
   std::string text;
   int line;
+  bool glued = false;  // follows the previous token with no space or comment between
 };
 
 bool word_start(char c) {
@@ -63,6 +64,15 @@ bool word_start(char c) {
 }
 bool word_char(char c) {
   return word_start(c) || (c >= '0' && c <= '9');
+}
+
+// A label: a letter, '_' or '$', then letters, digits, '_' or '$' (no dots).
+bool label_name(const std::string& w) {
+  if (w.empty() || !((w[0] >= 'a' && w[0] <= 'z') || (w[0] >= 'A' && w[0] <= 'Z') || w[0] == '_' || w[0] == '$'))
+    return false;
+  for (char c : w)
+    if (!(word_char(c) && c != '.' && c != '%')) return false;
+  return true;
 }
 
 // Splits the text into words (identifiers with their dots: "ld.global.f32",
@@ -76,6 +86,41 @@ std::vector<Tok> lex(const char* src, size_t len) {
     while (i < len && src[i] != '\n') ++i;
   };
   bool line_start = true;
+  size_t prev_end = (size_t)-1;  // end of the previous token
+  auto push = [&](TokKind k, std::string text, size_t at, size_t end) {
+    out.push_back({k, std::move(text), line, at == prev_end});
+    prev_end = end;
+  };
+  // The rest of a line-scoped directive: up to the end of its line with comments
+  // removed.  A block comment that spans lines ends the directive at its first
+  // newline; the text after the comment is on a later line and lexed as usual.
+  auto skip_directive_rest = [&]() {
+    while (i < len && src[i] != '\n') {
+      if (src[i] == '/' && i + 1 < len && src[i + 1] == '/') {
+        skip_line();
+        return;
+      }
+      if (src[i] == '/' && i + 1 < len && src[i + 1] == '*') {
+        size_t k = i + 2;
+        bool spans = false;
+        while (k + 1 < len && !(src[k] == '*' && src[k + 1] == '/')) {
+          if (src[k] == '\n') {
+            ++line;
+            spans = true;
+          }
+          ++k;
+        }
+        if (k + 1 >= len) raise(KS_E_PARSE, line, "unterminated comment");
+        i = k + 2;
+        if (spans) {
+          line_start = true;
+          return;
+        }
+        continue;
+      }
+      ++i;
+    }
+  };
   while (i < len) {
     char c = src[i];
     if (c == '\n') {
@@ -95,7 +140,10 @@ std::vector<Tok> lex(const char* src, size_t len) {
     if (c == '/' && i + 1 < len && src[i + 1] == '*') {
       i += 2;
       while (i + 1 < len && !(src[i] == '*' && src[i + 1] == '/')) {
-        if (src[i] == '\n') ++line;
+        if (src[i] == '\n') {
+          ++line;
+          line_start = true;  // what follows the comment starts its line
+        }
         ++i;
       }
       if (i + 1 >= len) raise(KS_E_PARSE, line, "unterminated comment");
@@ -109,41 +157,39 @@ std::vector<Tok> lex(const char* src, size_t len) {
       while (j < len && word_char(src[j])) ++j;
       std::string w(src + i, j - i);
       if (at_line_start && (w == ".loc" || w == ".file" || w == ".section")) {
-        i = j;
-        skip_line();
+        i = j;  // source-map directives are ignored
+        skip_directive_rest();
         continue;
       }
       if (w == ".version" || w == ".target" || w == ".address_size") {
-        // module header directive: the rest of the line is its argument
-        out.push_back({T_WORD, w, line});
+        // module header directive: the rest of its line is its argument (not used)
+        push(T_WORD, w, i, j);
         i = j;
-        size_t k = i;
-        while (k < len && src[k] != '\n') ++k;
-        std::string arg(src + i, k - i);
-        out.push_back({T_WORD, arg, line});
-        out.push_back({T_PUNCT, ";", line});
-        i = k;
+        const size_t k = i;
+        skip_directive_rest();
+        push(T_WORD, std::string(src + k, i - k), k, i);
+        push(T_PUNCT, ";", i, i);
         continue;
       }
-      out.push_back({T_WORD, w, line});
+      push(T_WORD, w, i, j);
       i = j;
       continue;
     }
     if (c >= '0' && c <= '9') {
       size_t j = i;
       while (j < len && (word_char(src[j]))) ++j;
-      out.push_back({T_NUM, std::string(src + i, j - i), line});
+      push(T_NUM, std::string(src + i, j - i), i, j);
       i = j;
       continue;
     }
     if (strchr(",;:[](){}+-@!<>", c)) {
-      out.push_back({T_PUNCT, std::string(1, c), line});
+      push(T_PUNCT, std::string(1, c), i, i + 1);
       ++i;
       continue;
     }
     raise(KS_E_PARSE, line, "unexpected character '%c'", c);
   }
-  out.push_back({T_END, "", line});
+  out.push_back({T_END, "", line, false});
   return out;
 }
 
@@ -325,12 +371,16 @@ class Front {
         TypeDesc td;
         if (ty.text.size() < 2 || !type_desc(ty.text.substr(1), td) || td.width == 1)
           raise(KS_E_UNSUPPORTED, ty.line, "unsupported parameter type '%s'", ty.text.c_str());
-        std::string nm = expect_word("parameter name").text;
+        const Tok& nt = expect_word("parameter name");
+        const std::string nm = nt.text;
         uint32_t size = (uint32_t)td.width / 8;
         off = (off + size - 1) / size * size;
         P->params.push_back({nm, off, size});
         off += size;
-        if (is_punct(",")) ++pos;
+        if (!is_punct(")")) {
+          if (!is_punct(",")) raise(KS_E_PARSE, nt.line, "expected ',' after parameter %s, got '%s'", nm.c_str(), peek().text.c_str());
+          ++pos;
+        }
       }
       ++pos;
     }
@@ -348,6 +398,8 @@ class Front {
     const Tok& t = peek();
     if (t.kind == T_PUNCT && t.text == "{") raise(KS_E_UNSUPPORTED, t.line, "nested blocks are not supported");
     if (t.kind == T_WORD && peek(1).kind == T_PUNCT && peek(1).text == ":") {
+      if (!label_name(t.text)) raise(KS_E_PARSE, t.line, "bad label name '%s'", t.text.c_str());
+      if (!peek(1).glued) raise(KS_E_PARSE, t.line, "space between label '%s' and its ':'", t.text.c_str());
       if (labels.count(t.text)) raise(KS_E_PARSE, t.line, "label '%s' defined twice", t.text.c_str());
       labels[t.text] = (int)P->code.size();
       pos += 2;
@@ -389,6 +441,7 @@ class Front {
     while (true) {
       std::string nm = expect_word("register name").text;
       if (is_punct("<")) {
+        if (!peek().glued) raise(KS_E_PARSE, line, "space between register name '%s' and its count", nm.c_str());
         ++pos;
         uint64_t n;
         if (peek().kind != T_NUM || !parse_u64(peek().text, n) || n == 0 || n > 4096) raise(KS_E_PARSE, line, "bad register count");
@@ -463,6 +516,7 @@ class Front {
         if (is_punct("-")) {  // "+-imm"
           minus = !minus;
           ++pos;
+          if (!peek().glued) raise(KS_E_PARSE, r.line, "space between '-' and its number");
         }
         uint64_t v;
         if (peek().kind != T_NUM || !parse_u64(peek().text, v) || v > (1ull << 62)) raise(KS_E_PARSE, r.line, "bad address offset");
@@ -475,6 +529,7 @@ class Front {
     if (is_punct("-")) {
       ++pos;
       r.neg = true;
+      if (!peek().glued) raise(KS_E_PARSE, r.line, "space between '-' and its number");
     }
     if (peek().kind == T_NUM) {
       r.kind = RawOperand::NUM;
@@ -598,9 +653,11 @@ class Front {
       ++pos;
       bool neg = false;
       if (is_punct("!")) {
+        if (!peek().glued) raise(KS_E_PARSE, peek().line, "space inside the guard");
         ++pos;
         neg = true;
       }
+      if (!peek().glued) raise(KS_E_PARSE, peek().line, "space inside the guard");
       RawOperand g;
       g.kind = RawOperand::WORD;
       g.line = peek().line;
@@ -611,6 +668,7 @@ class Front {
     }
     const Tok& opt = expect_word("instruction");
     std::vector<std::string> m = dotted(opt.text);
+    if (!is_punct(";") && peek().glued) raise(KS_E_PARSE, opt.line, "expected a space after '%s'", opt.text.c_str());
     std::vector<RawOperand> ops = operand_list();
     expect_punct(";");
     const std::string& base = m[0];

@@ -110,6 +110,16 @@ BAD = [
     ("mov.u32 %r2, %tid.x;", "mov.u32 %r2, 1.5;", -1, None),
     ("add.f32 %f3, %f1, %f2;", "add.f32 %f3, %f1, 1;", -2, "0fXXXXXXXX"),
     ("add.s64 %rd5, %rd1, %rd4;", "add.s64 %rd5, %rd1, %r4;", -1, "is 32-bit"),
+    # token spacing the subset's grammar fixes (the oracle splits on the same places)
+    (".param .u64 param_b,", ".param .u64 param_b", -1, "expected ','"),
+    ("    ret;", "    L.x:\n    ret;", -1, "bad label name"),
+    ("$L__exit:", "$L__exit :", -1, "space between label"),
+    (".reg .b32 %r<6>;", ".reg .b32 %r <6>;", -1, "space between register name"),
+    ("@%p1 bra $L__exit;", "@ %p1 bra $L__exit;", -1, "space inside the guard"),
+    ("@%p1 bra $L__exit;", "@! %p1 bra $L__exit;", -1, "space inside the guard"),
+    ("ld.global.f32 %f1, [%rd5];", "ld.global.f32 %f1, [%rd5+- 4];", -1, "space between '-'"),
+    ("mul.wide.s32 %rd4, %r5, 4;", "mul.wide.s32 %rd4, %r5, - 4;", -1, "space between '-'"),
+    ("st.global.f32 [%rd7], %f3;", "st.global.f32[%rd7], %f3;", -1, "expected a space after"),
 ]
 
 
@@ -125,6 +135,86 @@ def test_parse_errors(ks, old, new, code, msg):
         assert ("line %d:" % line) in e.value.msg
     if msg:
         assert msg in e.value.msg
+
+
+SPACING_OK = [
+    (".address_size 64", ".address_size 64 // pointer size", 19),
+    (".address_size 64", ".address_size 64 /* pointer\n size */", 19),
+    ("    mov.u32 %r2, %tid.x;", "    .loc 1 2 0 /* source */\n    mov.u32 %r2, %tid.x;", 19),
+    # a line-scoped directive runs to the end of its line, comments removed
+    ("    mov.u32 %r2, %tid.x;", "    .loc 1 2 0 /* source */ mov.u32 %r2, %tid.x;", 18),
+    ("    mov.u32 %r2, %tid.x;", "    .loc 1 2 0 /* source\n */ mov.u32 %r2, %tid.x;", 19),
+    ("    mov.u32 %r2, %tid.x;", "    /* a\n */ .loc 1 2 0\n    mov.u32 %r2, %tid.x;", 19),
+    ("ld.global.f32 %f1, [%rd5];", "ld.global.f32 %f1, [%rd5 + 4];", 19),
+    ("ld.global.f32 %f1, [%rd5];", "ld.global.f32 %f1, [%rd5+-4];", 19),
+    ("@%p1 bra $L__exit;", "@!%p1 bra $L__exit;", 19),
+    (".param .u64 param_b,", ".param .u64 param_b ,", 19),
+]
+
+
+@pytest.mark.parametrize("old,new,n", SPACING_OK)
+def test_spacing_forms_both_sides_accept(ks, oracle_mod, old, new, n):
+    """Comments around header and .loc directives, spaces around an address's '+',
+    a negative offset and a spaced comma: the library and the oracle read the same
+    program."""
+    ptx = W.VECTOR_ADD_PTX.replace(old, new)
+    assert ptx != W.VECTOR_ADD_PTX
+    p = ks.ks_load_program(ptx)
+    info = ks.ks_program_info(p)
+    o = oracle_mod.program_info(ptx)
+    assert (info["n_instrs"], info["param_bytes"]) == (o["n_instrs"], o["param_bytes"]) == (n, 28)
+    assert ks.ks_ipdom_table(p) == oracle_mod.ipdom_table(ptx)
+    ks.ks_program_free(p)
+
+
+def _mutate(rnd, t):
+    toks = ["%r1", "%rd1", "%p1", "[", "]", "+", "-", ",", ";", "{", "}", ".reg", ".b32", ".u64", "0x", "0f",
+            "99999999999999999999", "-2147483649", "@%p1", "@!", "bra", "$L", ":", ".shared", ".align", "<", ">",
+            "<0>", "<100000>", "ld.global.u32", "st.shared.b64", "setp.lt.f32", "mul.wide.s32", ".param", "(", ")",
+            "\n", " ", "\t", "//", "/*", "*/"]
+    for _ in range(rnd.randint(1, 4)):
+        k = rnd.randrange(len(t) + 1)
+        op = rnd.randrange(4)
+        if op == 0:
+            t = t[:k] + t[k + rnd.randint(1, 20):]
+        elif op == 1:
+            t = t[:k] + rnd.choice(toks) + t[k:]
+        elif op == 2:
+            j = rnd.randrange(len(t) + 1)
+            t = t[:k] + t[min(k, j):max(k, j)] + t[k:]
+        else:
+            t = t[:k]
+    return t
+
+
+def test_parser_differential_on_mutated_programs(ks, oracle_mod):
+    """6000 seeded mutations of valid programs (deleted, inserted, duplicated and
+    truncated text): the library never accepts a text the oracle rejects, and
+    where both accept they read the same program (instructions, parameters,
+    shared window, reconvergence table).  The oracle is the more lenient reader
+    of malformed text; the library rejects what the subset's grammar does not
+    define."""
+    import random
+    rnd = random.Random(20261202)
+    seeds = [W.VECTOR_ADD_PTX, W.STRIDED_PTX, W.bank_probe_ptx(), S.random_cfg_ptx(5, 40), S.block_reduce_ptx(64),
+             S.tile_transpose_ptx(1), S.setp_forms_ptx(), S.lcg64_ptx(), S.stencil3_ptx()]
+    both = 0
+    for _ in range(6000):
+        t = _mutate(rnd, rnd.choice(seeds))
+        try:
+            p = ks.ks_load_program(t)
+        except ks.KsError as e:
+            assert e.code in (-1, -2), e
+            continue
+        li = ks.ks_program_info(p)
+        lt = ks.ks_ipdom_table(p)
+        ks.ks_program_free(p)
+        o = oracle_mod.program_info(t)  # raises if the oracle rejects what the library took
+        assert (li["n_instrs"], li["n_params"], li["param_bytes"], li["shared_bytes"]) == \
+            (o["n_instrs"], o["n_params"], o["param_bytes"], o["shared_bytes"]), t
+        assert lt == oracle_mod.ipdom_table(t), t
+        both += 1
+    assert both > 20
 
 
 def test_layout_and_default_config(ks):

@@ -1000,12 +1000,17 @@ bool compare(const Inst& in, uint64_t a, uint64_t b) {
 //
 // A race is two accesses to one byte by different threads in one epoch, at least
 // one a write, whose outcome depends on their order: two writes of different
-// values, or a read of value r and a write of value v != r.  Epoch = the whole run
-// for global memory, one barrier interval of one block for shared memory.
+// values, or a read and a write that changes the byte.  A write changes the byte
+// when it stores a value other than the one the byte held at the epoch's first
+// access: a read by another thread could then see either value, whichever order
+// the simulation happened to take.  Epoch = the whole run for global memory, one
+// barrier interval of one block for shared memory.
 
 struct ByteLog {
-  // value -> up to two distinct thread ids that wrote / read it
-  std::map<uint8_t, std::vector<uint64_t>> writes, reads;
+  bool seen = false;
+  uint8_t init = 0;                                 // value at the epoch's first access
+  std::map<uint8_t, std::vector<uint64_t>> writes;  // value -> up to two distinct writers
+  std::vector<uint64_t> readers;                    // up to two distinct readers
 };
 
 struct RaceLog {
@@ -1021,19 +1026,23 @@ struct RaceLog {
       if (x != t) return true;
     return false;
   }
-  void note(const char* space, uint64_t addr, uint64_t tid, bool is_write, uint8_t val) {
+  // `cur` is the byte's value before the access, `val` the value read or written.
+  void note(const char* space, uint64_t addr, uint64_t tid, bool is_write, uint8_t val, uint8_t cur) {
     ByteLog& b = bytes[addr];
+    if (!b.seen) {
+      b.seen = true;
+      b.init = cur;
+    }
     bool race = false;
     if (is_write) {
       for (auto& kv : b.writes)
         if (kv.first != val && other_than(kv.second, tid)) race = true;
-      for (auto& kv : b.reads)
-        if (kv.first != val && other_than(kv.second, tid)) race = true;
+      if (val != b.init && other_than(b.readers, tid)) race = true;
       add_tid(b.writes[val], tid);
     } else {
       for (auto& kv : b.writes)
-        if (kv.first != val && other_than(kv.second, tid)) race = true;
-      add_tid(b.reads[val], tid);
+        if (kv.first != b.init && other_than(kv.second, tid)) race = true;
+      add_tid(b.readers, tid);
     }
     if (race && !raced) {
       raced = true;
@@ -1527,13 +1536,15 @@ struct Sim {
         memcpy(&v, base + a, (size_t)in.size);
         w.vals[(size_t)in.dst.reg * 32 + l] = v;
         if (races)
-          for (int k = 0; k < in.size; ++k) races->note(global ? "global" : "shared", a + k, tid, false, base[a + k]);
+          for (int k = 0; k < in.size; ++k)
+            races->note(global ? "global" : "shared", a + k, tid, false, base[a + k], base[a + k]);
       } else {
         uint64_t v = w.vals[(size_t)in.src[0].reg * 32 + l];
         if (races) {
           uint8_t bytes[8];
           memcpy(bytes, &v, 8);
-          for (int k = 0; k < in.size; ++k) races->note(global ? "global" : "shared", a + k, tid, true, bytes[k]);
+          for (int k = 0; k < in.size; ++k)
+            races->note(global ? "global" : "shared", a + k, tid, true, bytes[k], base[a + k]);
         }
         memcpy(base + a, &v, (size_t)in.size);
       }

@@ -668,6 +668,46 @@ def test_race_checker(oracle_mod):
     assert g[:4].view("<u4")[0] == 31
 
 
+RW_PTX = S.HEADER + """.visible .entry rw(.param .u64 param_out, .param .u32 param_wb, .param .u32 param_val)
+{
+    .reg .pred %p<2>;
+    .reg .b32 %r<6>;
+    .reg .b64 %rd<4>;
+    ld.param.u64 %rd1, [param_out];
+    ld.param.u32 %r1, [param_wb];
+    ld.param.u32 %r2, [param_val];
+    mov.u32 %r3, %tid.x;
+    mov.u32 %r4, %ctaid.x;
+    mul.wide.u32 %rd2, %r3, 4;
+    add.s64 %rd3, %rd1, %rd2;
+    setp.ne.u32 %p1, %r4, %r1;
+    @%p1 bra $L__read;
+    st.global.u32 [%rd3], %r2;
+$L__read:
+    ld.global.u32 %r5, [%rd3];
+    ret;
+}
+"""
+
+
+@pytest.mark.parametrize("grid,writer,val,racy", [
+    (2, 0, 7, True),    # the other block reads after the write in simulation order
+    (2, 1, 7, True),    # ... and before it
+    (2, 0, 0, False),   # the write stores the value the word already holds
+    (1, 0, 7, False),   # each thread reads back only its own write
+])
+def test_race_checker_independent_of_simulation_order(oracle_mod, grid, writer, val, racy):
+    """Block `writer` stores `val` to word tid and every thread then loads word tid.
+    A load by a thread of another block could see the word before or after the
+    store, whichever block runs first, unless the store leaves the word unchanged:
+    the checker must flag it in both simulation orders, and only then."""
+    g = np.zeros(4096, np.uint8)
+    pb = pack_params([("param_out", "u64", 0), ("param_wb", "u32", writer), ("param_val", "u32", val)])
+    _, _, rc = oracle_mod.run(RW_PTX, grid, 64, pb, g, check_races=True)
+    assert rc == (oracle_mod.E_RACE if racy else 0)
+    assert (g[:256].view("<u4") == val).all()
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_random_stress_full_programs_are_race_free(oracle_mod, seed):
     """The 2000-instruction stress programs (the parity set, seeds 0-2) at 64 x 256

@@ -1343,7 +1343,7 @@ struct Sim {
         }
         case OP_LD_GLOBAL: case OP_ST_GLOBAL: case OP_LD_SHARED: case OP_ST_SHARED: {
           const MemInfo mi = memory_access(w, in, g, block_linear, shared, shared_races);
-          if (in.op == OP_LD_GLOBAL && mi.cache_latency) dst_lat = mi.cache_latency;
+          if (in.op == OP_LD_GLOBAL && mi.cached) dst_lat = mi.cache_latency;
           const bool global = in.op == OP_LD_GLOBAL || in.op == OP_ST_GLOBAL;
           const bool load = in.op == OP_LD_GLOBAL || in.op == OP_LD_SHARED;
           kind = global ? (load ? ORACLE_EV_LD_GLOBAL : ORACLE_EV_ST_GLOBAL)
@@ -1444,7 +1444,8 @@ struct Sim {
   // What the analyser found for one warp access (all 0 when no lane passes the guard).
   struct MemInfo {
     uint32_t sectors = 0, lines = 0, degree = 0, faults = 0;
-    uint32_t cache_latency = 0;  // cache model: latency of the access (0 = no cache access)
+    bool cached = false;         // cache model: the access looked up a cache level
+    uint32_t cache_latency = 0;  // ... and that level's latency (any table value, 0 included)
   };
 
   MemInfo memory_access(Warp& w, const Inst& in, uint32_t g, uint64_t block_linear,
@@ -1484,6 +1485,7 @@ struct Sim {
           if (cache_access(w.l1, line)) level = 0;
           else if (cache_access(w.l2, line)) level = 1;
           w.cache_count[level]++;
+          mi.cached = true;
           mi.cache_latency = lat(level == 0 ? ORACLE_LAT_L1_HIT : level == 1 ? ORACLE_LAT_L2_HIT : ORACLE_LAT_DRAM);
           break;
         }

@@ -23,12 +23,12 @@ L1_SETS, L2_SETS, LINE = 1024, 49152, 128
 L1, L2, DRAM, FIXED = 28, 150, 400, 200
 
 
-def run_both(O, w):
+def run_both(O, w, latency=None):
     g0 = w.gmem.copy()
-    c0, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g0, trace_cap=0)
+    c0, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g0, trace_cap=0, latency=latency)
     g1 = w.gmem.copy()
     cache = np.zeros(w.n_warps * O.CACHE_WARP_BYTES, np.uint8)
-    c1, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g1, trace_cap=0, cache=cache)
+    c1, _, _ = O.run(w.ptx, w.grid, w.block, w.params_bytes, g1, trace_cap=0, cache=cache, latency=latency)
     assert np.array_equal(g0, g1)  # the model changes timing only
     hdr, l1, l2 = O.cache_state(cache, w.n_warps)
     return c0, c1, hdr, l1, l2
@@ -85,6 +85,30 @@ def test_l1_and_l2_conflicts_reach_dram(oracle_mod, m):
     lat = [DRAM] * (1 + 2 * m)
     assert int(c1["cycles"][0]) - int(c0["cycles"][0]) == sum(x - FIXED for x in lat)
     assert (hdr["l1_hits"][0], hdr["l2_hits"][0], hdr["misses"][0]) == (0, 0, 2 * m + 2)
+
+
+@pytest.mark.parametrize("l1,l2,dram", [(0, 0, 0), (0, 7, 1000), (5, 0, 65535), (1, 1, 1)])
+def test_level_latencies_come_from_the_table(oracle_mod, l1, l2, dram):
+    """Caller-set L1, L2 and DRAM latencies, 0 included: a hop that looked up a level
+    takes that level's table value.  A load issued at t makes its value ready at
+    t + x and the dependent mul.wide issues no earlier than t + 1, so a load of
+    latency x costs max(x, 1) cycles before the next hop; after the last load the
+    independent add.s64 issues at t + 1 and the store waits for it until t + 5, so
+    the last load costs max(x, 5).  With the fixed ld.global latency every load
+    costs 200."""
+    lat = oracle_mod.default_latency()
+    lat[14], lat[15], lat[16] = l1, l2, dram
+
+    def cost(loads):
+        return sum(max(x, 1) - FIXED for x in loads[:-1]) + max(loads[-1], 5) - FIXED
+
+    w = PR.chase_probe([0, 4, 8, 12], 4)
+    c0, c1, _, _, _ = run_both(oracle_mod, w, lat)
+    assert int(c1["cycles"][0]) - int(c0["cycles"][0]) == cost([dram, dram, l1, l1, l1])
+    m = 2
+    w = PR.chase_probe([k * L1_SETS * LINE for k in range(m)], 3 * m)
+    c0, c1, _, _, _ = run_both(oracle_mod, w, lat)
+    assert int(c1["cycles"][0]) - int(c0["cycles"][0]) == cost([dram] + [dram] * m + [l2] * (2 * m))
 
 
 def test_representative_is_the_lowest_valid_lane(oracle_mod):

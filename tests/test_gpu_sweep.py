@@ -62,8 +62,8 @@ def _case(rng):
     return w, cap, fmt, cache, budget, desc
 
 
-def _compare(K, O, w, cap, fmt, cache, budget):
-    kw = dict(trace_cap=cap, trace_format=fmt, max_warp_instrs=budget)
+def _compare(K, O, w, cap, fmt, cache, budget, latency=None):
+    kw = dict(trace_cap=cap, trace_format=fmt, max_warp_instrs=budget, latency=latency)
     if cache:
         kw["cache_model"] = K.KS_CACHE_WARP
     s = K.Session(w.ptx, w.grid, w.block, w.gmem.size, **kw)
@@ -77,7 +77,7 @@ def _compare(K, O, w, cap, fmt, cache, budget):
         s.close()
     go = w.gmem.copy()
     ofmt = O.TRACE_EXTENDED if fmt else O.TRACE_BASIC
-    okw = dict(trace_cap=cap, max_warp_instrs=budget, trace_format=ofmt)
+    okw = dict(trace_cap=cap, max_warp_instrs=budget, trace_format=ofmt, latency=latency)
     cbuf = None
     if cache:
         cbuf = np.zeros(w.n_warps * O.CACHE_WARP_BYTES, np.uint8)

@@ -93,3 +93,22 @@ def workload(rnd, text, params, mem_bytes=1 << 20, trace_cap=0):
     grid = rnd.choice([1, 2, 3])
     return Workload(name="mutant", ptx=text, grid=(grid, 1, 1), block=(block, 1, 1), params=vals, gmem=g,
                     trace_cap=trace_cap)
+
+
+def launch_shape(rnd):
+    """A grid of up to 6 x 3 x 2 blocks and a block of up to 64 x 4 x 2 threads (at
+    most 256, any count: warps are often ragged)."""
+    while True:
+        block = (rnd.randint(1, 64), rnd.choice([1, 1, 2, 3, 4]), rnd.choice([1, 1, 2]))
+        if block[0] * block[1] * block[2] <= 256:
+            break
+    grid = (rnd.randint(1, 6), rnd.choice([1, 1, 2, 3]), rnd.choice([1, 1, 2]))
+    return grid, block
+
+
+def latency_table(rnd, n):
+    """A caller-set latency table of n classes: every entry 65535, or each drawn from
+    values that include 0 and 65535."""
+    if rnd.random() < 0.3:
+        return [65535] * n
+    return [rnd.choice([0, 1, 4, 23, 200, 300, 1000, 65535]) for _ in range(n)]

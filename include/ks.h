@@ -198,7 +198,13 @@ typedef struct {
  * are dropped, and instructions are numbered in listing order: the pc).  Branch
  * reconvergence points are computed here too (the SIMT stack entry of that part
  * holds one); they are immediate post-dominators.
- * Errors: KS_E_PARSE (message "line N: ..."), KS_E_UNSUPPORTED, KS_E_INVALID_ARG. */
+ * Text outside the grammar is an error, never skipped: parameters are separated
+ * by commas; a label is an identifier without dots written against its ':';
+ * "%r<N>", "@%p", "@!%p" and negative numbers take no inner spaces; an opcode is
+ * followed by a space; .loc/.file/.section and the module header directives end
+ * at the end of their line, comments removed.
+ * Errors: KS_E_PARSE (message "line N: ..."), KS_E_UNSUPPORTED (an instruction,
+ * type or directive outside the subset, or a size limit), KS_E_INVALID_ARG. */
 ks_status ks_load_program(const char* ptx, size_t len, const char* entry, ks_program** out);
 
 /* Shape of a decoded program: instruction count, parameter block, shared window,

@@ -321,7 +321,10 @@ def param_block(ptx, values, entry=None):
             if isinstance(v, float):
                 if size != 4:
                     raise ValueError("parameter %s has %d bytes: a float needs 4" % (name, size))
-                raw = struct.pack("<f", v)
+                try:
+                    raw = struct.pack("<f", v)
+                except OverflowError:
+                    raise ValueError("value %r of parameter %s is beyond binary32" % (v, name)) from None
             else:
                 v = int(v)
                 if not -(1 << (8 * size - 1)) <= v < (1 << (8 * size)):
@@ -337,7 +340,10 @@ def param_block(ptx, values, entry=None):
 
 
 def _dims(text):
-    d = [int(x) for x in text.split(",")]
+    try:
+        d = [int(x) for x in text.split(",")]
+    except ValueError:
+        raise SystemExit("a grid or block is 1 to 3 comma-separated integers: %s" % text) from None
     if not 1 <= len(d) <= 3:
         raise SystemExit("a grid or block is 1 to 3 comma-separated sizes: %s" % text)
     return tuple(d + [1] * (3 - len(d)))

@@ -326,6 +326,10 @@ def test_param_block_uses_the_library_layout(A):
         A.param_block(W.VECTOR_ADD_PTX, {"param_n": 1 << 32})
     with pytest.raises(ValueError, match="a float needs 4"):
         A.param_block(W.VECTOR_ADD_PTX, {"param_a": 0.5})
+    with pytest.raises(ValueError, match="beyond binary32"):
+        A.param_block(W.VECTOR_ADD_PTX, {"param_n": 1e39})
+    with pytest.raises(SystemExit, match="comma-separated integers"):
+        A._dims("4,x")
 
 
 @pytest.mark.parametrize("pad", [0, 1])

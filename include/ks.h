@@ -13,10 +13,9 @@
  * It also writes a per-warp trace: {issue cycle, pc} records, or (extended
  * format) 16-byte records that add the instruction kind, the active mask and a
  * per-kind payload (sectors and lines of a global access, bank-conflict degree of
- * a shared access, the lanes taking a branch).  Extended records for programs of
- * more than 32 register slots support blocks of up to KS_EXT64_MAX_BLOCK_THREADS
- * threads, and ks_run covers an extended-record grid with launches of at most
- * KS_EXT_MAX_BLOCKS blocks each.
+ * a shared access, the lanes taking a branch).  Extended records support blocks
+ * of up to KS_EXT_MAX_BLOCK_THREADS threads, and ks_run covers an extended-record
+ * grid with launches of at most KS_EXT_MAX_BLOCKS blocks each.
  *
  * Sources of the semantics, by page and section:
  *   - KernelScope backend documentation (github.com/briefgaming/kernelscope).
@@ -144,11 +143,12 @@ enum {
  * the GPU.  A single 65536-block extended launch faulted, with the cause not yet
  * found, and is never made.  Basic and cache-model runs are one launch. */
 #define KS_EXT_MAX_BLOCKS 32
-/* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run of a program of
- * more than 32 register slots.  Extended runs of such programs with 768-thread
- * blocks (three waves per SIMD) gave wrong counters on the GPU now and then, with
- * no cause found yet, so larger blocks are refused (KS_E_UNSUPPORTED). */
-#define KS_EXT64_MAX_BLOCK_THREADS 256
+/* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run.  Extended runs
+ * with three or more waves of a workgroup on one SIMD (blocks of 644 to 1022
+ * threads, 32- and 64-slot programs) now and then wrote a wrong word into a
+ * record, or a wrong counter, on the GPU, with no cause found yet, so blocks above
+ * this size, at most one wave per SIMD, are refused (KS_E_UNSUPPORTED). */
+#define KS_EXT_MAX_BLOCK_THREADS 256
 /* Largest program (decoded instructions) a state bound by ks_alloc_state_static can
  * hold: the library's static device scratch is (KS_STATIC_MAX_INSTRS + 5) 128-byte
  * records plus 256 bytes, 1 MiB + 256 bytes per GPU. */

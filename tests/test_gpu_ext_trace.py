@@ -79,6 +79,15 @@ def test_ffma(K, oracle_mod, n_acc):
 
 @pytest.mark.parametrize("s", [1, 7, 32])
 def test_bank(K, oracle_mod, s):
+    ext_parity(K, oracle_mod, W.bank_probe(s, iters=4, grid=2, block=256, trace_cap=64))
+
+
+@pytest.mark.skip(reason="refused by the library: extended records with three or more waves of a workgroup on "
+                         "one SIMD (blocks of 644 to 1022 threads) wrote wrong record words or counters on the "
+                         "GPU now and then, in 32- and 64-slot programs; the cause is not found, so extended runs "
+                         "are refused above 256 threads per block")
+@pytest.mark.parametrize("s", [1, 7, 32])
+def test_bank_block_1024(K, oracle_mod, s):
     ext_parity(K, oracle_mod, W.bank_probe(s, iters=4, grid=2, block=1024, trace_cap=64))
 
 

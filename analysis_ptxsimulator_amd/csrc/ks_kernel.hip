@@ -645,13 +645,20 @@ __device__ __forceinline__ void interp(const KsArgs& a) {
   // Extended trace record of the instruction just issued by the warps of gm (after
   // KS_ISSUE: it is the warp's record wi - 1), written by the first lane of each
   // issuing half: issue cycle, pc | kind << 16, the warp's live lanes, payload.
+  // Four 32-bit LDS stores, not one 16-byte store: a 16-byte LDS store whose data
+  // registers the next instructions overwrite (the compiler inserts no wait there)
+  // now and then stored a word of the new value once three or more waves shared a
+  // SIMD; 32-bit stores read their data at issue.
 #define KS_EXT_REC(is_, pc_, kind_, pay_)                                            \
   if constexpr (EXT) {                                                              \
     const uint32_t k_ = wi - 1u;                                                    \
-    if (gl && sl == 0u && k_ < cap)                                                 \
-      *reinterpret_cast<uint4*>(my_ring + 16u * (k_ & 31u)) =                       \
-          make_uint4((is_), (pc_) | ((uint32_t)(kind_) << 16),                      \
-                     hl ? (uint32_t)(mm >> 32) : (uint32_t)mm, (pay_));             \
+    if (gl && sl == 0u && k_ < cap) {                                               \
+      volatile uint32_t* const rp_ = reinterpret_cast<volatile uint32_t*>(my_ring + 16u * (k_ & 31u)); \
+      rp_[0] = (is_);                                                               \
+      rp_[1] = (pc_) | ((uint32_t)(kind_) << 16);                                   \
+      rp_[2] = hl ? (uint32_t)(mm >> 32) : (uint32_t)mm;                            \
+      rp_[3] = (pay_);                                                              \
+    }                                                                               \
   }
 
   // A global store whose next index-mode register access may come within a few

@@ -146,8 +146,10 @@ enum {
 /* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run.  Extended runs
  * with three or more waves of a workgroup on one SIMD (blocks of 644 to 1022
  * threads, 32- and 64-slot programs) now and then wrote a wrong word into a
- * record, or a wrong counter, on the GPU, with no cause found yet, so blocks above
- * this size, at most one wave per SIMD, are refused (KS_E_UNSUPPORTED). */
+ * record, or a wrong counter, on the GPU.  The cause found, a 16-byte LDS store
+ * whose data registers were overwritten before it read them, is fixed; until the
+ * larger blocks have been checked again, blocks above this size, at most one wave
+ * per SIMD, are refused (KS_E_UNSUPPORTED). */
 #define KS_EXT_MAX_BLOCK_THREADS 256
 /* Largest program (decoded instructions) a state bound by ks_alloc_state_static can
  * hold: the library's static device scratch is (KS_STATIC_MAX_INSTRS + 5) 128-byte

@@ -1342,8 +1342,12 @@ ks_status ks_query_layout(const ks_program* p, const ks_config* cfg, ks_layout* 
     out->counters_bytes = out->n_warps * 80;
     if (cfg->trace_format != KS_TRACE_BASIC && cfg->trace_format != KS_TRACE_EXTENDED)
       raise(KS_E_INVALID_ARG, 0, "unknown trace format %u", cfg->trace_format);
-    if (cfg->trace_format == KS_TRACE_EXTENDED && tpb > KS_EXT_MAX_BLOCK_THREADS)
-      raise(KS_E_UNSUPPORTED, 0, "extended trace records support blocks of up to %d threads", KS_EXT_MAX_BLOCK_THREADS);
+    if (cfg->trace_format == KS_TRACE_EXTENDED) {
+      const uint32_t lim = ks_choose_variant(p->reg_slots, (uint32_t)tpb) == 64 ? KS_EXT64_MAX_BLOCK_THREADS : KS_EXT_MAX_BLOCK_THREADS;
+      if (tpb > lim)
+        raise(KS_E_UNSUPPORTED, 0, "extended trace records of programs with %u register slots support blocks of up to %u threads",
+              p->reg_slots, lim);
+    }
     if (cfg->cache_model != KS_CACHE_NONE && cfg->cache_model != KS_CACHE_WARP)
       raise(KS_E_INVALID_ARG, 0, "unknown cache model %u", cfg->cache_model);
     if (cfg->cache_model == KS_CACHE_WARP) {
@@ -1478,8 +1482,12 @@ ks_status ks_run(ks_state* st, ks_dim3 grid, ks_dim3 block, const void* params, 
       raise(KS_E_INVALID_ARG, 0, "grid/block larger than the allocation");
     if (tpb > KS_MAX_BLOCK_THREADS) raise(KS_E_INVALID_ARG, 0, "more than %d threads per block", KS_MAX_BLOCK_THREADS);
     if (nb > 0x7FFFFFFFull) raise(KS_E_INVALID_ARG, 0, "too many blocks");
-    if (st->cfg.trace_format == KS_TRACE_EXTENDED && tpb > KS_EXT_MAX_BLOCK_THREADS)
-      raise(KS_E_UNSUPPORTED, 0, "extended trace records support blocks of up to %d threads", KS_EXT_MAX_BLOCK_THREADS);
+    if (st->cfg.trace_format == KS_TRACE_EXTENDED) {
+      const uint32_t lim = ks_choose_variant(p->reg_slots, (uint32_t)tpb) == 64 ? KS_EXT64_MAX_BLOCK_THREADS : KS_EXT_MAX_BLOCK_THREADS;
+      if (tpb > lim)
+        raise(KS_E_UNSUPPORTED, 0, "extended trace records of programs with %u register slots support blocks of up to %u threads",
+              p->reg_slots, lim);
+    }
     if (params_len < p->param_bytes || (p->param_bytes && !params)) raise(KS_E_INVALID_ARG, 0, "parameter block shorter than %u bytes", p->param_bytes);
     KsArgs a;
     memset(&a, 0, sizeof a);

@@ -34,7 +34,7 @@ KS_MAX_PARAM_BYTES, KS_MAX_SHARED_BYTES, KS_MAX_BLOCK_THREADS = 512, 65536, 1024
 KS_TRACE_BASIC, KS_TRACE_EXTENDED = 0, 1
 KS_EXT_MAX_BLOCKS = 32  # blocks per launch of an extended-record run (ks_run chunks larger grids)
 KS_STATIC_MAX_INSTRS = 8187  # largest program a ks_alloc_state_static binding holds
-KS_EXT_MAX_BLOCK_THREADS = 256  # largest block of an extended-record run
+KS_EXT_MAX_BLOCK_THREADS, KS_EXT64_MAX_BLOCK_THREADS = 1024, 768  # largest block of an extended-record run (> 32 slots)
 # cache-latency model (ks_config.cache_model) and its per-warp state in d_cache
 KS_CACHE_NONE, KS_CACHE_WARP = 0, 1
 KS_LAT_L1_HIT, KS_LAT_L2_HIT, KS_LAT_DRAM = 14, 15, 16

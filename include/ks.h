@@ -14,7 +14,8 @@
  * format) 16-byte records that add the instruction kind, the active mask and a
  * per-kind payload (sectors and lines of a global access, bank-conflict degree of
  * a shared access, the lanes taking a branch).  Extended records support blocks
- * of up to KS_EXT_MAX_BLOCK_THREADS threads, and ks_run covers an extended-record
+ * of up to KS_EXT_MAX_BLOCK_THREADS threads (KS_EXT64_MAX_BLOCK_THREADS for
+ * programs of more than 32 register slots), and ks_run covers an extended-record
  * grid with launches of at most KS_EXT_MAX_BLOCKS blocks each.
  *
  * Sources of the semantics, by page and section:
@@ -143,14 +144,12 @@ enum {
  * the GPU.  A single 65536-block extended launch faulted, with the cause not yet
  * found, and is never made.  Basic and cache-model runs are one launch. */
 #define KS_EXT_MAX_BLOCKS 32
-/* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run.  Extended runs
- * with three or more waves of a workgroup on one SIMD (blocks of 644 to 1022
- * threads, 32- and 64-slot programs) now and then wrote a wrong word into a
- * record, or a wrong counter, on the GPU.  The cause found, a 16-byte LDS store
- * whose data registers were overwritten before it read them, is fixed; until the
- * larger blocks have been checked again, blocks above this size, at most one wave
- * per SIMD, are refused (KS_E_UNSUPPORTED). */
-#define KS_EXT_MAX_BLOCK_THREADS 256
+/* Largest block (threads) of a KS_TRACE_EXTENDED allocation or run: 1024, and 768
+ * for programs of more than 32 register slots (their extended kernel's 136 VGPRs
+ * leave room for three waves per SIMD).  Larger blocks are refused
+ * (KS_E_UNSUPPORTED). */
+#define KS_EXT_MAX_BLOCK_THREADS 1024
+#define KS_EXT64_MAX_BLOCK_THREADS 768
 /* Largest program (decoded instructions) a state bound by ks_alloc_state_static can
  * hold: the library's static device scratch is (KS_STATIC_MAX_INSTRS + 5) 128-byte
  * records plus 256 bytes, 1 MiB + 256 bytes per GPU. */

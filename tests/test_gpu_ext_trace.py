@@ -82,12 +82,9 @@ def test_bank(K, oracle_mod, s):
     ext_parity(K, oracle_mod, W.bank_probe(s, iters=4, grid=2, block=256, trace_cap=64))
 
 
-@pytest.mark.skip(reason="refused by the library: extended records with three or more waves of a workgroup on "
-                         "one SIMD (blocks of 644 to 1022 threads) wrote wrong record words or counters on the "
-                         "GPU now and then, in 32- and 64-slot programs; the cause is not found, so extended runs "
-                         "are refused above 256 threads per block")
 @pytest.mark.parametrize("s", [1, 7, 32])
 def test_bank_block_1024(K, oracle_mod, s):
+    """Four waves per SIMD: blocks of 1024 threads."""
     ext_parity(K, oracle_mod, W.bank_probe(s, iters=4, grid=2, block=1024, trace_cap=64))
 
 
@@ -98,11 +95,11 @@ def test_random_stress(K, oracle_mod, seed):
 
 
 def test_random_stress_cap_overflow(K, oracle_mod):
-    """Records past the cap dropped and counted, on the 64-slot extended variant's
-    largest block; larger blocks are refused."""
+    """Records past the cap dropped and counted; blocks above the 64-slot extended
+    variant's largest are refused."""
     ext_parity(K, oracle_mod, W.random_stress(prog_seed=2, grid=3, block=256, gmem_bytes=1 << 24, trace_cap=300))
-    w = W.random_stress(prog_seed=2, grid=1, block=512, gmem_bytes=1 << 22, trace_cap=8)
-    with pytest.raises(K.KsError, match="256"):
+    w = W.random_stress(prog_seed=2, grid=1, block=1024, gmem_bytes=1 << 22, trace_cap=8)
+    with pytest.raises(K.KsError, match="768"):
         K.Session(w.ptx, w.grid, w.block, w.gmem.size, trace_cap=8, trace_format=K.KS_TRACE_EXTENDED)
 
 
@@ -113,10 +110,8 @@ def test_long_program(K, oracle_mod):
                                               n_instr=32000))
 
 
-@pytest.mark.skip(reason="refused by the library: extended records of a 64-slot program on 768-thread blocks "
-                         "gave wrong gst_lines counters in one of three GPU runs (memory and the other counters "
-                         "equal); the cause is not found, so such runs are refused above 256 threads per block")
 def test_random_stress_block_768(K, oracle_mod):
+    """The 64-slot extended kernel's largest block: three waves per SIMD."""
     ext_parity(K, oracle_mod, W.random_stress(prog_seed=2, grid=3, block=768, gmem_bytes=1 << 24, trace_cap=300))
 
 

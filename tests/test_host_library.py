@@ -273,23 +273,30 @@ def test_extended_layout_any_grid(ks):
 
 
 def test_extended_block_limit(ks):
-    """Extended records are refused above KS_EXT_MAX_BLOCK_THREADS threads per block,
-    for 64- and 32-slot programs alike; the basic format is not limited."""
+    """Extended records run blocks up to the extended kernels' register budgets:
+    KS_EXT64_MAX_BLOCK_THREADS for a program of more than 32 register slots,
+    KS_EXT_MAX_BLOCK_THREADS (the block maximum) otherwise; the basic format runs
+    every block size."""
     from workloads.randprog import random_program
-    for ptx in (random_program(0, n_threads=1024)[0], W.bank_probe_ptx()):
-        p = ks.ks_load_program(ptx)
-        cfg = ks.ks_default_config()
-        cfg.trace_format = ks.KS_TRACE_EXTENDED
-        cfg.max_block = ks.ks_dim3(ks.KS_EXT_MAX_BLOCK_THREADS, 1, 1)
+    p = ks.ks_load_program(random_program(0, n_threads=1024)[0])
+    cfg = ks.ks_default_config()
+    cfg.trace_format = ks.KS_TRACE_EXTENDED
+    cfg.max_block = ks.ks_dim3(ks.KS_EXT64_MAX_BLOCK_THREADS, 1, 1)
+    ks.ks_query_layout(p, cfg)
+    cfg.max_block = ks.ks_dim3(ks.KS_EXT64_MAX_BLOCK_THREADS + 1, 1, 1)
+    with pytest.raises(ks.KsError) as e:
         ks.ks_query_layout(p, cfg)
-        cfg.max_block = ks.ks_dim3(ks.KS_EXT_MAX_BLOCK_THREADS + 1, 1, 1)
-        with pytest.raises(ks.KsError) as e:
-            ks.ks_query_layout(p, cfg)
-        assert e.value.code == -2 and "%d threads" % ks.KS_EXT_MAX_BLOCK_THREADS in e.value.msg
-        cfg.trace_format = ks.KS_TRACE_BASIC
-        cfg.max_block = ks.ks_dim3(1024, 1, 1)
-        ks.ks_query_layout(p, cfg)
-        ks.ks_program_free(p)
+    assert e.value.code == -2 and "%d threads" % ks.KS_EXT64_MAX_BLOCK_THREADS in e.value.msg
+    cfg.trace_format = ks.KS_TRACE_BASIC
+    cfg.max_block = ks.ks_dim3(1024, 1, 1)
+    ks.ks_query_layout(p, cfg)
+    ks.ks_program_free(p)
+    q = ks.ks_load_program(W.bank_probe_ptx())
+    cfg.trace_format = ks.KS_TRACE_EXTENDED
+    cfg.max_block = ks.ks_dim3(ks.KS_EXT_MAX_BLOCK_THREADS, 1, 1)
+    ks.ks_query_layout(q, cfg)
+    ks.ks_program_free(q)
+    assert ks.KS_EXT_MAX_BLOCK_THREADS == ks.KS_MAX_BLOCK_THREADS
 
 
 def test_static_binding_refuses_programs_beyond_its_scratch(ks):

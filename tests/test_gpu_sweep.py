@@ -40,7 +40,7 @@ def _case(rng):
     budget = int(rng.choice([0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 40, 777]))
     if rng.random() < 0.75:
         seed = int(rng.integers(0, 5000))
-        # extended records run blocks of up to 256 threads
+        # extended records on blocks of up to 256 threads here (larger ones: test_gpu_ext_trace)
         block = int(rng.choice([32, 64, 96, 160, 256] + ([] if fmt else [512, 768, 1024])))
         grid = int(rng.integers(1, 70))
         cap = int(rng.choice([0, 1, 17, 31, 32, 33, 64, 300, 2048]))
